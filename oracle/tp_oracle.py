@@ -1,0 +1,544 @@
+"""Oracle for the column->row tensor-parallel block: plain, slow, obviously correct NumPy in float64.
+
+TEST INFRASTRUCTURE.  Only the tests, __graft_entry__.smoke() and the CPU-baseline leg of bench.py may import or
+call anything in this package.  It shares no code with the HIP library and never imports it; the two meet only in
+the seeded inputs of tp_inputs.
+
+Pages followed (cited by title and section):
+  [ATLAS]  "Tensor Parallelism (TP) 与 Sequence Parallelism (SP)", llm-infra-atlas, parallel/02_tp_sp
+  [SPLIT]  111qqz.com, "tensor-parallelism-matrix-split" (the X in R^{Bx4}, W in R^{4x8}, two-GPU walk-through)
+  [MEGA]   blog.vllbc.top, visual reading of Megatron-LM tensor parallelism (calculator, divisibility rules)
+  [SPCP]   blog.vllbc.top, "Sequence Parallel 与 Context Parallel" (SP all-gather in / reduce-scatter out; the
+           online-softmax merge of CP step 3)
+
+What is computed: the unsharded block by its plain definition (Z = act(X A + a) B + c and its gradients; causal
+multi-head attention), each rank's shard by slicing the unsharded operands ([ATLAS] §2: the sum over shards equals
+the unsharded result in exact arithmetic), and the g / g-bar reductions as sums over the t partial buffers.
+Activations are [s, b, h] sequence-first ([ATLAS] §1); every GEMM sees them as [s*b, h] rows in s-major order.
+
+Readings where the pages are silent (each also listed in the design notes):
+  * GeLU is the erf form; the tanh form is provided as a variant.
+  * SwiGLU: the fc1 weight is [h, 2*ffn] = [gate | up]; Y = SiLU(X Ag + ag) * (X Au + au); rank i owns gate
+    columns C_i and up columns C_i, packed [gate_i | up_i].
+  * The row-parallel bias c is added once, after the reduction, never per partial.
+  * Attention: fused QKV weight [h, 3ad] = [Wq | Wk | Wv] with head-major columns; rank r's shard groups each
+    local head's columns as [q_j | k_j | v_j]; causal mask lets query q see keys k <= q; scale exactly 1/sqrt(d).
+  * Partial sums are stored in the activation dtype; the bit-exact reduction adds them in fp32 in rank order
+    0..t-1, adds the bias last, then rounds once to bf16 (nearest, ties to even); NaN stays NaN.
+
+Every function here is pinned by the CPU tests (tests/test_oracle_*.py) against values the pages print, closed
+forms, finite differences, brute force on tiny inputs, or an independent library routine.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+from scipy.special import erf as _erf
+
+# ---------------------------------------------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode raw bfloat16 patterns (uint16): a bf16 value is the fp32 value whose top 16 bits are the pattern."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 patterns: nearest, ties to even; NaN maps to a quiet NaN of the same sign.
+
+    The 16 discarded bits decide the rounding: above half rounds up, below half truncates, exactly half rounds to
+    the even kept pattern.  Overflow past the largest finite bf16 becomes infinity (carry into the exponent)."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    kept = u >> np.uint64(16)
+    low = u & np.uint64(0xFFFF)
+    half = np.uint64(0x8000)
+    round_up = (low > half) | ((low == half) & ((kept & np.uint64(1)) == np.uint64(1)))
+    out = kept + round_up.astype(np.uint64)
+    is_nan = ((u & np.uint64(0x7F800000)) == np.uint64(0x7F800000)) & ((u & np.uint64(0x007FFFFF)) != 0)
+    out = np.where(is_nan, kept | np.uint64(0x0040), out)
+    return out.astype(np.uint16)
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage form (uint16 bf16 patterns or float32) to float64."""
+    if dtype == "bf16":
+        return bf16_bits_to_f64(x)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Element-wise activations and their derivatives ([ATLAS] §2: the nonlinearity is element-wise, so it runs on
+# each column shard locally; [SPLIT] two-layer section uses ReLU)
+# ---------------------------------------------------------------------------------------------------------------
+
+_SQRT2 = math.sqrt(2.0)
+_INV_SQRT_2PI = 1.0 / math.sqrt(2.0 * math.pi)
+_TANH_C = math.sqrt(2.0 / math.pi)
+
+
+def gelu(x):
+    """GeLU(x) = x * Phi(x) with Phi the standard normal CDF = (1 + erf(x / sqrt 2)) / 2."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + _erf(x / _SQRT2))
+
+
+def gelu_grad(x):
+    """d/dx [x Phi(x)] = Phi(x) + x phi(x), phi the standard normal density."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * (1.0 + _erf(x / _SQRT2)) + x * _INV_SQRT_2PI * np.exp(-0.5 * x * x)
+
+
+def gelu_tanh(x):
+    """The tanh approximation of GeLU: x/2 * (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(_TANH_C * (x + 0.044715 * x ** 3)))
+
+
+def gelu_tanh_grad(x):
+    x = np.asarray(x, dtype=np.float64)
+    u = _TANH_C * (x + 0.044715 * x ** 3)
+    th = np.tanh(u)
+    du = _TANH_C * (1.0 + 3.0 * 0.044715 * x * x)
+    return 0.5 * (1.0 + th) + 0.5 * x * (1.0 - th * th) * du
+
+
+def sigmoid(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x * sigmoid(x)
+
+
+def silu_grad(x):
+    sg = sigmoid(x)
+    return sg * (1.0 + np.asarray(x, dtype=np.float64) * (1.0 - sg))
+
+
+def relu(x):
+    return np.maximum(np.asarray(x, dtype=np.float64), 0.0)
+
+
+def relu_grad(x):
+    return (np.asarray(x, dtype=np.float64) > 0.0).astype(np.float64)
+
+
+ACTS = {
+    "gelu": (gelu, gelu_grad),
+    "gelu_tanh": (gelu_tanh, gelu_tanh_grad),
+    "relu": (relu, relu_grad),
+}
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# One linear layer Y = X W split two ways across t devices ([SPLIT] "Column Parallel", "Row Parallel" and the
+# backward section; math layout W [in, out])
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def _col_ranges(n: int, t: int) -> List[slice]:
+    if n % t != 0:
+        raise ValueError(f"{n} is not divisible by t={t}")
+    w = n // t
+    return [slice(i * w, (i + 1) * w) for i in range(t)]
+
+
+def column_parallel_linear(X: np.ndarray, W: np.ndarray, t: int) -> List[np.ndarray]:
+    """Device i holds the output columns C_i of W and computes Y_i = X W[:, C_i]; the full Y is their concatenation."""
+    return [X @ W[:, c] for c in _col_ranges(W.shape[1], t)]
+
+
+def row_parallel_linear(X: np.ndarray, W: np.ndarray, t: int) -> List[np.ndarray]:
+    """Device i holds input rows R_i of W and the matching input columns of X; it returns the partial X_i W_i, all
+    of full output shape, whose sum is X W."""
+    return [X[:, r] @ W[r, :] for r in _col_ranges(W.shape[0], t)]
+
+
+def column_parallel_input_grad(dY_shards: Sequence[np.ndarray], W: np.ndarray, t: int) -> np.ndarray:
+    """X feeds every column shard, so by the multivariate chain rule dX is the sum over shards of dY_i W_i^T."""
+    total = None
+    for dYi, c in zip(dY_shards, _col_ranges(W.shape[1], t)):
+        g = dYi @ W[:, c].T
+        total = g if total is None else total + g
+    return total
+
+
+def row_parallel_input_grads(dY: np.ndarray, W: np.ndarray, t: int) -> List[np.ndarray]:
+    """Each X_i is a distinct variable used by one shard only: dX_i = dY W_i^T, no sum; dX is their concatenation."""
+    return [dY @ W[r, :].T for r in _col_ranges(W.shape[0], t)]
+
+
+def column_parallel_weight_grads(X: np.ndarray, dY_shards: Sequence[np.ndarray]) -> List[np.ndarray]:
+    """dW_i = X^T dY_i uses only what device i holds: no communication."""
+    return [X.T @ g for g in dY_shards]
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Dim-0 split / gather / reductions ([ATLAS] §1 split/gather/reduce-scatter along the first dim and the
+# divisibility assertion; §2 f/g; [SPCP] SP: all-gather in, reduce-scatter out)
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def split_dim0(x: np.ndarray, t: int, rank: int) -> np.ndarray:
+    """Rank r's contiguous slice of the sequence dim: rows [r*s/t, (r+1)*s/t).  s must be divisible by t."""
+    s = x.shape[0]
+    if s % t != 0:
+        raise ValueError(f"sequence length {s} is not divisible by t={t}")
+    loc = s // t
+    return x[rank * loc:(rank + 1) * loc]
+
+
+def gather_dim0(slices: Sequence[np.ndarray]) -> np.ndarray:
+    """All-gather along dim 0: concatenation of the ranks' slices in rank order."""
+    return np.concatenate(list(slices), axis=0)
+
+
+def allreduce_sum(partials: Sequence[np.ndarray], bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """g in forward (and f in backward): the element-wise sum of all ranks' partials (exact, fp64); the row bias,
+    if any, is added once."""
+    acc = np.zeros_like(np.asarray(partials[0], dtype=np.float64))
+    for p in partials:
+        acc = acc + np.asarray(p, dtype=np.float64)
+    if bias is not None:
+        acc = acc + np.asarray(bias, dtype=np.float64)
+    return acc
+
+
+def reduce_scatter_dim0(partials: Sequence[np.ndarray], t: int, rank: int,
+                        bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """g-bar under sequence parallelism: rank r keeps its dim-0 slice of the sum over ranks."""
+    return split_dim0(allreduce_sum(partials, bias), t, rank)
+
+
+def reduce_f32_rank_order(partials_f32: Sequence[np.ndarray], bias_f32: Optional[np.ndarray] = None) -> np.ndarray:
+    """The reduction as a device computes it: acc = p_0, then acc = fp32(acc + p_i) for i = 1..t-1 in rank order,
+    then acc = fp32(acc + bias); every add rounds to nearest-even fp32 (numpy float32 addition)."""
+    acc = np.array(partials_f32[0], dtype=np.float32, copy=True)
+    for p in partials_f32[1:]:
+        acc = (acc + np.asarray(p, dtype=np.float32)).astype(np.float32)
+    if bias_f32 is not None:
+        acc = (acc + np.asarray(bias_f32, dtype=np.float32)).astype(np.float32)
+    return acc
+
+
+def reduce_storage(partials: np.ndarray, dtype: str, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Bit-exact expected output of the on-device reduction, in storage form.
+
+    partials: [t, ...] in storage form (uint16 bf16 patterns or float32); bias: [h] broadcast over the last dim.
+    bf16: fp32 rank-order sum, bias last, one rounding to bf16.  f32: the fp32 rank-order sum itself."""
+    if dtype == "bf16":
+        p32 = [bf16_bits_to_f64(p).astype(np.float32) for p in partials]
+        b32 = None if bias is None else bf16_bits_to_f64(bias).astype(np.float32)
+        return f32_to_bf16_bits(reduce_f32_rank_order(p32, b32))
+    p32 = [np.asarray(p, dtype=np.float32) for p in partials]
+    b32 = None if bias is None else np.asarray(bias, dtype=np.float32)
+    return reduce_f32_rank_order(p32, b32)
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Shard layout ([ATLAS] §2-3 and [MEGA]: fc1 column-sharded, fc2 row-sharded, QKV column-sharded by head, output
+# projection row-sharded; [MEGA] divide() and the heads % t assertion)
+# ---------------------------------------------------------------------------------------------------------------
+
+W_FC1, W_FC1_GATE_UP, W_FC2, W_QKV, W_PROJ, B_FC1, B_FC1_GATE_UP, B_QKV = range(8)
+
+
+def _need_div(n: int, t: int, what: str):
+    if n % t != 0:
+        raise ValueError(f"{what}={n} is not divisible by t={t}")
+
+
+def local_head_ids(a: int, t: int, rank: int) -> List[int]:
+    _need_div(a, t, "heads")
+    hl = a // t
+    return list(range(rank * hl, (rank + 1) * hl))
+
+
+def qkv_shard_columns(a: int, d: int, t: int, rank: int) -> np.ndarray:
+    """Full-QKV column index of every column of rank r's grouped shard: for each local head j in order, the d
+    query columns of head j, then its d key columns, then its d value columns.  Full layout [Wq | Wk | Wv], each
+    a*d wide with head j at columns j*d .. j*d+d-1."""
+    cols = []
+    ad = a * d
+    for j in local_head_ids(a, t, rank):
+        for part in range(3):  # q, k, v
+            base = part * ad + j * d
+            cols.extend(range(base, base + d))
+    return np.asarray(cols, dtype=np.int64)
+
+
+def shard_weight(kind: int, full: np.ndarray, t: int, rank: int, ffn: int = 0, a: int = 0, d: int = 0):
+    """One rank's shard of a full weight or bias (any dtype; pure index selection)."""
+    if kind == W_FC1:
+        _need_div(full.shape[1], t, "ffn")
+        w = full.shape[1] // t
+        return full[:, rank * w:(rank + 1) * w].copy()
+    if kind == B_FC1:
+        _need_div(full.shape[0], t, "ffn")
+        w = full.shape[0] // t
+        return full[rank * w:(rank + 1) * w].copy()
+    if kind in (W_FC1_GATE_UP, B_FC1_GATE_UP):
+        f = full.shape[-1] // 2
+        _need_div(f, t, "ffn")
+        w = f // t
+        idx = np.concatenate([np.arange(rank * w, (rank + 1) * w), f + np.arange(rank * w, (rank + 1) * w)])
+        return np.take(full, idx, axis=-1).copy()
+    if kind == W_FC2:
+        _need_div(full.shape[0], t, "ffn")
+        w = full.shape[0] // t
+        return full[rank * w:(rank + 1) * w, :].copy()
+    if kind in (W_QKV, B_QKV):
+        return np.take(full, qkv_shard_columns(a, d, t, rank), axis=-1).copy()
+    if kind == W_PROJ:
+        hl = len(local_head_ids(a, t, rank))
+        return full[rank * hl * d:(rank + 1) * hl * d, :].copy()
+    raise ValueError(f"unknown weight kind {kind}")
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# MLP block Z = act(X A + a) B + c and its backward ([ATLAS] §2; [SPLIT] two-layer MLP forward and backward;
+# [MEGA] first layer GeLU(XA), second layer YB)
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def _act_fwd(U: np.ndarray, act: str) -> np.ndarray:
+    if act == "swiglu":
+        f = U.shape[1] // 2
+        return silu(U[:, :f]) * U[:, f:]
+    return ACTS[act][0](U)
+
+
+def _act_bwd(U: np.ndarray, dY: np.ndarray, act: str) -> np.ndarray:
+    """Gradient with respect to the pre-activation U given dY (the element-wise local step of the backward)."""
+    if act == "swiglu":
+        f = U.shape[1] // 2
+        g, u = U[:, :f], U[:, f:]
+        return np.concatenate([dY * u * silu_grad(g), dY * silu(g)], axis=1)
+    return dY * ACTS[act][1](U)
+
+
+def mlp_forward(X: np.ndarray, A: np.ndarray, B: np.ndarray, act: str = "gelu",
+                a_bias: Optional[np.ndarray] = None, c_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Unsharded block.  X [M, h] (M = s*b rows, s-major), A [h, ffn] (SwiGLU: [h, 2ffn] = [gate|up]), B [ffn, h].
+    Returns U = X A + a (pre-activation), Y = act(U), Z = Y B + c."""
+    U = X @ A
+    if a_bias is not None:
+        U = U + a_bias
+    Y = _act_fwd(U, act)
+    Z = Y @ B
+    if c_bias is not None:
+        Z = Z + c_bias
+    return {"U": U, "Y": Y, "Z": Z}
+
+
+def mlp_backward(X: np.ndarray, A: np.ndarray, B: np.ndarray, U: np.ndarray, Y: np.ndarray, dZ: np.ndarray,
+                 act: str = "gelu") -> Dict[str, np.ndarray]:
+    """Gradients of the unsharded block for upstream gradient dZ:
+    dY = dZ B^T, dB = Y^T dZ, dc = column sums of dZ, dU = dY * act'(U), dA = X^T dU, da = column sums of dU,
+    dX = dU A^T."""
+    dY = dZ @ B.T
+    dB = Y.T @ dZ
+    dc = dZ.sum(axis=0)
+    dU = _act_bwd(U, dY, act)
+    dA = X.T @ dU
+    da = dU.sum(axis=0)
+    dX = dU @ A.T
+    return {"dY": dY, "dB": dB, "dc": dc, "dU": dU, "dA": dA, "da": da, "dX": dX}
+
+
+def mlp_shard_columns(ffn: int, t: int, rank: int, act: str) -> np.ndarray:
+    """Columns of the full fc1 output (U) that rank r owns, in its packed order."""
+    _need_div(ffn, t, "ffn")
+    w = ffn // t
+    own = np.arange(rank * w, (rank + 1) * w)
+    if act == "swiglu":
+        return np.concatenate([own, ffn + own])
+    return own
+
+
+def mlp_shard_forward(X: np.ndarray, A: np.ndarray, B: np.ndarray, t: int, rank: int, act: str = "gelu",
+                      a_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Rank r's part of the forward, by slicing the unsharded operands: U_i = X A[:, C_i] + a[C_i], Y_i = act(U_i),
+    Z_i = Y_i B[R_i, :] is a partial sum of full shape (no row bias)."""
+    ffn = B.shape[0]
+    cols = mlp_shard_columns(ffn, t, rank, act)
+    w = ffn // t
+    Ui = X @ A[:, cols]
+    if a_bias is not None:
+        Ui = Ui + a_bias[cols]
+    Yi = _act_fwd(Ui, act)
+    Zi = Yi @ B[rank * w:(rank + 1) * w, :]
+    return {"U": Ui, "Y": Yi, "Z": Zi}
+
+
+def mlp_shard_backward(X: np.ndarray, A: np.ndarray, B: np.ndarray, dZ: np.ndarray, t: int, rank: int,
+                       act: str = "gelu", a_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Rank r's part of the backward ([SPLIT] backward section): row layer dY_i = dZ B_i^T (no sum) and
+    dB_i = Y_i^T dZ; local act' step; column layer dA_i = X^T dU_i (local) and the partial dX_i = dU_i A_i^T, whose
+    sum over ranks is dX."""
+    ffn = B.shape[0]
+    cols = mlp_shard_columns(ffn, t, rank, act)
+    w = ffn // t
+    fw = mlp_shard_forward(X, A, B, t, rank, act, a_bias)
+    Bi = B[rank * w:(rank + 1) * w, :]
+    dYi = dZ @ Bi.T
+    dBi = fw["Y"].T @ dZ
+    dUi = _act_bwd(fw["U"], dYi, act)
+    dAi = X.T @ dUi
+    dai = dUi.sum(axis=0)
+    dXi = dUi @ A[:, cols].T
+    return {"dY": dYi, "dB": dBi, "dU": dUi, "dA": dAi, "da": dai, "dX": dXi}
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Attention block ([ATLAS] §3; [MEGA]: QKV column-parallel by head, per-head softmax(Q K^T / sqrt d) V locally,
+# output projection row-parallel, one reduction at the exit)
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def attention_core(Q: np.ndarray, K: np.ndarray, V: np.ndarray, causal: bool = True):
+    """One head of one sequence: Q, K, V [s, d].  S = Q K^T / sqrt(d) with S[q, k] = -inf for k > q when causal;
+    P = row softmax of S; O = P V.  Also returns lse[q] = log sum_k exp(S[q, k]) over the visible keys."""
+    s, d = Q.shape
+    S = (Q @ K.T) / math.sqrt(d)
+    if causal:
+        mask = np.triu(np.ones((s, K.shape[0]), dtype=bool), k=1)
+        S = np.where(mask, -np.inf, S)
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    den = E.sum(axis=1, keepdims=True)
+    O = (E / den) @ V
+    lse = (m + np.log(den))[:, 0]
+    return O, lse
+
+
+def attention_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: int, b: int, a: int, d: int,
+                      causal: bool = True, bqkv: Optional[np.ndarray] = None,
+                      c_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Unsharded attention block.  X [M = s*b, h] rows s-major; Wqkv [h, 3ad] = [Wq|Wk|Wv]; Wo [ad, h].
+    Returns QKV [M, 3ad], O [M, ad] (head j at columns j*d..), lse [b, a, s], Z = O Wo + c."""
+    QKV = X @ Wqkv
+    if bqkv is not None:
+        QKV = QKV + bqkv
+    ad = a * d
+    O = np.zeros((s * b, ad))
+    lse = np.zeros((b, a, s))
+    for bi in range(b):
+        rows = np.arange(s) * b + bi
+        for j in range(a):
+            q = QKV[rows, j * d:(j + 1) * d]
+            k = QKV[rows, ad + j * d:ad + (j + 1) * d]
+            v = QKV[rows, 2 * ad + j * d:2 * ad + (j + 1) * d]
+            o, l = attention_core(q, k, v, causal)
+            O[rows, j * d:(j + 1) * d] = o
+            lse[bi, j, :] = l
+    Z = O @ Wo
+    if c_bias is not None:
+        Z = Z + c_bias
+    return {"QKV": QKV, "O": O, "lse": lse, "Z": Z}
+
+
+def attention_shard_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: int, b: int, a: int, d: int,
+                            t: int, rank: int, causal: bool = True,
+                            bqkv: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Rank r's part: QKV_i in grouped [q_j k_j v_j] column order for its local heads, O_i = those heads' outputs
+    (head-major), lse_i [b, a/t, s], and the partial Z_i = O_i Wo[rows of its heads] (no row bias)."""
+    cols = qkv_shard_columns(a, d, t, rank)
+    QKVi = X @ Wqkv[:, cols]
+    if bqkv is not None:
+        QKVi = QKVi + bqkv[cols]
+    heads = local_head_ids(a, t, rank)
+    hl = len(heads)
+    Oi = np.zeros((s * b, hl * d))
+    lsei = np.zeros((b, hl, s))
+    for bi in range(b):
+        rows = np.arange(s) * b + bi
+        for jj in range(hl):
+            base = jj * 3 * d
+            o, l = attention_core(QKVi[rows, base:base + d], QKVi[rows, base + d:base + 2 * d],
+                                  QKVi[rows, base + 2 * d:base + 3 * d], causal)
+            Oi[rows, jj * d:(jj + 1) * d] = o
+            lsei[bi, jj, :] = l
+    Zi = Oi @ Wo[rank * hl * d:(rank + 1) * hl * d, :]
+    return {"QKV": QKVi, "O": Oi, "lse": lsei, "Z": Zi}
+
+
+def attention_rows(QKV_i: np.ndarray, s: int, b: int, hl: int, d: int, q_rows: Sequence[int],
+                   causal: bool = True) -> Dict[str, np.ndarray]:
+    """Attention outputs for selected token rows only (row index = s_idx*b + b_idx), from a rank's grouped QKV_i.
+    Each output row needs just its own query and the keys/values of its sequence, so sampling rows is exact."""
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    O = np.zeros((len(q_rows), hl * d))
+    lse = np.zeros((len(q_rows), hl))
+    for n, r in enumerate(q_rows):
+        si, bi = divmod(int(r), b)
+        nk = si + 1 if causal else s
+        krows = np.arange(nk) * b + bi
+        for jj in range(hl):
+            base = jj * 3 * d
+            q = QKV_i[r, base:base + d]
+            k = QKV_i[krows, base + d:base + 2 * d]
+            v = QKV_i[krows, base + 2 * d:base + 3 * d]
+            sc = (k @ q) / math.sqrt(d)
+            m = sc.max()
+            e = np.exp(sc - m)
+            O[n, jj * d:(jj + 1) * d] = (e / e.sum()) @ v
+            lse[n, jj] = m + math.log(e.sum())
+    return {"O": O, "lse": lse}
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Accounting ([MEGA] calculator: per-rank linear parameters (2hf + 4h^2)/t with MHA attention, all-reduce payload
+# b*s*h elements per call, four calls per layer, ring traffic 8 b s h (t-1)/t elements per card; [ATLAS] §6)
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def linear_params_per_rank(h: int, f: int, t: int) -> int:
+    """Linear-layer weights one rank holds per layer: fc1 h*f + fc2 f*h + QKV 3h^2 + projection h^2, over t."""
+    total = h * f + f * h + 3 * h * h + h * h
+    if total % t != 0:
+        raise ValueError("parameter count not divisible by t")
+    return total // t
+
+
+def allreduce_payload_elems(b: int, s: int, h: int) -> int:
+    """One g (or f) all-reduce moves the whole activation [s, b, h], independent of t."""
+    return b * s * h
+
+
+def allreduce_calls_per_layer() -> int:
+    """Attention and MLP each reduce once in forward (g) and once in backward (f)."""
+    return 4
+
+
+def ring_elems_per_card_per_layer(b: int, s: int, h: int, t: int) -> float:
+    """A ring all-reduce moves 2 N (t-1)/t elements per card; four calls per layer."""
+    return allreduce_calls_per_layer() * 2.0 * allreduce_payload_elems(b, s, h) * (t - 1) / t
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Error measures used by the parity tests
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def rel_frobenius(got: np.ndarray, ref: np.ndarray) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    return float(np.linalg.norm((got - ref).ravel()) / (den if den > 0 else 1.0))
+
+
+def max_abs_unit(got: np.ndarray, ref: np.ndarray) -> float:
+    """Max absolute error after scaling both by the RMS of the reference (outputs brought to unit scale)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 1.0
+    rms = rms if rms > 0 else 1.0
+    return float(np.max(np.abs(got - ref))) / rms if ref.size else 0.0
