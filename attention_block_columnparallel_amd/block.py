@@ -1,0 +1,144 @@
+"""Rank-loop driver: runs all t shards of a block back to back on one GPU through the C ABI.
+
+Device memory comes from torch; every computation is a call into libtpshard.  The t ranks' partial sums are
+written side by side ([t][s, b, h]) and reduced on the device by tp_partial_reduce (g / f, all-reduce form) or
+tp_reduce_scatter_dim0 (g-bar under sequence parallelism) -- the arrangement of "Tensor Parallelism (TP) 与
+Sequence Parallelism (SP)" §2 (f / g) and §5 (their SP variants), with the collectives replaced by an on-device
+reduction over local buffers.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import load
+
+
+def _dt(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+class MlpBlock:
+    """All t shards of one MLP block Z = act(X A + a) B (+ c).
+
+    A_full [h, ffn] (SwiGLU: [h, 2ffn] = [gate | up]), B_full [ffn, h], a_full / c_full optional, all device
+    tensors of the activation dtype.  The shards are packed once by tp_shard_weights."""
+
+    def __init__(self, s: int, b: int, h: int, ffn: int, t: int, act: str, A_full: torch.Tensor,
+                 B_full: torch.Tensor, a_full: Optional[torch.Tensor] = None, c_full: Optional[torch.Tensor] = None,
+                 stream=None):
+        L = load()
+        self.L = L
+        self.s, self.b, self.h, self.ffn, self.t, self.act = s, b, h, ffn, t, act
+        self.dims = L.make_dims(s=s, b=b, h=h, ffn=ffn, t=t)
+        dev, dt = A_full.device, A_full.dtype
+        self.dtype = dt
+        f = ffn // t
+        self.f = f
+        self.n1 = 2 * f if act == "swiglu" else f
+        M = s * b
+        self.M = M
+        wk = "fc1_gate_up" if act == "swiglu" else "fc1"
+        bk = "b_fc1_gate_up" if act == "swiglu" else "b_fc1"
+        self.A = torch.empty((t, h, self.n1), dtype=dt, device=dev)
+        self.B = torch.empty((t, f, h), dtype=dt, device=dev)
+        self.a = torch.empty((t, self.n1), dtype=dt, device=dev) if a_full is not None else None
+        self.c = c_full
+        for r in range(t):
+            L.tp_shard_weights(self.dims, r, wk, A_full, self.A[r], stream)
+            L.tp_shard_weights(self.dims, r, "fc2", B_full, self.B[r], stream)
+            if a_full is not None:
+                L.tp_shard_weights(self.dims, r, bk, a_full, self.a[r], stream)
+        # saved activations and partial sums, one slot per rank
+        self.U = torch.empty((t, M, self.n1), dtype=dt, device=dev)
+        self.Y = torch.empty((t, M, f), dtype=dt, device=dev)
+        self.Zp = torch.empty((t, M, h), dtype=dt, device=dev)
+        self.Z = torch.empty((M, h), dtype=dt, device=dev)
+        self.dU = torch.empty((M, self.n1), dtype=dt, device=dev)  # workspace reused by every rank
+        self.dA = torch.empty((t, h, self.n1), dtype=dt, device=dev)
+        self.da = torch.empty((t, self.n1), dtype=dt, device=dev) if a_full is not None else None
+        self.dB = torch.empty((t, f, h), dtype=dt, device=dev)
+        self.dXp = torch.empty((t, M, h), dtype=dt, device=dev)
+        self.dX = torch.empty((M, h), dtype=dt, device=dev)
+
+    # -- forward: every rank's column + row GEMMs, then g
+    def forward_ranks(self, X: torch.Tensor, stream=None):
+        for r in range(self.t):
+            self.L.tp_mlp_fwd(self.dims, r, self.act, X, self.A[r], None if self.a is None else self.a[r], self.B[r],
+                              self.U[r], self.Y[r], self.Zp[r], stream)
+
+    def reduce_forward(self, sp: bool = False, stream=None, out: Optional[torch.Tensor] = None):
+        out = self.Z if out is None else out
+        if sp:
+            self.L.tp_reduce_scatter_dim0(self.dims, -1, self.Zp, self.c, out, stream)
+        else:
+            self.L.tp_partial_reduce(self.M * self.h, self.h, self.t, self.Zp, self.c, out, stream)
+        return out
+
+    def forward(self, X: torch.Tensor, sp: bool = False, stream=None) -> torch.Tensor:
+        self.forward_ranks(X, stream)
+        return self.reduce_forward(sp, stream)
+
+    # -- backward: every rank's dgrad / wgrad GEMMs, then f on the dX partials
+    def backward_ranks(self, X: torch.Tensor, dZ: torch.Tensor, stream=None):
+        for r in range(self.t):
+            self.L.tp_mlp_bwd(self.dims, r, self.act, X, self.A[r], self.B[r], self.U[r], self.Y[r], dZ, self.dU,
+                              self.dA[r], None if self.da is None else self.da[r], self.dB[r], self.dXp[r], stream)
+
+    def reduce_backward(self, sp: bool = False, stream=None, out: Optional[torch.Tensor] = None):
+        out = self.dX if out is None else out
+        if sp:
+            self.L.tp_reduce_scatter_dim0(self.dims, -1, self.dXp, None, out, stream)
+        else:
+            self.L.tp_partial_reduce(self.M * self.h, self.h, self.t, self.dXp, None, out, stream)
+        return out
+
+    def backward(self, X: torch.Tensor, dZ: torch.Tensor, sp: bool = False, stream=None) -> torch.Tensor:
+        self.backward_ranks(X, dZ, stream)
+        return self.reduce_backward(sp, stream)
+
+
+class AttnBlock:
+    """All t shards of one attention block: QKV column-parallel by head, local causal attention, row-parallel
+    output projection, partial sums reduced on the device."""
+
+    def __init__(self, s: int, b: int, h: int, a: int, d: int, t: int, Wqkv_full: torch.Tensor,
+                 Wo_full: torch.Tensor, bqkv_full: Optional[torch.Tensor] = None,
+                 c_full: Optional[torch.Tensor] = None, causal: bool = True, stream=None):
+        L = load()
+        self.L = L
+        self.s, self.b, self.h, self.a, self.d, self.t, self.causal = s, b, h, a, d, t, causal
+        self.dims = L.make_dims(s=s, b=b, h=h, a=a, d=d, t=t)
+        dev, dt = Wqkv_full.device, Wqkv_full.dtype
+        hl = a // t
+        self.hl = hl
+        M = s * b
+        self.M = M
+        self.Wqkv = torch.empty((t, h, 3 * hl * d), dtype=dt, device=dev)
+        self.Wo = torch.empty((t, hl * d, h), dtype=dt, device=dev)
+        self.bqkv = torch.empty((t, 3 * hl * d), dtype=dt, device=dev) if bqkv_full is not None else None
+        self.c = c_full
+        for r in range(t):
+            L.tp_shard_weights(self.dims, r, "qkv", Wqkv_full, self.Wqkv[r], stream)
+            L.tp_shard_weights(self.dims, r, "proj", Wo_full, self.Wo[r], stream)
+            if bqkv_full is not None:
+                L.tp_shard_weights(self.dims, r, "b_qkv", bqkv_full, self.bqkv[r], stream)
+        self.QKV = torch.empty((t, M, 3 * hl * d), dtype=dt, device=dev)
+        self.O = torch.empty((t, M, hl * d), dtype=dt, device=dev)
+        self.lse = torch.empty((t, b, hl, s), dtype=torch.float32, device=dev)
+        self.Zp = torch.empty((t, M, h), dtype=dt, device=dev)
+        self.Z = torch.empty((M, h), dtype=dt, device=dev)
+
+    def forward_ranks(self, X: torch.Tensor, stream=None):
+        for r in range(self.t):
+            self.L.tp_attn_fwd(self.dims, r, self.causal, X, self.Wqkv[r], None if self.bqkv is None else self.bqkv[r],
+                               self.Wo[r], self.QKV[r], self.O[r], self.lse[r], self.Zp[r], stream)
+
+    def forward(self, X: torch.Tensor, sp: bool = True, stream=None) -> torch.Tensor:
+        self.forward_ranks(X, stream)
+        if sp:
+            self.L.tp_reduce_scatter_dim0(self.dims, -1, self.Zp, self.c, self.Z, stream)
+        else:
+            self.L.tp_partial_reduce(self.M * self.h, self.h, self.t, self.Zp, self.c, self.Z, stream)
+        return self.Z

@@ -1,0 +1,370 @@
+// The C ABI of libtpshard: host-side validation of every argument (before any HIP call, so it is testable on a
+// machine without a GPU) and the launch sequence of each entry point.  Divisibility rules follow the pages: the
+// sequence dim must split evenly across the t ranks for the dim-0 split / gather / reduce-scatter
+// ("Tensor Parallelism (TP) 与 Sequence Parallelism (SP)" §1); output columns, input rows and heads must divide by
+// t, and h = a * d (Megatron-LM visual reading, divisibility rules; §1 of the same atlas page for h = a * d).
+#include <stdio.h>
+
+#include "tp_common.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct TimingLog {
+  hipEvent_t* starts = nullptr;
+  hipEvent_t* stops = nullptr;
+  int cap = 0;
+  int n = 0;
+  bool armed = false;
+  bool open = false;  // a start was recorded for slot n
+  const char* names[4096];
+};
+thread_local TimingLog g_timing;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return TP_OK;
+  g_last_hip_error = (int)e;
+  return TP_E_HIP;
+}
+
+bool bad_dtype(tp_dtype dt) { return dt != TP_F32 && dt != TP_BF16; }
+int64_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
+
+struct Buf {
+  const void* p;
+  int64_t bytes;
+};
+
+bool overlaps(const Buf& a, const Buf& b) {
+  if (a.p == nullptr || b.p == nullptr || a.bytes <= 0 || b.bytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + (uintptr_t)a.bytes;
+  const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + (uintptr_t)b.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Any output overlapping any input, or two outputs overlapping each other.
+bool any_alias(const Buf* outs, int no, const Buf* ins, int ni) {
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j)
+      if (overlaps(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < no; ++j)
+      if (overlaps(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+bool misaligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p != nullptr && ((uintptr_t)p & 15u) != 0) return true;
+  return false;
+}
+
+// 2^31 elements is the largest single tensor the kernels index with 32-bit row / column counts.
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+}  // namespace
+
+namespace tp {
+void timing_start(hipStream_t st) {
+  TimingLog& T = g_timing;
+  T.open = false;
+  if (!T.armed || T.n >= T.cap) return;
+  if (hipEventRecord(T.starts[T.n], st) == hipSuccess) T.open = true;
+}
+void timing_stop(hipStream_t st, const char* name) {
+  TimingLog& T = g_timing;
+  if (!T.open) return;
+  T.open = false;
+  if (hipEventRecord(T.stops[T.n], st) == hipSuccess) {
+    if (T.n < (int)(sizeof(T.names) / sizeof(T.names[0]))) T.names[T.n] = name;
+    ++T.n;
+  }
+}
+}  // namespace tp
+
+extern "C" {
+
+int tp_timing_begin(hipEvent_t* starts, hipEvent_t* stops, int capacity) {
+  if (starts == nullptr || stops == nullptr) return TP_E_NULL;
+  if (capacity <= 0) return TP_E_SHAPE;
+  TimingLog& T = g_timing;
+  T.starts = starts;
+  T.stops = stops;
+  T.cap = capacity < 4096 ? capacity : 4096;
+  T.n = 0;
+  T.open = false;
+  T.armed = true;
+  return TP_OK;
+}
+
+int tp_timing_end(void) {
+  g_timing.armed = false;
+  return g_timing.n;
+}
+
+const char* tp_timing_kernel(int i) {
+  if (i < 0 || i >= g_timing.n) return nullptr;
+  return g_timing.names[i];
+}
+
+const char* tp_status_str(int status) {
+  switch (status) {
+    case TP_OK: return "ok";
+    case TP_E_NULL: return "a required pointer is NULL";
+    case TP_E_SHAPE: return "a size is non-positive or out of range";
+    case TP_E_DIVISIBILITY: return "divisibility rule violated (s, ffn or heads not divisible by t, or h != a*d)";
+    case TP_E_DTYPE: return "unknown dtype";
+    case TP_E_RANK: return "rank outside [0, t)";
+    case TP_E_ALIAS: return "an output buffer overlaps an input buffer";
+    case TP_E_UNSUPPORTED: return "unsupported combination (activation/dtype, alignment or head dim)";
+    case TP_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int tp_last_hip_error(void) { return g_last_hip_error; }
+
+int tp_abi_version(void) { return TPSHARD_ABI_VERSION; }
+
+int tp_shard_weights(const tp_dims* dims, int rank, tp_wkind kind, tp_dtype dtype, const void* full, void* shard,
+                     hipStream_t stream) {
+  if (dims == nullptr || full == nullptr || shard == nullptr) return TP_E_NULL;
+  const int64_t h = dims->h, t = dims->t, ffn = dims->ffn, a = dims->a, d = dims->d;
+  const bool mlp = kind == TP_W_FC1 || kind == TP_W_FC1_GATE_UP || kind == TP_W_FC2 || kind == TP_B_FC1 ||
+                   kind == TP_B_FC1_GATE_UP;
+  const bool att = kind == TP_W_QKV || kind == TP_W_PROJ || kind == TP_B_QKV;
+  if (!mlp && !att) return TP_E_UNSUPPORTED;
+  if (t <= 0 || h <= 0 || (mlp && ffn <= 0) || (att && (a <= 0 || d <= 0))) return TP_E_SHAPE;
+  if (h >= kMaxDim || ffn >= kMaxDim) return TP_E_SHAPE;
+  if (mlp && ffn % t != 0) return TP_E_DIVISIBILITY;
+  if (att && (a % t != 0 || h != a * d)) return TP_E_DIVISIBILITY;
+  if (rank < 0 || rank >= t) return TP_E_RANK;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  const int64_t es = esize(dtype);
+  const int64_t f_l = mlp ? ffn / t : 0, hl = att ? a / t : 0, ad = a * d;
+  int64_t rows = 0, full_cols = 0, shard_cols = 0;
+  switch (kind) {
+    case TP_W_FC1: rows = h; full_cols = ffn; shard_cols = f_l; break;
+    case TP_W_FC1_GATE_UP: rows = h; full_cols = 2 * ffn; shard_cols = 2 * f_l; break;
+    case TP_W_FC2: rows = ffn; full_cols = h; shard_cols = h; break;
+    case TP_W_QKV: rows = h; full_cols = 3 * ad; shard_cols = 3 * hl * d; break;
+    case TP_W_PROJ: rows = ad; full_cols = h; shard_cols = h; break;
+    case TP_B_FC1: rows = 1; full_cols = ffn; shard_cols = f_l; break;
+    case TP_B_FC1_GATE_UP: rows = 1; full_cols = 2 * ffn; shard_cols = 2 * f_l; break;
+    case TP_B_QKV: rows = 1; full_cols = 3 * ad; shard_cols = 3 * hl * d; break;
+  }
+  const Buf out[] = {{shard, (kind == TP_W_FC2 ? f_l : kind == TP_W_PROJ ? hl * d : rows) * shard_cols * es}};
+  const Buf in[] = {{full, rows * full_cols * es}};
+  if (any_alias(out, 1, in, 1)) return TP_E_ALIAS;
+  if (kind == TP_W_FC2 || kind == TP_W_PROJ) {
+    // row-parallel shards are a contiguous run of rows
+    const int64_t rl = kind == TP_W_FC2 ? f_l : hl * d;
+    const uint8_t* src = static_cast<const uint8_t*>(full) + (int64_t)rank * rl * h * es;
+    return hip_status(tp::copy_bytes(src, shard, rl * h * es, stream));
+  }
+  return hip_status(tp::pack_columns(dtype, full, rows, full_cols, shard, shard_cols, (int)kind, f_l, ffn, rank, hl,
+                                     d, ad, stream));
+}
+
+int tp_mlp_fwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const void* X, const void* A_i,
+               const void* a_i, const void* B_i, void* U_i, void* Y_i, void* Z_i, hipStream_t stream) {
+  if (dims == nullptr || X == nullptr || A_i == nullptr || B_i == nullptr || U_i == nullptr || Y_i == nullptr ||
+      Z_i == nullptr)
+    return TP_E_NULL;
+  const int64_t s = dims->s, b = dims->b, h = dims->h, ffn = dims->ffn, t = dims->t;
+  if (s <= 0 || b <= 0 || h <= 0 || ffn <= 0 || t <= 0) return TP_E_SHAPE;
+  if (s * b >= kMaxDim || h >= kMaxDim || ffn >= kMaxDim) return TP_E_SHAPE;
+  if (ffn % t != 0) return TP_E_DIVISIBILITY;
+  if (rank < 0 || rank >= t) return TP_E_RANK;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  if (act != TP_ACT_GELU && act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU && act != TP_ACT_RELU)
+    return TP_E_UNSUPPORTED;
+  const int64_t M = s * b, f = ffn / t, n1 = act == TP_ACT_SWIGLU ? 2 * f : f, es = esize(dtype);
+  if (dtype == TP_BF16 && (h % 8 != 0 || f % 8 != 0 || misaligned16({X, A_i, a_i, B_i, U_i, Y_i, Z_i})))
+    return TP_E_UNSUPPORTED;
+  const Buf outs[] = {{U_i, M * n1 * es}, {Y_i, M * f * es}, {Z_i, M * h * es}};
+  const Buf ins[] = {{X, M * h * es}, {A_i, h * n1 * es}, {a_i, n1 * es}, {B_i, f * h * es}};
+  if (any_alias(outs, 3, ins, 4)) return TP_E_ALIAS;
+
+  tp::GemmParams g1 = {};
+  g1.A = X; g1.lda = h;
+  g1.B = A_i; g1.ldb = n1;
+  g1.M = (int)M; g1.N = (int)n1; g1.K = (int)h;
+  g1.C = U_i; g1.ldc = n1;
+  g1.C2 = Y_i; g1.ldc2 = f;
+  g1.bias = a_i;
+  g1.fhalf = (int)f;
+  g1.act = (int)act;
+  const int epi1 = act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU_FWD : tp::EPI_BIAS_ACT;
+  tp::GemmParams g2 = {};
+  g2.A = Y_i; g2.lda = f;
+  g2.B = B_i; g2.ldb = h;
+  g2.M = (int)M; g2.N = (int)h; g2.K = (int)f;
+  g2.C = Z_i; g2.ldc = h;
+  hipError_t e;
+  if (dtype == TP_BF16) {
+    e = tp::gemm_bf16(g1, true, false, epi1, stream);
+    if (e == hipSuccess) e = tp::gemm_bf16(g2, true, false, tp::EPI_STORE, stream);
+  } else {
+    e = tp::gemm_f32(g1, true, false, epi1, stream);
+    if (e == hipSuccess) e = tp::gemm_f32(g2, true, false, tp::EPI_STORE, stream);
+  }
+  return hip_status(e);
+}
+
+int tp_mlp_bwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const void* X, const void* A_i,
+               const void* B_i, const void* U_i, const void* Y_i, const void* dZ, void* dU_ws, void* dA_i,
+               void* da_i, void* dB_i, void* dX_i, hipStream_t stream) {
+  if (dims == nullptr || X == nullptr || A_i == nullptr || B_i == nullptr || U_i == nullptr || Y_i == nullptr ||
+      dZ == nullptr || dU_ws == nullptr || dA_i == nullptr || dB_i == nullptr || dX_i == nullptr)
+    return TP_E_NULL;
+  const int64_t s = dims->s, b = dims->b, h = dims->h, ffn = dims->ffn, t = dims->t;
+  if (s <= 0 || b <= 0 || h <= 0 || ffn <= 0 || t <= 0) return TP_E_SHAPE;
+  if (s * b >= kMaxDim || h >= kMaxDim || ffn >= kMaxDim) return TP_E_SHAPE;
+  if (ffn % t != 0) return TP_E_DIVISIBILITY;
+  if (rank < 0 || rank >= t) return TP_E_RANK;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  if (act != TP_ACT_GELU && act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU && act != TP_ACT_RELU)
+    return TP_E_UNSUPPORTED;
+  const int64_t M = s * b, f = ffn / t, n1 = act == TP_ACT_SWIGLU ? 2 * f : f, es = esize(dtype);
+  if (dtype == TP_BF16 &&
+      (h % 8 != 0 || f % 8 != 0 || misaligned16({X, A_i, B_i, U_i, Y_i, dZ, dU_ws, dA_i, da_i, dB_i, dX_i})))
+    return TP_E_UNSUPPORTED;
+  const Buf outs[] = {{dU_ws, M * n1 * es}, {dA_i, h * n1 * es}, {da_i, n1 * es}, {dB_i, f * h * es},
+                      {dX_i, M * h * es}};
+  const Buf ins[] = {{X, M * h * es}, {A_i, h * n1 * es}, {B_i, f * h * es}, {U_i, M * n1 * es},
+                     {Y_i, M * f * es}, {dZ, M * h * es}};
+  if (any_alias(outs, 5, ins, 6)) return TP_E_ALIAS;
+
+  // dU = (dZ B_i^T) * act'(U):  A = dZ [M,h] K-major, B = B_i [f,h] read as rows n, K-major.
+  tp::GemmParams gy = {};
+  gy.A = dZ; gy.lda = h;
+  gy.B = B_i; gy.ldb = h;
+  gy.M = (int)M; gy.N = (int)f; gy.K = (int)h;
+  gy.C = dU_ws; gy.ldc = n1;
+  gy.aux = U_i; gy.ldaux = n1;
+  gy.fhalf = (int)f;
+  gy.act = (int)act;
+  const int epiy = act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU_BWD : tp::EPI_ACT_BWD;
+  // dB = Y^T dZ: C [f,h], A(m=f, k=tok) = Y [tok,f] MN-major, B(n=h, k=tok) = dZ [tok,h] MN-major.
+  tp::GemmParams gb = {};
+  gb.A = Y_i; gb.lda = f;
+  gb.B = dZ; gb.ldb = h;
+  gb.M = (int)f; gb.N = (int)h; gb.K = (int)M;
+  gb.C = dB_i; gb.ldc = h;
+  // dA = X^T dU: C [h,n1], A(m=h, k=tok) = X MN-major, B(n, k=tok) = dU MN-major.
+  tp::GemmParams ga = {};
+  ga.A = X; ga.lda = h;
+  ga.B = dU_ws; ga.ldb = n1;
+  ga.M = (int)h; ga.N = (int)n1; ga.K = (int)M;
+  ga.C = dA_i; ga.ldc = n1;
+  // dX = dU A^T: C [tok,h], A = dU [tok,n1] K-major, B(n=h, k=n1) = A_i [h,n1] K-major.
+  tp::GemmParams gx = {};
+  gx.A = dU_ws; gx.lda = n1;
+  gx.B = A_i; gx.ldb = n1;
+  gx.M = (int)M; gx.N = (int)h; gx.K = (int)n1;
+  gx.C = dX_i; gx.ldc = h;
+
+  auto gemm = dtype == TP_BF16 ? tp::gemm_bf16 : tp::gemm_f32;
+  hipError_t e = gemm(gy, true, true, epiy, stream);
+  if (e == hipSuccess) e = gemm(gb, false, false, tp::EPI_STORE, stream);
+  if (e == hipSuccess) e = gemm(ga, false, false, tp::EPI_STORE, stream);
+  if (e == hipSuccess && da_i != nullptr) e = tp::colsum(dtype, dU_ws, M, n1, da_i, stream);
+  if (e == hipSuccess) e = gemm(gx, true, true, tp::EPI_STORE, stream);
+  return hip_status(e);
+}
+
+int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const void* X, const void* Wqkv_i,
+                const void* bqkv_i, const void* Wo_i, void* QKV_i, void* O_i, float* lse_i, void* Z_i,
+                hipStream_t stream) {
+  if (dims == nullptr || X == nullptr || Wqkv_i == nullptr || Wo_i == nullptr || QKV_i == nullptr ||
+      O_i == nullptr || Z_i == nullptr)
+    return TP_E_NULL;
+  const int64_t s = dims->s, b = dims->b, h = dims->h, a = dims->a, d = dims->d, t = dims->t;
+  if (s <= 0 || b <= 0 || h <= 0 || a <= 0 || d <= 0 || t <= 0) return TP_E_SHAPE;
+  if (s * b >= kMaxDim || h >= kMaxDim) return TP_E_SHAPE;
+  if (a % t != 0 || h != a * d) return TP_E_DIVISIBILITY;
+  if (rank < 0 || rank >= t) return TP_E_RANK;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  if (d > 128) return TP_E_UNSUPPORTED;
+  const int64_t M = s * b, hl = a / t, n = 3 * hl * d, es = esize(dtype);
+  if (dtype == TP_BF16 && (h % 8 != 0 || d % 8 != 0 || misaligned16({X, Wqkv_i, bqkv_i, Wo_i, QKV_i, O_i, Z_i})))
+    return TP_E_UNSUPPORTED;
+  const Buf outs[] = {{QKV_i, M * n * es}, {O_i, M * hl * d * es}, {lse_i, b * hl * s * 4}, {Z_i, M * h * es}};
+  const Buf ins[] = {{X, M * h * es}, {Wqkv_i, h * n * es}, {bqkv_i, n * es}, {Wo_i, hl * d * h * es}};
+  if (any_alias(outs, 4, ins, 4)) return TP_E_ALIAS;
+
+  tp::GemmParams gq = {};
+  gq.A = X; gq.lda = h;
+  gq.B = Wqkv_i; gq.ldb = n;
+  gq.M = (int)M; gq.N = (int)n; gq.K = (int)h;
+  gq.C = QKV_i; gq.ldc = n;
+  gq.bias = bqkv_i;
+  tp::AttnParams ap = {};
+  ap.qkv = QKV_i; ap.o = O_i; ap.lse = lse_i;
+  ap.s = (int)s; ap.b = (int)b; ap.hl = (int)hl; ap.d = (int)d;
+  ap.causal = causal ? 1 : 0;
+  ap.scale = (float)(1.0 / __builtin_sqrt((double)d));
+  tp::GemmParams go = {};
+  go.A = O_i; go.lda = hl * d;
+  go.B = Wo_i; go.ldb = h;
+  go.M = (int)M; go.N = (int)h; go.K = (int)(hl * d);
+  go.C = Z_i; go.ldc = h;
+  hipError_t e;
+  if (dtype == TP_BF16) {
+    e = tp::gemm_bf16(gq, true, false, tp::EPI_BIAS, stream);
+    if (e == hipSuccess) e = tp::attention_bf16(ap, stream);
+    if (e == hipSuccess) e = tp::gemm_bf16(go, true, false, tp::EPI_STORE, stream);
+  } else {
+    e = tp::gemm_f32(gq, true, false, tp::EPI_BIAS, stream);
+    if (e == hipSuccess) e = tp::attention_f32(ap, stream);
+    if (e == hipSuccess) e = tp::gemm_f32(go, true, false, tp::EPI_STORE, stream);
+  }
+  return hip_status(e);
+}
+
+int tp_partial_reduce(int64_t n, int64_t h, int t, tp_dtype dtype, const void* partials, const void* bias_c,
+                      void* out, hipStream_t stream) {
+  if (partials == nullptr || out == nullptr) return TP_E_NULL;
+  if (n <= 0 || h <= 0 || t <= 0) return TP_E_SHAPE;
+  if (n % h != 0) return TP_E_SHAPE;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  const int64_t es = esize(dtype);
+  const Buf outs[] = {{out, n * es}};
+  const Buf ins[] = {{partials, (int64_t)t * n * es}, {bias_c, h * es}};
+  if (any_alias(outs, 1, ins, 2)) return TP_E_ALIAS;
+  return hip_status(tp::reduce_partials(dtype, partials, t, n, 0, n, bias_c, h, out, stream));
+}
+
+int tp_reduce_scatter_dim0(const tp_dims* dims, int rank, tp_dtype dtype, const void* partials, const void* bias_c,
+                           void* out, hipStream_t stream) {
+  if (dims == nullptr || partials == nullptr || out == nullptr) return TP_E_NULL;
+  const int64_t s = dims->s, b = dims->b, h = dims->h, t = dims->t;
+  if (s <= 0 || b <= 0 || h <= 0 || t <= 0) return TP_E_SHAPE;
+  if (s % t != 0) return TP_E_DIVISIBILITY;
+  if (rank < -1 || rank >= t) return TP_E_RANK;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  const int64_t es = esize(dtype), n = s * b * h, slice = (s / t) * b * h;
+  const int64_t count = rank < 0 ? n : slice;
+  const Buf outs[] = {{out, count * es}};
+  const Buf ins[] = {{partials, t * n * es}, {bias_c, h * es}};
+  if (any_alias(outs, 1, ins, 2)) return TP_E_ALIAS;
+  const int64_t in_off = rank < 0 ? 0 : (int64_t)rank * slice;
+  return hip_status(tp::reduce_partials(dtype, partials, (int)t, n, in_off, count, bias_c, h, out, stream));
+}
+
+int tp_gather_dim0(const tp_dims* dims, tp_dtype dtype, const void* slices, void* out, hipStream_t stream) {
+  if (dims == nullptr || slices == nullptr || out == nullptr) return TP_E_NULL;
+  const int64_t s = dims->s, b = dims->b, h = dims->h, t = dims->t;
+  if (s <= 0 || b <= 0 || h <= 0 || t <= 0) return TP_E_SHAPE;
+  if (s % t != 0) return TP_E_DIVISIBILITY;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  const int64_t bytes = s * b * h * esize(dtype);
+  const Buf outs[] = {{out, bytes}};
+  const Buf ins[] = {{slices, bytes}};
+  if (any_alias(outs, 1, ins, 1)) return TP_E_ALIAS;
+  return hip_status(tp::copy_bytes(slices, out, bytes, stream));
+}
+
+}  // extern "C"

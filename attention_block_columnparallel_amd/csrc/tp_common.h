@@ -1,0 +1,142 @@
+// Internal declarations shared by the HIP sources of libtpshard (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tpshard.h"
+
+namespace tp {
+
+// ------------------------------------------------------------------------------------------------------------------
+// bfloat16 <-> float.  A bf16 value is the fp32 value whose top 16 bits are its pattern.
+// ------------------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round to nearest, ties to even, with NaN mapped to a quiet NaN of the same sign.  Written out so that the
+// reduction's output bits are fixed by this rule alone (used where outputs are compared bit for bit).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Hardware conversion (v_cvt_pk_bf16_f32, nearest-even) for GEMM epilogues.
+__device__ __forceinline__ uint32_t f32_to_bf16_hw(float f) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f);
+}
+
+// ------------------------------------------------------------------------------------------------------------------
+// Element-wise activations (device math library for erf / exp / tanh).
+// ------------------------------------------------------------------------------------------------------------------
+__device__ __forceinline__ float act_gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float act_gelu_grad(float x) {
+  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * expf(-0.5f * x * x);
+}
+__device__ __forceinline__ float act_gelu_tanh(float x) {
+  float u = 0.79788456080286536f * (x + 0.044715f * x * x * x);
+  return 0.5f * x * (1.0f + tanhf(u));
+}
+__device__ __forceinline__ float act_gelu_tanh_grad(float x) {
+  float u = 0.79788456080286536f * (x + 0.044715f * x * x * x);
+  float th = tanhf(u);
+  float du = 0.79788456080286536f * (1.0f + 3.0f * 0.044715f * x * x);
+  return 0.5f * (1.0f + th) + 0.5f * x * (1.0f - th * th) * du;
+}
+__device__ __forceinline__ float act_sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+__device__ __forceinline__ float act_apply(int act, float x) {
+  switch (act) {
+    case TP_ACT_GELU: return act_gelu(x);
+    case TP_ACT_GELU_TANH: return act_gelu_tanh(x);
+    case TP_ACT_RELU: return x > 0.0f ? x : 0.0f;
+    default: return x;
+  }
+}
+__device__ __forceinline__ float act_grad(int act, float x) {
+  switch (act) {
+    case TP_ACT_GELU: return act_gelu_grad(x);
+    case TP_ACT_GELU_TANH: return act_gelu_tanh_grad(x);
+    case TP_ACT_RELU: return x > 0.0f ? 1.0f : 0.0f;
+    default: return 1.0f;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------------------------
+// Launch timing: when the calling thread is armed (tp_timing_begin), a LaunchTimer records the caller's start event
+// before a launch and its stop event after it, on the launch stream, and logs the kernel name.
+// ------------------------------------------------------------------------------------------------------------------
+void timing_start(hipStream_t st);
+void timing_stop(hipStream_t st, const char* name);
+struct LaunchTimer {
+  hipStream_t st;
+  const char* name;
+  LaunchTimer(hipStream_t s, const char* n) : st(s), name(n) { timing_start(st); }
+  ~LaunchTimer() { timing_stop(st, name); }
+};
+
+// Launch `kernel` on `stream` and evaluate to the launch status (hipGetLastError taken before the stop event).
+#define TP_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                 \
+  ([&]() -> hipError_t {                                                         \
+    ::tp::LaunchTimer tp_launch_timer_((stream), (name));                        \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);         \
+    return hipGetLastError();                                                    \
+  }())
+
+// ------------------------------------------------------------------------------------------------------------------
+// GEMM description: C[m][n] = sum_k Aop(m, k) * Bop(n, k), then an epilogue.
+// An operand is "K-major" when k is its contiguous index (row-major [rows][K]) and "MN-major" when m (or n) is
+// ([K][rows]).  The forward column GEMM X A_i has K-major X and MN-major A_i; the dgrad GEMMs (x W^T) are K-major
+// on both sides; the wgrad GEMMs (x^T y) are MN-major on both sides.
+// ------------------------------------------------------------------------------------------------------------------
+enum Epi {
+  EPI_STORE = 0,       // C = acc
+  EPI_BIAS = 1,        // C = acc + bias[n]
+  EPI_BIAS_ACT = 2,    // C = u = acc + bias[n] (bias nullable); C2 = act(u)
+  EPI_SWIGLU_FWD = 3,  // column pair (j, fhalf + j): C = [g | u] (+bias), C2[:, j] = silu(g) * u
+  EPI_ACT_BWD = 4,     // C = acc * act'(aux[m][n])
+  EPI_SWIGLU_BWD = 5   // acc = dY[m][j]; aux = [g | u]: C[:, j] = dY*u*silu'(g), C[:, fhalf+j] = dY*silu(g)
+};
+
+struct GemmParams {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  int M, N, K;  // SwiGLU forward: N = 2 * fhalf (both halves)
+  void* C;
+  int64_t ldc;
+  void* C2;
+  int64_t ldc2;
+  const void* bias;
+  const void* aux;
+  int64_t ldaux;
+  int fhalf;
+  int act;
+};
+
+// Launchers (return hipGetLastError after the launch).
+hipError_t gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, hipStream_t st);
+hipError_t gemm_f32(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, hipStream_t st);
+hipError_t colsum(tp_dtype dt, const void* x, int64_t rows, int64_t cols, void* out, hipStream_t st);
+
+hipError_t reduce_partials(tp_dtype dt, const void* partials, int t, int64_t stride, int64_t in_off, int64_t count,
+                           const void* bias, int64_t h, void* out, hipStream_t st);
+hipError_t copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t st);
+hipError_t pack_columns(tp_dtype dt, const void* full, int64_t rows, int64_t full_cols, void* shard,
+                        int64_t shard_cols, int kind, int64_t f_l, int64_t ffn, int64_t rank, int64_t hl, int64_t d,
+                        int64_t ad, hipStream_t st);
+
+struct AttnParams {
+  const void* qkv;  // [s, b, hl*3d] grouped [q_j k_j v_j]
+  void* o;          // [s, b, hl*d]
+  float* lse;       // [b, hl, s] or null
+  int s, b, hl, d;
+  int causal;
+  float scale;      // 1/sqrt(d)
+};
+hipError_t attention_bf16(const AttnParams& p, hipStream_t st);
+hipError_t attention_f32(const AttnParams& p, hipStream_t st);
+
+}  // namespace tp

@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the tensor-parallel MLP block on one MI355X.
+
+One step = the whole hot path over one batch of seeded synthetic input at the default-calculator width
+(h=4096, ffn=16384, t=8, b=8, s=2048, GeLU, bf16): for every rank i the column GEMM with fused GeLU, the row GEMM
+into partial buffer i; the g reduction (dim-0 reduce-scatter over the 8 partial buffers, every rank's slice);
+for every rank the backward dgrad / wgrad GEMMs into dX partial i; the f reduction of the dX partials (same
+kernel).  Inputs and weights are resident in HBM before the timed region; the shards are packed once, before it.
+
+Prints ONE JSON line.  value = algorithmic GEMM flops of the step / wall time of the step (whole job, including
+both reductions), in TFLOP/s.  roofline = the kernel with the largest share of the step's time, its algorithmic
+flops per launch over its average HIP-event duration inside the timed region, against the dense bf16 MFMA peak.
+rs_dim0 = the reduce-scatter kernel against HBM bandwidth.  cpu_baseline = the fp64 oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "TP-shard MLP fwd+bwd TFLOP/s & % bf16 MFMA peak; dim0 reduce-scatter GB/s"
+PEAK_BF16_FLOPS = 2.5e15  # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12   # MI355X HBM3E
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mlp_h4096_ffn16384_t8_b8_s2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one dim-0 gather (a plain copy) of this many MiB, for counter calibration")
+    return ap.parse_args(argv)
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(w, inp, target_s: float) -> dict:
+    """The oracle (fp64 NumPy, as it stands) on one rank's shard fwd + bwd over a sample of R token rows -- the
+    same computation as the GPU's per-rank work for a batch of R tokens.  Reported in algorithmic TFLOP/s."""
+    import numpy as np
+
+    import oracle as O
+
+    X = O.as_f64(inp["X"], w.dtype).reshape(w.M, w.h)
+    dZ = O.as_f64(inp["dZ"], w.dtype).reshape(w.M, w.h)
+    A, B = O.as_f64(inp["A"], w.dtype), O.as_f64(inp["B"], w.dtype)
+
+    def run(R):
+        t0 = time.perf_counter()
+        O.mlp_shard_forward(X[:R], A, B, w.t, 0, w.act)
+        O.mlp_shard_backward(X[:R], A, B, dZ[:R], w.t, 0, w.act)
+        return time.perf_counter() - t0
+
+    R = 128
+    dt = run(R)
+    while dt < 0.5 and R < w.M:
+        R = min(w.M, R * 4)
+        dt = run(R)
+    R2 = int(min(w.M, max(R, R * target_s / max(dt, 1e-6))))
+    R2 = max(64, (R2 // 64) * 64)
+    dt2 = run(R2) if R2 != R else dt
+    flops = 12.0 * R2 * w.h * w.f_l
+    return {"value": flops / dt2 / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"rank 0 shard fwd+bwd (fp64 NumPy) over {R2} of {w.M} token rows: {flops / 1e9:.1f} "
+                      f"algorithmic GFLOP in {dt2:.2f} s"}
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): every rank's "
+              "shard runs back to back on that GPU and the reductions are on-device kernels; there is no "
+              "multi-GPU path in this build.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import attention_block_columnparallel_amd as pkg
+    import tp_inputs as TI
+    from attention_block_columnparallel_amd.block import MlpBlock
+
+    L = pkg.load()
+    w = TI.WORKLOADS[args.workload]
+    if w.kind != "mlp":
+        print("bench.py times the MLP block workloads", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    inp = TI.mlp_inputs(w)
+    X = dev(inp["X"])
+    dZ = dev(inp["dZ"])
+    blk = MlpBlock(w.s, w.b, w.h, w.ffn, w.t, w.act, dev(inp["A"]), dev(inp["B"]))
+    dims = blk.dims
+    Zrs = torch.empty((w.t, w.s // w.t, w.b, w.h), dtype=dt, device="cuda")
+    dXrs = torch.empty((w.t, w.s // w.t, w.b, w.h), dtype=dt, device="cuda")
+
+    def step():
+        blk.forward_ranks(X)
+        L.tp_reduce_scatter_dim0(dims, -1, blk.Zp, None, Zrs)  # g-bar, every rank's slice
+        blk.backward_ranks(X, dZ)
+        L.tp_reduce_scatter_dim0(dims, -1, blk.dXp, None, dXrs)  # f on the dX partials
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, bracketed by synchronisation; every library launch bracketed by HIP events
+    launches_per_step = 6 * w.t + 2
+    timer = L.LaunchTimer(capacity=args.steps * launches_per_step + 8)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    with timer:
+        for _ in range(args.steps):
+            step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    ms_wall = wall * 1e3 / args.steps
+    ms_step = max(ms_per_step, ms_wall)
+
+    M, h, f, t = w.M, w.h, w.f_l, w.t
+    gemm_flops = 2.0 * M * h * f  # every GEMM of the step has this size
+    step_flops = 12.0 * M * h * f * t
+    value = step_flops / (ms_step * 1e-3) / 1e12
+
+    kern = {}
+    for name, ms in timer.results():
+        k = kern.setdefault(name, {"launches": 0, "total_ms": 0.0})
+        k["launches"] += 1
+        k["total_ms"] += ms
+    rs_name = next((n for n in kern if n.startswith("reduce_bf16") or n.startswith("reduce_f32")), None)
+    n_el = w.s * w.b * w.h
+    rs_bytes = (t + 1) * n_el * (2 if w.dtype == "bf16" else 4)
+    for name, k in kern.items():
+        k["avg_us"] = 1e3 * k["total_ms"] / k["launches"]
+        k["share"] = k["total_ms"] / (ms_per_step * args.steps)
+        if name.startswith("gemm"):
+            k["tflops"] = gemm_flops / (k["avg_us"] * 1e-6) / 1e12
+        if name == rs_name:
+            k["gbps"] = rs_bytes / (k["avg_us"] * 1e-6) / 1e9
+    dom = max((n for n in kern if n.startswith("gemm")), key=lambda n: kern[n]["total_ms"])
+    ach = kern[dom]["tflops"]
+    roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": round(ach * 1e12 / PEAK_BF16_FLOPS, 4), "traffic": None, "kernel": dom,
+                "flops_per_launch": gemm_flops, "avg_us": round(kern[dom]["avg_us"], 2)}
+    gemm_ms = sum(k["total_ms"] for n, k in kern.items() if n.startswith("gemm")) / args.steps
+    rs = kern[rs_name]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "s": w.s, "b": w.b, "h": w.h, "ffn": w.ffn, "t": w.t, "act": w.act,
+                   "ranks": f"all {t} TP shards back to back on one GPU", "step_gflop": round(step_flops / 1e9, 1)},
+        "frac_of_bf16_peak": round(value * 1e12 / PEAK_BF16_FLOPS, 4),
+        "gemm_tflops_aggregate": round(step_flops / (gemm_ms * 1e-3) / 1e12, 2),
+        "roofline": roofline,
+        "rs_dim0": {"kernel": rs_name, "gbps": round(rs["gbps"], 1), "frac_hbm": round(rs["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
+                    "bytes_per_launch": rs_bytes, "avg_us": round(rs["avg_us"], 2)},
+        "kernels": {n: {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in k.items()} for n, k in kern.items()},
+    }
+    if args.calib_copy_mib > 0:
+        nbytes = args.calib_copy_mib << 20
+        src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").zero_()
+        dst = torch.empty_like(src)
+        cd = L.make_dims(s=nbytes // 2 // 8, b=1, h=8, t=1)
+        with L.LaunchTimer(capacity=4) as ct:
+            L.tp_gather_dim0(cd, src, dst)
+        torch.cuda.synchronize()
+        (cname, cms), = ct.results()
+        out["calib_copy"] = {"kernel": cname, "bytes_read": nbytes, "bytes_written": nbytes, "ms": round(cms, 4)}
+    del blk, X, dZ, Zrs, dXrs
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

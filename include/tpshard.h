@@ -1,0 +1,160 @@
+/* tpshard.h -- C ABI of libtpshard: one tensor-parallel rank's compute of a Megatron-style column->row block on an
+ * AMD Instinct MI355X (gfx950), plus the on-device g / g-bar / f reductions over t partial-sum buffers.
+ *
+ * Pages cited (by title and section):
+ *   [ATLAS] "Tensor Parallelism (TP) 与 Sequence Parallelism (SP)", llm-infra-atlas parallel/02_tp_sp
+ *   [SPLIT] 111qqz.com "tensor-parallelism-matrix-split" (column / row split of one linear layer and its backward)
+ *   [MEGA]  blog.vllbc.top visual reading of Megatron-LM tensor parallelism
+ *   [SPCP]  blog.vllbc.top "Sequence Parallel 与 Context Parallel"
+ *
+ * Notation follows the pages: s sequence length, b micro-batch, h hidden size, ffn the MLP inner width, a heads,
+ * d head dim (h = a*d), t the tensor-parallel degree.  Activations are sequence-first [s, b, h] ([ATLAS] §1): a
+ * GEMM sees them as M = s*b rows of h, in s-major order.  Weights use the math layout [in, out] ([SPLIT], the
+ * remark on nn.Linear storage): a column shard is [h, ffn/t], a row shard [ffn/t, h].
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are caller-owned, device-resident, dense row-major.  The library allocates nothing, frees nothing
+ *     and keeps no state between calls (apart from the opt-in, thread-local launch-timing log below); code objects
+ *     are linked into the shared object.
+ *   - bf16 (TP_BF16) tensors hold bfloat16 values; the bf16 path needs every row length that is a GEMM K or N
+ *     dimension (h, ffn/t, d, 3*(a/t)*d) to be a multiple of 8 and every pointer 16-byte aligned.  fp32 (TP_F32)
+ *     tensors hold IEEE binary32 and have no alignment rule.
+ *   - Every call only enqueues kernels on `stream` (0 = the null stream) and returns; nothing synchronises.
+ *     The status is that of host validation and of the launches (hipGetLastError right after them).
+ *   - Validation happens before any HIP call, in this order: null dims / pointers (TP_E_NULL), non-positive sizes
+ *     (TP_E_SHAPE), divisibility rules of the pages (TP_E_DIVISIBILITY), rank (TP_E_RANK), dtype / activation
+ *     (TP_E_DTYPE, TP_E_UNSUPPORTED), alignment (TP_E_UNSUPPORTED), output-aliases-input (TP_E_ALIAS).
+ *   - Calls are stateless and re-entrant; two calls that write the same buffer on different streams race.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPSHARD_ABI_VERSION 1
+
+/* Sizes in the pages' notation.  MLP calls read s, b, h, ffn, t; attention calls read s, b, h, a, d, t; the
+ * reductions read s, b, h, t. */
+typedef struct {
+  int64_t s, b, h, ffn, a, d, t;
+} tp_dims;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Element-wise activation between the column and the row GEMM ([ATLAS] §2, [MEGA]: GeLU; [ATLAS] §1: SwiGLU
+ * computes over 2 x ffn; [SPLIT] two-layer example: ReLU).  TP_ACT_GELU is the erf form x*Phi(x); TP_ACT_SWIGLU
+ * is SiLU(gate) * up with the fc1 weight [h, 2*ffn] = [gate | up]. */
+typedef enum { TP_ACT_GELU = 0, TP_ACT_GELU_TANH = 1, TP_ACT_SWIGLU = 2, TP_ACT_RELU = 3 } tp_act;
+
+/* Which full weight (or bias) tp_shard_weights slices. */
+typedef enum {
+  TP_W_FC1 = 0,         /* full [h, ffn]            -> shard [h, ffn/t]  (column-parallel)                    */
+  TP_W_FC1_GATE_UP = 1, /* full [h, 2ffn]=[Wg|Wu]   -> shard [h, 2ffn/t] = [Wg_i | Wu_i]                      */
+  TP_W_FC2 = 2,         /* full [ffn, h]            -> shard [ffn/t, h]  (row-parallel)                       */
+  TP_W_QKV = 3,         /* full [h, 3ad]=[Wq|Wk|Wv] -> shard [h, (a/t)*3d], per local head j: [q_j | k_j | v_j] */
+  TP_W_PROJ = 4,        /* full [ad, h]             -> shard [(a/t)*d, h] (row-parallel)                      */
+  TP_B_FC1 = 5,         /* full [ffn]               -> [ffn/t]                                                */
+  TP_B_FC1_GATE_UP = 6, /* full [2ffn]=[bg|bu]      -> [2ffn/t] = [bg_i | bu_i]                               */
+  TP_B_QKV = 7          /* full [3ad]=[bq|bk|bv]    -> [(a/t)*3d] grouped per local head                      */
+} tp_wkind;
+
+enum {
+  TP_OK = 0,
+  TP_E_NULL = -1,         /* a required pointer (or dims) is NULL                                  */
+  TP_E_SHAPE = -2,        /* a size is non-positive or out of the supported range                 */
+  TP_E_DIVISIBILITY = -3, /* s % t, ffn % t, a % t or h != a*d ([ATLAS] §1, [MEGA] divide())       */
+  TP_E_DTYPE = -4,        /* unknown dtype                                                        */
+  TP_E_RANK = -5,         /* rank outside [0, t) (or -1 where not allowed)                         */
+  TP_E_ALIAS = -6,        /* an output buffer overlaps an input buffer                            */
+  TP_E_UNSUPPORTED = -7,  /* valid but not built: activation/dtype combination, alignment, d range  */
+  TP_E_HIP = -8           /* a HIP launch failed; tp_last_hip_error() names it                      */
+};
+
+/* Text of a status code (static storage). */
+const char* tp_status_str(int status);
+
+/* hipError_t of the last failed launch in this thread (0 if none). */
+int tp_last_hip_error(void);
+
+/* TPSHARD_ABI_VERSION of the built library. */
+int tp_abi_version(void);
+
+/* Shard packer ([ATLAS] §2-3, [MEGA]: fc1/QKV split by output columns -- QKV by head -- and fc2/projection by
+ * input rows).  Copies rank `rank`'s shard of `full` into `shard` (layouts in tp_wkind), bit for bit.
+ * Uses s, b of dims not at all; needs ffn % t == 0 (FC kinds) or a % t == 0 and h == a*d (QKV/PROJ kinds).
+ * full and shard must not overlap. */
+int tp_shard_weights(const tp_dims* dims, int rank, tp_wkind kind, tp_dtype dtype, const void* full, void* shard,
+                     hipStream_t stream);
+
+/* MLP forward of rank `rank` ([ATLAS] §2 column->act->row; [SPLIT] two-layer forward):
+ *   U_i = X A_i (+ a_i)        column GEMM, saved for the backward        [s, b, N1]
+ *   Y_i = act(U_i)             element-wise, local to the shard           [s, b, ffn/t]
+ *   Z_i = Y_i B_i              row GEMM: a partial sum of the block output [s, b, h]; no row bias here
+ * N1 = ffn/t, or 2*ffn/t for SwiGLU (U_i = [U_gate | U_up]).  A_i [h, N1], a_i [N1] (nullable), B_i [ffn/t, h].
+ * Running ranks 0..t-1 with Z_i pointing at partials + i*s*b*h and then tp_partial_reduce (g, all-reduce form)
+ * or tp_reduce_scatter_dim0 (g-bar under sequence parallelism) gives the block output. */
+int tp_mlp_fwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const void* X, const void* A_i,
+               const void* a_i, const void* B_i, void* U_i, void* Y_i, void* Z_i, hipStream_t stream);
+
+/* MLP backward of rank `rank` ([SPLIT] backward of both layers; [ATLAS] §2 f/g):
+ *   dY_i = dZ B_i^T, fused with dU_i = dY_i * act'(U_i)     -> dU_ws [s, b, N1] (caller workspace)
+ *   dB_i = Y_i^T dZ                                          -> [ffn/t, h]   local weight gradient
+ *   dA_i = X^T dU_i                                          -> [h, N1]      local weight gradient
+ *   da_i = column sums of dU_i (nullable)                    -> [N1]
+ *   dX_i = dU_i A_i^T                                        -> [s, b, h]    a partial: f sums them over ranks
+ * dZ is the full upstream gradient (g is the identity in backward; after the dim-0 all-gather under SP). */
+int tp_mlp_bwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const void* X, const void* A_i,
+               const void* B_i, const void* U_i, const void* Y_i, const void* dZ, void* dU_ws, void* dA_i,
+               void* da_i, void* dB_i, void* dX_i, hipStream_t stream);
+
+/* Attention forward of rank `rank` for its a/t local heads ([ATLAS] §3, [MEGA]: QKV column-parallel by head,
+ * per-head softmax(Q K^T / sqrt d) V on the local heads, output projection row-parallel; [SPCP] CP step 3: the
+ * online-softmax merge over key blocks):
+ *   QKV_i = X Wqkv_i (+ bqkv_i)     [s, b, (a/t)*3d], per local head j the columns [q_j | k_j | v_j]
+ *   O_i   = per head softmax(Q_j K_j^T / sqrt(d), causal: key k visible to query q iff k <= q) V_j
+ *                                   [s, b, (a/t)*d], head j at columns j*d .. j*d+d-1
+ *   lse_i = log sum_k exp(S[q, k]) per (b, local head, q), fp32 [b, a/t, s] (nullable)
+ *   Z_i   = O_i Wo_i                [s, b, h], a partial sum (no row bias)
+ * Wqkv_i [h, (a/t)*3d] and Wo_i [(a/t)*d, h] as produced by tp_shard_weights.  bf16 path: d % 16 == 0, d <= 128.
+ * fp32 path: d <= 128. */
+int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const void* X, const void* Wqkv_i,
+                const void* bqkv_i, const void* Wo_i, void* QKV_i, void* O_i, float* lse_i, void* Z_i,
+                hipStream_t stream);
+
+/* g in forward / f in backward, all-reduce form ([ATLAS] §2; [SPLIT] row-parallel merge is a sum):
+ *   out[e] = sum_{i=0}^{t-1} partials[i*n + e]  (+ bias_c[e % h])
+ * partials is [t][n] contiguous.  Sum in fp32 in rank order 0..t-1, the bias (nullable, [h]) added last, one
+ * rounding to the output dtype (bf16: nearest, ties to even; NaN stays NaN).  Needs n % h == 0. */
+int tp_partial_reduce(int64_t n, int64_t h, int t, tp_dtype dtype, const void* partials, const void* bias_c,
+                      void* out, hipStream_t stream);
+
+/* g-bar under sequence parallelism: reduce-scatter along dim 0 of [s, b, h] ([ATLAS] §1, §5; [SPCP] SP section):
+ * rank r receives rows [r*s/t, (r+1)*s/t) of the sum over the t partials [t][s, b, h], same arithmetic as
+ * tp_partial_reduce.  rank == -1 writes every rank's slice, out = [t][s/t, b, h].  Needs s % t == 0. */
+int tp_reduce_scatter_dim0(const tp_dims* dims, int rank, tp_dtype dtype, const void* partials, const void* bias_c,
+                           void* out, hipStream_t stream);
+
+/* SP entry (forward all-gather along dim 0, [ATLAS] §1 gather along the first dim; [SPCP] SP section):
+ * out [s, b, h] = concatenation of the t slices [t][s/t, b, h] in rank order, bit for bit.  Needs s % t == 0. */
+int tp_gather_dim0(const tp_dims* dims, tp_dtype dtype, const void* slices, void* out, hipStream_t stream);
+
+/* Launch timing, a profiling aid (not part of the block's arithmetic).  tp_timing_begin arms the calling thread:
+ * every kernel launched by a later tp_* call on this thread is bracketed by hipEventRecord(starts[i], stream) and
+ * hipEventRecord(stops[i], stream), for the first `capacity` launches (later ones run unrecorded).  The events are
+ * created and owned by the caller (hipEventCreate).  tp_timing_end disarms and returns the number of launches
+ * recorded; tp_timing_kernel(i) names the i-th (static storage; NULL if out of range).  Arming the thread again
+ * restarts the log.  Returns TP_E_NULL for NULL arrays, TP_E_SHAPE for capacity <= 0. */
+int tp_timing_begin(hipEvent_t* starts, hipEvent_t* stops, int capacity);
+int tp_timing_end(void);
+const char* tp_timing_kernel(int i);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

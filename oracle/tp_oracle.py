@@ -64,6 +64,15 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return out.astype(np.uint16)
 
 
+def stored(x: np.ndarray, dtype: str) -> np.ndarray:
+    """The value a device keeps when it stores x in `dtype`: fp32 rounding of x, then (bf16) one more rounding to
+    bfloat16 nearest-even -- the storage precision of an intermediate the ABI hands back (e.g. QKV_i)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if dtype == "bf16":
+        return bf16_bits_to_f64(f32_to_bf16_bits(x32))
+    return x32.astype(np.float64)
+
+
 def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     """Storage form (uint16 bf16 patterns or float32) to float64."""
     if dtype == "bf16":
@@ -395,6 +404,52 @@ def mlp_shard_backward(X: np.ndarray, A: np.ndarray, B: np.ndarray, dZ: np.ndarr
     dai = dUi.sum(axis=0)
     dXi = dUi @ A[:, cols].T
     return {"dY": dYi, "dB": dBi, "dU": dUi, "dA": dAi, "da": dai, "dX": dXi}
+
+
+def mlp_shard_rows(X_rows: np.ndarray, dZ_rows: np.ndarray, A: np.ndarray, B: np.ndarray, t: int, rank: int,
+                   act: str = "gelu", a_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Rank r's per-token results for a subset of token rows.  Every row of U_i, Y_i, Z_i, dU_i and dX_i depends
+    only on the same row of X (and of dZ), so computing them for sampled rows is exact."""
+    ffn = B.shape[0]
+    cols = mlp_shard_columns(ffn, t, rank, act)
+    w = ffn // t
+    Bi = B[rank * w:(rank + 1) * w, :]
+    Ai = A[:, cols]
+    U = X_rows @ Ai
+    if a_bias is not None:
+        U = U + a_bias[cols]
+    Y = _act_fwd(U, act)
+    Z = Y @ Bi
+    dY = dZ_rows @ Bi.T
+    dU = _act_bwd(U, dY, act)
+    dX = dU @ Ai.T
+    return {"U": U, "Y": Y, "Z": Z, "dU": dU, "dX": dX}
+
+
+def mlp_shard_weight_grad_cols(X: np.ndarray, dZ: np.ndarray, A: np.ndarray, B: np.ndarray, t: int, rank: int,
+                               j_cols: Sequence[int], act: str = "gelu",
+                               a_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Rank r's weight gradients restricted to shard columns j of the GeLU/ReLU output (for SwiGLU: j indexes the
+    f/t output columns and both the gate column j and the up column f/t + j of dA_i are returned).
+    dB_i[j, :] = Y_i[:, j]^T dZ and dA_i[:, j] = X^T dU_i[:, j] each need only column j of the activations, over
+    all token rows, so sampling columns is exact."""
+    ffn = B.shape[0]
+    w = ffn // t
+    j = np.asarray(j_cols, dtype=np.int64)
+    Bj = B[rank * w + j, :]                      # rows of B_i for the sampled columns
+    full_cols = mlp_shard_columns(ffn, t, rank, act)
+    if act == "swiglu":
+        sel = np.concatenate([j, w + j])          # gate j and up j within the packed shard
+    else:
+        sel = j
+    cols = full_cols[sel]
+    U = X @ A[:, cols]
+    if a_bias is not None:
+        U = U + a_bias[cols]
+    Y = _act_fwd(U, act)                          # [M, len(j)]
+    dY = dZ @ Bj.T
+    dU = _act_bwd(U, dY, act)                     # [M, len(sel)]
+    return {"dB_rows": Y.T @ dZ, "dA_cols": X.T @ dU, "da_cols": dU.sum(axis=0), "sel": sel}
 
 
 # ---------------------------------------------------------------------------------------------------------------

@@ -1,0 +1,143 @@
+"""The C ABI on the CPU: the library loads, exports every function include/tpshard.h declares, and every invalid
+argument is rejected with its documented status before any HIP call (so none of these calls touches a GPU).
+
+Pointers here are fake, well-aligned addresses: validation never dereferences them, and every case below fails
+validation, so nothing is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import attention_block_columnparallel_amd as pkg
+
+    return pkg.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(tp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for n in ["tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd", "tp_attn_fwd", "tp_partial_reduce",
+              "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_status_str"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+    assert set(L.EXPORTED) == set(declared_functions())
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.lib.tp_abi_version() == 1
+    for code in range(0, -9, -1):
+        s = L.status_str(code)
+        assert isinstance(s, str) and s and s != "unknown status"
+    assert L.status_str(-99) == "unknown status"
+
+
+A = 0x100000  # fake 16-byte-aligned addresses, far apart (no overlap)
+
+
+def addr(i):
+    return A * (i + 1)
+
+
+def mlp_args(L, **over):
+    d = dict(s=16, b=2, h=64, ffn=256, t=2)
+    d.update({k: v for k, v in over.items() if k in d})
+    dims = L.make_dims(**d)
+    return dims
+
+
+BF16, F32 = 1, 0
+
+
+def test_mlp_fwd_validation(L):
+    dims = mlp_args(L)
+    P = [addr(i) for i in range(7)]
+    call = lambda dims, rank=0, act=0, dt=BF16, p=P: L.tp_mlp_fwd(dims, rank, act, p[0], p[1], p[2], p[3], p[4],
+                                                                  p[5], p[6], stream=0, dtype=dt, check=False)
+    assert L.lib.tp_mlp_fwd(None, 0, 0, BF16, *P, None) == -1
+    assert call(dims, p=[None] + P[1:]) == -1                       # X NULL
+    assert call(dims, rank=2, p=P[:2] + [None] + P[3:]) == -5       # a NULL bias is allowed: the rank check decides
+    assert call(mlp_args(L, s=0)) == -2
+    assert call(mlp_args(L, ffn=255)) == -3                         # ffn % t
+    assert call(dims, rank=2) == -5
+    assert call(dims, rank=-1) == -5
+    assert call(dims, dt=7) == -4
+    assert call(dims, act=9) == -7
+    assert call(mlp_args(L, h=60)) == -7                            # bf16 rows must be multiples of 8
+    assert call(dims, p=[P[0] + 2] + P[1:]) == -7                   # misaligned bf16 pointer
+    # Y_i overlapping X
+    assert call(dims, p=P[:5] + [P[0] + 64] + P[6:]) == -6
+    # two outputs overlapping each other
+    assert call(dims, p=P[:4] + [P[4], P[4] + 128, P[6]]) == -6
+
+
+def test_mlp_bwd_validation(L):
+    dims = mlp_args(L)
+    P = [addr(i) for i in range(11)]
+    call = lambda dims, rank=0, act=0, dt=BF16, p=P: L.tp_mlp_bwd(dims, rank, act, *p, stream=0, dtype=dt, check=False)
+    assert call(dims, p=P[:6] + [None] + P[7:]) == -1               # dU workspace required
+    assert call(mlp_args(L, ffn=100, t=3)) == -3
+    assert call(dims, rank=5) == -5
+    assert call(dims, act=-1) == -7
+    assert call(dims, p=P[:9] + [P[0]] + P[10:]) == -6              # dB_i aliases X
+
+
+def test_attn_fwd_validation(L):
+    P = [addr(i) for i in range(8)]
+    call = lambda dims, rank=0, dt=BF16, p=P: L.tp_attn_fwd(dims, rank, True, *p, stream=0, dtype=dt, check=False)
+    ok = dict(s=64, b=1, h=128, a=4, d=32, t=2)
+    assert call(L.make_dims(**{**ok, "a": 3})) == -3               # heads % t
+    assert call(L.make_dims(**{**ok, "d": 16})) == -3              # h != a*d
+    assert call(L.make_dims(**{**ok, "h": 1024, "d": 256})) == -7  # d > 128
+    assert call(L.make_dims(**{**ok, "h": 48, "d": 12})) == -7     # bf16 needs d % 8 == 0
+    assert call(L.make_dims(**ok), rank=2) == -5
+    assert call(L.make_dims(**ok), p=P[:4] + [P[0]] + P[5:]) == -6  # QKV_i aliases X
+
+
+def test_reduce_and_gather_validation(L):
+    P = [addr(i) for i in range(3)]
+    assert L.tp_partial_reduce(0, 8, 2, P[0], None, P[1], stream=0, dtype=BF16, check=False) == -2
+    assert L.tp_partial_reduce(100, 64, 2, P[0], None, P[1], stream=0, dtype=BF16, check=False) == -2  # n % h
+    assert L.tp_partial_reduce(128, 64, 2, None, None, P[1], stream=0, dtype=BF16, check=False) == -1
+    assert L.tp_partial_reduce(128, 64, 2, P[0], None, P[0] + 256, stream=0, dtype=BF16, check=False) == -6
+    assert L.tp_partial_reduce(128, 64, 2, P[0], None, P[1], stream=0, dtype=3, check=False) == -4
+    dims = L.make_dims(s=10, b=2, h=8, t=4)                          # s % t != 0
+    assert L.tp_reduce_scatter_dim0(dims, 0, P[0], None, P[1], stream=0, dtype=BF16, check=False) == -3
+    assert L.tp_gather_dim0(dims, P[0], P[1], stream=0, dtype=BF16, check=False) == -3
+    dims = L.make_dims(s=8, b=2, h=8, t=4)
+    assert L.tp_reduce_scatter_dim0(dims, 4, P[0], None, P[1], stream=0, dtype=BF16, check=False) == -5
+    assert L.tp_reduce_scatter_dim0(dims, -2, P[0], None, P[1], stream=0, dtype=BF16, check=False) == -5
+
+
+def test_shard_weights_validation(L):
+    P = [addr(i) for i in range(2)]
+    dims = L.make_dims(h=64, ffn=256, t=3)
+    assert L.tp_shard_weights(dims, 0, "fc1", P[0], P[1], stream=0, dtype=BF16, check=False) == -3
+    dims = L.make_dims(h=64, ffn=256, t=2)
+    assert L.tp_shard_weights(dims, 2, "fc1", P[0], P[1], stream=0, dtype=BF16, check=False) == -5
+    assert L.tp_shard_weights(dims, 0, 99, P[0], P[1], stream=0, dtype=BF16, check=False) == -7
+    assert L.tp_shard_weights(dims, 0, "fc1", P[0], P[0] + 64, stream=0, dtype=BF16, check=False) == -6
+    dims = L.make_dims(h=96, a=4, d=24, t=8)
+    assert L.tp_shard_weights(dims, 0, "qkv", P[0], P[1], stream=0, dtype=BF16, check=False) == -3
+
+
+def test_python_wrapper_raises_tperror(L):
+    with pytest.raises(L.TpError) as ei:
+        L.tp_partial_reduce(100, 64, 2, addr(0), None, addr(1), stream=0, dtype=BF16)
+    assert "TP_E_SHAPE" in str(ei.value)

@@ -459,3 +459,39 @@ def test_llama70b_activation_sizes():
     assert n * g["elem_bytes"] / MIB == g["activation_mib_per_card_no_sp"]
     sl = O.split_dim0(np.zeros((g["s"], 1, 1)), g["t"], 0).shape[0]
     assert sl * g["b"] * g["h"] * g["elem_bytes"] / MIB == g["activation_mib_per_card_sp"]
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu", "relu"])
+def test_sampled_mlp_helpers_match_full_oracle(act):
+    rng = np.random.default_rng(12)
+    M, h, f, t = 14, 6, 16, 4
+    wa = 2 * f if act == "swiglu" else f
+    X = rng.standard_normal((M, h))
+    A = rng.standard_normal((h, wa)) * 0.5
+    B = rng.standard_normal((f, h)) * 0.5
+    a = rng.standard_normal(wa) * 0.1
+    dZ = rng.standard_normal((M, h))
+    rows = [0, 3, 13, 7]
+    for r in range(t):
+        fw = O.mlp_shard_forward(X, A, B, t, r, act, a)
+        bw = O.mlp_shard_backward(X, A, B, dZ, t, r, act, a)
+        sr = O.mlp_shard_rows(X[rows], dZ[rows], A, B, t, r, act, a)
+        for k in ("U", "Y", "Z"):
+            assert np.allclose(sr[k], fw[k][rows], atol=1e-13)
+        for k in ("dU", "dX"):
+            assert np.allclose(sr[k], bw[k][rows], atol=1e-13)
+        js = [0, 2, 3]
+        wc = O.mlp_shard_weight_grad_cols(X, dZ, A, B, t, r, js, act, a)
+        assert np.allclose(wc["dB_rows"], bw["dB"][js], atol=1e-13)
+        assert np.allclose(wc["dA_cols"], bw["dA"][:, wc["sel"]], atol=1e-13)
+        assert np.allclose(wc["da_cols"], bw["da"][wc["sel"]], atol=1e-13)
+
+
+def test_stored_rounding_is_fp32_then_bf16():
+    x = np.array([1.0 + 2.0 ** -8 + 2.0 ** -30, 1.0 + 2.0 ** -9, -3.0, 1e-3])
+    got = O.stored(x, "bf16")
+    # 1 + 2^-8 + 2^-30: fp32 keeps 1 + 2^-8 (2^-30 is below fp32's half ulp), then the bf16 tie goes to even 1.0
+    assert got[0] == 1.0
+    assert got[1] == 1.0 and got[2] == -3.0
+    assert abs(got[3] - 1e-3) <= 2.0 ** -9 * 1e-3
+    assert np.array_equal(O.stored(x, "f32"), x.astype(np.float32).astype(np.float64))
