@@ -313,6 +313,350 @@ __global__ __launch_bounds__(NWM* NWN * 64) void gemm_bf16_kernel(GemmParams p) 
 }
 
 // ------------------------------------------------------------------------------------------------------------------
+// Large-tile kernel: 256 x 256 output tile, 4 waves (2 x 2), each wave 128 x 128 = 8 x 8 MFMA subtiles whose 256
+// fp32 accumulators per lane live in the accumulation registers (one wave per SIMD, 512 registers).  Needs
+// K % 64 == 0 (an even number of 32-deep K tiles).  Out-of-range rows of either operand are clamped to the last valid row: they only feed output rows
+// or columns that are never stored, so no load needs a bounds branch.
+//
+// Each operand tile is kept in LDS in the orientation it has in HBM, 32 k deep:
+//   * K-major ([rows][k]): 256 rows x 64 bytes; 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 3).  An MFMA
+//     fragment (16 rows x 8 consecutive k per lane) is one 16-byte read.
+//   * MN-major ([k][cols]): 32 k rows x 512 bytes; chunk c of row k sits at chunk c ^ (2 (k & 3)).  A fragment is
+//     built by two transposing reads (ds_read_b64_tr_b16): in each 16-lane group, lane k' points at row k0 + k'/4,
+//     columns n0 + 4 (k' % 4) .. +3, and lane i receives column n0 + i of rows k0 .. k0 + 3.
+// Both swizzles make the 16 lanes served together touch distinct bank groups.
+//
+// Pipeline per K tile kt (LDS stage kt & 1 holds tile kt, fragment set F holds its fragments, registers P hold
+// tile kt+1):  P -> stage (kt+1)&1;  global loads of tile kt+2 -> P;  barrier;  fragments of tile kt+1 -> F';
+// 64 MFMAs on F.  Every LDS read is issued one MFMA burst (1024 cycles) ahead of its use.
+// Two GEMMs of the same layout can share one launch (the two weight gradients): workgroups [0, tiles0) take the
+// first, the rest the second.
+// ------------------------------------------------------------------------------------------------------------------
+template <int TM, int TN>
+__device__ __forceinline__ void mfma_block(f32x4_t (&acc)[TM][TN], const bf16x8_t (&af)[TM],
+                                           const bf16x8_t (&bfr)[TN]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+}
+
+template <int T0, int T1, int TN, int TM>
+__device__ __forceinline__ void mfma_rows(f32x4_t (&acc)[TM][TN], const bf16x8_t (&af)[TM], const bf16x8_t (&bfr)[TN]) {
+#pragma unroll
+  for (int i = T0; i < T1; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+}
+
+struct GemmPair {
+  GemmParams g[2];
+  int tiles0;
+};
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+constexpr int BK2 = 32;
+
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 3; }   // K-major tiles (4 chunks per row)
+__device__ __forceinline__ int swz_mn(int k) { return 2 * (k & 3); }   // MN-major tiles (32 chunks per row)
+
+// Global -> register prefetch of one operand tile (256 rows/cols x 32 k), 4 x 16 bytes per thread, held in native
+// vector registers (u32x4_t).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool KMAJ, bool SWIG>
+struct Tile2;
+
+template <bool SWIG>
+struct Tile2<true, SWIG> {  // K-major: thread t: chunk t & 3 of rows (t >> 2) + 64 i
+  const uint16_t* ptr;      // row (t >> 2) of the tile; rows + 64 i are ld * 64 i further (clamped rows: see below)
+  int64_t step[4];
+  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld, int tile, int rows, int fhalf, int tid) {
+    const int r0 = min(tile * 256 + (tid >> 2), rows - 1);
+    ptr = b + (int64_t)r0 * ld + (tid & 3) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) step[i] = (int64_t)(min(tile * 256 + (tid >> 2) + 64 * i, rows - 1) - r0) * ld;
+  }
+  __device__ __forceinline__ void load(u32x4_t (&v)[4], int64_t ld, int k0) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(ptr + step[i] + k0);
+  }
+  __device__ __forceinline__ void store(const u32x4_t (&v)[4], u32x4_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 2) + 64 * i;
+      lds[r * 4 + ((tid & 3) ^ swz_k(r))] = v[i];
+    }
+  }
+};
+
+template <bool SWIG>
+struct Tile2<false, SWIG> {  // MN-major: thread t: chunk t & 31 of k rows (t >> 5) + 8 i
+  const uint16_t* ptr;
+  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld, int tile, int rows, int fhalf, int tid) {
+    const int c = (tid & 31) * 8;  // first of 8 logical columns
+    int col;
+    if (SWIG) {
+      // per 128-column wave slice: 64 gate columns then the same 64 up columns
+      const int wn = c / 128, cw = c % 128;
+      const int half = cw / 64, j = min(tile * 128 + wn * 64 + (cw % 64), fhalf - 8);
+      col = half * fhalf + j;
+    } else {
+      col = min(tile * 256 + c, rows - 8);
+    }
+    ptr = b + col + (int64_t)(tid >> 5) * ld;
+  }
+  __device__ __forceinline__ void load(u32x4_t (&v)[4], int64_t ld, int k0) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(ptr + (int64_t)(k0 + 8 * i) * ld);
+  }
+  __device__ __forceinline__ void store(const u32x4_t (&v)[4], u32x4_t* lds, int tid) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = (tid >> 5) + 8 * i;
+      lds[k * 32 + ((tid & 31) ^ swz_mn(k))] = v[i];
+    }
+  }
+};
+
+// Fragments of one operand for a wave's 128 rows (8 subtiles of 16) over the tile's 32 k.
+template <bool KMAJ>
+__device__ __forceinline__ void frags2(const u32x4_t* lds, int rbase, int lane, bf16x8_t (&f)[8]) {
+  if constexpr (KMAJ) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = rbase + i * 16 + (lane & 15);
+      f[i] = __builtin_bit_cast(bf16x8_t, lds[r * 4 + ((lane >> 4) ^ swz_k(r))]);
+    }
+  } else {
+    const int g = lane >> 4, kq = lane & 15;
+    const int k1 = 8 * g + (kq >> 2), k2 = k1 + 4;
+    const int cq = 4 * (kq & 3);  // column offset of this lane's 4-element piece
+    const char* base = reinterpret_cast<const char*>(lds);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int col = rbase + i * 16 + cq;
+      const int ch = col >> 3, hf = (col >> 2) & 1;
+      const int o1 = k1 * 512 + ((ch ^ swz_mn(k1)) << 4) + (hf << 3);
+      const int o2 = k2 * 512 + ((ch ^ swz_mn(k2)) << 4) + (hf << 3);
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o1));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o2));
+      typedef short v8i16_t __attribute__((ext_vector_type(8)));
+      const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f[i] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_hw(lo) | (f32_to_bf16_hw(hi) << 16);
+}
+__device__ __forceinline__ void stg_bf16x2(void* p, int64_t i, float lo, float hi) {
+  *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + i) = pack_bf16x2(lo, hi);
+}
+__device__ __forceinline__ float2 ldg_bf16x2(const void* p, int64_t i) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + i);
+  return make_float2(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
+}
+
+// One wave's 16 x 128 chunk of fp32 results in LDS (pitch ep_pitch) -> epilogue -> HBM.  Plain epilogues: lane l
+// owns columns 2l, 2l+1 of each row.  SwiGLU forward: the wave's 128 columns are 64 gate then 64 up columns of the
+// same 64 outputs j; lane l owns output j = l.
+__device__ __forceinline__ float2 lds_bf16x2(const uint16_t* ax, int i) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(ax + i);
+  return make_float2(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
+}
+
+// ax: this wave's 16 x 128 tile of the epilogue's auxiliary input (U for act', [gate | up] at +2048 for SwiGLU),
+// staged in LDS.
+template <int EPI>
+__device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float* ep, int ep_pitch, int m0, int tile_n,
+                                               int wn, int lane, const uint16_t* ax) {
+  if constexpr (EPI == EPI_SWIGLU_FWD) {
+    const int j = tile_n * 128 + wn * 64 + lane;
+    if (j >= p.fhalf) return;
+    const float bg = p.bias ? bf16_to_f32(ldg_bf16(p.bias, j)) : 0.f;
+    const float bu = p.bias ? bf16_to_f32(ldg_bf16(p.bias, p.fhalf + j)) : 0.f;
+    const int rows = min(16, p.M - m0);
+    for (int r = 0; r < rows; ++r) {
+      const float g = ep[r * ep_pitch + lane] + bg;
+      const float u = ep[r * ep_pitch + 64 + lane] + bu;
+      const int64_t m = m0 + r;
+      stg_bf16(p.C, m * p.ldc + j, g);
+      stg_bf16(p.C, m * p.ldc + p.fhalf + j, u);
+      stg_bf16(p.C2, m * p.ldc2 + j, g * act_sigmoid(g) * u);
+    }
+  } else {
+    const int col = tile_n * 256 + wn * 128 + 2 * lane;
+    if (col >= p.N) return;  // N % 8 == 0: a column pair is entirely in or out
+    float b0 = 0.f, b1 = 0.f;
+    if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_ACT) {
+      if (p.bias) {
+        const float2 bb = ldg_bf16x2(p.bias, col);
+        b0 = bb.x;
+        b1 = bb.y;
+      }
+    }
+    const int rows = min(16, p.M - m0);
+    for (int r = 0; r < rows; ++r) {
+      const float v0 = ep[r * ep_pitch + 2 * lane], v1 = ep[r * ep_pitch + 2 * lane + 1];
+      const int64_t m = m0 + r;
+      if constexpr (EPI == EPI_STORE) {
+        stg_bf16x2(p.C, m * p.ldc + col, v0, v1);
+      } else if constexpr (EPI == EPI_BIAS) {
+        stg_bf16x2(p.C, m * p.ldc + col, v0 + b0, v1 + b1);
+      } else if constexpr (EPI == EPI_BIAS_ACT) {
+        const float u0 = v0 + b0, u1 = v1 + b1;
+        stg_bf16x2(p.C, m * p.ldc + col, u0, u1);
+        stg_bf16x2(p.C2, m * p.ldc2 + col, act_apply(p.act, u0), act_apply(p.act, u1));
+      } else if constexpr (EPI == EPI_ACT_BWD) {
+        const float2 u = lds_bf16x2(ax, r * 128 + 2 * lane);
+        stg_bf16x2(p.C, m * p.ldc + col, v0 * act_grad(p.act, u.x), v1 * act_grad(p.act, u.y));
+      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        const float2 g = lds_bf16x2(ax, r * 128 + 2 * lane);
+        const float2 u = lds_bf16x2(ax, 2048 + r * 128 + 2 * lane);
+        const float s0 = act_sigmoid(g.x), s1 = act_sigmoid(g.y);
+        stg_bf16x2(p.C, m * p.ldc + col, v0 * u.x * s0 * (1.f + g.x * (1.f - s0)),
+                   v1 * u.y * s1 * (1.f + g.y * (1.f - s1)));
+        stg_bf16x2(p.C, m * p.ldc + p.fhalf + col, v0 * g.x * s0, v1 * g.y * s1);
+      }
+    }
+  }
+}
+
+template <bool AK, bool BKM, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 8, TN = 8;
+  constexpr int STAGE = (BM + BN) * BK2 * 2 / 16;  // uint4 per stage
+  constexpr bool SWIG = (EPI == EPI_SWIGLU_FWD);
+  constexpr int EP = 132;                            // epilogue fp32 pitch: rows 4 apart land 16 banks apart
+  constexpr int NAUX = EPI == EPI_SWIGLU_BWD ? 8 : EPI == EPI_ACT_BWD ? 4 : 0;  // 16-byte aux loads per lane
+  constexpr int EPW = 16 * EP * 4 + NAUX * 1024;     // epilogue bytes per wave
+  constexpr int LDS_U4 = (2 * STAGE * 16 > 4 * EPW ? 2 * STAGE * 16 : 4 * EPW) / 16;
+  __shared__ u32x4_t lds[LDS_U4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- problem and tile: XCD-aware remap over the whole launch, then split between the two problems
+  int bid = blockIdx.x;
+  {
+    const int nb = gridDim.x;
+    const int q = nb / 8, r = nb % 8;
+    const int xcd = bid % 8, idx = bid / 8;
+    bid = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  }
+  const int which = bid < pp.tiles0 ? 0 : 1;
+  const GemmParams& p = pp.g[which];
+  if (which) bid -= pp.tiles0;
+  const int nbm = (p.M + BM - 1) / BM;
+  const int nbn = SWIG ? (p.fhalf + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
+  const int group = bid / (GROUP_M * nbn);
+  const int first_m = group * GROUP_M;
+  const int gsz = min(nbm - first_m, GROUP_M);
+  const int tile_m = first_m + (bid % (GROUP_M * nbn)) % gsz;
+  const int tile_n = (bid % (GROUP_M * nbn)) / gsz;
+
+  Tile2<AK, false> ta;
+  Tile2<BKM, SWIG> tb;
+  ta.init(static_cast<const uint16_t*>(p.A), p.lda, tile_m, p.M, p.fhalf, tid);
+  tb.init(static_cast<const uint16_t*>(p.B), p.ldb, tile_n, p.N, p.fhalf, tid);
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = p.K / BK2;
+  u32x4_t* As0 = &lds[0];
+  u32x4_t* Bs0 = &lds[BM * BK2 * 2 / 16];
+  // two prefetch register sets: tile j+1 waits in set (j+1)&1 from iteration j-2 until it is staged at iteration j
+  u32x4_t pa0[4], pb0[4], pa1[4], pb1[4];
+
+  ta.load(pa0, p.lda, 0);
+  tb.load(pb0, p.ldb, 0);
+  ta.store(pa0, As0, tid);
+  tb.store(pb0, Bs0, tid);
+  ta.load(pa1, p.lda, min(1, nk - 1) * BK2);
+  tb.load(pb1, p.ldb, min(1, nk - 1) * BK2);
+  ta.load(pa0, p.lda, min(2, nk - 1) * BK2);
+  tb.load(pb0, p.ldb, min(2, nk - 1) * BK2);
+  __syncthreads();
+  bf16x8_t fa[TM], fb[TN], ga[TM], gb[TN];
+  frags2<AK>(As0, wm * WM, lane, fa);
+  frags2<BKM>(Bs0, wn * WN, lane, fb);
+
+  // Iteration j (current fragments FC = tile j): first half of tile j's MFMAs, with tile j+1 staged from
+  // registers PS into LDS stage (j+1)&1 and tile j+3 loaded into PS behind them; barrier; fragments of tile j+1
+  // into FN; second half of the MFMAs.  Loads that would run past the last tile re-read it (in bounds).
+#define TP_GEMM_STEP(J, PSA, PSB, FCA, FCB, FNA, FNB)                                            \
+  {                                                                                              \
+    const int j_ = (J);                                                                          \
+    u32x4_t* An_ = As0 + ((j_ + 1) & 1) * STAGE;                                                 \
+    u32x4_t* Bn_ = Bs0 + ((j_ + 1) & 1) * STAGE;                                                 \
+    mfma_rows<0, TM / 2, TN>(acc, FCA, FCB);                                                     \
+    ta.store(PSA, An_, tid);                                                                     \
+    tb.store(PSB, Bn_, tid);                                                                     \
+    ta.load(PSA, p.lda, min(j_ + 3, nk - 1) * BK2);                                              \
+    tb.load(PSB, p.ldb, min(j_ + 3, nk - 1) * BK2);                                              \
+    __syncthreads();                                                                             \
+    frags2<AK>(An_, wm * WM, lane, FNA);                                                         \
+    frags2<BKM>(Bn_, wn * WN, lane, FNB);                                                        \
+    mfma_rows<TM / 2, TM, TN>(acc, FCA, FCB);                                                    \
+  }
+  // nk is even; the last step stages and reads a tile nobody uses (in bounds) instead of branching
+  for (int kt = 0; kt < nk; kt += 2) {
+    TP_GEMM_STEP(kt, pa1, pb1, fa, fb, ga, gb)
+    TP_GEMM_STEP(kt + 1, pa0, pb0, ga, gb, fa, fb)
+  }
+#undef TP_GEMM_STEP
+
+  // ---- epilogue, staged through LDS one 16-row chunk at a time: each wave writes the fp32 accumulators of its
+  // rows 16 tm .. 16 tm + 15 (all 128 of its columns) to a padded buffer of its own, then walks the chunk row by
+  // row with consecutive lanes on consecutive column pairs, so the math runs in a compact loop and every row
+  // leaves as one contiguous 256-byte store.
+  __syncthreads();
+  float* ep = reinterpret_cast<float*>(reinterpret_cast<char*>(&lds[0]) + wave * EPW);
+  uint16_t* ax = reinterpret_cast<uint16_t*>(ep + 16 * EP);
+  const int row0 = tile_m * BM + wm * WM;
+  // aux prefetch: lane covers rows lane/16 + 4q of the chunk, 8 columns at 8 (lane % 16); q >= 4: the up half
+  u32x4_t xr[NAUX > 0 ? NAUX : 1];
+  const int xcol = min(tile_n * BN + wn * WN + 8 * (lane & 15), p.N - 8);
+#define TP_AUX_LOAD(TMC)                                                                                       \
+  _Pragma("unroll") for (int q = 0; q < NAUX; ++q) {                                                           \
+    const int xrow = min(row0 + (TMC) * 16 + (lane >> 4) + 4 * (q & 3), p.M - 1);                              \
+    xr[q] = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p.aux) + (int64_t)xrow * p.ldaux +  \
+                                             (q >> 2) * p.fhalf + xcol);                                       \
+  }
+  if constexpr (NAUX > 0) { TP_AUX_LOAD(0) }
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ep[((lane >> 4) * 4 + e) * EP + tn * 16 + (lane & 15)] = acc[tm][tn][e];
+    if constexpr (NAUX > 0) {
+#pragma unroll
+      for (int q = 0; q < NAUX; ++q)
+        *reinterpret_cast<u32x4_t*>(ax + (q >> 2) * 2048 + ((lane >> 4) + 4 * (q & 3)) * 128 + 8 * (lane & 15)) = xr[q];
+      if (tm + 1 < TM) { TP_AUX_LOAD(tm + 1) }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    epilogue_chunk<EPI>(p, ep, EP, row0 + tm * 16, tile_n, wn, lane, ax);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+#undef TP_AUX_LOAD
+}
+
+// ------------------------------------------------------------------------------------------------------------------
 // Tile configurations and dispatch.
 // ------------------------------------------------------------------------------------------------------------------
 struct Cfg {
@@ -361,10 +705,33 @@ hipError_t launch_one(const GemmParams& p, hipStream_t st) {
                    dim3(NWM * NWN * 64), 0, st, p);
 }
 
+int big_tiles(const GemmParams& p, bool swig) {
+  const int nbm = (p.M + 255) / 256;
+  const int nbn = swig ? (p.fhalf + 127) / 128 : (p.N + 255) / 256;
+  return nbm * nbn;
+}
+
+template <bool AK, bool BKM, int EPI>
+hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st) {
+  GemmPair pp;
+  pp.g[0] = p0;
+  pp.g[1] = p1 ? *p1 : p0;
+  pp.tiles0 = big_tiles(p0, EPI == EPI_SWIGLU_FWD);
+  const int total = pp.tiles0 + (p1 ? big_tiles(*p1, EPI == EPI_SWIGLU_FWD) : 0);
+  static const std::string name = std::string("gemm_bf16_big_") + (AK ? "K" : "M") + (BKM ? "K" : "M") + "_" +
+                                  kEpiNames[EPI];
+  static const std::string name2 = std::string("gemm_bf16_big_pair_") + (AK ? "K" : "M") + (BKM ? "K" : "M") + "_" +
+                                   kEpiNames[EPI];
+  return TP_LAUNCH(p1 ? name2.c_str() : name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI>), dim3((unsigned)total),
+                   dim3(256), 0, st, pp);
+}
+
 template <bool AK, bool BKM, int EPI>
 hipError_t launch_cfg(int ci, const GemmParams& p, hipStream_t st) {
   switch (ci) {
-    case 0: return launch_one<256, 256, 2, 4, AK, BKM, EPI>(p, st);
+    case 0:
+      if (p.K % (2 * BK2) == 0) return launch_big<AK, BKM, EPI>(p, nullptr, st);
+      return launch_one<256, 256, 2, 4, AK, BKM, EPI>(p, st);
     case 1: return launch_one<256, 128, 2, 2, AK, BKM, EPI>(p, st);
     case 2: return launch_one<128, 128, 2, 2, AK, BKM, EPI>(p, st);
     default: return launch_one<64, 64, 2, 2, AK, BKM, EPI>(p, st);
@@ -397,6 +764,19 @@ hipError_t gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi,
   }
   if (!a_kmajor && !b_kmajor && epi == EPI_STORE) return launch_cfg<false, false, EPI_STORE>(ci, p, st);  // wgrad
   return hipErrorInvalidValue;
+}
+
+// The two weight-gradient GEMMs of a backward (both MN-major x MN-major, same K = s*b): one launch over both tile
+// sets when the large-tile kernel applies to both and together they fill the GPU better than each alone.
+hipError_t gemm_bf16_wgrad_pair(const GemmParams& p0, const GemmParams& p1, hipStream_t st) {
+  if (p0.M > 0 && p0.N > 0 && p1.M > 0 && p1.N > 0 && p0.K == p1.K && p0.K % (2 * BK2) == 0) {
+    const int t = big_tiles(p0, false) + big_tiles(p1, false);
+    const int c0 = choose_cfg(p0.M, 0, p0.N, false, 0), c1 = choose_cfg(p1.M, 0, p1.N, false, 0);
+    if (t >= kNumCUs * 3 / 4 || (c0 == 0 && c1 == 0)) return launch_big<false, false, EPI_STORE>(p0, &p1, st);
+  }
+  hipError_t e = gemm_bf16(p0, false, false, EPI_STORE, st);
+  if (e == hipSuccess) e = gemm_bf16(p1, false, false, EPI_STORE, st);
+  return e;
 }
 
 }  // namespace tp

@@ -268,8 +268,14 @@ int tp_mlp_bwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const 
 
   auto gemm = dtype == TP_BF16 ? tp::gemm_bf16 : tp::gemm_f32;
   hipError_t e = gemm(gy, true, true, epiy, stream);
-  if (e == hipSuccess) e = gemm(gb, false, false, tp::EPI_STORE, stream);
-  if (e == hipSuccess) e = gemm(ga, false, false, tp::EPI_STORE, stream);
+  if (e == hipSuccess) {
+    if (dtype == TP_BF16) {
+      e = tp::gemm_bf16_wgrad_pair(gb, ga, stream);
+    } else {
+      e = gemm(gb, false, false, tp::EPI_STORE, stream);
+      if (e == hipSuccess) e = gemm(ga, false, false, tp::EPI_STORE, stream);
+    }
+  }
   if (e == hipSuccess && da_i != nullptr) e = tp::colsum(dtype, dU_ws, M, n1, da_i, stream);
   if (e == hipSuccess) e = gemm(gx, true, true, tp::EPI_STORE, stream);
   return hip_status(e);

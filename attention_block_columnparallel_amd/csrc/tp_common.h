@@ -118,6 +118,7 @@ struct GemmParams {
 
 // Launchers (return hipGetLastError after the launch).
 hipError_t gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, hipStream_t st);
+hipError_t gemm_bf16_wgrad_pair(const GemmParams& p0, const GemmParams& p1, hipStream_t st);
 hipError_t gemm_f32(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, hipStream_t st);
 hipError_t colsum(tp_dtype dt, const void* x, int64_t rows, int64_t cols, void* out, hipStream_t st);
 

@@ -162,14 +162,15 @@ def main(argv=None) -> int:
         k["avg_us"] = 1e3 * k["total_ms"] / k["launches"]
         k["share"] = k["total_ms"] / (ms_per_step * args.steps)
         if name.startswith("gemm"):
-            k["tflops"] = gemm_flops / (k["avg_us"] * 1e-6) / 1e12
+            k["flops_per_launch"] = gemm_flops * (2 if "_pair_" in name else 1)
+            k["tflops"] = k["flops_per_launch"] / (k["avg_us"] * 1e-6) / 1e12
         if name == rs_name:
             k["gbps"] = rs_bytes / (k["avg_us"] * 1e-6) / 1e9
     dom = max((n for n in kern if n.startswith("gemm")), key=lambda n: kern[n]["total_ms"])
     ach = kern[dom]["tflops"]
     roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": round(ach * 1e12 / PEAK_BF16_FLOPS, 4), "traffic": None, "kernel": dom,
-                "flops_per_launch": gemm_flops, "avg_us": round(kern[dom]["avg_us"], 2)}
+                "flops_per_launch": kern[dom]["flops_per_launch"], "avg_us": round(kern[dom]["avg_us"], 2)}
     gemm_ms = sum(k["total_ms"] for n, k in kern.items() if n.startswith("gemm")) / args.steps
     rs = kern[rs_name]
     out = {

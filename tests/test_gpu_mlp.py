@@ -146,11 +146,19 @@ def _sampled_check(L, w, r, nrows=192, ncols=24, with_bias=False, seed=0):
         check_close(f64(got["da"])[wc["sel"]], wc["da_cols"], "bf16", "da")
 
 
-def test_bf16_large_ragged_sampled(L):
-    # large enough that the 256x256 tile configuration is chosen, with ragged edges in M, N and K
+def test_bf16_large_ragged_k_sampled(L):
+    # large enough that 256x256 tiles are chosen, ragged in M, N and K (K % 32 != 0: the general-K kernel)
     w = TI.Workload("large_ragged", "mlp", s=2043, b=8, h=1000, ffn=2 * 2040, t=2, act="gelu", dtype="bf16")
     say("bf16 MLP large ragged M=16344 h=1000 f_l=2040 (sampled)")
     _sampled_check(L, w, 1, with_bias=True, seed=7)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_bf16_large_ragged_mn_sampled(L, act):
+    # K % 32 == 0 everywhere (the large-tile kernel) with ragged M = 16352 and N in {1056, 2080, 2 x 2080}
+    w = TI.Workload("large_ragged_mn", "mlp", s=2044, b=8, h=1056, ffn=2 * 2080, t=2, act=act, dtype="bf16")
+    say(f"bf16 MLP large ragged M=16352 h=1056 f_l=2080 act={act} (sampled)")
+    _sampled_check(L, w, 0, with_bias=True, seed=8)
 
 
 @pytest.mark.parametrize("name,rank", [("mlp_h3072_ffn12288_t8_b8_s1024", 5),
