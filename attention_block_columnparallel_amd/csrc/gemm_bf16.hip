@@ -360,64 +360,74 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 constexpr int BK2 = 32;
 
 __device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 3; }   // K-major tiles (4 chunks per row)
-__device__ __forceinline__ int swz_mn(int k) { return 2 * (k & 3); }   // MN-major tiles (32 chunks per row)
+__device__ __forceinline__ int swz_mn(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }  // MN-major tiles
 
-// Global -> register prefetch of one operand tile (256 rows/cols x 32 k), 4 x 16 bytes per thread, held in native
-// vector registers (u32x4_t).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte address m0 + 16 l.  Issued as
+// inline assembly so that the compiler does not wait for these copies at every barrier; the kernel waits for them
+// itself (s_waitcnt vmcnt) before the barrier that publishes a stage.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_vmcnt16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One operand tile (256 rows or columns x 32 k) is 16 KB = 16 wave-wide copies of 1 KB; wave w issues copies
+// 4w .. 4w+3.  The source address of each lane is chosen so that the lane's fixed LDS slot receives the chunk the
+// swizzled layout puts there.
 template <bool KMAJ, bool SWIG>
-struct Tile2;
+struct Dma;
 
 template <bool SWIG>
-struct Tile2<true, SWIG> {  // K-major: thread t: chunk t & 3 of rows (t >> 2) + 64 i
-  const uint16_t* ptr;      // row (t >> 2) of the tile; rows + 64 i are ld * 64 i further (clamped rows: see below)
-  int64_t step[4];
-  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld, int tile, int rows, int fhalf, int tid) {
-    const int r0 = min(tile * 256 + (tid >> 2), rows - 1);
-    ptr = b + (int64_t)r0 * ld + (tid & 3) * 8;
+struct Dma<true, SWIG> {  // K-major: copy i holds rows 16 i .. 16 i + 15 (64 bytes each)
+  const uint16_t* src[4];
+  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld, int tile, int rows, int fhalf, int wave,
+                                       int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) step[i] = (int64_t)(min(tile * 256 + (tid >> 2) + 64 * i, rows - 1) - r0) * ld;
-  }
-  __device__ __forceinline__ void load(u32x4_t (&v)[4], int64_t ld, int k0) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(ptr + step[i] + k0);
-  }
-  __device__ __forceinline__ void store(const u32x4_t (&v)[4], u32x4_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (tid >> 2) + 64 * i;
-      lds[r * 4 + ((tid & 3) ^ swz_k(r))] = v[i];
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * (4 * wave + q) + (lane >> 2);
+      const int c = (lane & 3) ^ swz_k(r);
+      const int row = min(tile * 256 + r, rows - 1);
+      src[q] = b + (int64_t)row * ld + c * 8;
     }
+  }
+  __device__ __forceinline__ void issue(int64_t ld, int k0, uint32_t lds_op, int wave) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dma16(src[q] + k0, __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
   }
 };
 
 template <bool SWIG>
-struct Tile2<false, SWIG> {  // MN-major: thread t: chunk t & 31 of k rows (t >> 5) + 8 i
-  const uint16_t* ptr;
-  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld, int tile, int rows, int fhalf, int tid) {
-    const int c = (tid & 31) * 8;  // first of 8 logical columns
-    int col;
-    if (SWIG) {
-      // per 128-column wave slice: 64 gate columns then the same 64 up columns
-      const int wn = c / 128, cw = c % 128;
-      const int half = cw / 64, j = min(tile * 128 + wn * 64 + (cw % 64), fhalf - 8);
-      col = half * fhalf + j;
-    } else {
-      col = min(tile * 256 + c, rows - 8);
-    }
-    ptr = b + col + (int64_t)(tid >> 5) * ld;
-  }
-  __device__ __forceinline__ void load(u32x4_t (&v)[4], int64_t ld, int k0) const {
+struct Dma<false, SWIG> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 bytes each)
+  const uint16_t* src[4];
+  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld, int tile, int rows, int fhalf, int wave,
+                                       int lane) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4_t*>(ptr + (int64_t)(k0 + 8 * i) * ld);
-  }
-  __device__ __forceinline__ void store(const u32x4_t (&v)[4], u32x4_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = (tid >> 5) + 8 * i;
-      lds[k * 32 + ((tid & 31) ^ swz_mn(k))] = v[i];
+    for (int q = 0; q < 4; ++q) {
+      const int k = 2 * (4 * wave + q) + (lane >> 5);
+      const int cl = 8 * ((lane & 31) ^ swz_mn(k));  // first logical column of the chunk this slot holds
+      int col;
+      if (SWIG) {
+        // per 128-column wave slice: 64 gate columns then the same 64 up columns
+        const int wn = cl / 128, cw = cl % 128;
+        const int half = cw / 64, jj = min(tile * 128 + wn * 64 + (cw % 64), fhalf - 8);
+        col = half * fhalf + jj;
+      } else {
+        col = min(tile * 256 + cl, rows - 8);
+      }
+      src[q] = b + col + (int64_t)k * ld;
     }
+  }
+  __device__ __forceinline__ void issue(int64_t ld, int k0, uint32_t lds_op, int wave) const {
+    const int64_t off = (int64_t)k0 * ld;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dma16(src[q] + off, __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
   }
 };
 
@@ -529,12 +539,13 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
 template <bool AK, bool BKM, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 8, TN = 8;
-  constexpr int STAGE = (BM + BN) * BK2 * 2 / 16;  // uint4 per stage
+  constexpr int NSTAGE = 4;                         // LDS stages of one 32-deep K tile (A then B)
+  constexpr int STAGE_B = (BM + BN) * BK2 * 2;      // bytes per stage
   constexpr bool SWIG = (EPI == EPI_SWIGLU_FWD);
   constexpr int EP = 132;                            // epilogue fp32 pitch: rows 4 apart land 16 banks apart
   constexpr int NAUX = EPI == EPI_SWIGLU_BWD ? 8 : EPI == EPI_ACT_BWD ? 4 : 0;  // 16-byte aux loads per lane
   constexpr int EPW = 16 * EP * 4 + NAUX * 1024;     // epilogue bytes per wave
-  constexpr int LDS_U4 = (2 * STAGE * 16 > 4 * EPW ? 2 * STAGE * 16 : 4 * EPW) / 16;
+  constexpr int LDS_U4 = (NSTAGE * STAGE_B > 4 * EPW ? NSTAGE * STAGE_B : 4 * EPW) / 16;
   __shared__ u32x4_t lds[LDS_U4];
 
   const int tid = threadIdx.x;
@@ -560,10 +571,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   const int tile_m = first_m + (bid % (GROUP_M * nbn)) % gsz;
   const int tile_n = (bid % (GROUP_M * nbn)) / gsz;
 
-  Tile2<AK, false> ta;
-  Tile2<BKM, SWIG> tb;
-  ta.init(static_cast<const uint16_t*>(p.A), p.lda, tile_m, p.M, p.fhalf, tid);
-  tb.init(static_cast<const uint16_t*>(p.B), p.ldb, tile_n, p.N, p.fhalf, tid);
+  Dma<AK, false> da;
+  Dma<BKM, SWIG> db;
+  da.init(static_cast<const uint16_t*>(p.A), p.lda, tile_m, p.M, p.fhalf, wave, lane);
+  db.init(static_cast<const uint16_t*>(p.B), p.ldb, tile_n, p.N, p.fhalf, wave, lane);
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -571,49 +582,50 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = p.K / BK2;
-  u32x4_t* As0 = &lds[0];
-  u32x4_t* Bs0 = &lds[BM * BK2 * 2 / 16];
-  // two prefetch register sets: tile j+1 waits in set (j+1)&1 from iteration j-2 until it is staged at iteration j
-  u32x4_t pa0[4], pb0[4], pa1[4], pb1[4];
+  const int nk = p.K / BK2;  // even
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
+  auto stage_a = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B); };
+  auto stage_b = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B + BM * BK2 * 2); };
+  // every iteration issues exactly 8 copies per wave (past the last tile it re-copies tile nk-1 into a free stage),
+  // so "tile j+1 has landed" is always "at most 16 copies outstanding"
+  auto issue_tile = [&](int kt) {
+    const int kc = min(kt, nk - 1);
+    const uint32_t sb = lds0 + (kt & (NSTAGE - 1)) * STAGE_B;
+    da.issue(p.lda, kc * BK2, sb, wave);
+    db.issue(p.ldb, kc * BK2, sb + BM * BK2 * 2, wave);
+  };
 
-  ta.load(pa0, p.lda, 0);
-  tb.load(pb0, p.ldb, 0);
-  ta.store(pa0, As0, tid);
-  tb.store(pb0, Bs0, tid);
-  ta.load(pa1, p.lda, min(1, nk - 1) * BK2);
-  tb.load(pb1, p.ldb, min(1, nk - 1) * BK2);
-  ta.load(pa0, p.lda, min(2, nk - 1) * BK2);
-  tb.load(pb0, p.ldb, min(2, nk - 1) * BK2);
+  issue_tile(0);
+  issue_tile(1);
+  issue_tile(2);
+  wait_vmcnt16();
   __syncthreads();
   bf16x8_t fa[TM], fb[TN], ga[TM], gb[TN];
-  frags2<AK>(As0, wm * WM, lane, fa);
-  frags2<BKM>(Bs0, wn * WN, lane, fb);
+  frags2<AK>(stage_a(0), wm * WM, lane, fa);
+  frags2<BKM>(stage_b(0), wn * WN, lane, fb);
 
-  // Iteration j (current fragments FC = tile j): first half of tile j's MFMAs, with tile j+1 staged from
-  // registers PS into LDS stage (j+1)&1 and tile j+3 loaded into PS behind them; barrier; fragments of tile j+1
-  // into FN; second half of the MFMAs.  Loads that would run past the last tile re-read it (in bounds).
-#define TP_GEMM_STEP(J, PSA, PSB, FCA, FCB, FNA, FNB)                                            \
+  // Iteration j (fragments FC = tile j): copy tile j+3 into stage (j+3)%4; first half of tile j's MFMAs; wait for
+  // this wave's copies of tile j+1; barrier; fragments of tile j+1 into FN; second half of the MFMAs.
+#define TP_GEMM_STEP(J, FCA, FCB, FNA, FNB)                                                      \
   {                                                                                              \
     const int j_ = (J);                                                                          \
-    u32x4_t* An_ = As0 + ((j_ + 1) & 1) * STAGE;                                                 \
-    u32x4_t* Bn_ = Bs0 + ((j_ + 1) & 1) * STAGE;                                                 \
+    issue_tile(j_ + 3);                                                                          \
     mfma_rows<0, TM / 2, TN>(acc, FCA, FCB);                                                     \
-    ta.store(PSA, An_, tid);                                                                     \
-    tb.store(PSB, Bn_, tid);                                                                     \
-    ta.load(PSA, p.lda, min(j_ + 3, nk - 1) * BK2);                                              \
-    tb.load(PSB, p.ldb, min(j_ + 3, nk - 1) * BK2);                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    wait_vmcnt16();                                                                              \
     __syncthreads();                                                                             \
-    frags2<AK>(An_, wm * WM, lane, FNA);                                                         \
-    frags2<BKM>(Bn_, wn * WN, lane, FNB);                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    frags2<AK>(stage_a((j_ + 1) & (NSTAGE - 1)), wm * WM, lane, FNA);                            \
+    frags2<BKM>(stage_b((j_ + 1) & (NSTAGE - 1)), wn * WN, lane, FNB);                           \
     mfma_rows<TM / 2, TM, TN>(acc, FCA, FCB);                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
   }
-  // nk is even; the last step stages and reads a tile nobody uses (in bounds) instead of branching
   for (int kt = 0; kt < nk; kt += 2) {
-    TP_GEMM_STEP(kt, pa1, pb1, fa, fb, ga, gb)
-    TP_GEMM_STEP(kt + 1, pa0, pb0, ga, gb, fa, fb)
+    TP_GEMM_STEP(kt, fa, fb, ga, gb)
+    TP_GEMM_STEP(kt + 1, ga, gb, fa, fb)
   }
 #undef TP_GEMM_STEP
+  wait_vmcnt0();
 
   // ---- epilogue, staged through LDS one 16-row chunk at a time: each wave writes the fp32 accumulators of its
   // rows 16 tm .. 16 tm + 15 (all 128 of its columns) to a padded buffer of its own, then walks the chunk row by
