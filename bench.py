@@ -10,7 +10,9 @@ kernel).  Inputs and weights are resident in HBM before the timed region; the sh
 Prints ONE JSON line.  value = algorithmic GEMM flops of the step / wall time of the step (whole job, including
 both reductions), in TFLOP/s.  roofline = the kernel with the largest share of the step's time, its algorithmic
 flops per launch over its average HIP-event duration inside the timed region, against the dense bf16 MFMA peak.
-rs_dim0 = the reduce-scatter kernel against HBM bandwidth.  cpu_baseline = the fp64 oracle on a bounded sample.
+rs_dim0 = the reduce-scatter kernel against HBM bandwidth.  traffic = HBM bytes per launch from the committed
+rocprofv3 counter summary under profiles/ (null once the kernel source differs from the one profiled).
+cpu_baseline = the fp64 oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -48,6 +50,26 @@ def blas_threads() -> int:
     except Exception:
         pass
     return os.cpu_count() or 1
+
+
+def profiled_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE,
+    scaled by a plain copy's readings), or None when there is none or the kernel's source has changed since."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    src = "comm_kernels.hip" if kernel.startswith("reduce") else "gemm_bf16.hip"
+    with open(os.path.join(root, "attention_block_columnparallel_amd", "csrc", src), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) == 4 and parts[0] == "traffic" and parts[1] == kernel:
+                return int(parts[2]) if parts[3] == sha else None
+    return None
 
 
 def cpu_baseline(w, inp, target_s: float) -> dict:
@@ -169,7 +191,7 @@ def main(argv=None) -> int:
     dom = max((n for n in kern if n.startswith("gemm")), key=lambda n: kern[n]["total_ms"])
     ach = kern[dom]["tflops"]
     roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                "frac": round(ach * 1e12 / PEAK_BF16_FLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(ach * 1e12 / PEAK_BF16_FLOPS, 4), "traffic": profiled_traffic(w.name, dom), "kernel": dom,
                 "flops_per_launch": kern[dom]["flops_per_launch"], "avg_us": round(kern[dom]["avg_us"], 2)}
     gemm_ms = sum(k["total_ms"] for n, k in kern.items() if n.startswith("gemm")) / args.steps
     rs = kern[rs_name]
@@ -192,7 +214,8 @@ def main(argv=None) -> int:
         "gemm_tflops_aggregate": round(step_flops / (gemm_ms * 1e-3) / 1e12, 2),
         "roofline": roofline,
         "rs_dim0": {"kernel": rs_name, "gbps": round(rs["gbps"], 1), "frac_hbm": round(rs["gbps"] * 1e9 / PEAK_HBM_BYTES, 4),
-                    "bytes_per_launch": rs_bytes, "avg_us": round(rs["avg_us"], 2)},
+                    "bytes_per_launch": rs_bytes, "avg_us": round(rs["avg_us"], 2),
+                    "traffic": profiled_traffic(w.name, rs_name)},
         "kernels": {n: {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in k.items()} for n, k in kern.items()},
     }
     if args.calib_copy_mib > 0:
