@@ -375,6 +375,7 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_vmcnt16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 
 // One operand tile (256 rows or columns x 32 k) is 16 KB = 16 wave-wide copies of 1 KB; wave w issues copies
 // 4w .. 4w+3.  The source address of each lane is chosen so that the lane's fixed LDS slot receives the chunk the
@@ -588,11 +589,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   auto stage_b = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B + BM * BK2 * 2); };
   // every iteration issues exactly 8 copies per wave (past the last tile it re-copies tile nk-1 into a free stage),
   // so "tile j+1 has landed" is always "at most 16 copies outstanding"
+  const int64_t lda = p.lda, ldb = p.ldb;  // held in registers: no argument loads inside the K loop
   auto issue_tile = [&](int kt) {
     const int kc = min(kt, nk - 1);
     const uint32_t sb = lds0 + (kt & (NSTAGE - 1)) * STAGE_B;
-    da.issue(p.lda, kc * BK2, sb, wave);
-    db.issue(p.ldb, kc * BK2, sb + BM * BK2 * 2, wave);
+    da.issue(lda, kc * BK2, sb, wave);
+    db.issue(ldb, kc * BK2, sb + BM * BK2 * 2, wave);
   };
 
   issue_tile(0);
@@ -604,20 +606,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   frags2<AK>(stage_a(0), wm * WM, lane, fa);
   frags2<BKM>(stage_b(0), wn * WN, lane, fb);
 
-  // Iteration j (fragments FC = tile j): copy tile j+3 into stage (j+3)%4; first half of tile j's MFMAs; wait for
-  // this wave's copies of tile j+1; barrier; fragments of tile j+1 into FN; second half of the MFMAs.
+  // Step j (fragments FC = k-tile j already in registers): wait until this wave's copies of k-tile j+1 have
+  // landed (k-tiles j+1 and j+2 were in flight, so at most 8 copies may remain) and barrier, which publishes k-tile
+  // j+1 and also proves every wave is done reading the stage k-tile j-1 used; copy k-tile j+3 into that stage; then
+  // the 64 MFMAs of k-tile j with the LDS reads of k-tile j+1's fragments spread over them (one read per RS MFMAs,
+  // leaving the last MFMAs to cover the read latency).
+  constexpr int NDS = (AK ? 8 : 16) + (BKM ? 8 : 16);  // LDS read instructions for one k-tile's fragments
+  constexpr int RS = NDS <= 24 ? 2 : 1;
 #define TP_GEMM_STEP(J, FCA, FCB, FNA, FNB)                                                      \
   {                                                                                              \
     const int j_ = (J);                                                                          \
-    issue_tile(j_ + 3);                                                                          \
-    mfma_rows<0, TM / 2, TN>(acc, FCA, FCB);                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                                           \
-    wait_vmcnt16();                                                                              \
+    wait_vmcnt8();                                                                               \
     __syncthreads();                                                                             \
     __builtin_amdgcn_sched_barrier(0);                                                           \
+    issue_tile(j_ + 3);                                                                          \
     frags2<AK>(stage_a((j_ + 1) & (NSTAGE - 1)), wm * WM, lane, FNA);                            \
     frags2<BKM>(stage_b((j_ + 1) & (NSTAGE - 1)), wn * WN, lane, FNB);                           \
-    mfma_rows<TM / 2, TM, TN>(acc, FCA, FCB);                                                    \
+    mfma_rows<0, TM, TN>(acc, FCA, FCB);                                                         \
+    _Pragma("unroll") for (int g_ = 0; g_ < NDS; ++g_) {                                         \
+      __builtin_amdgcn_sched_group_barrier(0x008, RS, 0);                                        \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
+    }                                                                                            \
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - RS * NDS, 0);                          \
     __builtin_amdgcn_sched_barrier(0);                                                           \
   }
   for (int kt = 0; kt < nk; kt += 2) {

@@ -28,11 +28,37 @@ __device__ __forceinline__ uint32_t f32_to_bf16_hw(float f) {
 }
 
 // ------------------------------------------------------------------------------------------------------------------
-// Element-wise activations (device math library for erf / exp / tanh).
+// Element-wise activations.
+//
+// GeLU (erf form) x * Phi(x) and its derivative Phi(x) + x * phi(x) take Phi from the rational approximation of
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26: for z >= 0,
+//   erfc(z) = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2) + eps(z),  t = 1 / (1 + p z),  |eps| <= 1.5e-7,
+// evaluated at z = |x| / sqrt(2), so exp(-z^2) = exp(-x^2 / 2) is also the Gaussian density's exponential.  One
+// hardware reciprocal, one hardware exp2 and five FMAs replace the device library's erff (whose cost dominated the
+// fused GeLU epilogues); the 1.5e-7 absolute error is far below bf16 output resolution.
 // ------------------------------------------------------------------------------------------------------------------
-__device__ __forceinline__ float act_gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+struct NormalParts {
+  float cdf;  // Phi(x)
+  float pdf;  // phi(x) = exp(-x^2/2) / sqrt(2 pi)
+};
+__device__ __forceinline__ NormalParts normal_parts(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.44269504088896341f);  // exp(-z^2)
+  float q = fmaf(1.061405429f, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  q = q * t * e;  // erfc(z)
+  NormalParts r;
+  r.cdf = x >= 0.0f ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
+  r.pdf = 0.39894228040143268f * e;  // a NaN x fails x >= 0 and reaches cdf through q
+  return r;
+}
+__device__ __forceinline__ float act_gelu(float x) { return x * normal_parts(x).cdf; }
 __device__ __forceinline__ float act_gelu_grad(float x) {
-  return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * expf(-0.5f * x * x);
+  const NormalParts n = normal_parts(x);
+  return fmaf(x, n.pdf, n.cdf);
 }
 __device__ __forceinline__ float act_gelu_tanh(float x) {
   float u = 0.79788456080286536f * (x + 0.044715f * x * x * x);
@@ -44,7 +70,10 @@ __device__ __forceinline__ float act_gelu_tanh_grad(float x) {
   float du = 0.79788456080286536f * (1.0f + 3.0f * 0.044715f * x * x);
   return 0.5f * (1.0f + th) + 0.5f * x * (1.0f - th * th) * du;
 }
-__device__ __forceinline__ float act_sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+// logistic sigmoid with the hardware exp2 and reciprocal (relative error a few ulp for |x| < 80; exact limits 0, 1)
+__device__ __forceinline__ float act_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.44269504088896341f));
+}
 
 __device__ __forceinline__ float act_apply(int act, float x) {
   switch (act) {
