@@ -4,19 +4,23 @@
 // ("Tensor Parallelism (TP) 与 Sequence Parallelism (SP)" §2; the backward section of the 111qqz
 // "tensor-parallelism-matrix-split" post).
 //
-// Design (one workgroup = one BM x BN output tile, NWM x NWN waves of 64 lanes, K stepped by 64):
-//   * Operand tiles are staged through LDS as [row][k] with 64 k per row (8 chunks of 16 bytes).  A K-major
-//     operand is copied chunk for chunk; an MN-major operand (the weight in X A_i, both operands of a wgrad) is
-//     read as 8(k) x 4(mn) blocks and transposed in registers before the LDS store, so every MFMA fragment is one
-//     16-byte LDS read no matter how the operand sits in HBM.
-//   * Chunk c of row r is stored at chunk c ^ ((r ^ (r >> 2)) & 7): eight consecutive rows read at one logical
-//     chunk hit eight distinct 16-byte bank groups, and so do the transposed stores of eight consecutive blocks.
-//   * Two LDS stages; the next K tile's global loads are issued into registers before the current tile's MFMAs
+// Two kernels.  The large-tile kernel (gemm_bf16_big_kernel: 256 x 256 tiles, one wave per SIMD with 128 x 128
+// each, a 4-stage LDS ring fed by direct global -> LDS copies, transposing LDS reads for MN-major operands) runs
+// every GEMM whose K is a multiple of 64 and whose tile count fills the GPU; its design is described above it.
+// The register-staged kernel (gemm_bf16_kernel) takes the rest:
+//   * one workgroup = one BM x BN output tile, NWM x NWN waves of 64 lanes, K stepped by 64;
+//   * operand tiles are staged through LDS as [row][k] with 64 k per row (8 chunks of 16 bytes).  A K-major
+//     operand is copied chunk for chunk; an MN-major operand is read as 8(k) x 4(mn) blocks and transposed in
+//     registers before the LDS store, so every MFMA fragment is one 16-byte LDS read;
+//   * chunk c of row r is stored at chunk c ^ ((r ^ (r >> 2)) & 7): eight consecutive rows read at one logical
+//     chunk hit eight distinct 16-byte bank groups, and so do the transposed stores of eight consecutive blocks;
+//   * two LDS stages; the next K tile's global loads are issued into registers before the current tile's MFMAs
 //     and written to the other stage after them, with one barrier per K tile.
-//   * Tiles are ordered XCD-aware: the hardware deals workgroup i to XCD i % 8, so the launch index is remapped
-//     to give each XCD a contiguous run of tiles, walked in groups of GROUP_M row tiles so the A rows and B
-//     columns an XCD touches stay in its own L2.
+// Both order tiles XCD-aware: the hardware deals workgroup i to XCD i % 8, so the launch index is remapped to give
+// each XCD a contiguous run of tiles, walked in groups of GROUP_M row tiles so the A rows and B columns an XCD
+// touches stay in its own L2.
 #include <string>
+#include <type_traits>
 
 #include "tp_common.h"
 
@@ -349,9 +353,19 @@ __device__ __forceinline__ void mfma_rows(f32x4_t (&acc)[TM][TN], const bf16x8_t
     for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
 }
 
+// Transposed 16x16 blocks: the B fragment goes first, so the accumulator holds (A B)^T block by block.
+template <int T0, int T1, int TN, int TM>
+__device__ __forceinline__ void mfma_rows_t(f32x4_t (&acc)[TM][TN], const bf16x8_t (&af)[TM],
+                                            const bf16x8_t (&bfr)[TN]) {
+#pragma unroll
+  for (int i = T0; i < T1; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+}
+
 struct GemmPair {
   GemmParams g[2];
-  int tiles0;
+  int tiles0, tiles1;
 };
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -383,31 +397,35 @@ __device__ __forceinline__ void wait_vmcnt8() { asm volatile("s_waitcnt vmcnt(8)
 template <bool KMAJ, bool SWIG>
 struct Dma;
 
+// Per-lane source positions are 32-bit element offsets from the operand's base (the launcher only takes this
+// kernel when every offset fits).
 template <bool SWIG>
 struct Dma<true, SWIG> {  // K-major: copy i holds rows 16 i .. 16 i + 15 (64 bytes each)
-  const uint16_t* src[4];
-  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld, int tile, int rows, int fhalf, int wave,
-                                       int lane) {
+  uint32_t off[4];
+  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 16 * (4 * wave + q) + (lane >> 2);
       const int c = (lane & 3) ^ swz_k(r);
       const int row = min(tile * 256 + r, rows - 1);
-      src[q] = b + (int64_t)row * ld + c * 8;
+      off[q] = (uint32_t)((int64_t)row * ld + c * 8);
     }
   }
-  __device__ __forceinline__ void issue(int64_t ld, int k0, uint32_t lds_op, int wave) const {
+  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, int k0, uint32_t lds_op, int wave) const {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      dma16(src[q] + k0, __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
+      dma16(base + (off[q] + (uint32_t)k0), __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
+  }
+  // copy q only; koff = k0 (the k offset of the k-tile)
+  __device__ __forceinline__ void issue1(int q, const uint16_t* base, uint32_t koff, uint32_t lds_op, int wave) const {
+    dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
   }
 };
 
 template <bool SWIG>
 struct Dma<false, SWIG> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 bytes each)
-  const uint16_t* src[4];
-  __device__ __forceinline__ void init(const uint16_t* b, int64_t ld, int tile, int rows, int fhalf, int wave,
-                                       int lane) {
+  uint32_t off[4];
+  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int k = 2 * (4 * wave + q) + (lane >> 5);
@@ -421,14 +439,18 @@ struct Dma<false, SWIG> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 by
       } else {
         col = min(tile * 256 + cl, rows - 8);
       }
-      src[q] = b + col + (int64_t)k * ld;
+      off[q] = (uint32_t)(col + (int64_t)k * ld);
     }
   }
-  __device__ __forceinline__ void issue(int64_t ld, int k0, uint32_t lds_op, int wave) const {
-    const int64_t off = (int64_t)k0 * ld;
+  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, int k0, uint32_t lds_op, int wave) const {
+    const uint32_t koff = (uint32_t)((int64_t)k0 * ld);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      dma16(src[q] + off, __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
+      dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
+  }
+  // copy q only; koff = k0 * ld (the element offset of the k-tile's first row)
+  __device__ __forceinline__ void issue1(int q, const uint16_t* base, uint32_t koff, uint32_t lds_op, int wave) const {
+    dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
   }
 };
 
@@ -459,6 +481,40 @@ __device__ __forceinline__ void frags2(const u32x4_t* lds, int rbase, int lane, 
       f[i] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
+}
+
+// One fragment (subtile i) of the same.
+template <bool KMAJ>
+__device__ __forceinline__ void frag1(const u32x4_t* lds, int rbase, int lane, int i, bf16x8_t& f) {
+  if constexpr (KMAJ) {
+    const int r = rbase + i * 16 + (lane & 15);
+    f = __builtin_bit_cast(bf16x8_t, lds[r * 4 + ((lane >> 4) ^ swz_k(r))]);
+  } else {
+    const int g = lane >> 4, kq = lane & 15;
+    const int k1 = 8 * g + (kq >> 2), k2 = k1 + 4;
+    const int col = rbase + i * 16 + 4 * (kq & 3);
+    const int ch = col >> 3, hf = (col >> 2) & 1;
+    const char* base = reinterpret_cast<const char*>(lds);
+    const int o1 = k1 * 512 + ((ch ^ swz_mn(k1)) << 4) + (hf << 3);
+    const int o2 = k2 * 512 + ((ch ^ swz_mn(k2)) << 4) + (hf << 3);
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o1));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o2));
+    typedef short v8i16_t __attribute__((ext_vector_type(8)));
+    const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    f = __builtin_bit_cast(bf16x8_t, w);
+  }
+}
+
+// Fragment reads of one k-tile, spread over the first NSEGR of a step's 8 MFMA segments: fragments are taken in
+// the order A0 B0 A1 B1 ... A7 B7 and fragment f goes to segment f * NSEGR / 16.
+constexpr int NSEGR = 6;
+constexpr int frag_seg(int f) { return f * NSEGR / 16; }
+template <bool AK, bool BKM>
+constexpr int seg_ds_count(int s) {
+  int n = 0;
+  for (int f = 0; f < 16; ++f)
+    if (frag_seg(f) == s) n += (f % 2 == 0) ? (AK ? 1 : 2) : (BKM ? 1 : 2);
+  return n;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -537,15 +593,21 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
   }
 }
 
+// Large-tile kernel: one 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (one wave per SIMD, fp32
+// accumulators in AGPRs), K in steps of 32 through a ring of 4 LDS stages fed by direct global -> LDS copies that
+// run 3 k-tiles ahead of the MFMAs.  The MFMAs take the B fragment first, so each 16 x 16 accumulator block is the
+// transposed product: lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3 of the wave's sub-tile,
+// which the epilogue stages through LDS with one 16-byte write per block.
 template <bool AK, bool BKM, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 8, TN = 8;
-  constexpr int NSTAGE = 4;                         // LDS stages of one 32-deep K tile (A then B)
-  constexpr int STAGE_B = (BM + BN) * BK2 * 2;      // bytes per stage
+  constexpr int NSTAGE = 4;
+  constexpr int D = NSTAGE - 1;                 // k-tiles in flight ahead of the one being multiplied
+  constexpr int STAGE_B = (BM + BN) * BK2 * 2;  // bytes per stage (A tile then B tile)
   constexpr bool SWIG = (EPI == EPI_SWIGLU_FWD);
-  constexpr int EP = 132;                            // epilogue fp32 pitch: rows 4 apart land 16 banks apart
+  constexpr int EP = 132;  // epilogue fp32 row pitch: 16-byte writes of 16 consecutive rows hit distinct banks
   constexpr int NAUX = EPI == EPI_SWIGLU_BWD ? 8 : EPI == EPI_ACT_BWD ? 4 : 0;  // 16-byte aux loads per lane
-  constexpr int EPW = 16 * EP * 4 + NAUX * 1024;     // epilogue bytes per wave
+  constexpr int EPW = 16 * EP * 4 + NAUX * 1024;                                  // epilogue bytes per wave
   constexpr int LDS_U4 = (NSTAGE * STAGE_B > 4 * EPW ? NSTAGE * STAGE_B : 4 * EPW) / 16;
   __shared__ u32x4_t lds[LDS_U4];
 
@@ -553,7 +615,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- problem and tile: XCD-aware remap over the whole launch, then split between the two problems
+  // ---- problem and tile: XCD-aware remap over the whole launch (the hardware deals workgroup i to XCD i % 8;
+  // each XCD gets a contiguous run of tiles), then split between the two problems of a pair
   int bid = blockIdx.x;
   {
     const int nb = gridDim.x;
@@ -574,8 +637,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
 
   Dma<AK, false> da;
   Dma<BKM, SWIG> db;
-  da.init(static_cast<const uint16_t*>(p.A), p.lda, tile_m, p.M, p.fhalf, wave, lane);
-  db.init(static_cast<const uint16_t*>(p.B), p.ldb, tile_n, p.N, p.fhalf, wave, lane);
+  da.init(p.lda, tile_m, p.M, p.fhalf, wave, lane);
+  db.init(p.ldb, tile_n, p.N, p.fhalf, wave, lane);
+  const uint16_t* const Ab = static_cast<const uint16_t*>(p.A);
+  const uint16_t* const Bb = static_cast<const uint16_t*>(p.B);
+  const int64_t lda = p.lda, ldb = p.ldb;  // held in registers: no argument loads inside the K loop
+  const int nk = p.K / BK2;                // even, > D
+
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
+  auto stage_a = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B); };
+  auto stage_b = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B + BM * BK2 * 2); };
+
+  // prologue: k-tiles 0 .. D-1 into stages 0 .. D-1
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    da.issue(Ab, lda, d * BK2, lds0 + d * STAGE_B, wave);
+    db.issue(Bb, ldb, d * BK2, lds0 + d * STAGE_B + BM * BK2 * 2, wave);
+  }
+  wait_vmcnt16();  // k-tile 0 has landed (D - 1 = 2 k-tiles, 16 copies, may still be in flight)
+  __syncthreads();
+  bf16x8_t fa[TM], fb[TN], ga[TM], gb[TN];
+  frags2<AK>(stage_a(0), wm * WM, lane, fa);
+  frags2<BKM>(stage_b(0), wn * WN, lane, fb);
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -583,52 +666,82 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = p.K / BK2;  // even
-  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
-  auto stage_a = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B); };
-  auto stage_b = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B + BM * BK2 * 2); };
-  // every iteration issues exactly 8 copies per wave (past the last tile it re-copies tile nk-1 into a free stage),
-  // so "tile j+1 has landed" is always "at most 16 copies outstanding"
-  const int64_t lda = p.lda, ldb = p.ldb;  // held in registers: no argument loads inside the K loop
-  auto issue_tile = [&](int kt) {
-    const int kc = min(kt, nk - 1);
-    const uint32_t sb = lds0 + (kt & (NSTAGE - 1)) * STAGE_B;
-    da.issue(lda, kc * BK2, sb, wave);
-    db.issue(ldb, kc * BK2, sb + BM * BK2 * 2, wave);
+  // Segment S of a step: copy S of k-tile j+D (S < 4: A rows, else B), this segment's share of the reads of
+  // k-tile j+1's fragments, and the 8 MFMAs of fragment row S of k-tile j, the copy and reads slotted between the
+  // MFMAs (a wave waits at each MFMA issue, so anything else placed there runs while the matrix core is busy).
+  auto segment = [&](auto sc, bf16x8_t(&FCA)[TM], bf16x8_t(&FCB)[TN], bf16x8_t(&FNA)[TM], bf16x8_t(&FNB)[TN],
+                     const u32x4_t* na, const u32x4_t* nb, uint32_t sb, uint32_t ka, uint32_t kb) {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S < 4) da.issue1(S, Ab, ka, sb, wave);
+    else db.issue1(S - 4, Bb, kb, sb + BM * BK2 * 2, wave);
+#pragma unroll
+    for (int f = 0; f < 16; ++f) {
+      if (frag_seg(f) == S) {
+        if (f % 2 == 0) frag1<AK>(na, wm * WM, lane, f / 2, FNA[f / 2]);
+        else frag1<BKM>(nb, wn * WN, lane, f / 2, FNB[f / 2]);
+      }
+    }
+    mfma_rows_t<S, S + 1, TN>(acc, FCA, FCB);
+    constexpr int nds = seg_ds_count<AK, BKM>(S);
+    if constexpr (nds > 0) {
+#pragma unroll
+      for (int r = 0; r < nds; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, TN - nds, 0);
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  using I6 = std::integral_constant<int, 6>;
+  using I7 = std::integral_constant<int, 7>;
 
-  issue_tile(0);
-  issue_tile(1);
-  issue_tile(2);
-  wait_vmcnt16();
-  __syncthreads();
-  bf16x8_t fa[TM], fb[TN], ga[TM], gb[TN];
-  frags2<AK>(stage_a(0), wm * WM, lane, fa);
-  frags2<BKM>(stage_b(0), wn * WN, lane, fb);
-
-  // Step j (fragments FC = k-tile j already in registers): wait until this wave's copies of k-tile j+1 have
-  // landed (k-tiles j+1 and j+2 were in flight, so at most 8 copies may remain) and barrier, which publishes k-tile
-  // j+1 and also proves every wave is done reading the stage k-tile j-1 used; copy k-tile j+3 into that stage; then
-  // the 64 MFMAs of k-tile j with the LDS reads of k-tile j+1's fragments spread over them (one read per RS MFMAs,
-  // leaving the last MFMAs to cover the read latency).
-  constexpr int NDS = (AK ? 8 : 16) + (BKM ? 8 : 16);  // LDS read instructions for one k-tile's fragments
-  constexpr int RS = NDS <= 24 ? 2 : 1;
+  // Step j (fragments of k-tile j in FC): wait until this wave's copies of k-tile j+1 have landed (k-tiles j+1
+  // and j+2 were in flight, so at most 8 copies may remain) and barrier, which publishes k-tile j+1 and proves that
+  // every wave is done with the stage k-tile j-1 used; then the 8 segments, which copy k-tile j+D into that stage
+  // (past the last k-tile: a harmless re-copy of it, so every step issues the same 8 copies).
 #define TP_GEMM_STEP(J, FCA, FCB, FNA, FNB)                                                      \
   {                                                                                              \
     const int j_ = (J);                                                                          \
     wait_vmcnt8();                                                                               \
     __syncthreads();                                                                             \
     __builtin_amdgcn_sched_barrier(0);                                                           \
-    issue_tile(j_ + 3);                                                                          \
-    frags2<AK>(stage_a((j_ + 1) & (NSTAGE - 1)), wm * WM, lane, FNA);                            \
-    frags2<BKM>(stage_b((j_ + 1) & (NSTAGE - 1)), wn * WN, lane, FNB);                           \
-    mfma_rows<0, TM, TN>(acc, FCA, FCB);                                                         \
-    _Pragma("unroll") for (int g_ = 0; g_ < NDS; ++g_) {                                         \
-      __builtin_amdgcn_sched_group_barrier(0x008, RS, 0);                                        \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
-    }                                                                                            \
-    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - RS * NDS, 0);                          \
+    const int kt_ = min(j_ + D, nk - 1);                                                         \
+    const uint32_t sb_ = lds0 + ((j_ + D) & (NSTAGE - 1)) * STAGE_B;                             \
+    const uint32_t ka_ = AK ? (uint32_t)(kt_ * BK2) : (uint32_t)((int64_t)kt_ * BK2 * lda);      \
+    const uint32_t kb_ = BKM ? (uint32_t)(kt_ * BK2) : (uint32_t)((int64_t)kt_ * BK2 * ldb);     \
+    const u32x4_t* na_ = stage_a((j_ + 1) & (NSTAGE - 1));                                       \
+    const u32x4_t* nb_ = stage_b((j_ + 1) & (NSTAGE - 1));                                       \
     __builtin_amdgcn_sched_barrier(0);                                                           \
+    if constexpr (!AK && !BKM) {                                                                 \
+      /* both operands MN-major (the weight-gradient pair): measured faster with the eight */    \
+      /* copies first and the 32 transposing reads one per MFMA over the first half */           \
+      da.issue(Ab, lda, kt_ * BK2, sb_, wave);                                                   \
+      db.issue(Bb, ldb, kt_ * BK2, sb_ + BM * BK2 * 2, wave);                                    \
+      frags2<AK>(na_, wm * WM, lane, FNA);                                                       \
+      frags2<BKM>(nb_, wn * WN, lane, FNB);                                                      \
+      mfma_rows_t<0, TM, TN>(acc, FCA, FCB);                                                     \
+      _Pragma("unroll") for (int s_ = 0; s_ < 32; ++s_) {                                        \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
+      }                                                                                          \
+      __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                         \
+    } else {                                                                                     \
+    segment(I0{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
+    segment(I1{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
+    segment(I2{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
+    segment(I3{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
+    segment(I4{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
+    segment(I5{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
+    segment(I6{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
+    segment(I7{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
+    }                                                                                            \
   }
   for (int kt = 0; kt < nk; kt += 2) {
     TP_GEMM_STEP(kt, fa, fb, ga, gb)
@@ -638,9 +751,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   wait_vmcnt0();
 
   // ---- epilogue, staged through LDS one 16-row chunk at a time: each wave writes the fp32 accumulators of its
-  // rows 16 tm .. 16 tm + 15 (all 128 of its columns) to a padded buffer of its own, then walks the chunk row by
-  // row with consecutive lanes on consecutive column pairs, so the math runs in a compact loop and every row
-  // leaves as one contiguous 256-byte store.
+  // rows 16 tm .. 16 tm + 15 (all 128 of its columns) to a padded buffer of its own, one 16-byte write per block,
+  // then walks the chunk row by row with consecutive lanes on consecutive column pairs, so the math runs in a
+  // compact loop and every row leaves as one contiguous 256-byte store.
   __syncthreads();
   float* ep = reinterpret_cast<float*>(reinterpret_cast<char*>(&lds[0]) + wave * EPW);
   uint16_t* ax = reinterpret_cast<uint16_t*>(ep + 16 * EP);
@@ -659,8 +772,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ep[((lane >> 4) * 4 + e) * EP + tn * 16 + (lane & 15)] = acc[tm][tn][e];
+      *reinterpret_cast<f32x4_t*>(ep + (lane & 15) * EP + tn * 16 + 4 * (lane >> 4)) = acc[tm][tn];
     if constexpr (NAUX > 0) {
 #pragma unroll
       for (int q = 0; q < NAUX; ++q)
@@ -739,7 +851,9 @@ hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st
   pp.g[0] = p0;
   pp.g[1] = p1 ? *p1 : p0;
   pp.tiles0 = big_tiles(p0, EPI == EPI_SWIGLU_FWD);
-  const int total = pp.tiles0 + (p1 ? big_tiles(*p1, EPI == EPI_SWIGLU_FWD) : 0);
+  pp.tiles1 = p1 ? big_tiles(*p1, EPI == EPI_SWIGLU_FWD) : 0;
+  const int total = pp.tiles0 + pp.tiles1;
+
   static const std::string name = std::string("gemm_bf16_big_") + (AK ? "K" : "M") + (BKM ? "K" : "M") + "_" +
                                   kEpiNames[EPI];
   static const std::string name2 = std::string("gemm_bf16_big_pair_") + (AK ? "K" : "M") + (BKM ? "K" : "M") + "_" +
@@ -748,11 +862,21 @@ hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st
                    dim3(256), 0, st, pp);
 }
 
+// The large-tile kernel needs an even number of 32-deep k-tiles, more than it keeps in flight (K >= 128), and
+// every element offset of its operands below 2^32.
+bool big_fits(const GemmParams& p, bool a_kmajor, bool b_kmajor) {
+  if (p.K % (2 * BK2) != 0 || p.K < 4 * BK2) return false;
+  const int64_t lim = (int64_t)1 << 32;
+  const int64_t a_end = a_kmajor ? (int64_t)(p.M - 1) * p.lda + p.K : (int64_t)(p.K - 1) * p.lda + p.M;
+  const int64_t b_end = b_kmajor ? (int64_t)(p.N - 1) * p.ldb + p.K : (int64_t)(p.K - 1) * p.ldb + p.N;
+  return a_end < lim && b_end < lim;
+}
+
 template <bool AK, bool BKM, int EPI>
 hipError_t launch_cfg(int ci, const GemmParams& p, hipStream_t st) {
   switch (ci) {
     case 0:
-      if (p.K % (2 * BK2) == 0) return launch_big<AK, BKM, EPI>(p, nullptr, st);
+      if (big_fits(p, AK, BKM)) return launch_big<AK, BKM, EPI>(p, nullptr, st);
       return launch_one<256, 256, 2, 4, AK, BKM, EPI>(p, st);
     case 1: return launch_one<256, 128, 2, 2, AK, BKM, EPI>(p, st);
     case 2: return launch_one<128, 128, 2, 2, AK, BKM, EPI>(p, st);
@@ -791,7 +915,8 @@ hipError_t gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi,
 // The two weight-gradient GEMMs of a backward (both MN-major x MN-major, same K = s*b): one launch over both tile
 // sets when the large-tile kernel applies to both and together they fill the GPU better than each alone.
 hipError_t gemm_bf16_wgrad_pair(const GemmParams& p0, const GemmParams& p1, hipStream_t st) {
-  if (p0.M > 0 && p0.N > 0 && p1.M > 0 && p1.N > 0 && p0.K == p1.K && p0.K % (2 * BK2) == 0) {
+  if (p0.M > 0 && p0.N > 0 && p1.M > 0 && p1.N > 0 && p0.K == p1.K && big_fits(p0, false, false) &&
+      big_fits(p1, false, false)) {
     const int t = big_tiles(p0, false) + big_tiles(p1, false);
     const int c0 = choose_cfg(p0.M, 0, p0.N, false, 0), c1 = choose_cfg(p1.M, 0, p1.N, false, 0);
     if (t >= kNumCUs * 3 / 4 || (c0 == 0 && c1 == 0)) return launch_big<false, false, EPI_STORE>(p0, &p1, st);
