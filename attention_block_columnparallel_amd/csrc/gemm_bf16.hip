@@ -390,6 +390,15 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
 __device__ __forceinline__ void wait_vmcnt16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmcnt8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmcnt24() { asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); }
+// wait until at most T k-tiles' copies (8 per wave each) are still in flight
+template <int T>
+__device__ __forceinline__ void wait_vmcnt_tiles() {
+  static_assert(T >= 1 && T <= 3, "k-tiles in flight");
+  if constexpr (T == 1) wait_vmcnt8();
+  else if constexpr (T == 2) wait_vmcnt16();
+  else wait_vmcnt24();
+}
 
 // One operand tile (256 rows or columns x 32 k) is 16 KB = 16 wave-wide copies of 1 KB; wave w issues copies
 // 4w .. 4w+3.  The source address of each lane is chosen so that the lane's fixed LDS slot receives the chunk the
@@ -601,7 +610,7 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
 template <bool AK, bool BKM, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 8, TN = 8;
-  constexpr int NSTAGE = 4;
+  constexpr int NSTAGE = 4;  // (a fifth 32 KB stage, filling the 160 KB LDS, measured slower)
   constexpr int D = NSTAGE - 1;                 // k-tiles in flight ahead of the one being multiplied
   constexpr int STAGE_B = (BM + BN) * BK2 * 2;  // bytes per stage (A tile then B tile)
   constexpr bool SWIG = (EPI == EPI_SWIGLU_FWD);
@@ -654,7 +663,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
     da.issue(Ab, lda, d * BK2, lds0 + d * STAGE_B, wave);
     db.issue(Bb, ldb, d * BK2, lds0 + d * STAGE_B + BM * BK2 * 2, wave);
   }
-  wait_vmcnt16();  // k-tile 0 has landed (D - 1 = 2 k-tiles, 16 copies, may still be in flight)
+  wait_vmcnt_tiles<D - 1>();  // k-tile 0 has landed (D - 1 k-tiles, 8 copies each, may still be in flight)
   __syncthreads();
   bf16x8_t fa[TM], fb[TN], ga[TM], gb[TN];
   frags2<AK>(stage_a(0), wm * WM, lane, fa);
@@ -708,15 +717,15 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
 #define TP_GEMM_STEP(J, FCA, FCB, FNA, FNB)                                                      \
   {                                                                                              \
     const int j_ = (J);                                                                          \
-    wait_vmcnt8();                                                                               \
+    wait_vmcnt_tiles<D - 2>();                                                                   \
     __syncthreads();                                                                             \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     const int kt_ = min(j_ + D, nk - 1);                                                         \
-    const uint32_t sb_ = lds0 + ((j_ + D) & (NSTAGE - 1)) * STAGE_B;                             \
+    const uint32_t sb_ = lds0 + ((j_ + D) & (NSTAGE - 1)) * STAGE_B;                                   \
     const uint32_t ka_ = AK ? (uint32_t)(kt_ * BK2) : (uint32_t)((int64_t)kt_ * BK2 * lda);      \
     const uint32_t kb_ = BKM ? (uint32_t)(kt_ * BK2) : (uint32_t)((int64_t)kt_ * BK2 * ldb);     \
-    const u32x4_t* na_ = stage_a((j_ + 1) & (NSTAGE - 1));                                       \
-    const u32x4_t* nb_ = stage_b((j_ + 1) & (NSTAGE - 1));                                       \
+    const u32x4_t* na_ = stage_a((j_ + 1) & (NSTAGE - 1));                                             \
+    const u32x4_t* nb_ = stage_b((j_ + 1) & (NSTAGE - 1));                                             \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     if constexpr (!AK && !BKM) {                                                                 \
       /* both operands MN-major (the weight-gradient pair): measured faster with the eight */    \
