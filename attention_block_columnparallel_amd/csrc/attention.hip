@@ -4,15 +4,20 @@
 // to its rank; "Sequence Parallel 与 Context Parallel", CP step 3: block statistics merged by online softmax).
 //
 // bf16 kernel, one workgroup = 64 queries of one (batch, head), 4 waves x 16 queries, key blocks of 64:
-//   * S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): K rows come from LDS, the wave's 16 queries sit
-//     in registers for the whole kernel.  In the transposed product every lane owns one query (lane & 15), so the
-//     row statistics need only a max over the 4 lane groups that share it.
+//   * K and V tiles are copied as they sit in HBM (direct global -> LDS copies, 16 bytes per lane) into a ring of
+//     3 LDS stages, so the copies of block kt+2 are in flight while block kt is multiplied.  Within a row the
+//     16-byte chunks are rotated by the row index, so the 16 rows one fragment read touches fall in different
+//     banks.
+//   * S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): K fragments are 16-byte LDS reads, the wave's
+//     16 queries sit in registers for the whole kernel.  In the transposed product every lane owns one query
+//     (lane & 15), so the row statistics need only a max over the 4 lane groups that share it.
 //   * O^T = V^T P^T: the probabilities never leave registers.  A lane holds scores for keys 4g..4g+3 and
-//     16+4g..16+4g+3 of each 32-key step (g = lane >> 4); the V^T fragment is read with the same key order, so the
-//     pair of operands agree on k and the product is exact whatever order the 32 keys take.
-//   * V is transposed on its way into LDS (8 keys x 4 dims per thread), K is copied as is; both are double
-//     buffered with the next block's loads in flight during the current block's math.
-//   * Query tiles are issued heaviest first (causal work grows with the tile index).
+//     16+4g..16+4g+3 of each 32-key step (g = lane >> 4); the V^T fragment is gathered from the untransposed V
+//     tile by two transposing LDS reads (ds_read_b64_tr_b16) whose row addresses follow the same key order, so the
+//     pair of operands agree on k.
+//   * Softmax in base 2 with the scale folded into one FMA per score (exp2(s c - m c), c = scale log2 e) and the
+//     hardware exp2; the running output is rescaled only in blocks where some query's maximum rose.
+//   * Query tiles are issued heaviest first over all heads (causal work grows with the tile index).
 #include <math.h>
 
 #include <string>
@@ -25,38 +30,52 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 constexpr int QT = 64;   // queries per workgroup
 constexpr int KT = 64;   // keys per block
-constexpr int VP = KT + 8;  // V^T row pitch in elements (odd number of 16-byte chunks)
+constexpr int NSTG = 3;  // LDS stages
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte address m0 + 16 l.  Inline
+// assembly, so that the compiler does not wait for these copies at every barrier; the kernel waits itself.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <int DP>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnParams p) {
-  constexpr int KP = DP + 8;       // K row pitch in elements (odd number of 16-byte chunks)
-  constexpr int NDS = DP / 32;     // 32-wide d steps of S^T
-  constexpr int NST = DP / 16;     // 16-row d subtiles of O^T
-  constexpr int KCH = DP / 8;      // 16-byte chunks per K row
-  constexpr int KLD = (KT * KCH + 255) / 256;  // K chunks per thread
-  constexpr int VBLK = (KT / 8) * (DP / 4);     // 8x4 blocks in a V tile
-  constexpr int VLD = (VBLK + 255) / 256;
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
+  constexpr int CH = DP / 8;            // 16-byte chunks per K or V row in LDS
+  constexpr int TILE_B = KT * CH * 16;  // bytes of one K (or V) tile
+  constexpr int STAGE_B = 2 * TILE_B;   // K tile then V tile
+  constexpr int CPW = CH / 4;           // copies of 64 lanes per wave per tile and operand
+  constexpr int NC = 2 * CPW;           // copies per wave per block (K and V)
+  constexpr int NDS = DP / 32;          // 32-wide d steps of S^T
+  constexpr int NST = DP / 16;          // 16-row d subtiles of O^T
+  __shared__ __attribute__((aligned(16))) char lds[NSTG * STAGE_B];
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DP * VP];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int nq = (p.s + QT - 1) / QT;
-  const int qtile = nq - 1 - (int)blockIdx.x;
-  const int bh = blockIdx.y;
+  const int nbh = p.b * p.hl;
+  const int qtile = nq - 1 - (int)blockIdx.x / nbh;  // heaviest first over all (batch, head) pairs
+  const int bh = (int)blockIdx.x % nbh;
   const int bidx = bh / p.hl, jj = bh % p.hl;
   const int d = p.d;
   const int64_t ldq = (int64_t)p.hl * 3 * d;  // elements per token row of QKV
   const int64_t tok_stride = ldq * p.b;        // consecutive sequence positions
   const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
-  const uint16_t* __restrict__ kbase = qkv + d;
-  const uint16_t* __restrict__ vbase = qkv + 2 * d;
+  const uint16_t* __restrict__ kbase = qkv + d;  // V follows K at + d
 
   // ---- this lane's query and its fragments (k = d: lane supplies d = 32u + 8g .. +8)
-  const int q = qtile * QT + wave * 16 + (lane & 15);
+  const int q = qtile * QT + wave * 16 + l16;
   bf16x8_t qf[NDS];
 #pragma unroll
   for (int u = 0; u < NDS; ++u) {
@@ -66,84 +85,69 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnParams p) {
     qf[u] = __builtin_bit_cast(bf16x8_t, v);
   }
 
-  uint4 kreg[KLD];
-  uint2 vreg[VLD][8];
-  auto load_tile = [&](int kt) {
-    const int kv0 = kt * KT;
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / KCH, ch = c % KCH;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (c < KT * KCH && kv0 + r < p.s && ch * 8 < d)
-        v = *reinterpret_cast<const uint4*>(kbase + (int64_t)(kv0 + r) * tok_stride + ch * 8);
-      kreg[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int bq = tid + 256 * i;
-      const int gd = bq % (DP / 4), kg = bq / (DP / 4);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kv = kv0 + kg * 8 + j;
-        uint2 v = make_uint2(0u, 0u);
-        if (bq < VBLK && kv < p.s && gd * 4 < d)
-          v = *reinterpret_cast<const uint2*>(vbase + (int64_t)kv * tok_stride + gd * 4);
-        vreg[i][j] = v;
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int c = tid + 256 * i;
-      if (c < KT * KCH) {
-        const int r = c / KCH, ch = c % KCH;
-        *reinterpret_cast<uint4*>(&Ks[buf][r * KP + ch * 8]) = kreg[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VLD; ++i) {
-      const int bq = tid + 256 * i;
-      if (bq < VBLK) {
-        const int gd = bq % (DP / 4), kg = bq / (DP / 4);
-        uint32_t w[4][4];
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const uint32_t x0 = vreg[i][2 * pp].x, x1 = vreg[i][2 * pp + 1].x;
-          const uint32_t y0 = vreg[i][2 * pp].y, y1 = vreg[i][2 * pp + 1].y;
-          w[0][pp] = (x0 & 0xFFFFu) | (x1 << 16);
-          w[1][pp] = (x0 >> 16) | (x1 & 0xFFFF0000u);
-          w[2][pp] = (y0 & 0xFFFFu) | (y1 << 16);
-          w[3][pp] = (y0 >> 16) | (y1 & 0xFFFF0000u);
-        }
-#pragma unroll
-        for (int jn = 0; jn < 4; ++jn)
-          *reinterpret_cast<uint4*>(&Vt[buf][(gd * 4 + jn) * VP + kg * 8]) =
-              make_uint4(w[jn][0], w[jn][1], w[jn][2], w[jn][3]);
-      }
-    }
-  };
+  const int nkt_all = (p.s + KT - 1) / KT;
+  const int nkt = p.causal ? min(nkt_all, qtile + 1) : nkt_all;
 
-  const float sl2 = p.scale * 1.4426950408889634f;  // scores in log2 units
+  // ---- copies: copy c (0 .. CH-1) of a tile fills LDS chunks 64 c .. 64 c + 63; wave w issues copies w + 4 i.
+  // LDS chunk position P = r CH + slot holds chunk (slot - r) mod CH of row r (chunks past d repeat chunk 0).
+  int crow[CPW], ccol[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int P = (wave + 4 * i) * 64 + lane;
+    const int r = P / CH, slot = P % CH;
+    int c = slot - r % CH;
+    if (c < 0) c += CH;
+    crow[i] = r;
+    ccol[i] = (c * 8 < d) ? c * 8 : 0;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
+  auto issue_tile = [&](int kt, int st) {
+    const int kv0 = min(kt, nkt - 1) * KT;  // past the last block: a harmless re-copy of it
+    const uint32_t sb = lds0 + st * STAGE_B;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int row = min(kv0 + crow[i], p.s - 1);
+      const uint16_t* src = kbase + (int64_t)row * tok_stride + ccol[i];
+      const uint32_t dst = sb + (wave + 4 * i) * 1024;
+      dma16(src, __builtin_amdgcn_readfirstlane(dst));
+      dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
+    }
+  };
+  // ---- fragment read offsets (bytes within a tile), loop invariant
+  auto chunk_off = [&](int r, int c) { return r * CH * 16 + ((c + r) % CH) * 16; };
+  int koff[4][NDS];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int u = 0; u < NDS; ++u) koff[ks][u] = chunk_off(16 * ks + l16, 4 * u + g);
+  int voff[2][NST][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int R = 32 * u + 16 * hh + 4 * g + (l16 >> 2);
+        const int dc = 16 * st + 4 * (l16 & 3);
+        voff[u][st][hh] = chunk_off(R, dc >> 3) + ((dc >> 2) & 1) * 8;
+      }
+
+  const float c2 = p.scale * 1.4426950408889634f;  // scores -> log2 units
   float m_run = -INFINITY, l_part = 0.f;
   f32x4_t acc_o[NST];
 #pragma unroll
   for (int st = 0; st < NST; ++st) acc_o[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nkt_all = (p.s + KT - 1) / KT;
-  const int nkt = p.causal ? min(nkt_all, qtile + 1) : nkt_all;
-
-  load_tile(0);
-  store_tile(0);
+  issue_tile(0, 0);
+  issue_tile(1, 1);
+  wait_vmcnt<NC>();  // block 0 has landed (block 1 may still be in flight)
   __syncthreads();
 
+  int st_cur = 0, st_new = 2;
   for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) load_tile(kt + 1);
-    const uint16_t* K_ = Ks[cur];
-    const uint16_t* V_ = Vt[cur];
+    issue_tile(kt + 2, st_new);
+    const char* Kt = &lds[st_cur * STAGE_B];
+    const char* Vt = Kt + TILE_B;
     const int kv0 = kt * KT;
 
     // S^T [64 keys x 16 queries] in 4 subtiles of 16 keys
@@ -151,32 +155,36 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       sc[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int kr = ks * 16 + (lane & 15);
 #pragma unroll
       for (int u = 0; u < NDS; ++u) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&K_[kr * KP + 32 * u + 8 * g]));
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Kt + koff[ks][u]));
         sc[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[u], sc[ks], 0, 0, 0);
       }
     }
-    // scale, mask, block max
+    // mask (diagonal and ragged blocks only), block max of the raw scores
     const bool need_mask = (p.causal && kt == qtile) || (kv0 + KT > p.s);
     float mx = -INFINITY;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x = sc[ks][e] * sl2;
         if (need_mask) {
           const int kv = kv0 + ks * 16 + 4 * g + e;
-          if (kv >= p.s || (p.causal && kv > q)) x = -INFINITY;
+          if (kv >= p.s || (p.causal && kv > q)) sc[ks][e] = -INFINITY;
         }
-        sc[ks][e] = x;
-        mx = fmaxf(mx, x);
+        mx = fmaxf(mx, sc[ks][e]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    const float corr = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+    if (__any(m_new > m_run)) {  // some query's maximum rose: rescale (corr = 1 where it did not)
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_part *= corr;
+#pragma unroll
+      for (int st = 0; st < NST; ++st) acc_o[st] *= corr;
+      m_run = m_new;
+    }
+    const float nm = -m_run * c2;
     float psum = 0.f;
     uint32_t pk[4][2];
 #pragma unroll
@@ -184,16 +192,13 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnParams p) {
       float pe[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pe[e] = (m_new == -INFINITY) ? 0.f : exp2f(sc[ks][e] - m_new);
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[ks][e], c2, nm));
         psum += pe[e];
       }
       pk[ks][0] = f32_to_bf16_hw(pe[0]) | (f32_to_bf16_hw(pe[1]) << 16);
       pk[ks][1] = f32_to_bf16_hw(pe[2]) | (f32_to_bf16_hw(pe[3]) << 16);
     }
-    l_part = l_part * corr + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int st = 0; st < NST; ++st) acc_o[st] *= corr;
+    l_part += psum;
 
     // O^T [d x 16 queries] += V^T P^T, two 32-key steps
 #pragma unroll
@@ -201,16 +206,18 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnParams p) {
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pk[2 * u][0], pk[2 * u][1], pk[2 * u + 1][0], pk[2 * u + 1][1]));
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
-        const int dr = st * 16 + (lane & 15);
-        const uint2 lo = *reinterpret_cast<const uint2*>(&V_[dr * VP + 32 * u + 4 * g]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&V_[dr * VP + 32 * u + 16 + 4 * g]);
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        acc_o[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc_o[st], 0, 0, 0);
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[u][st][0]));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[u][st][1]));
+        const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc_o[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pf, acc_o[st], 0, 0, 0);
       }
     }
-    if (more) store_tile(cur ^ 1);
-    __syncthreads();
+    wait_vmcnt<NC>();  // block kt+1 has landed (block kt+2 may still be in flight)
+    __syncthreads();   // publishes block kt+1; every wave is done with stage st_cur, refilled next iteration
+    st_cur = st_cur == NSTG - 1 ? 0 : st_cur + 1;
+    st_new = st_new == NSTG - 1 ? 0 : st_new + 1;
   }
+  wait_vmcnt<0>();
 
   float l_tot = l_part;
   l_tot += __shfl_xor(l_tot, 16);
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_kernel(AttnParams p) {
       }
     }
     if (p.lse != nullptr && g == 0)
-      p.lse[((int64_t)bidx * p.hl + jj) * p.s + q] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+      p.lse[((int64_t)bidx * p.hl + jj) * p.s + q] = (m_run * c2 + log2f(l_tot)) * 0.69314718055994531f;
   }
 }
 
@@ -270,8 +277,7 @@ template <int DP>
 hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
   const int nq = (p.s + QT - 1) / QT;
   static const std::string name = "attn_fwd_bf16_d" + std::to_string(DP);
-  return TP_LAUNCH(name.c_str(), (attn_fwd_bf16_kernel<DP>), dim3((unsigned)nq, (unsigned)(p.b * p.hl)), dim3(256), 0,
-                   st, p);
+  return TP_LAUNCH(name.c_str(), (attn_fwd_bf16_kernel<DP>), dim3((unsigned)(nq * p.b * p.hl)), dim3(256), 0, st, p);
 }
 
 }  // namespace

@@ -806,11 +806,12 @@ struct Cfg {
   int bm, bn, nwm, nwn;
   float eff;  // relative per-tile efficiency used to trade tile size against filling 256 CUs
 };
+// eff: measured throughput of a full wave of tiles relative to the large-tile kernel (at K in the thousands)
 constexpr Cfg kCfgs[] = {
     {256, 256, 2, 4, 1.00f},
-    {256, 128, 2, 2, 0.92f},
-    {128, 128, 2, 2, 0.78f},
-    {64, 64, 2, 2, 0.40f},
+    {256, 128, 2, 2, 0.50f},
+    {128, 128, 2, 2, 0.50f},
+    {64, 64, 2, 2, 0.25f},
 };
 constexpr int kNumCUs = 256;
 const char* const kEpiNames[] = {"store", "bias", "bias_act", "swiglu_fwd", "act_bwd", "swiglu_bwd"};
