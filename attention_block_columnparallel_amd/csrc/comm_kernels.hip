@@ -168,9 +168,22 @@ hipError_t launch_reduce_bf16_t(const uint16_t* P, int64_t stride, int64_t in_of
 // ------------------------------------------------------------------------------------------------------------------
 // Copy (dim-0 gather of contiguous slices) and packer.
 // ------------------------------------------------------------------------------------------------------------------
+// Each thread moves COPY_VPT 16-byte vectors, all loads in flight before the first store; consecutive threads
+// take consecutive vectors, so every wave-wide access is 1 KB contiguous.
+constexpr int COPY_VPT = 8;
 __global__ __launch_bounds__(256) void copy16(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t nvec) {
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride) dst[v] = src[v];
+  const int64_t v0 = (int64_t)blockIdx.x * (256 * COPY_VPT) + threadIdx.x;
+  uint4 r[COPY_VPT];
+#pragma unroll
+  for (int u = 0; u < COPY_VPT; ++u) {
+    const int64_t v = v0 + (int64_t)u * 256;
+    if (v < nvec) r[u] = ld_stream(src + v);
+  }
+#pragma unroll
+  for (int u = 0; u < COPY_VPT; ++u) {
+    const int64_t v = v0 + (int64_t)u * 256;
+    if (v < nvec) st_stream(dst + v, r[u]);
+  }
 }
 __global__ __launch_bounds__(256) void copy1(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -296,8 +309,7 @@ hipError_t copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t st)
   if ((uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0) {
     const int64_t nvec = bytes / 16;
     if (nvec > 0) {
-      int64_t blocks = (nvec + 255) / 256;
-      if (blocks > 256 * 16) blocks = 256 * 16;
+      const int64_t blocks = (nvec + 256 * COPY_VPT - 1) / (256 * COPY_VPT);
       hipError_t e = TP_LAUNCH("copy16", copy16, dim3((unsigned)blocks), dim3(256), 0, st,
                                static_cast<const uint4*>(src), static_cast<uint4*>(dst), nvec);
       if (e != hipSuccess) return e;

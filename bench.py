@@ -12,7 +12,9 @@ both reductions), in TFLOP/s.  roofline = the kernel with the largest share of t
 flops per launch over its average HIP-event duration inside the timed region, against the dense bf16 MFMA peak.
 rs_dim0 = the reduce-scatter kernel against HBM bandwidth.  traffic = HBM bytes per launch from the committed
 rocprofv3 counter summary under profiles/ (null once the kernel source differs from the one profiled).
-cpu_baseline = the fp64 oracle on a bounded sample.
+cpu_baseline = the fp64 oracle on a bounded sample.  attention_block and gather_dim0 = the other rows of the hot
+path, timed after the step (not part of value): the attention block forward at the 22B-class shape and the dim-0
+gather at the Llama-70B-sized SP shape.
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default="mlp_h4096_ffn16384_t8_b8_s2048")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-extra", action="store_true", help="skip the attention-block and gather measurements")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one dim-0 gather (a plain copy) of this many MiB, for counter calibration")
     return ap.parse_args(argv)
@@ -70,6 +73,88 @@ def profiled_traffic(workload: str, kernel: str):
             if len(parts) == 4 and parts[0] == "traffic" and parts[1] == kernel:
                 return int(parts[2]) if parts[3] == sha else None
     return None
+
+
+def attention_block_measure(L, steps: int, warmup: int) -> dict:
+    """The attention block forward at the 22B-class shape (h=6144, 64 heads of 96, s=4096, t=8, causal): for every
+    rank the QKV GEMM, local causal attention and output projection into partial i, then the dim-0 reduce-scatter.
+    Per-kernel HIP-event durations; causal attention counts only unmasked query-key pairs."""
+    import numpy as np
+    import torch
+
+    import tp_inputs as TI
+    from attention_block_columnparallel_amd.block import AttnBlock
+
+    w = TI.ATTN_22B
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    inp = TI.attn_inputs(w)
+    X = dev(inp["X"])
+    blk = AttnBlock(w.s, w.b, w.h, w.a, w.d, w.t, dev(inp["Wqkv"]), dev(inp["Wo"]), causal=True)
+    for _ in range(warmup):
+        blk.forward(X, sp=True)
+    torch.cuda.synchronize()
+    timer = L.LaunchTimer(capacity=steps * (3 * w.t + 1) + 8)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    with timer:
+        for _ in range(steps):
+            blk.forward(X, sp=True)
+    e1.record()
+    torch.cuda.synchronize()
+    hl, M = w.a // w.t, w.s * w.b
+    fl = {"qkv": 2.0 * M * w.h * 3 * hl * w.d, "attention": 4.0 * w.d * (w.s * (w.s + 1) / 2) * w.b * hl,
+          "proj": 2.0 * M * hl * w.d * w.h}
+    # launch order per step: for each rank QKV GEMM, attention, output projection; then the reduce-scatter
+    res = timer.results()
+    per_step = 3 * w.t + 1
+    roles = {}
+    for i, (name, ms) in enumerate(res):
+        j = i % per_step
+        role = "reduce_scatter" if j == 3 * w.t else ("qkv", "attention", "proj")[j % 3]
+        r = roles.setdefault(role, {"kernel": name, "ms": []})
+        r["ms"].append(ms)
+    out = {"workload": w.name, "ms_per_step": round(e0.elapsed_time(e1) / steps, 4), "kernels": {}}
+    total_fl = w.t * sum(fl.values())
+    out["tflops_block"] = round(total_fl / (out["ms_per_step"] * 1e-3) / 1e12, 1)
+    for role, r in roles.items():
+        avg = sum(r["ms"]) / len(r["ms"])
+        k = {"kernel": r["kernel"], "launches_per_step": len(r["ms"]) // steps, "avg_us": round(1e3 * avg, 2)}
+        if role in fl:
+            k["flops_per_launch"] = fl[role]
+            k["tflops"] = round(fl[role] / (avg * 1e-3) / 1e12, 1)
+            k["frac_bf16_peak"] = round(fl[role] / (avg * 1e-3) / PEAK_BF16_FLOPS, 4)
+        else:
+            nbytes = (w.t + 1) * M * w.h * 2
+            k["bytes_per_launch"] = nbytes
+            k["gbps"] = round(nbytes / (avg * 1e-3) / 1e9, 1)
+        out["kernels"][role] = k
+    del blk, X
+    return out
+
+
+def gather_measure(L, reps: int) -> dict:
+    """The sequence-parallel entry gather: t = 8 slices [s/t, b, h] -> [s, b, h] at the Llama-70B-sized SP shape
+    (s=4096, b=1, h=8192, bf16): reads and writes 64 MiB."""
+    import torch
+
+    t, s, b, h = 8, 4096, 1, 8192
+    sl = torch.randn((t, s // t, b, h), device="cuda").to(torch.bfloat16)
+    out = torch.empty((s, b, h), dtype=torch.bfloat16, device="cuda")
+    dims = L.make_dims(s=s, b=b, h=h, t=t)
+    L.tp_gather_dim0(dims, sl, out)
+    torch.cuda.synchronize()
+    with L.LaunchTimer(capacity=reps + 2) as lt:
+        for _ in range(reps):
+            L.tp_gather_dim0(dims, sl, out)
+    torch.cuda.synchronize()
+    ms = sorted(m for _, m in lt.results())
+    med = ms[len(ms) // 2]
+    nbytes = 2 * s * b * h * 2
+    return {"workload": "gather_dim0_t8_s4096_b1_h8192", "bytes_per_launch": nbytes, "median_us": round(1e3 * med, 2),
+            "gbps": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (med * 1e-3) / PEAK_HBM_BYTES, 4)}
 
 
 def cpu_baseline(w, inp, target_s: float) -> dict:
@@ -230,6 +315,10 @@ def main(argv=None) -> int:
         out["calib_copy"] = {"kernel": cname, "bytes_read": nbytes, "bytes_written": nbytes, "ms": round(cms, 4)}
     del blk, X, dZ, Zrs, dXrs
     torch.cuda.empty_cache()
+    if not args.no_extra:
+        out["attention_block"] = attention_block_measure(L, max(2, args.steps // 2), 2)
+        out["gather_dim0"] = gather_measure(L, 20)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     else:
