@@ -26,6 +26,10 @@ Readings where the pages are silent (each also listed in the design notes):
   * Partial sums are stored in the activation dtype; the bit-exact reduction adds them in fp32 in rank order
     0..t-1, adds the bias last, then rounds once to bf16 (nearest, ties to even); NaN stays NaN.
 
+The attention backward (core and block) follows the chain rule through the row softmax as written out in
+attention_core_backward; it is pinned by finite differences of the forward, torch's fp64 autograd, closed forms
+and softmax invariants (tests/test_oracle_attention_bwd.py).
+
 Every function here is pinned by the CPU tests (tests/test_oracle_*.py) against values the pages print, closed
 forms, finite differences, brute force on tiny inputs, or an independent library routine.
 """
@@ -547,6 +551,73 @@ def attention_rows(QKV_i: np.ndarray, s: int, b: int, hl: int, d: int, q_rows: S
             O[n, jj * d:(jj + 1) * d] = (e / e.sum()) @ v
             lse[n, jj] = m + math.log(e.sum())
     return {"O": O, "lse": lse}
+
+
+def attention_core_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.ndarray, causal: bool = True):
+    """Gradients of one head's O = softmax(Q K^T / sqrt(d), causal) V for the upstream gradient dO, by the chain rule
+    written out: dV = P^T dO; dP = dO V^T; the row softmax's Jacobian gives dS = P * (dP - rowsum(P * dP)); then
+    S = Q K^T / sqrt(d) gives dQ = dS K / sqrt(d) and dK = dS^T Q / sqrt(d).  Masked entries have P = 0 and so no
+    gradient.  Returns dQ, dK, dV (each [s, d])."""
+    s, d = Q.shape
+    S = (Q @ K.T) / math.sqrt(d)
+    if causal:
+        S = np.where(np.triu(np.ones((s, K.shape[0]), dtype=bool), k=1), -np.inf, S)
+    E = np.exp(S - S.max(axis=1, keepdims=True))
+    P = E / E.sum(axis=1, keepdims=True)
+    dV = P.T @ dO
+    dP = dO @ V.T
+    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+    dQ = dS @ K / math.sqrt(d)
+    dK = dS.T @ Q / math.sqrt(d)
+    return dQ, dK, dV
+
+
+def attention_backward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, dZ: np.ndarray, s: int, b: int, a: int,
+                       d: int, causal: bool = True, bqkv: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Gradients of the unsharded attention block Z = O Wo + c for the upstream dZ [M, h]: dO = dZ Wo^T,
+    dWo = O^T dZ, dc = column sums of dZ; per (sequence, head) the core gradients into dQKV [M, 3ad] ([Wq|Wk|Wv]
+    column order); dWqkv = X^T dQKV, dbqkv = column sums of dQKV, dX = dQKV Wqkv^T."""
+    fw = attention_forward(X, Wqkv, Wo, s, b, a, d, causal, bqkv)
+    QKV, O = fw["QKV"], fw["O"]
+    ad = a * d
+    dO = dZ @ Wo.T
+    dQKV = np.zeros_like(QKV)
+    for bi in range(b):
+        rows = np.arange(s) * b + bi
+        for j in range(a):
+            cq, ck, cv = (slice(j * d, (j + 1) * d), slice(ad + j * d, ad + (j + 1) * d),
+                          slice(2 * ad + j * d, 2 * ad + (j + 1) * d))
+            gq, gk, gv = attention_core_backward(QKV[rows, cq], QKV[rows, ck], QKV[rows, cv], dO[rows, cq], causal)
+            dQKV[rows, cq], dQKV[rows, ck], dQKV[rows, cv] = gq, gk, gv
+    return {"dO": dO, "dWo": O.T @ dZ, "dc": dZ.sum(axis=0), "dQKV": dQKV, "dWqkv": X.T @ dQKV,
+            "dbqkv": dQKV.sum(axis=0), "dX": dQKV @ Wqkv.T, "O": O, "QKV": QKV, "lse": fw["lse"]}
+
+
+def attention_shard_backward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, dZ: np.ndarray, s: int, b: int,
+                             a: int, d: int, t: int, rank: int, causal: bool = True,
+                             bqkv: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Rank r's part of the attention backward: its heads' dO_i = dZ Wo_i^T (Wo_i = the rows of its heads), the
+    weight gradients dWo_i = O_i^T dZ, dQKV_i in the grouped [q_j k_j v_j] order, dWqkv_i = X^T dQKV_i,
+    dbqkv_i, and the partial dX_i = dQKV_i Wqkv_i^T (the f reduction sums these over ranks)."""
+    fw = attention_shard_forward(X, Wqkv, Wo, s, b, a, d, t, rank, causal, bqkv)
+    QKVi, Oi = fw["QKV"], fw["O"]
+    hl = a // t
+    Wo_i = Wo[rank * hl * d:(rank + 1) * hl * d, :]
+    Wqkv_i = Wqkv[:, qkv_shard_columns(a, d, t, rank)]
+    dOi = dZ @ Wo_i.T
+    dQKVi = np.zeros_like(QKVi)
+    for bi in range(b):
+        rows = np.arange(s) * b + bi
+        for jj in range(hl):
+            base = jj * 3 * d
+            gq, gk, gv = attention_core_backward(QKVi[rows, base:base + d], QKVi[rows, base + d:base + 2 * d],
+                                                 QKVi[rows, base + 2 * d:base + 3 * d],
+                                                 dOi[rows, jj * d:(jj + 1) * d], causal)
+            dQKVi[rows, base:base + d] = gq
+            dQKVi[rows, base + d:base + 2 * d] = gk
+            dQKVi[rows, base + 2 * d:base + 3 * d] = gv
+    return {"dO": dOi, "dWo": Oi.T @ dZ, "dQKV": dQKVi, "dWqkv": X.T @ dQKVi, "dbqkv": dQKVi.sum(axis=0),
+            "dX": dQKVi @ Wqkv_i.T, "O": Oi, "QKV": QKVi, "lse": fw["lse"]}
 
 
 # ---------------------------------------------------------------------------------------------------------------
