@@ -22,7 +22,7 @@ WKINDS = {"fc1": TP_W_FC1, "fc1_gate_up": TP_W_FC1_GATE_UP, "fc2": TP_W_FC2, "qk
 STATUS = {0: "TP_OK", -1: "TP_E_NULL", -2: "TP_E_SHAPE", -3: "TP_E_DIVISIBILITY", -4: "TP_E_DTYPE", -5: "TP_E_RANK",
           -6: "TP_E_ALIAS", -7: "TP_E_UNSUPPORTED", -8: "TP_E_HIP"}
 EXPORTED = ["tp_status_str", "tp_last_hip_error", "tp_abi_version", "tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd",
-            "tp_attn_fwd", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_timing_begin",
+            "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_timing_begin",
             "tp_timing_end", "tp_timing_kernel"]
 
 
@@ -62,6 +62,7 @@ def _load() -> ctypes.CDLL:
         "tp_mlp_fwd": ([D, I, I, I, P, P, P, P, P, P, P, P], I),
         "tp_mlp_bwd": ([D, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_attn_fwd": ([D, I, I, I, P, P, P, P, P, P, P, P, P], I),
+        "tp_attn_bwd": ([D, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_partial_reduce": ([I64, I64, I, I, P, P, P, P], I),
         "tp_reduce_scatter_dim0": ([D, I, I, P, P, P, P], I),
         "tp_gather_dim0": ([D, I, P, P, P], I),
@@ -158,6 +159,15 @@ def tp_attn_fwd(dims: tp_dims, rank: int, causal: bool, X, Wqkv_i, bqkv_i, Wo_i,
                          _ptr(Wqkv_i), _ptr(bqkv_i), _ptr(Wo_i), _ptr(QKV_i), _ptr(O_i), _ptr(lse_i), _ptr(Z_i),
                          _stream(stream))
     return _check(st, "tp_attn_fwd", check)
+
+
+def tp_attn_bwd(dims: tp_dims, rank: int, causal: bool, X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dZ, dO_ws, rec_ws, dQKV_i,
+                dWqkv_i, dbqkv_i, dWo_i, dX_i, stream=None, dtype=None, check=True) -> int:
+    st = lib.tp_attn_bwd(ctypes.byref(dims), int(rank), _dtype_code(X, dtype), 1 if causal else 0, _ptr(X),
+                         _ptr(Wqkv_i), _ptr(Wo_i), _ptr(QKV_i), _ptr(O_i), _ptr(lse_i), _ptr(dZ), _ptr(dO_ws),
+                         _ptr(rec_ws), _ptr(dQKV_i), _ptr(dWqkv_i), _ptr(dbqkv_i), _ptr(dWo_i), _ptr(dX_i),
+                         _stream(stream))
+    return _check(st, "tp_attn_bwd", check)
 
 
 def tp_partial_reduce(n: int, h: int, t: int, partials, bias_c, out, stream=None, dtype=None, check=True) -> int:

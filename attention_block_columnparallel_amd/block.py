@@ -130,6 +130,37 @@ class AttnBlock:
         self.Zp = torch.empty((t, M, h), dtype=dt, device=dev)
         self.Z = torch.empty((M, h), dtype=dt, device=dev)
 
+    def _alloc_backward(self):
+        if getattr(self, "dQKV", None) is not None:
+            return
+        t, M, hl, d, h = self.t, self.M, self.hl, self.d, self.h
+        dev, dt = self.Wqkv.device, self.Wqkv.dtype
+        nqb = (self.s + 63) // 64
+        self.dO = torch.empty((M, hl * d), dtype=dt, device=dev)  # workspace reused by every rank
+        self.rec = torch.empty((self.b, hl, nqb, 256), dtype=torch.float32, device=dev)  # workspace
+        self.dQKV = torch.empty((t, M, 3 * hl * d), dtype=dt, device=dev)
+        self.dWqkv = torch.empty((t, h, 3 * hl * d), dtype=dt, device=dev)
+        self.dbqkv = torch.empty((t, 3 * hl * d), dtype=dt, device=dev) if self.bqkv is not None else None
+        self.dWo = torch.empty((t, hl * d, h), dtype=dt, device=dev)
+        self.dXp = torch.empty((t, M, h), dtype=dt, device=dev)
+        self.dX = torch.empty((M, h), dtype=dt, device=dev)
+
+    # -- backward: every rank's gradients (after forward_ranks on the same X), then f on the dX partials
+    def backward_ranks(self, X: torch.Tensor, dZ: torch.Tensor, stream=None):
+        self._alloc_backward()
+        for r in range(self.t):
+            self.L.tp_attn_bwd(self.dims, r, self.causal, X, self.Wqkv[r], self.Wo[r], self.QKV[r], self.O[r],
+                               self.lse[r], dZ, self.dO, self.rec, self.dQKV[r], self.dWqkv[r],
+                               None if self.dbqkv is None else self.dbqkv[r], self.dWo[r], self.dXp[r], stream)
+
+    def backward(self, X: torch.Tensor, dZ: torch.Tensor, sp: bool = False, stream=None) -> torch.Tensor:
+        self.backward_ranks(X, dZ, stream)
+        if sp:
+            self.L.tp_reduce_scatter_dim0(self.dims, -1, self.dXp, None, self.dX, stream)
+        else:
+            self.L.tp_partial_reduce(self.M * self.h, self.h, self.t, self.dXp, None, self.dX, stream)
+        return self.dX
+
     def forward_ranks(self, X: torch.Tensor, stream=None):
         for r in range(self.t):
             self.L.tp_attn_fwd(self.dims, r, self.causal, X, self.Wqkv[r], None if self.bqkv is None else self.bqkv[r],

@@ -273,6 +273,528 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams p) {
   if (p.lse != nullptr) p.lse[((int64_t)bidx * p.hl + jj) * p.s + q] = m + logf(l);
 }
 
+// ================================================================================================================
+// Backward.  With P = exp(S scale - lse) recomputed from the forward's log-sum-exp and D[q] = sum_e dO[q,e] O[q,e]
+// (equal to the row sum of P * dP, since O = P V): dV = P^T dO, dS = P * (dO V^T - D), dQ = dS K scale,
+// dK = dS^T Q scale.  Two kernels share no accumulators, so no atomics and the results are deterministic:
+//   * dK, dV: one workgroup = 64 keys of one (batch, head), 4 waves x 16 keys, walking the 64-query blocks that
+//     see them (causal: from the diagonal block on); Q, dO tiles and the blocks' (lse, D) record come by direct
+//     copies into a 3-stage ring.  S = Q K^T and dP = dO V^T take Q / dO rows from LDS and the wave's K / V
+//     fragments from registers; dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T with transposing LDS reads
+//     whose row addresses follow the query order of the P / dS operand (the forward's V trick).
+//   * dQ: the forward's structure (64 queries per workgroup, K and V tiles in the ring): S^T = K Q^T,
+//     dP^T = V dO^T, dQ^T += K^T dS^T with K^T gathered by transposing reads.
+// ================================================================================================================
+
+// Per (batch, head, 64-query block) record: [lse(64) | D(64) | 0(128)].
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdParams p) {
+  const int nqb = (p.s + 63) / 64;
+  const int rec_id = blockIdx.x;  // bh * nqb + qb
+  const int bh = rec_id / nqb, qb = rec_id % nqb;
+  const int bidx = bh / p.hl, jj = bh % p.hl;
+  const int t = threadIdx.x;
+  float* rec = p.rec + (int64_t)rec_id * 256;
+  if (t < 64) {
+    const int q = qb * 64 + t;
+    rec[t] = q < p.s ? p.lse[(int64_t)bh * p.s + q] : 0.f;
+  } else if (t < 128) {
+    // fp32 path: D from the stored O (fp32, so as good as the row sum of P * dP); the bf16 path gets D from its
+    // own pass over the keys (attn_bwd_dq_bf16_kernel<DP, true>) and starts from zero here
+    const int q = qb * 64 + (t - 64);
+    float acc = 0.f;
+    if (sizeof(T) == 4 && q < p.s) {
+      const int64_t off = ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * p.d) + (int64_t)jj * p.d;
+      const T* dO = static_cast<const T*>(p.dout) + off;
+      const T* O = static_cast<const T*>(p.o) + off;
+      for (int e = 0; e < p.d; ++e) {
+        float a, b;
+        if constexpr (sizeof(T) == 2) {
+          a = bf16_to_f32(dO[e]);
+          b = bf16_to_f32(O[e]);
+        } else {
+          a = dO[e];
+          b = O[e];
+        }
+        acc = fmaf(a, b, acc);
+      }
+    }
+    rec[t] = acc;
+  } else {
+    rec[t] = 0.f;
+  }
+}
+
+template <int DP>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams p) {
+  constexpr int CH = DP / 8;
+  constexpr int TILE_B = 64 * CH * 16;          // one Q (or dO) tile
+  constexpr int STAGE_B = 2 * TILE_B + 1024;    // Q tile, dO tile, (lse, D) record
+  constexpr int CPW = CH / 4;
+  constexpr int NDS = DP / 32, NST = DP / 16;
+  __shared__ __attribute__((aligned(16))) char lds[NSTG * STAGE_B];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int nqb = (p.s + 63) / 64;
+  const int nbh = p.b * p.hl;
+  const int ktile = (int)blockIdx.x / nbh;  // key block 0 sees the most queries: issued first
+  const int bh = (int)blockIdx.x % nbh;
+  const int bidx = bh / p.hl, jj = bh % p.hl;
+  const int d = p.d;
+  const int64_t ldq = (int64_t)p.hl * 3 * d;
+  const int64_t tok_stride = ldq * p.b;
+  const int64_t ldo = (int64_t)p.hl * d * p.b;  // dO row stride (consecutive sequence positions)
+  const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
+  const uint16_t* __restrict__ dob = static_cast<const uint16_t*>(p.dout) + (int64_t)bidx * p.hl * d + (int64_t)jj * d;
+  const float* __restrict__ recb = p.rec + (int64_t)bh * nqb * 256;
+
+  // ---- this lane's key: K and V fragments (k = d: lane supplies d = 32u + 8g .. +8)
+  const int key = ktile * 64 + wave * 16 + l16;
+  bf16x8_t kf[NDS], vf[NDS];
+#pragma unroll
+  for (int u = 0; u < NDS; ++u) {
+    const int dd = 32 * u + 8 * g;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+    if (key < p.s && dd < d) {
+      a = *reinterpret_cast<const uint4*>(qkv + (int64_t)key * tok_stride + d + dd);
+      b = *reinterpret_cast<const uint4*>(qkv + (int64_t)key * tok_stride + 2 * d + dd);
+    }
+    kf[u] = __builtin_bit_cast(bf16x8_t, a);
+    vf[u] = __builtin_bit_cast(bf16x8_t, b);
+  }
+  const int qb0 = p.causal ? ktile : 0;
+  const int nblk = nqb - qb0;
+
+  // ---- copies (same chunk rotation as the forward's K / V tiles); wave 0 also copies the block's record
+  int crow[CPW], ccol[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int P = (wave + 4 * i) * 64 + lane;
+    const int r = P / CH, slot = P % CH;
+    int c = slot - r % CH;
+    if (c < 0) c += CH;
+    crow[i] = r;
+    ccol[i] = (c * 8 < d) ? c * 8 : 0;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
+  auto issue_tile = [&](int i, int st) {
+    const int qb = qb0 + min(i, nblk - 1);  // past the last block: a harmless re-copy of it
+    const uint32_t sb = lds0 + st * STAGE_B;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int row = min(qb * 64 + crow[c], p.s - 1);
+      const uint32_t dst = sb + (wave + 4 * c) * 1024;
+      dma16(qkv + (int64_t)row * tok_stride + ccol[c], __builtin_amdgcn_readfirstlane(dst));
+      dma16(dob + (int64_t)row * ldo + ccol[c], __builtin_amdgcn_readfirstlane(dst + TILE_B));
+    }
+    if (wave == 0) dma16(recb + (int64_t)qb * 256 + 4 * lane, __builtin_amdgcn_readfirstlane(sb + 2 * TILE_B));
+  };
+  auto chunk_off = [&](int r, int c) { return r * CH * 16 + ((c + r) % CH) * 16; };
+  int roff[4][NDS];  // A fragments of Q / dO rows (queries 16 qs + l16), d = 32u + 8g
+#pragma unroll
+  for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+    for (int u = 0; u < NDS; ++u) roff[qs][u] = chunk_off(16 * qs + l16, 4 * u + g);
+  int toff[2][NST][2];  // transposing reads: rows = queries in the P / dS operand's order, columns = d
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int R = 32 * u + 16 * hh + 4 * g + (l16 >> 2);
+        const int dc = 16 * st + 4 * (l16 & 3);
+        toff[u][st][hh] = chunk_off(R, dc >> 3) + ((dc >> 2) & 1) * 8;
+      }
+  auto trfrag = [&](const char* base, int u, int st) {
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + toff[u][st][0]));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + toff[u][st][1]));
+    const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, w);
+  };
+
+  const float c2 = p.scale * 1.4426950408889634f;
+  f32x4_t dv[NST], dk[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) dv[st] = dk[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  issue_tile(0, 0);
+  issue_tile(1, 1);
+  if (wave == 0) wait_vmcnt<2 * CPW + 1>(); else wait_vmcnt<2 * CPW>();
+  __syncthreads();
+
+  int st_cur = 0, st_new = 2;
+  for (int i = 0; i < nblk; ++i) {
+    issue_tile(i + 2, st_new);
+    const char* Qt = &lds[st_cur * STAGE_B];
+    const char* Dt = Qt + TILE_B;
+    const float* R = reinterpret_cast<const float*>(Qt + 2 * TILE_B);
+    const int q0 = (qb0 + i) * 64;
+
+    f32x4_t sc[4], dp[4];
+#pragma unroll
+    for (int qs = 0; qs < 4; ++qs) {
+      sc[qs] = dp[qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NDS; ++u) {
+        const bf16x8_t qa = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Qt + roff[qs][u]));
+        const bf16x8_t da = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Dt + roff[qs][u]));
+        sc[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[u], sc[qs], 0, 0, 0);
+        dp[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[u], dp[qs], 0, 0, 0);
+      }
+    }
+    // P and dS for queries q0 + 16 qs + 4 g + e and this lane's key
+    const bool diag = p.causal && (qb0 + i) == ktile;
+    const bool ragged = q0 + 64 > p.s;
+    // P goes to the matrix cores as a bf16 pair hi + lo (lo = P - hi rounded again): with near-uniform weights
+    // a single bf16 P carries 2^-9 relative error into every term of dV's sum over queries
+    uint32_t pp[4][2], pl[4][2], dd2[4][2], dl2[4][2];
+#pragma unroll
+    for (int qs = 0; qs < 4; ++qs) {
+      const f32x4_t lse4 = *reinterpret_cast<const f32x4_t*>(R + 16 * qs + 4 * g);
+      const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(R + 64 + 16 * qs + 4 * g);
+      float pe[4], ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = fmaf(sc[qs][e], c2, -lse4[e] * 1.4426950408889634f);
+        if (diag || ragged) {
+          const int q = q0 + 16 * qs + 4 * g + e;
+          if (q >= p.s || (p.causal && key > q)) x = -INFINITY;
+        }
+        pe[e] = __builtin_amdgcn_exp2f(x);
+        ds[e] = pe[e] * (dp[qs][e] - D4[e]);
+      }
+      uint32_t hb[4];
+      float lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hb[e] = f32_to_bf16_hw(pe[e]);
+        lo[e] = pe[e] - bf16_to_f32(hb[e]);
+      }
+      pp[qs][0] = hb[0] | (hb[1] << 16);
+      pp[qs][1] = hb[2] | (hb[3] << 16);
+      pl[qs][0] = f32_to_bf16_hw(lo[0]) | (f32_to_bf16_hw(lo[1]) << 16);
+      pl[qs][1] = f32_to_bf16_hw(lo[2]) | (f32_to_bf16_hw(lo[3]) << 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hb[e] = f32_to_bf16_hw(ds[e]);
+        lo[e] = ds[e] - bf16_to_f32(hb[e]);
+      }
+      dd2[qs][0] = hb[0] | (hb[1] << 16);
+      dd2[qs][1] = hb[2] | (hb[3] << 16);
+      dl2[qs][0] = f32_to_bf16_hw(lo[0]) | (f32_to_bf16_hw(lo[1]) << 16);
+      dl2[qs][1] = f32_to_bf16_hw(lo[2]) | (f32_to_bf16_hw(lo[3]) << 16);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS over two 32-query steps (P and dS as hi + lo bf16 pairs)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pp[2 * u][0], pp[2 * u][1], pp[2 * u + 1][0], pp[2 * u + 1][1]));
+      const bf16x8_t plf = __builtin_bit_cast(bf16x8_t, make_uint4(pl[2 * u][0], pl[2 * u][1], pl[2 * u + 1][0], pl[2 * u + 1][1]));
+      const bf16x8_t sf = __builtin_bit_cast(bf16x8_t, make_uint4(dd2[2 * u][0], dd2[2 * u][1], dd2[2 * u + 1][0], dd2[2 * u + 1][1]));
+      const bf16x8_t slf = __builtin_bit_cast(bf16x8_t, make_uint4(dl2[2 * u][0], dl2[2 * u][1], dl2[2 * u + 1][0], dl2[2 * u + 1][1]));
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const bf16x8_t dot = trfrag(Dt, u, st);
+        dv[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dot, pf, dv[st], 0, 0, 0);
+        dv[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dot, plf, dv[st], 0, 0, 0);
+        const bf16x8_t qt = trfrag(Qt, u, st);
+        dk[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, sf, dk[st], 0, 0, 0);
+        dk[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, slf, dk[st], 0, 0, 0);
+      }
+    }
+    if (wave == 0) wait_vmcnt<2 * CPW + 1>(); else wait_vmcnt<2 * CPW>();
+    __syncthreads();
+    st_cur = st_cur == NSTG - 1 ? 0 : st_cur + 1;
+    st_new = st_new == NSTG - 1 ? 0 : st_new + 1;
+  }
+  wait_vmcnt<0>();
+
+  if (key < p.s) {
+    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + ((int64_t)key * p.b + bidx) * ldq + (int64_t)jj * 3 * d;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int dd = st * 16 + 4 * g;
+      if (dd < d) {
+        uint2 w;
+        w.x = f32_to_bf16_hw(dk[st][0] * p.scale) | (f32_to_bf16_hw(dk[st][1] * p.scale) << 16);
+        w.y = f32_to_bf16_hw(dk[st][2] * p.scale) | (f32_to_bf16_hw(dk[st][3] * p.scale) << 16);
+        *reinterpret_cast<uint2*>(out + d + dd) = w;
+        w.x = f32_to_bf16_hw(dv[st][0]) | (f32_to_bf16_hw(dv[st][1]) << 16);
+        w.y = f32_to_bf16_hw(dv[st][2]) | (f32_to_bf16_hw(dv[st][3]) << 16);
+        *reinterpret_cast<uint2*>(out + 2 * d + dd) = w;
+      }
+    }
+  }
+}
+
+// DPASS: instead of dQ, compute each query's D = sum_k P[q, k] dP[q, k] over all the keys it sees and write it into
+// the record (run before the dK / dV and dQ passes, which read it).  Taking D as the row sum of dO * O instead
+// would use the forward's bf16-rounded O, whose rounding reaches every element of dS = P * (dP - D).
+template <int DP, bool DPASS>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams p) {
+  constexpr int CH = DP / 8;
+  constexpr int TILE_B = KT * CH * 16;
+  constexpr int STAGE_B = 2 * TILE_B;   // K tile then V tile
+  constexpr int CPW = CH / 4;
+  constexpr int NC = 2 * CPW;
+  constexpr int NDS = DP / 32, NST = DP / 16;
+  __shared__ __attribute__((aligned(16))) char lds[NSTG * STAGE_B];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int nq = (p.s + QT - 1) / QT;
+  const int nbh = p.b * p.hl;
+  const int qtile = nq - 1 - (int)blockIdx.x / nbh;
+  const int bh = (int)blockIdx.x % nbh;
+  const int bidx = bh / p.hl, jj = bh % p.hl;
+  const int d = p.d;
+  const int64_t ldq = (int64_t)p.hl * 3 * d;
+  const int64_t tok_stride = ldq * p.b;
+  const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
+  const uint16_t* __restrict__ kbase = qkv + d;
+
+  // ---- this lane's query: Q and dO fragments, lse (log2 units) and D
+  const int q = qtile * QT + wave * 16 + l16;
+  bf16x8_t qf[NDS], df[NDS];
+#pragma unroll
+  for (int u = 0; u < NDS; ++u) {
+    const int dd = 32 * u + 8 * g;
+    uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
+    if (q < p.s && dd < d) {
+      a = *reinterpret_cast<const uint4*>(qkv + (int64_t)q * tok_stride + dd);
+      b = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.dout) +
+                                          ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jj * d + dd);
+    }
+    qf[u] = __builtin_bit_cast(bf16x8_t, a);
+    df[u] = __builtin_bit_cast(bf16x8_t, b);
+  }
+  const float lse2 = q < p.s ? p.lse[(int64_t)bh * p.s + q] * 1.4426950408889634f : 0.f;
+  float* const drec = p.rec + ((int64_t)bh * ((p.s + 63) / 64) + q / 64) * 256 + 64 + (q % 64);
+  const float Dq = (!DPASS && q < p.s) ? *drec : 0.f;
+  float dsum = 0.f;
+
+  const int nkt_all = (p.s + KT - 1) / KT;
+  const int nkt = p.causal ? min(nkt_all, qtile + 1) : nkt_all;
+
+  int crow[CPW], ccol[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int P = (wave + 4 * i) * 64 + lane;
+    const int r = P / CH, slot = P % CH;
+    int c = slot - r % CH;
+    if (c < 0) c += CH;
+    crow[i] = r;
+    ccol[i] = (c * 8 < d) ? c * 8 : 0;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
+  auto issue_tile = [&](int kt, int st) {
+    const int kv0 = min(kt, nkt - 1) * KT;
+    const uint32_t sb = lds0 + st * STAGE_B;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int row = min(kv0 + crow[i], p.s - 1);
+      const uint16_t* src = kbase + (int64_t)row * tok_stride + ccol[i];
+      const uint32_t dst = sb + (wave + 4 * i) * 1024;
+      dma16(src, __builtin_amdgcn_readfirstlane(dst));
+      dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
+    }
+  };
+  auto chunk_off = [&](int r, int c) { return r * CH * 16 + ((c + r) % CH) * 16; };
+  int koff[4][NDS];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int u = 0; u < NDS; ++u) koff[ks][u] = chunk_off(16 * ks + l16, 4 * u + g);
+  int toff[2][NST][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int R = 32 * u + 16 * hh + 4 * g + (l16 >> 2);
+        const int dc = 16 * st + 4 * (l16 & 3);
+        toff[u][st][hh] = chunk_off(R, dc >> 3) + ((dc >> 2) & 1) * 8;
+      }
+
+  const float c2 = p.scale * 1.4426950408889634f;
+  f32x4_t dq[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) dq[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  issue_tile(0, 0);
+  issue_tile(1, 1);
+  wait_vmcnt<NC>();
+  __syncthreads();
+
+  int st_cur = 0, st_new = 2;
+  for (int kt = 0; kt < nkt; ++kt) {
+    issue_tile(kt + 2, st_new);
+    const char* Kt = &lds[st_cur * STAGE_B];
+    const char* Vt = Kt + TILE_B;
+    const int kv0 = kt * KT;
+    f32x4_t sc[4], dp[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      sc[ks] = dp[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NDS; ++u) {
+        const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Kt + koff[ks][u]));
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Vt + koff[ks][u]));
+        sc[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[u], sc[ks], 0, 0, 0);
+        dp[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, df[u], dp[ks], 0, 0, 0);
+      }
+    }
+    const bool need_mask = (p.causal && kt == qtile) || (kv0 + KT > p.s);
+    uint32_t dk2[4][2], dl2[4][2];  // dS as a hi + lo bf16 pair
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float ds[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = fmaf(sc[ks][e], c2, -lse2);
+        if (need_mask) {
+          const int kv = kv0 + ks * 16 + 4 * g + e;
+          if (kv >= p.s || (p.causal && kv > q)) x = -INFINITY;
+        }
+        const float pe = __builtin_amdgcn_exp2f(x);
+        if constexpr (DPASS) dsum = fmaf(pe, dp[ks][e], dsum);
+        ds[e] = pe * (dp[ks][e] - Dq);
+      }
+      uint32_t hb[4];
+      float lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hb[e] = f32_to_bf16_hw(ds[e]);
+        lo[e] = ds[e] - bf16_to_f32(hb[e]);
+      }
+      dk2[ks][0] = hb[0] | (hb[1] << 16);
+      dk2[ks][1] = hb[2] | (hb[3] << 16);
+      dl2[ks][0] = f32_to_bf16_hw(lo[0]) | (f32_to_bf16_hw(lo[1]) << 16);
+      dl2[ks][1] = f32_to_bf16_hw(lo[2]) | (f32_to_bf16_hw(lo[3]) << 16);
+    }
+#pragma unroll
+    for (int u = 0; u < (DPASS ? 0 : 2); ++u) {
+      const bf16x8_t sf = __builtin_bit_cast(bf16x8_t, make_uint4(dk2[2 * u][0], dk2[2 * u][1], dk2[2 * u + 1][0], dk2[2 * u + 1][1]));
+      const bf16x8_t slf = __builtin_bit_cast(bf16x8_t, make_uint4(dl2[2 * u][0], dl2[2 * u][1], dl2[2 * u + 1][0], dl2[2 * u + 1][1]));
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Kt + toff[u][st][0]));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Kt + toff[u][st][1]));
+        const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8_t kt_ = __builtin_bit_cast(bf16x8_t, w);
+        dq[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt_, sf, dq[st], 0, 0, 0);
+        dq[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt_, slf, dq[st], 0, 0, 0);
+      }
+    }
+    wait_vmcnt<NC>();
+    __syncthreads();
+    st_cur = st_cur == NSTG - 1 ? 0 : st_cur + 1;
+    st_new = st_new == NSTG - 1 ? 0 : st_new + 1;
+  }
+  wait_vmcnt<0>();
+
+  if constexpr (DPASS) {
+    dsum += __shfl_xor(dsum, 16);
+    dsum += __shfl_xor(dsum, 32);
+    if (q < p.s && g == 0) *drec = dsum;
+    return;
+  }
+  if (q < p.s) {
+    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + ((int64_t)q * p.b + bidx) * ldq + (int64_t)jj * 3 * d;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int dd = st * 16 + 4 * g;
+      if (dd < d) {
+        uint2 w;
+        w.x = f32_to_bf16_hw(dq[st][0] * p.scale) | (f32_to_bf16_hw(dq[st][1] * p.scale) << 16);
+        w.y = f32_to_bf16_hw(dq[st][2] * p.scale) | (f32_to_bf16_hw(dq[st][3] * p.scale) << 16);
+        *reinterpret_cast<uint2*>(out + dd) = w;
+      }
+    }
+  }
+}
+
+// fp32 backward: one thread per query (dQ) or per key (dK, dV), plain loops over the other side.
+__global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(AttnBwdParams p) {
+  constexpr int DMAX = 128;
+  const int q = blockIdx.x * 64 + threadIdx.x;
+  const int bh = blockIdx.y;
+  const int bidx = bh / p.hl, jj = bh % p.hl;
+  if (q >= p.s) return;
+  const int d = p.d;
+  const int64_t ldq = (int64_t)p.hl * 3 * d, tok = ldq * p.b;
+  const float* qkv = static_cast<const float*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
+  const float* qv = qkv + (int64_t)q * tok;
+  const float* dov = static_cast<const float*>(p.dout) + ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jj * d;
+  const float lse = p.lse[(int64_t)bh * p.s + q];
+  const float D = p.rec[((int64_t)bh * ((p.s + 63) / 64) + q / 64) * 256 + 64 + (q % 64)];
+  float acc[DMAX];
+  for (int e = 0; e < d; ++e) acc[e] = 0.f;
+  const int nk = p.causal ? q + 1 : p.s;
+  for (int k = 0; k < nk; ++k) {
+    const float* kv = qkv + (int64_t)k * tok;
+    float sdot = 0.f, dpv = 0.f;
+    for (int e = 0; e < d; ++e) {
+      sdot = fmaf(qv[e], kv[d + e], sdot);
+      dpv = fmaf(dov[e], kv[2 * d + e], dpv);
+    }
+    const float ds = expf(sdot * p.scale - lse) * (dpv - D);
+    for (int e = 0; e < d; ++e) acc[e] = fmaf(ds, kv[d + e], acc[e]);
+  }
+  float* out = static_cast<float*>(p.dqkv) + ((int64_t)q * p.b + bidx) * ldq + (int64_t)jj * 3 * d;
+  for (int e = 0; e < d; ++e) out[e] = acc[e] * p.scale;
+}
+
+__global__ __launch_bounds__(64) void attn_bwd_dkv_f32_kernel(AttnBwdParams p) {
+  constexpr int DMAX = 128;
+  const int k = blockIdx.x * 64 + threadIdx.x;
+  const int bh = blockIdx.y;
+  const int bidx = bh / p.hl, jj = bh % p.hl;
+  if (k >= p.s) return;
+  const int d = p.d;
+  const int64_t ldq = (int64_t)p.hl * 3 * d, tok = ldq * p.b;
+  const float* qkv = static_cast<const float*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
+  const float* kv = qkv + (int64_t)k * tok;
+  const int nqb = (p.s + 63) / 64;
+  float dk[DMAX], dv[DMAX];
+  for (int e = 0; e < d; ++e) dk[e] = dv[e] = 0.f;
+  for (int q = p.causal ? k : 0; q < p.s; ++q) {
+    const float* qv = qkv + (int64_t)q * tok;
+    const float* dov = static_cast<const float*>(p.dout) + ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jj * d;
+    const float lse = p.lse[(int64_t)bh * p.s + q];
+    const float D = p.rec[((int64_t)bh * nqb + q / 64) * 256 + 64 + (q % 64)];
+    float sdot = 0.f, dpv = 0.f;
+    for (int e = 0; e < d; ++e) {
+      sdot = fmaf(qv[e], kv[d + e], sdot);
+      dpv = fmaf(dov[e], kv[2 * d + e], dpv);
+    }
+    const float pe = expf(sdot * p.scale - lse);
+    const float ds = pe * (dpv - D);
+    for (int e = 0; e < d; ++e) {
+      dv[e] = fmaf(pe, dov[e], dv[e]);
+      dk[e] = fmaf(ds, qv[e], dk[e]);
+    }
+  }
+  float* out = static_cast<float*>(p.dqkv) + ((int64_t)k * p.b + bidx) * ldq + (int64_t)jj * 3 * d;
+  for (int e = 0; e < d; ++e) {
+    out[d + e] = dk[e] * p.scale;
+    out[2 * d + e] = dv[e];
+  }
+}
+
+template <int DP>
+hipError_t launch_bwd_bf16(const AttnBwdParams& p, hipStream_t st) {
+  const int nq = (p.s + 63) / 64;
+  const unsigned grid = (unsigned)(nq * p.b * p.hl);
+  static const std::string n0 = "attn_bwd_delta_bf16_d" + std::to_string(DP);
+  static const std::string n1 = "attn_bwd_dkv_bf16_d" + std::to_string(DP);
+  static const std::string n2 = "attn_bwd_dq_bf16_d" + std::to_string(DP);
+  hipError_t e = TP_LAUNCH(n0.c_str(), (attn_bwd_dq_bf16_kernel<DP, true>), dim3(grid), dim3(256), 0, st, p);
+  if (e == hipSuccess) e = TP_LAUNCH(n1.c_str(), (attn_bwd_dkv_bf16_kernel<DP>), dim3(grid), dim3(256), 0, st, p);
+  if (e == hipSuccess) e = TP_LAUNCH(n2.c_str(), (attn_bwd_dq_bf16_kernel<DP, false>), dim3(grid), dim3(256), 0, st, p);
+  return e;
+}
+
 template <int DP>
 hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
   const int nq = (p.s + QT - 1) / QT;
@@ -288,6 +810,28 @@ hipError_t attention_bf16(const AttnParams& p, hipStream_t st) {
   if (p.d <= 64) return launch_bf16<64>(p, st);
   if (p.d <= 96) return launch_bf16<96>(p, st);
   return launch_bf16<128>(p, st);
+}
+
+hipError_t attention_bwd(tp_dtype dt, const AttnBwdParams& p, hipStream_t st) {
+  if (p.s <= 0 || p.b <= 0 || p.hl <= 0) return hipSuccess;
+  const int nqb = (p.s + 63) / 64;
+  hipError_t e;
+  if (dt == TP_BF16) {
+    e = TP_LAUNCH("attn_bwd_prep_bf16", attn_bwd_prep_kernel<uint16_t>, dim3((unsigned)(nqb * p.b * p.hl)), dim3(256), 0,
+                  st, p);
+    if (e != hipSuccess) return e;
+    if (p.d <= 32) return launch_bwd_bf16<32>(p, st);
+    if (p.d <= 64) return launch_bwd_bf16<64>(p, st);
+    if (p.d <= 96) return launch_bwd_bf16<96>(p, st);
+    return launch_bwd_bf16<128>(p, st);
+  }
+  e = TP_LAUNCH("attn_bwd_prep_f32", attn_bwd_prep_kernel<float>, dim3((unsigned)(nqb * p.b * p.hl)), dim3(256), 0, st,
+                p);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((p.s + 63) / 64), (unsigned)(p.b * p.hl));
+  e = TP_LAUNCH("attn_bwd_dkv_f32", attn_bwd_dkv_f32_kernel, grid, dim3(64), 0, st, p);
+  if (e == hipSuccess) e = TP_LAUNCH("attn_bwd_dq_f32", attn_bwd_dq_f32_kernel, grid, dim3(64), 0, st, p);
+  return e;
 }
 
 hipError_t attention_f32(const AttnParams& p, hipStream_t st) {

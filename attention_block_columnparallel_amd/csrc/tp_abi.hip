@@ -330,6 +330,79 @@ int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
   return hip_status(e);
 }
 
+int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const void* X, const void* Wqkv_i,
+                const void* Wo_i, const void* QKV_i, const void* O_i, const float* lse_i, const void* dZ, void* dO_ws,
+                float* rec_ws, void* dQKV_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i, void* dX_i,
+                hipStream_t stream) {
+  if (dims == nullptr || X == nullptr || Wqkv_i == nullptr || Wo_i == nullptr || QKV_i == nullptr ||
+      O_i == nullptr || lse_i == nullptr || dZ == nullptr || dO_ws == nullptr || rec_ws == nullptr ||
+      dQKV_i == nullptr || dWqkv_i == nullptr || dWo_i == nullptr || dX_i == nullptr)
+    return TP_E_NULL;
+  const int64_t s = dims->s, b = dims->b, h = dims->h, a = dims->a, d = dims->d, t = dims->t;
+  if (s <= 0 || b <= 0 || h <= 0 || a <= 0 || d <= 0 || t <= 0) return TP_E_SHAPE;
+  if (s * b >= kMaxDim || h >= kMaxDim) return TP_E_SHAPE;
+  if (a % t != 0 || h != a * d) return TP_E_DIVISIBILITY;
+  if (rank < 0 || rank >= t) return TP_E_RANK;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  if (d > 128) return TP_E_UNSUPPORTED;
+  const int64_t M = s * b, hl = a / t, n = 3 * hl * d, es = esize(dtype), nqb = (s + 63) / 64;
+  if (dtype == TP_BF16 && (h % 8 != 0 || d % 8 != 0 ||
+                           misaligned16({X, Wqkv_i, Wo_i, QKV_i, O_i, dZ, dO_ws, rec_ws, dQKV_i, dWqkv_i, dbqkv_i,
+                                         dWo_i, dX_i})))
+    return TP_E_UNSUPPORTED;
+  const Buf outs[] = {{dO_ws, M * hl * d * es}, {rec_ws, b * hl * nqb * 256 * 4}, {dQKV_i, M * n * es},
+                      {dWqkv_i, h * n * es},     {dbqkv_i, n * es},                  {dWo_i, hl * d * h * es},
+                      {dX_i, M * h * es}};
+  const Buf ins[] = {{X, M * h * es},     {Wqkv_i, h * n * es},     {Wo_i, hl * d * h * es}, {QKV_i, M * n * es},
+                     {O_i, M * hl * d * es}, {lse_i, b * hl * s * 4}, {dZ, M * h * es}};
+  if (any_alias(outs, 7, ins, 7)) return TP_E_ALIAS;
+
+  // dO = dZ Wo_i^T (the projection's data gradient)
+  tp::GemmParams gd = {};
+  gd.A = dZ; gd.lda = h;
+  gd.B = Wo_i; gd.ldb = h;
+  gd.M = (int)M; gd.N = (int)(hl * d); gd.K = (int)h;
+  gd.C = dO_ws; gd.ldc = hl * d;
+  // attention core backward into dQKV_i
+  tp::AttnBwdParams bp = {};
+  bp.qkv = QKV_i; bp.o = O_i; bp.dout = dO_ws; bp.lse = lse_i; bp.rec = rec_ws; bp.dqkv = dQKV_i;
+  bp.s = (int)s; bp.b = (int)b; bp.hl = (int)hl; bp.d = (int)d;
+  bp.causal = causal ? 1 : 0;
+  bp.scale = (float)(1.0 / __builtin_sqrt((double)d));
+  // weight gradients dWo_i = O_i^T dZ and dWqkv_i = X^T dQKV_i (both over K = s*b)
+  tp::GemmParams gwo = {};
+  gwo.A = O_i; gwo.lda = hl * d;
+  gwo.B = dZ; gwo.ldb = h;
+  gwo.M = (int)(hl * d); gwo.N = (int)h; gwo.K = (int)M;
+  gwo.C = dWo_i; gwo.ldc = h;
+  tp::GemmParams gwq = {};
+  gwq.A = X; gwq.lda = h;
+  gwq.B = dQKV_i; gwq.ldb = n;
+  gwq.M = (int)h; gwq.N = (int)n; gwq.K = (int)M;
+  gwq.C = dWqkv_i; gwq.ldc = n;
+  // the partial dX_i = dQKV_i Wqkv_i^T
+  tp::GemmParams gx = {};
+  gx.A = dQKV_i; gx.lda = n;
+  gx.B = Wqkv_i; gx.ldb = n;
+  gx.M = (int)M; gx.N = (int)h; gx.K = (int)n;
+  gx.C = dX_i; gx.ldc = h;
+
+  auto gemm = dtype == TP_BF16 ? tp::gemm_bf16 : tp::gemm_f32;
+  hipError_t e = gemm(gd, true, true, tp::EPI_STORE, stream);
+  if (e == hipSuccess) e = tp::attention_bwd(dtype, bp, stream);
+  if (e == hipSuccess) {
+    if (dtype == TP_BF16) {
+      e = tp::gemm_bf16_wgrad_pair(gwo, gwq, stream);
+    } else {
+      e = gemm(gwo, false, false, tp::EPI_STORE, stream);
+      if (e == hipSuccess) e = gemm(gwq, false, false, tp::EPI_STORE, stream);
+    }
+  }
+  if (e == hipSuccess && dbqkv_i != nullptr) e = tp::colsum(dtype, dQKV_i, M, n, dbqkv_i, stream);
+  if (e == hipSuccess) e = gemm(gx, true, true, tp::EPI_STORE, stream);
+  return hip_status(e);
+}
+
 int tp_partial_reduce(int64_t n, int64_t h, int t, tp_dtype dtype, const void* partials, const void* bias_c,
                       void* out, hipStream_t stream) {
   if (partials == nullptr || out == nullptr) return TP_E_NULL;

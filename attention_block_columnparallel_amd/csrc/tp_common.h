@@ -169,4 +169,19 @@ struct AttnParams {
 hipError_t attention_bf16(const AttnParams& p, hipStream_t st);
 hipError_t attention_f32(const AttnParams& p, hipStream_t st);
 
+// Attention backward core.  rec: per (batch, head, 64-query block) one 256-float record [lse(64) | D(64) | 0(128)]
+// with D[q] = sum_e dO[q, e] O[q, e]; written by attention_bwd_prep, read by the dK/dV and dQ kernels.
+struct AttnBwdParams {
+  const void* qkv;   // [s, b, hl*3d] grouped [q_j k_j v_j]
+  const void* o;     // [s, b, hl*d]
+  const void* dout;  // [s, b, hl*d]
+  const float* lse;  // [b, hl, s]
+  float* rec;        // [b, hl, ceil(s/64), 256]
+  void* dqkv;        // [s, b, hl*3d] grouped like qkv
+  int s, b, hl, d;
+  int causal;
+  float scale;       // 1/sqrt(d)
+};
+hipError_t attention_bwd(tp_dtype dt, const AttnBwdParams& p, hipStream_t st);
+
 }  // namespace tp

@@ -76,9 +76,11 @@ def profiled_traffic(workload: str, kernel: str):
 
 
 def attention_block_measure(L, steps: int, warmup: int) -> dict:
-    """The attention block forward at the 22B-class shape (h=6144, 64 heads of 96, s=4096, t=8, causal): for every
+    """The attention block at the 22B-class shape (h=6144, 64 heads of 96, s=4096, t=8, causal).  Forward: for every
     rank the QKV GEMM, local causal attention and output projection into partial i, then the dim-0 reduce-scatter.
-    Per-kernel HIP-event durations; causal attention counts only unmasked query-key pairs."""
+    Backward: for every rank tp_attn_bwd (dO GEMM, attention core backward, the weight-gradient pair, the dX GEMM),
+    then the reduce-scatter of the dX partials.  Per-kernel HIP-event durations; causal attention counts only
+    unmasked query-key pairs (forward 4 d, backward 10 d flops per pair)."""
     import numpy as np
     import torch
 
@@ -96,7 +98,7 @@ def attention_block_measure(L, steps: int, warmup: int) -> dict:
     for _ in range(warmup):
         blk.forward(X, sp=True)
     torch.cuda.synchronize()
-    timer = L.LaunchTimer(capacity=steps * (3 * w.t + 1) + 8)
+    timer = L.LaunchTimer(capacity=steps * (3 * w.t + 1) + 8)  # forward
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     with timer:
@@ -131,7 +133,50 @@ def attention_block_measure(L, steps: int, warmup: int) -> dict:
             k["bytes_per_launch"] = nbytes
             k["gbps"] = round(nbytes / (avg * 1e-3) / 1e9, 1)
         out["kernels"][role] = k
-    del blk, X
+    # backward: every rank's tp_attn_bwd, then the f reduction of the dX partials (dim-0 reduce-scatter)
+    dZ = dev(inp["dZ"])
+    for _ in range(warmup):
+        blk.backward(X, dZ, sp=True)
+    torch.cuda.synchronize()
+    timer = L.LaunchTimer(capacity=steps * (10 * w.t + 1) + 8)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    with timer:
+        for _ in range(steps):
+            blk.backward(X, dZ, sp=True)
+    e1.record()
+    torch.cuda.synchronize()
+    pairs = w.s * (w.s + 1) / 2 * w.b * hl
+    bfl = {"dO_gemm": 2.0 * M * w.h * hl * w.d, "attention_core_bwd": 10.0 * w.d * pairs,
+           "wgrad_pair": 2.0 * M * hl * w.d * w.h + 2.0 * M * w.h * 3 * hl * w.d, "dX_gemm": 2.0 * M * 3 * hl * w.d * w.h}
+    roles = {}
+    seq = []
+    for name, ms in timer.results():
+        if name.startswith("reduce"):
+            role = "reduce_scatter"
+        elif name.startswith("attn_bwd"):
+            role = "attention_core_bwd"
+        elif "_pair_" in name or name.endswith("MM_store"):
+            role = "wgrad_pair"
+        else:  # the two data-gradient GEMMs of a rank: dO first, dX last
+            role = "dO_gemm" if not seq or seq[-1] in ("dX_gemm", "reduce_scatter") else "dX_gemm"
+        seq.append(role)
+        r = roles.setdefault(role, {"kernels": {}, "ms": 0.0})
+        r["ms"] += ms
+        r["kernels"][name] = r["kernels"].get(name, 0.0) + ms
+    bwd = {"ms_per_step": round(e0.elapsed_time(e1) / steps, 4), "roles": {}}
+    bwd["tflops_block"] = round(w.t * sum(bfl.values()) / (bwd["ms_per_step"] * 1e-3) / 1e12, 1)
+    for role, r in roles.items():
+        per_rank_us = 1e3 * r["ms"] / steps / (1 if role == "reduce_scatter" else w.t)
+        k = {"us_per_rank" if role != "reduce_scatter" else "us_per_step": round(per_rank_us, 2),
+             "kernels_us_per_rank": {n: round(1e3 * v / steps / (1 if role == "reduce_scatter" else w.t), 2)
+                                    for n, v in r["kernels"].items()}}
+        if role in bfl:
+            k["tflops"] = round(bfl[role] / (per_rank_us * 1e-6) / 1e12, 1)
+            k["frac_bf16_peak"] = round(bfl[role] / (per_rank_us * 1e-6) / PEAK_BF16_FLOPS, 4)
+        bwd["roles"][role] = k
+    out["backward"] = bwd
+    del blk, X, dZ
     return out
 
 

@@ -120,10 +120,30 @@ int tp_mlp_bwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const 
  *                                   [s, b, (a/t)*d], head j at columns j*d .. j*d+d-1
  *   lse_i = log sum_k exp(S[q, k]) per (b, local head, q), fp32 [b, a/t, s] (nullable)
  *   Z_i   = O_i Wo_i                [s, b, h], a partial sum (no row bias)
- * Wqkv_i [h, (a/t)*3d] and Wo_i [(a/t)*d, h] as produced by tp_shard_weights.  bf16 path: d % 16 == 0, d <= 128.
+ * Wqkv_i [h, (a/t)*3d] and Wo_i [(a/t)*d, h] as produced by tp_shard_weights.  bf16 path: d % 8 == 0, d <= 128.
  * fp32 path: d <= 128. */
 int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const void* X, const void* Wqkv_i,
                 const void* bqkv_i, const void* Wo_i, void* QKV_i, void* O_i, float* lse_i, void* Z_i,
+                hipStream_t stream);
+
+/* Attention backward of rank `rank` for its a/t local heads, given the upstream gradient dZ of the block output
+ * ([ATLAS] §2 and §5: g's backward is the identity, so every rank receives the full dZ (gathered under SP); the
+ * row-parallel projection's weight gradient and the column-parallel QKV's weight gradient stay local, the data
+ * gradient dX is a partial that f sums over ranks; [SPLIT] backward of the column and row splits):
+ *   dO_ws   = dZ Wo_i^T                          [s, b, (a/t)*d]    caller workspace (activation dtype)
+ *   rec_ws  = per (b, local head, 64-query block) [lse(64) | D(64) | 0(128)], D[q] = sum_e dO[q,e] O[q,e]
+ *                                                fp32 [b, a/t, ceil(s/64), 256], caller workspace
+ *   dQKV_i  = per head dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO with P recomputed from lse_i
+ *             (P = exp(S - lse)) and dS = P * (dO V^T - D)          [s, b, (a/t)*3d], grouped like QKV_i
+ *   dWqkv_i = X^T dQKV_i                         [h, (a/t)*3d]     local weight gradient
+ *   dbqkv_i = column sums of dQKV_i (nullable)   [(a/t)*3d]
+ *   dWo_i   = O_i^T dZ                           [(a/t)*d, h]      local weight gradient
+ *   dX_i    = dQKV_i Wqkv_i^T                    [s, b, h]         a partial: f sums them over ranks
+ * QKV_i, O_i and lse_i (not nullable here) are the forward's outputs for the same inputs and `causal`.  The
+ * alignment and head-size rules of tp_attn_fwd apply; outputs and workspaces must not overlap the inputs. */
+int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const void* X, const void* Wqkv_i,
+                const void* Wo_i, const void* QKV_i, const void* O_i, const float* lse_i, const void* dZ, void* dO_ws,
+                float* rec_ws, void* dQKV_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i, void* dX_i,
                 hipStream_t stream);
 
 /* g in forward / f in backward, all-reduce form ([ATLAS] §2; [SPLIT] row-parallel merge is a sum):

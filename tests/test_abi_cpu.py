@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
-    for n in ["tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd", "tp_attn_fwd", "tp_partial_reduce",
+    for n in ["tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce",
               "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_status_str"]:
         assert n in names
 
@@ -108,6 +108,25 @@ def test_attn_fwd_validation(L):
     assert call(L.make_dims(**{**ok, "h": 48, "d": 12})) == -7     # bf16 needs d % 8 == 0
     assert call(L.make_dims(**ok), rank=2) == -5
     assert call(L.make_dims(**ok), p=P[:4] + [P[0]] + P[5:]) == -6  # QKV_i aliases X
+
+
+def test_attn_bwd_validation(L):
+    # X, Wqkv_i, Wo_i, QKV_i, O_i, lse_i, dZ, dO_ws, rec_ws, dQKV_i, dWqkv_i, dbqkv_i, dWo_i, dX_i
+    P = [addr(i) for i in range(14)]
+    call = lambda dims, rank=0, dt=BF16, p=P: L.tp_attn_bwd(dims, rank, True, *p, stream=0, dtype=dt, check=False)
+    ok = dict(s=64, b=1, h=128, a=4, d=32, t=2)
+    for i in range(14):
+        if i != 11:                                                  # dbqkv_i is nullable
+            assert call(L.make_dims(**ok), p=P[:i] + [None] + P[i + 1:]) == -1, i
+    assert call(L.make_dims(**{**ok, "s": 0})) == -2
+    assert call(L.make_dims(**{**ok, "a": 3})) == -3               # heads % t
+    assert call(L.make_dims(**{**ok, "d": 16})) == -3              # h != a*d
+    assert call(L.make_dims(**ok), rank=2) == -5
+    assert call(L.make_dims(**ok), dt=5) == -4
+    assert call(L.make_dims(**{**ok, "h": 1024, "d": 256})) == -7  # d > 128
+    assert call(L.make_dims(**{**ok, "h": 48, "d": 12})) == -7     # bf16 needs d % 8 == 0
+    assert call(L.make_dims(**ok), p=P[:9] + [P[0]] + P[10:]) == -6  # dQKV_i aliases X
+    assert call(L.make_dims(**ok), p=P[:8] + [P[5]] + P[9:]) == -6   # rec_ws aliases lse_i
 
 
 def test_reduce_and_gather_validation(L):

@@ -120,13 +120,15 @@ def mlp_inputs(w: Workload, with_bias: bool = False, seed: Optional[int] = None)
 
 
 def attn_inputs(w: Workload, with_bias: bool = False, seed: Optional[int] = None) -> dict:
-    """Full attention inputs: X [s,b,h], Wqkv [h, 3ad] = [Wq|Wk|Wv] (head-major columns), Wo [ad, h]."""
+    """Full attention inputs: X [s,b,h], Wqkv [h, 3ad] = [Wq|Wk|Wv] (head-major columns), Wo [ad, h], and the
+    upstream gradient dZ [s,b,h] for the backward."""
     sd = w.seed if seed is None else seed
     ad = w.a * w.d
     out = {
         "X": tensor(sd, T_X, (w.s, w.b, w.h), 1.0, w.dtype),
         "Wqkv": tensor(sd, T_A, (w.h, 3 * ad), WEIGHT_STD, w.dtype),
         "Wo": tensor(sd, T_B, (ad, w.h), WEIGHT_STD, w.dtype),
+        "dZ": tensor(sd, T_DZ, (w.s, w.b, w.h), 1.0, w.dtype),
         "bqkv": None,
         "c": None,
     }
