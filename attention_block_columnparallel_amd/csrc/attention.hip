@@ -15,8 +15,11 @@
 //     16+4g..16+4g+3 of each 32-key step (g = lane >> 4); the V^T fragment is gathered from the untransposed V
 //     tile by two transposing LDS reads (ds_read_b64_tr_b16) whose row addresses follow the same key order, so the
 //     pair of operands agree on k.
+//   * Each block reads all its K fragments before the S^T MFMAs and all its V^T fragments right after them, so
+//     the read latency overlaps the MFMAs and the softmax arithmetic; the causal mask is one select per score.
 //   * Softmax in base 2 with the scale folded into one FMA per score (exp2(s c - m c), c = scale log2 e) and the
-//     hardware exp2; the running output is rescaled only in blocks where some query's maximum rose.
+//     hardware exp2; row statistics combine the 4 lane groups with the gfx950 lane swaps; the running output is
+//     rescaled only in blocks where some query's maximum rose.
 //   * Query tiles are issued heaviest first over all heads (causal work grows with the tile index).
 #include <math.h>
 
@@ -36,7 +39,10 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 constexpr int QT = 64;   // queries per workgroup
 constexpr int KT = 64;   // keys per block
-constexpr int NSTG = 3;  // LDS stages
+// LDS stages (forward and backward kernels); 2 stages with three workgroups per CU and 4 stages with one each
+// measured slower for the forward kernel at d = 96
+constexpr int NSTG_F = 3;
+constexpr int NSTG = 3;
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -46,6 +52,22 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
 }
 #pragma clang diagnostic pop
+// Max / sum over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48) with the gfx950 lane swaps: with
+// both operands equal, permlane32_swap returns {v[l], v[l^32]} in some order in its two results, permlane16_swap
+// {v[l], v[l^16]}.  Every lane of a column ends with the same value.
+__device__ __forceinline__ float max_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -60,7 +82,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
   constexpr int NC = 2 * CPW;           // copies per wave per block (K and V)
   constexpr int NDS = DP / 32;          // 32-wide d steps of S^T
   constexpr int NST = DP / 16;          // 16-row d subtiles of O^T
-  __shared__ __attribute__((aligned(16))) char lds[NSTG * STAGE_B];
+  __shared__ __attribute__((aligned(16))) char lds[NSTG_F * STAGE_B];
+  constexpr int D = NSTG_F - 1;  // blocks in flight ahead of the one being multiplied
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int nq = (p.s + QT - 1) / QT;
@@ -87,6 +110,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
 
   const int nkt_all = (p.s + KT - 1) / KT;
   const int nkt = p.causal ? min(nkt_all, qtile + 1) : nkt_all;
+  const int klim = p.causal ? min(q, p.s - 1) : p.s - 1;  // last key this lane's query sees
 
   // ---- copies: copy c (0 .. CH-1) of a tile fills LDS chunks 64 c .. 64 c + 63; wave w issues copies w + 4 i.
   // LDS chunk position P = r CH + slot holds chunk (slot - r) mod CH of row r (chunks past d repeat chunk 0).
@@ -138,44 +162,58 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
 #pragma unroll
   for (int st = 0; st < NST; ++st) acc_o[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  issue_tile(0, 0);
-  issue_tile(1, 1);
-  wait_vmcnt<NC>();  // block 0 has landed (block 1 may still be in flight)
+#pragma unroll
+  for (int i = 0; i < D; ++i) issue_tile(i, i);
+  wait_vmcnt<(D - 1) * NC>();  // block 0 has landed (blocks 1 .. D-1 may still be in flight)
   __syncthreads();
 
-  int st_cur = 0, st_new = 2;
+  int st_cur = 0, st_new = D;
   for (int kt = 0; kt < nkt; ++kt) {
-    issue_tile(kt + 2, st_new);
+    issue_tile(kt + D, st_new);
     const char* Kt = &lds[st_cur * STAGE_B];
     const char* Vt = Kt + TILE_B;
     const int kv0 = kt * KT;
 
+    // all K fragment reads of the block first, then the S^T MFMAs (each finds its operand landed)
+    bf16x8_t kfr[4][NDS];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int u = 0; u < NDS; ++u) kfr[ks][u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Kt + koff[ks][u]));
+    __builtin_amdgcn_sched_barrier(0);
     // S^T [64 keys x 16 queries] in 4 subtiles of 16 keys
     f32x4_t sc[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       sc[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < NDS; ++u) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Kt + koff[ks][u]));
-        sc[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[u], sc[ks], 0, 0, 0);
-      }
+      for (int u = 0; u < NDS; ++u) sc[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[ks][u], qf[u], sc[ks], 0, 0, 0);
     }
-    // mask (diagonal and ragged blocks only), block max of the raw scores
-    const bool need_mask = (p.causal && kt == qtile) || (kv0 + KT > p.s);
+    // V^T fragments for the PV step, read now so their latency overlaps the softmax arithmetic
+    bf16x8_t vfr[2][NST];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[u][st][0]));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[u][st][1]));
+        const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        vfr[u][st] = __builtin_bit_cast(bf16x8_t, w);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    // mask (diagonal and ragged blocks only): key kv is visible iff kv <= klim; block max of the raw scores
+    if ((p.causal && kt == qtile) || (kv0 + KT > p.s)) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[ks][e] = (kv0 + ks * 16 + 4 * g + e > klim) ? -INFINITY : sc[ks][e];
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (need_mask) {
-          const int kv = kv0 + ks * 16 + 4 * g + e;
-          if (kv >= p.s || (p.causal && kv > q)) sc[ks][e] = -INFINITY;
-        }
-        mx = fmaxf(mx, sc[ks][e]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[ks][e]);
+    mx = max_over_groups(mx);
     const float m_new = fmaxf(m_run, mx);
     if (__any(m_new > m_run)) {  // some query's maximum rose: rescale (corr = 1 where it did not)
       const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
@@ -205,23 +243,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
     for (int u = 0; u < 2; ++u) {
       const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pk[2 * u][0], pk[2 * u][1], pk[2 * u + 1][0], pk[2 * u + 1][1]));
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[u][st][0]));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[u][st][1]));
-        const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc_o[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pf, acc_o[st], 0, 0, 0);
-      }
+      for (int st = 0; st < NST; ++st) acc_o[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[u][st], pf, acc_o[st], 0, 0, 0);
     }
-    wait_vmcnt<NC>();  // block kt+1 has landed (block kt+2 may still be in flight)
+    wait_vmcnt<(D - 1) * NC>();  // block kt+1 has landed (blocks kt+2 .. kt+D may still be in flight)
     __syncthreads();   // publishes block kt+1; every wave is done with stage st_cur, refilled next iteration
-    st_cur = st_cur == NSTG - 1 ? 0 : st_cur + 1;
-    st_new = st_new == NSTG - 1 ? 0 : st_new + 1;
+    st_cur = st_cur == NSTG_F - 1 ? 0 : st_cur + 1;
+    st_new = st_new == NSTG_F - 1 ? 0 : st_new + 1;
   }
   wait_vmcnt<0>();
 
-  float l_tot = l_part;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_over_groups(l_part);
   if (q < p.s) {
     const float inv = 1.f / l_tot;
     uint16_t* o = static_cast<uint16_t*>(p.o) + ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jj * d;
@@ -694,8 +725,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
   wait_vmcnt<0>();
 
   if constexpr (DPASS) {
-    dsum += __shfl_xor(dsum, 16);
-    dsum += __shfl_xor(dsum, 32);
+    dsum = sum_over_groups(dsum);
     if (q < p.s && g == 0) *drec = dsum;
     return;
   }
