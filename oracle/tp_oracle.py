@@ -26,6 +26,9 @@ Readings where the pages are silent (each also listed in the design notes):
   * Partial sums are stored in the activation dtype; the bit-exact reduction adds them in fp32 in rank order
     0..t-1, adds the bias last, then rounds once to bf16 (nearest, ties to even); NaN stays NaN.
 
+The SP-region ops (LayerNorm, dropout + residual) are the plain per-row / per-element definitions; dropout takes
+its random words as an input (tp_inputs draws them), so both sides make the same keep decisions.
+
 The attention backward (core and block) follows the chain rule through the row softmax as written out in
 attention_core_backward; it is pinned by finite differences of the forward, torch's fp64 autograd, closed forms
 and softmax invariants (tests/test_oracle_attention_bwd.py).
@@ -618,6 +621,52 @@ def attention_shard_backward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, dZ
             dQKVi[rows, base + 2 * d:base + 3 * d] = gv
     return {"dO": dOi, "dWo": Oi.T @ dZ, "dQKV": dQKVi, "dWqkv": X.T @ dQKVi, "dbqkv": dQKVi.sum(axis=0),
             "dX": dQKVi @ Wqkv_i.T, "O": Oi, "QKV": QKVi, "lse": fw["lse"]}
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Sequence-parallel region ([ATLAS] §5 "SP: g -> RS" / "SP: f -> AG" rows and §6; [MEGA] sequence_parallel note;
+# [SPCP] "SP: all-gather in, reduce-scatter out": LayerNorm, dropout and the residual add are per-token / per-element
+# and run on each rank's [s/t, b, h] slice between the reduce-scatter of one block and the all-gather of the next)
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def layernorm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float):
+    """Per row of x [rows, h]: mean, biased variance, y = (x - mean) / sqrt(var + eps) * gamma + beta.
+    Returns y, mean [rows], rstd [rows] = 1 / sqrt(var + eps)."""
+    x = np.asarray(x, dtype=np.float64)
+    mean = x.mean(axis=1)
+    var = ((x - mean[:, None]) ** 2).mean(axis=1)
+    rstd = 1.0 / np.sqrt(var + eps)
+    return (x - mean[:, None]) * rstd[:, None] * gamma[None, :] + beta[None, :], mean, rstd
+
+
+def layernorm_backward(x: np.ndarray, gamma: np.ndarray, dy: np.ndarray, eps: float):
+    """Gradients of layernorm for the upstream dy: with xh = (x - mean) rstd and g = dy * gamma,
+    dx = rstd (g - mean_h(g) - xh mean_h(g xh)); dgamma = sum over rows of dy xh; dbeta = sum over rows of dy."""
+    x = np.asarray(x, dtype=np.float64)
+    _, mean, rstd = layernorm(x, np.ones(x.shape[1]), np.zeros(x.shape[1]), eps)
+    xh = (x - mean[:, None]) * rstd[:, None]
+    g = dy * gamma[None, :]
+    dx = rstd[:, None] * (g - g.mean(axis=1, keepdims=True) - xh * (g * xh).mean(axis=1, keepdims=True))
+    return dx, (dy * xh).sum(axis=0), dy.sum(axis=0)
+
+
+def dropout_keep(bits: np.ndarray, p: float) -> np.ndarray:
+    """Keep decision from 32-bit random words: keep iff bits >= floor(p * 2^32), so P(keep) = 1 - p to 2^-32."""
+    return np.asarray(bits, dtype=np.uint64) >= np.uint64(math.floor(p * 2.0 ** 32))
+
+
+def dropout_add(z: np.ndarray, residual: np.ndarray, bits: np.ndarray, p: float) -> np.ndarray:
+    """out = residual + keep * z / (1 - p) (inverted dropout on the block output, then the residual add)."""
+    keep = dropout_keep(bits, p)
+    return np.asarray(residual, dtype=np.float64) + np.where(keep, np.asarray(z, dtype=np.float64) / (1.0 - p), 0.0)
+
+
+def dropout_add_backward(dout: np.ndarray, bits: np.ndarray, p: float):
+    """Gradients of dropout_add: dz = keep * dout / (1 - p); dresidual = dout."""
+    keep = dropout_keep(bits, p)
+    dout = np.asarray(dout, dtype=np.float64)
+    return np.where(keep, dout / (1.0 - p), 0.0), dout
 
 
 # ---------------------------------------------------------------------------------------------------------------

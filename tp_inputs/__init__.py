@@ -20,6 +20,7 @@ from typing import Optional
 import numpy as np
 
 T_X, T_A, T_B, T_DZ, T_BIAS_COL, T_BIAS_ROW = 0, 1, 2, 3, 4, 5
+T_GAMMA, T_BETA, T_RESID, T_BITS, T_DY = 8, 9, 10, 11, 12
 WEIGHT_STD = 0.02
 
 
@@ -136,6 +137,28 @@ def attn_inputs(w: Workload, with_bias: bool = False, seed: Optional[int] = None
         out["bqkv"] = tensor(sd, T_BIAS_COL, (3 * ad,), WEIGHT_STD, w.dtype)
         out["c"] = tensor(sd, T_BIAS_ROW, (w.h,), WEIGHT_STD, w.dtype)
     return out
+
+
+def random_words(seed: int, tensor_id: int, shape) -> np.ndarray:
+    """Uniform 32-bit random words (the dropout decisions' randomness, passed to both sides as an input)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, tensor_id]))
+    return rng.integers(0, 2 ** 32, size=shape, dtype=np.uint64).astype(np.uint32)
+
+
+def sp_region_inputs(rows: int, h: int, dtype: str = "bf16", seed: int = 0) -> dict:
+    """One rank's sequence-parallel slice [rows = s/t * b, h]: LayerNorm input x, gamma ~ 1 + N(0, 0.1^2),
+    beta ~ N(0, 0.1^2), the block output z (after the reduce-scatter), the residual, upstream gradients dy / dout,
+    and the dropout random words."""
+    return {
+        "x": tensor(seed, T_X, (rows, h), 1.0, dtype),
+        "gamma": to_bf16_bits(1.0 + normal_f32(seed, T_GAMMA, (h,), 0.1)) if dtype == "bf16"
+        else 1.0 + normal_f32(seed, T_GAMMA, (h,), 0.1),
+        "beta": tensor(seed, T_BETA, (h,), 0.1, dtype),
+        "z": tensor(seed, T_DZ, (rows, h), 1.0, dtype),
+        "residual": tensor(seed, T_RESID, (rows, h), 1.0, dtype),
+        "dy": tensor(seed, T_DY, (rows, h), 1.0, dtype),
+        "bits": random_words(seed, T_BITS, (rows, h)),
+    }
 
 
 def partials(seed: int, t: int, shape, dtype: str = "bf16", tensor_id: int = 7) -> np.ndarray:
