@@ -22,8 +22,9 @@ WKINDS = {"fc1": TP_W_FC1, "fc1_gate_up": TP_W_FC1_GATE_UP, "fc2": TP_W_FC2, "qk
 STATUS = {0: "TP_OK", -1: "TP_E_NULL", -2: "TP_E_SHAPE", -3: "TP_E_DIVISIBILITY", -4: "TP_E_DTYPE", -5: "TP_E_RANK",
           -6: "TP_E_ALIAS", -7: "TP_E_UNSUPPORTED", -8: "TP_E_HIP"}
 EXPORTED = ["tp_status_str", "tp_last_hip_error", "tp_abi_version", "tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd",
-            "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_timing_begin",
-            "tp_timing_end", "tp_timing_kernel"]
+            "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd",
+            "tp_sp_dropout_add_ln_bwd", "tp_sp_ln_bwd_workspace", "tp_timing_begin", "tp_timing_end",
+            "tp_timing_kernel"]
 
 
 class TpError(RuntimeError):
@@ -52,7 +53,7 @@ def _load() -> ctypes.CDLL:
     except Exception:
         pass
     lib = ctypes.CDLL(LIB_PATH)
-    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    P, I64, I, F64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_double
     D = ctypes.POINTER(tp_dims)
     sig = {
         "tp_status_str": ([I], ctypes.c_char_p),
@@ -66,6 +67,9 @@ def _load() -> ctypes.CDLL:
         "tp_partial_reduce": ([I64, I64, I, I, P, P, P, P], I),
         "tp_reduce_scatter_dim0": ([D, I, I, P, P, P, P], I),
         "tp_gather_dim0": ([D, I, P, P, P], I),
+        "tp_sp_dropout_add_ln_fwd": ([I64, I64, I, F64, F64, P, P, P, P, P, P, P, P, P, P, P], I),
+        "tp_sp_dropout_add_ln_bwd": ([I64, I64, I, F64, P, P, P, P, P, P, P, P, P, P, P, P, P], I),
+        "tp_sp_ln_bwd_workspace": ([I64, I64], I64),
         "tp_timing_begin": ([ctypes.POINTER(P), ctypes.POINTER(P), I], I),
         "tp_timing_end": ([], I),
         "tp_timing_kernel": ([I], ctypes.c_char_p),
@@ -186,6 +190,26 @@ def tp_reduce_scatter_dim0(dims: tp_dims, rank: int, partials, bias_c, out, stre
 def tp_gather_dim0(dims: tp_dims, slices, out, stream=None, dtype=None, check=True) -> int:
     st = lib.tp_gather_dim0(ctypes.byref(dims), _dtype_code(slices, dtype), _ptr(slices), _ptr(out), _stream(stream))
     return _check(st, "tp_gather_dim0", check)
+
+
+def tp_sp_dropout_add_ln_fwd(rows: int, h: int, p: float, eps: float, z, residual, bits, gamma, beta, out, y, mean,
+                             rstd, mask, stream=None, dtype=None, check=True) -> int:
+    st = lib.tp_sp_dropout_add_ln_fwd(int(rows), int(h), _dtype_code(z, dtype), float(p), float(eps), _ptr(z),
+                                      _ptr(residual), _ptr(bits), _ptr(gamma), _ptr(beta), _ptr(out), _ptr(y),
+                                      _ptr(mean), _ptr(rstd), _ptr(mask), _stream(stream))
+    return _check(st, "tp_sp_dropout_add_ln_fwd", check)
+
+
+def tp_sp_dropout_add_ln_bwd(rows: int, h: int, p: float, u, gamma, mean, rstd, dy, dres_in, mask, dres, dz, dgamma,
+                             dbeta, ws, stream=None, dtype=None, check=True) -> int:
+    st = lib.tp_sp_dropout_add_ln_bwd(int(rows), int(h), _dtype_code(u, dtype), float(p), _ptr(u), _ptr(gamma),
+                                      _ptr(mean), _ptr(rstd), _ptr(dy), _ptr(dres_in), _ptr(mask), _ptr(dres),
+                                      _ptr(dz), _ptr(dgamma), _ptr(dbeta), _ptr(ws), _stream(stream))
+    return _check(st, "tp_sp_dropout_add_ln_bwd", check)
+
+
+def tp_sp_ln_bwd_workspace(rows: int, h: int) -> int:
+    return int(lib.tp_sp_ln_bwd_workspace(int(rows), int(h)))
 
 
 class LaunchTimer:

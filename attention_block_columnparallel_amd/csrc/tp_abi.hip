@@ -446,4 +446,89 @@ int tp_gather_dim0(const tp_dims* dims, tp_dtype dtype, const void* slices, void
   return hip_status(tp::copy_bytes(slices, out, bytes, stream));
 }
 
+int64_t tp_sp_ln_bwd_workspace(int64_t rows, int64_t h) {
+  if (rows <= 0 || h <= 0) return 0;
+  return tp::sp_bwd_blocks(rows) * 2 * h * (int64_t)sizeof(float);
+}
+
+namespace {
+// Size / dtype / alignment rules shared by the two sequence-parallel region calls.
+int sp_check_sizes(int64_t rows, int64_t h, tp_dtype dtype, double p) {
+  if (rows <= 0 || h <= 0 || rows >= kMaxDim || !(p >= 0.0 && p < 1.0)) return TP_E_SHAPE;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  if (h % 8 != 0 || h > tp::SP_MAX_H) return TP_E_UNSUPPORTED;
+  return TP_OK;
+}
+}  // namespace
+
+int tp_sp_dropout_add_ln_fwd(int64_t rows, int64_t h, tp_dtype dtype, double p, double eps, const void* z,
+                             const void* residual, const uint32_t* bits, const void* gamma, const void* beta,
+                             void* out, void* y, float* mean, float* rstd, uint8_t* mask, hipStream_t stream) {
+  if (z == nullptr || gamma == nullptr || beta == nullptr || y == nullptr) return TP_E_NULL;
+  if (p > 0.0 && bits == nullptr) return TP_E_NULL;
+  if (!(eps >= 0.0) || eps > 1e30) return TP_E_SHAPE;
+  int st = sp_check_sizes(rows, h, dtype, p);
+  if (st != TP_OK) return st;
+  const uint32_t* bits_used = p > 0.0 ? bits : nullptr;
+  if (misaligned16({z, residual, (const void*)bits_used, gamma, beta, out, y})) return TP_E_UNSUPPORTED;
+  const int64_t es = esize(dtype), n = rows * h;
+  const Buf outs[] = {{out, n * es}, {y, n * es}, {mean, rows * 4}, {rstd, rows * 4}, {mask, n / 8}};
+  const Buf ins[] = {{z, n * es}, {residual, n * es}, {bits_used, n * 4}, {gamma, h * es}, {beta, h * es}};
+  if (any_alias(outs, 5, ins, 5)) return TP_E_ALIAS;
+  tp::SpFwdArgs a;
+  a.z = z;
+  a.residual = residual;
+  a.bits = bits_used;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.out = out;
+  a.y = y;
+  a.mean = mean;
+  a.rstd = rstd;
+  a.mask = mask;
+  a.rows = rows;
+  a.h = h;
+  a.p = p;
+  a.eps = eps;
+  return hip_status(tp::sp_dropout_add_ln_fwd(dtype, a, stream));
+}
+
+int tp_sp_dropout_add_ln_bwd(int64_t rows, int64_t h, tp_dtype dtype, double p, const void* u, const void* gamma,
+                             const float* mean, const float* rstd, const void* dy, const void* dres_in,
+                             const uint8_t* mask, void* dres, void* dz, float* dgamma, float* dbeta, float* ws,
+                             hipStream_t stream) {
+  if (u == nullptr || gamma == nullptr || mean == nullptr || rstd == nullptr || dy == nullptr ||
+      dgamma == nullptr || dbeta == nullptr || ws == nullptr)
+    return TP_E_NULL;
+  if (p > 0.0 && mask == nullptr) return TP_E_NULL;
+  int st = sp_check_sizes(rows, h, dtype, p);
+  if (st != TP_OK) return st;
+  if (misaligned16({u, gamma, dy, dres_in, dres, dz, (const void*)dgamma, (const void*)dbeta, (const void*)ws}))
+    return TP_E_UNSUPPORTED;
+  const uint8_t* mask_used = p > 0.0 ? mask : nullptr;
+  const int64_t es = esize(dtype), n = rows * h;
+  const Buf outs[] = {{dres, n * es}, {dz, n * es}, {dgamma, h * 4}, {dbeta, h * 4},
+                      {ws, tp_sp_ln_bwd_workspace(rows, h)}};
+  const Buf ins[] = {{u, n * es}, {gamma, h * es}, {mean, rows * 4}, {rstd, rows * 4}, {dy, n * es},
+                     {dres_in, n * es}, {mask_used, n / 8}};
+  if (any_alias(outs, 5, ins, 7)) return TP_E_ALIAS;
+  tp::SpBwdArgs a;
+  a.u = u;
+  a.gamma = gamma;
+  a.mean = mean;
+  a.rstd = rstd;
+  a.dy = dy;
+  a.dres_in = dres_in;
+  a.mask = mask_used;
+  a.dres = dres;
+  a.dz = dz;
+  a.dgamma = dgamma;
+  a.dbeta = dbeta;
+  a.ws = ws;
+  a.rows = rows;
+  a.h = h;
+  a.p = p;
+  return hip_status(tp::sp_dropout_add_ln_bwd(dtype, a, stream));
+}
+
 }  // extern "C"

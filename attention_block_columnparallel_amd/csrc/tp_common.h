@@ -184,4 +184,41 @@ struct AttnBwdParams {
 };
 hipError_t attention_bwd(tp_dtype dt, const AttnBwdParams& p, hipStream_t st);
 
+// Sequence-parallel region: dropout + residual add + LayerNorm on one rank's [rows = s/t * b, h] slice.
+struct SpFwdArgs {
+  const void* z;
+  const void* residual;  // nullable
+  const uint32_t* bits;  // [rows, h], read only when p > 0
+  const void* gamma;
+  const void* beta;
+  void* out;             // nullable
+  void* y;
+  float* mean;           // nullable
+  float* rstd;           // nullable
+  uint8_t* mask;         // nullable, [rows, h/8]
+  int64_t rows, h;
+  double p, eps;
+};
+struct SpBwdArgs {
+  const void* u;
+  const void* gamma;
+  const float* mean;
+  const float* rstd;
+  const void* dy;
+  const void* dres_in;   // nullable
+  const uint8_t* mask;   // read only when p > 0
+  void* dres;            // nullable
+  void* dz;              // nullable
+  float* dgamma;
+  float* dbeta;
+  float* ws;             // sp_bwd_blocks(rows) * 2h floats
+  int64_t rows, h;
+  double p;
+};
+constexpr int64_t SP_MAX_H = 12288;
+constexpr int64_t SP_BWD_MAX_BLOCKS = 256;
+int64_t sp_bwd_blocks(int64_t rows);
+hipError_t sp_dropout_add_ln_fwd(tp_dtype dt, const SpFwdArgs& a, hipStream_t st);
+hipError_t sp_dropout_add_ln_bwd(tp_dtype dt, const SpBwdArgs& a, hipStream_t st);
+
 }  // namespace tp

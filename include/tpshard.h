@@ -163,6 +163,46 @@ int tp_reduce_scatter_dim0(const tp_dims* dims, int rank, tp_dtype dtype, const 
  * out [s, b, h] = concatenation of the t slices [t][s/t, b, h] in rank order, bit for bit.  Needs s % t == 0. */
 int tp_gather_dim0(const tp_dims* dims, tp_dtype dtype, const void* slices, void* out, hipStream_t stream);
 
+/* Sequence-parallel region, forward: dropout + residual add + LayerNorm on one rank's slice of the residual
+ * stream.  Under sequence parallelism the per-token ops between two tensor-parallel blocks run on the rank's own
+ * rows [s/t, b, h] ([ATLAS] §5 SP rows, §6; [MEGA] sequence_parallel remark; [SPCP] SP section): the block output
+ * z arrives by the dim-0 reduce-scatter, and y leaves by the dim-0 all-gather into the next column GEMM.  The pages
+ * name these ops without formulas; this computes the standard definitions, per row of rows = (s/t)*b rows of h:
+ *   keep = (bits >= floor(p * 2^32))                    element-wise, one uint32 random word per element
+ *   u    = (residual or 0) + (keep ? z / (1 - p) : 0)   rounded once to dtype; written to out if out != NULL
+ *   y    = (u - mean) * rstd * gamma + beta,  mean / biased variance over the row, rstd = 1 / sqrt(var + eps)
+ * with the LayerNorm reading the rounded u.  mean, rstd: fp32 [rows] (nullable; the backward needs them).
+ * mask (nullable): [rows, h/8] bytes, bit i of byte k = keep of column 8k + i (LSB first); the backward reads it
+ * instead of the words.  p == 0 keeps every element (bits may be NULL; scale 1).  y may point into rank r's rows
+ * of the gathered [s, b, h] buffer (offset r*(s/t)*b*h): the local part of the all-gather is then this write.
+ * Tensors are dtype except bits, mean, rstd, mask; gamma, beta [h].  Needs 0 <= p < 1, eps >= 0, h % 8 == 0,
+ * h <= 12288 and every tensor pointer except mean, rstd and mask 16-byte aligned (else TP_E_UNSUPPORTED /
+ * TP_E_SHAPE).  Outputs must not overlap inputs or each other (TP_E_ALIAS). */
+int tp_sp_dropout_add_ln_fwd(int64_t rows, int64_t h, tp_dtype dtype, double p, double eps, const void* z,
+                             const void* residual, const uint32_t* bits, const void* gamma, const void* beta,
+                             void* out, void* y, float* mean, float* rstd, uint8_t* mask, hipStream_t stream);
+
+/* Sequence-parallel region, backward of tp_sp_dropout_add_ln_fwd on the same rank's rows.  dy is the gradient
+ * of y (it arrives by the dim-0 reduce-scatter of the next block's dX, [ATLAS] §5: the backward of SP's f is a
+ * reduce-scatter); dres_in (nullable = 0) is the residual stream's gradient from above.  With xh = (u - mean) *
+ * rstd and g = dy * gamma:
+ *   G      = dres_in + rstd * (g - mean_h(g) - xh * mean_h(g * xh))   -> dres (nullable), the gradient of residual
+ *   dz     = keep ? G / (1 - p) : 0                                    -> dz (nullable), the gradient of z
+ *   dgamma = sum over rows of dy * xh,  dbeta = sum over rows of dy    -> fp32 [h] each, this rank's rows only
+ * u, mean, rstd and mask are the forward's out, mean, rstd and mask (mask read only when p > 0).  Under sequence
+ * parallelism each rank holds part of the LayerNorm weight gradient: sum the t ranks' dgamma / dbeta (e.g.
+ * tp_partial_reduce with TP_F32).  ws: fp32 scratch of tp_sp_ln_bwd_workspace(rows, h) bytes, 16-byte aligned;
+ * dgamma and dbeta 16-byte aligned.  Sums over rows run in a fixed order: results are deterministic.  Same size,
+ * alignment and alias rules as the forward. */
+int tp_sp_dropout_add_ln_bwd(int64_t rows, int64_t h, tp_dtype dtype, double p, const void* u, const void* gamma,
+                             const float* mean, const float* rstd, const void* dy, const void* dres_in,
+                             const uint8_t* mask, void* dres, void* dz, float* dgamma, float* dbeta, float* ws,
+                             hipStream_t stream);
+
+/* Bytes of fp32 scratch tp_sp_dropout_add_ln_bwd needs for rows x h (one partial [dgamma | dbeta] row per
+ * workgroup of the row loop); <= 0 for non-positive sizes. */
+int64_t tp_sp_ln_bwd_workspace(int64_t rows, int64_t h);
+
 /* Launch timing, a profiling aid (not part of the block's arithmetic).  tp_timing_begin arms the calling thread:
  * every kernel launched by a later tp_* call on this thread is bracketed by hipEventRecord(starts[i], stream) and
  * hipEventRecord(stops[i], stream), for the first `capacity` launches (later ones run unrecorded).  The events are

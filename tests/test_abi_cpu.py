@@ -29,7 +29,8 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for n in ["tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce",
-              "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_status_str"]:
+              "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd", "tp_sp_dropout_add_ln_bwd",
+              "tp_sp_ln_bwd_workspace", "tp_status_str"]:
         assert n in names
 
 
@@ -160,3 +161,42 @@ def test_python_wrapper_raises_tperror(L):
     with pytest.raises(L.TpError) as ei:
         L.tp_partial_reduce(100, 64, 2, addr(0), None, addr(1), stream=0, dtype=BF16)
     assert "TP_E_SHAPE" in str(ei.value)
+
+
+def test_sp_region_validation(L):
+    P = [addr(i) for i in range(16)]
+    rows, h = 16, 64
+
+    def fwd(rows=rows, h=h, p=0.1, eps=1e-5, dt=BF16, ptrs=None):
+        q = ptrs or P[:10]  # z, residual, bits, gamma, beta, out, y, mean, rstd, mask
+        return L.tp_sp_dropout_add_ln_fwd(rows, h, p, eps, *q, stream=0, dtype=dt, check=False)
+
+    def bwd(rows=rows, h=h, p=0.1, dt=BF16, ptrs=None):
+        q = ptrs or P[:12]  # u, gamma, mean, rstd, dy, dres_in, mask, dres, dz, dgamma, dbeta, ws
+        return L.tp_sp_dropout_add_ln_bwd(rows, h, p, *q, stream=0, dtype=dt, check=False)
+
+    for i in (0, 3, 4, 6):                                   # z, gamma, beta, y are required
+        assert fwd(ptrs=P[:i] + [None] + P[i + 1:10]) == -1, i
+    assert fwd(ptrs=P[:2] + [None] + P[3:10]) == -1          # random words required when p > 0
+    # ... not when p == 0: then the misaligned y decides (every case here must fail validation: nothing launches)
+    assert fwd(p=0.0, ptrs=P[:2] + [None] + P[3:6] + [P[6] + 2] + P[7:10]) == -7
+    assert fwd(rows=0) == -2
+    assert fwd(p=1.0) == -2 and fwd(p=-0.1) == -2 and fwd(p=float("nan")) == -2
+    assert fwd(eps=-1.0) == -2
+    assert fwd(dt=9) == -4
+    assert fwd(h=60) == -7                                   # h % 8
+    assert fwd(h=12288 + 8) == -7                            # largest supported row
+    assert fwd(ptrs=P[:6] + [P[6] + 2] + P[7:10]) == -7      # misaligned y
+    assert fwd(ptrs=P[:5] + [P[0]] + P[6:10]) == -6          # out aliases z
+    assert fwd(ptrs=P[:9] + [P[7]]) == -6                    # mask overlaps mean
+    for i in (0, 1, 2, 3, 4, 9, 10, 11):                     # u, gamma, mean, rstd, dy, dgamma, dbeta, ws required
+        assert bwd(ptrs=P[:i] + [None] + P[i + 1:12]) == -1, i
+    assert bwd(ptrs=P[:6] + [None] + P[7:12]) == -1          # mask required when p > 0
+    assert bwd(rows=-3) == -2
+    assert bwd(h=20) == -7
+    assert bwd(ptrs=P[:11] + [P[11] + 4]) == -7              # misaligned workspace
+    assert bwd(ptrs=P[:8] + [P[4]] + P[9:12]) == -6          # dz aliases dy
+    assert bwd(ptrs=P[:11] + [P[9] + 16]) == -6              # workspace overlaps dgamma
+    assert L.tp_sp_ln_bwd_workspace(2048, 4096) == 256 * 2 * 4096 * 4
+    assert L.tp_sp_ln_bwd_workspace(3, 64) == 3 * 2 * 64 * 4
+    assert L.tp_sp_ln_bwd_workspace(0, 64) == 0

@@ -8,9 +8,12 @@ Recipe (one stream per tensor, so adding a tensor never shifts another):
   values = rng.standard_normal(shape, dtype=float32) * std
   bf16 storage: round-to-nearest-even of those fp32 values (torch's CPU conversion); fp32 storage keeps them as is.
 
-Tensor ids: X=0, A (or Wqkv)=1, B (or Wo)=2, dZ=3, column bias=4, row bias=5.  Distributions follow the
-workloads of the pages: activations and upstream gradients N(0,1), weights N(0, 0.02^2) (0.02 is the standard
-deviation, the GPT/Megatron init convention), biases N(0, 0.02^2).
+Tensor ids: X=0, A (or Wqkv)=1, B (or Wo)=2, dZ=3, column bias=4, row bias=5, partial sums=7; the
+sequence-parallel region adds LayerNorm gamma=8, beta=9, residual=10, dropout random words=11, dy=12.
+Distributions follow the workloads of the pages: activations and upstream gradients N(0,1), weights N(0, 0.02^2)
+(0.02 is the standard deviation, the GPT/Megatron init convention), biases N(0, 0.02^2); LayerNorm gamma
+1 + N(0, 0.1^2) and beta N(0, 0.1^2) (a trained-looking affine, not the identity, so a dropped gamma or beta
+shows).  Random words: rng.integers(0, 2^32) from the same per-tensor stream, one uint32 per element.
 """
 from __future__ import annotations
 
