@@ -12,9 +12,10 @@ both reductions), in TFLOP/s.  roofline = the kernel with the largest share of t
 flops per launch over its average HIP-event duration inside the timed region, against the dense bf16 MFMA peak.
 rs_dim0 = the reduce-scatter kernel against HBM bandwidth.  traffic = HBM bytes per launch from the committed
 rocprofv3 counter summary under profiles/ (null once the kernel source differs from the one profiled).
-cpu_baseline = the fp64 oracle on a bounded sample.  attention_block and gather_dim0 = the other rows of the hot
-path, timed after the step (not part of value): the attention block forward at the 22B-class shape and the dim-0
-gather at the Llama-70B-sized SP shape.
+cpu_baseline = the fp64 oracle on a bounded sample.  attention_block, gather_dim0 and sp_region = the other rows
+of the hot path, timed after the step (not part of value): the attention block forward and backward at the
+22B-class shape, the dim-0 gather at the Llama-70B-sized SP shape, and the sequence-parallel region (dropout +
+residual + LayerNorm, forward and backward) on every rank's rows at that same shape.
 """
 from __future__ import annotations
 
@@ -37,7 +38,7 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default="mlp_h4096_ffn16384_t8_b8_s2048")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--no-extra", action="store_true", help="skip the attention-block and gather measurements")
+    ap.add_argument("--no-extra", action="store_true", help="skip the attention-block, gather and SP-region measurements")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one dim-0 gather (a plain copy) of this many MiB, for counter calibration")
     return ap.parse_args(argv)
@@ -202,6 +203,72 @@ def gather_measure(L, reps: int) -> dict:
             "gbps": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (med * 1e-3) / PEAK_HBM_BYTES, 4)}
 
 
+def sp_region_measure(L, reps: int) -> dict:
+    """The sequence-parallel region at the SP SwiGLU shape (s=4096, b=1, h=8192, t=8, bf16; p=0.1): for each rank,
+    dropout + residual + LayerNorm forward on its 512 rows, writing y into its rows of the gathered buffer; then
+    for each rank the backward (with a residual-stream gradient coming in).  Algorithmic bytes per element:
+    forward z, residual, out, y (2 each) + random word (4) + mask bit (1/8); backward u, dy, dres_in, dres, dz
+    (2 each) + mask bit.  The per-workgroup partial rows of dgamma / dbeta are scratch, not counted."""
+    import numpy as np
+    import torch
+
+    import tp_inputs as TI
+
+    s, b, h, t, p, eps = 4096, 1, 8192, 8, 0.1, 1e-5
+    rows = s // t * b
+    inp = TI.sp_region_inputs(s * b, h, "bf16", seed=0)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    z, res, gam, bet, dy = (dev(inp[k]) for k in ("z", "residual", "gamma", "beta", "dy"))
+    bits = torch.from_numpy(inp["bits"].view(np.int32)).cuda()
+    U, Yg, dres, dz = (torch.empty_like(z) for _ in range(4))
+    mean = torch.empty(s * b, dtype=torch.float32, device="cuda")
+    rstd = torch.empty_like(mean)
+    mask = torch.empty((s * b, h // 8), dtype=torch.uint8, device="cuda")
+    parts = torch.empty((2 * t, h), dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.tp_sp_ln_bwd_workspace(rows, h) // 4, dtype=torch.float32, device="cuda")
+
+    def step():
+        for r in range(t):
+            sl = slice(r * rows, (r + 1) * rows)
+            L.tp_sp_dropout_add_ln_fwd(rows, h, p, eps, z[sl], res[sl], bits[sl], gam, bet, U[sl], Yg[sl], mean[sl],
+                                       rstd[sl], mask[sl])
+        for r in range(t):
+            sl = slice(r * rows, (r + 1) * rows)
+            L.tp_sp_dropout_add_ln_bwd(rows, h, p, U[sl], gam, mean[sl], rstd[sl], dy[sl], res[sl], mask[sl],
+                                       dres[sl], dz[sl], parts[r], parts[t + r], ws)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    with L.LaunchTimer(capacity=reps * 3 * t + 8) as lt:
+        for _ in range(reps):
+            step()
+    torch.cuda.synchronize()
+    n = rows * h
+    alg = {"sp_dropout_add_ln_fwd": n * (2 * 4 + 4 + 0.125) + 2 * h * 2 + rows * 8,
+           "sp_dropout_add_ln_bwd": n * (2 * 5 + 0.125) + h * 2 + rows * 8}
+    kern = {}
+    for name, ms in lt.results():
+        kern.setdefault(name, []).append(ms)
+    out = {"workload": "sp_region_t8_s4096_b1_h8192", "rows_per_rank": rows, "p": p, "kernels": {}}
+    total_us = 0.0
+    for name, v in kern.items():
+        med = 1e3 * float(np.median(v))
+        total_us += med * len(v) / reps
+        k = {"launches_per_step": len(v) // reps, "median_us": round(med, 2)}
+        if name in alg:
+            k["bytes_per_launch"] = int(alg[name])
+            k["gbps"] = round(alg[name] / (med * 1e-6) / 1e9, 1)
+            k["frac_hbm"] = round(alg[name] / (med * 1e-6) / PEAK_HBM_BYTES, 4)
+        out["kernels"][name] = k
+    out["us_per_step_all_ranks"] = round(total_us, 1)
+    del z, res, gam, bet, dy, bits, U, Yg, dres, dz
+    return out
+
+
 def cpu_baseline(w, inp, target_s: float) -> dict:
     """The oracle (fp64 NumPy, as it stands) on one rank's shard fwd + bwd over a sample of R token rows -- the
     same computation as the GPU's per-rank work for a batch of R tokens.  Reported in algorithmic TFLOP/s."""
@@ -363,6 +430,7 @@ def main(argv=None) -> int:
     if not args.no_extra:
         out["attention_block"] = attention_block_measure(L, max(2, args.steps // 2), 2)
         out["gather_dim0"] = gather_measure(L, 20)
+        out["sp_region"] = sp_region_measure(L, 10)
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
