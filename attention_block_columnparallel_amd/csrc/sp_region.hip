@@ -154,10 +154,15 @@ __global__ __launch_bounds__(NT) void sp_fwd_kernel(SpFwd p) {
   const int64_t rbase = row * p.h;
   float u[NV][8];
   uint32_t kb[NV];
+  uint4 wg[NV][Io<T>::W], wb[NV][Io<T>::W];  // gamma, beta: loaded with the row, used after the reductions
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int c = tid + j * NT;
     kb[j] = 0xFFu;
+    if (c < nch) {
+      Io<T>::load(p.gamma, 8 * c, wg[j]);
+      Io<T>::load(p.beta, 8 * c, wb[j]);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) u[j][i] = 0.0f;
     if (c < nch) {
@@ -215,12 +220,9 @@ __global__ __launch_bounds__(NT) void sp_fwd_kernel(SpFwd p) {
     if (c < nch) {
       const int64_t e = rbase + 8 * c;
       if (p.out != nullptr) Io<T>::store(p.out, e, u[j]);
-      uint4 wg[Io<T>::W], wb[Io<T>::W];
-      Io<T>::load(p.gamma, 8 * c, wg);
-      Io<T>::load(p.beta, 8 * c, wb);
       float g[8], b[8], y[8];
-      Io<T>::unpack(wg, g);
-      Io<T>::unpack(wb, b);
+      Io<T>::unpack(wg[j], g);
+      Io<T>::unpack(wb[j], b);
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = fmaf((u[j][i] - mean) * rstd, g[i], b[i]);
       Io<T>::store(p.y, e, y);
@@ -366,35 +368,43 @@ __global__ __launch_bounds__(NT) void sp_bwd_kernel(SpBwd p) {
 }
 
 // out[col] = sum over k = 0..nblk-1 of ws[k][col], col < n2 (n2 = 2h: dgamma then dbeta), summed in a fixed order:
-// 16 row groups each add rows g, g + 16, ... in increasing k; the groups are then added in order 0..15.
+// 16 row groups each add rows g, g + 16, ... in increasing k; the groups are then added in order 0..15.  Every
+// thread issues all of its (at most SP_BWD_MAX_BLOCKS / 16) loads before the first add.
 constexpr int CS_COLS = 64;  // columns per workgroup (16 threads x float4)
+constexpr int CS_GROUPS = 16;
+constexpr int CS_MAXK = (int)(SP_BWD_MAX_BLOCKS / CS_GROUPS);
 __global__ __launch_bounds__(SP_THREADS) void sp_partial_colsum_kernel(const float* __restrict__ ws, int nblk,
                                                                        int n2, int h, float* __restrict__ dgamma,
                                                                        float* __restrict__ dbeta) {
-  __shared__ float4 part[16][CS_COLS / 4];
+  __shared__ float4 part[CS_GROUPS][CS_COLS / 4];
   const int tid = threadIdx.x;
   const int cq = tid & 15, grp = tid >> 4;
   const int col = blockIdx.x * CS_COLS + 4 * cq;
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if (col < n2) {
-    for (int k = grp; k < nblk; k += 16) {
-      const float4 v = *reinterpret_cast<const float4*>(ws + (int64_t)k * n2 + col);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
-    }
+  float4 v[CS_MAXK];
+#pragma unroll
+  for (int i = 0; i < CS_MAXK; ++i) {
+    const int k = grp + i * CS_GROUPS;
+    v[i] = (col < n2 && k < nblk) ? *reinterpret_cast<const float4*>(ws + (int64_t)k * n2 + col)
+                                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
+  float4 acc = v[0];
+#pragma unroll
+  for (int i = 1; i < CS_MAXK; ++i) {
+    acc.x += v[i].x;
+    acc.y += v[i].y;
+    acc.z += v[i].z;
+    acc.w += v[i].w;
   }
   part[grp][cq] = acc;
   __syncthreads();
   if (tid < 16 && col < n2) {
     float4 s = part[0][tid];
-    for (int g = 1; g < 16; ++g) {
-      const float4 v = part[g][tid];
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
+    for (int g = 1; g < CS_GROUPS; ++g) {
+      const float4 w = part[g][tid];
+      s.x += w.x;
+      s.y += w.y;
+      s.z += w.z;
+      s.w += w.w;
     }
     // h is a multiple of 8, so a float4 never straddles the dgamma / dbeta boundary
     float* dst = col < h ? dgamma + col : dbeta + (col - h);
