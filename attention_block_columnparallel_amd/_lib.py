@@ -16,15 +16,17 @@ LIB_PATH = os.path.join(PKG, "libtpshard.so")
 
 TP_F32, TP_BF16 = 0, 1
 ACTS = {"gelu": 0, "gelu_tanh": 1, "swiglu": 2, "relu": 3}
+BWD_PHASES = {"all": 0, "dgrad": 1, "wgrad": 2}
 (TP_W_FC1, TP_W_FC1_GATE_UP, TP_W_FC2, TP_W_QKV, TP_W_PROJ, TP_B_FC1, TP_B_FC1_GATE_UP, TP_B_QKV) = range(8)
 WKINDS = {"fc1": TP_W_FC1, "fc1_gate_up": TP_W_FC1_GATE_UP, "fc2": TP_W_FC2, "qkv": TP_W_QKV, "proj": TP_W_PROJ,
           "b_fc1": TP_B_FC1, "b_fc1_gate_up": TP_B_FC1_GATE_UP, "b_qkv": TP_B_QKV}
 STATUS = {0: "TP_OK", -1: "TP_E_NULL", -2: "TP_E_SHAPE", -3: "TP_E_DIVISIBILITY", -4: "TP_E_DTYPE", -5: "TP_E_RANK",
           -6: "TP_E_ALIAS", -7: "TP_E_UNSUPPORTED", -8: "TP_E_HIP"}
 EXPORTED = ["tp_status_str", "tp_last_hip_error", "tp_abi_version", "tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd",
+            "tp_mlp_bwd_phase",
             "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd",
             "tp_sp_dropout_add_ln_bwd", "tp_sp_ln_bwd_workspace", "tp_timing_begin", "tp_timing_end",
-            "tp_timing_kernel"]
+            "tp_timing_kernel", "tp_timing_filter"]
 
 
 class TpError(RuntimeError):
@@ -62,6 +64,7 @@ def _load() -> ctypes.CDLL:
         "tp_shard_weights": ([D, I, I, I, P, P, P], I),
         "tp_mlp_fwd": ([D, I, I, I, P, P, P, P, P, P, P, P], I),
         "tp_mlp_bwd": ([D, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P], I),
+        "tp_mlp_bwd_phase": ([D, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_attn_fwd": ([D, I, I, I, P, P, P, P, P, P, P, P, P], I),
         "tp_attn_bwd": ([D, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_partial_reduce": ([I64, I64, I, I, P, P, P, P], I),
@@ -73,6 +76,7 @@ def _load() -> ctypes.CDLL:
         "tp_timing_begin": ([ctypes.POINTER(P), ctypes.POINTER(P), I], I),
         "tp_timing_end": ([], I),
         "tp_timing_kernel": ([I], ctypes.c_char_p),
+        "tp_timing_filter": ([ctypes.c_char_p], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -157,6 +161,15 @@ def tp_mlp_bwd(dims: tp_dims, rank: int, act, X, A_i, B_i, U_i, Y_i, dZ, dU_ws, 
     return _check(st, "tp_mlp_bwd", check)
 
 
+def tp_mlp_bwd_phase(dims: tp_dims, rank: int, act, phase, X, A_i, B_i, U_i, Y_i, dZ, dU_ws, dA_i, da_i, dB_i, dX_i,
+                     stream=None, dtype=None, check=True) -> int:
+    ph = BWD_PHASES[phase] if isinstance(phase, str) else int(phase)
+    st = lib.tp_mlp_bwd_phase(ctypes.byref(dims), int(rank), _act(act), _dtype_code(dZ, dtype), ph, _ptr(X),
+                              _ptr(A_i), _ptr(B_i), _ptr(U_i), _ptr(Y_i), _ptr(dZ), _ptr(dU_ws), _ptr(dA_i), _ptr(da_i),
+                              _ptr(dB_i), _ptr(dX_i), _stream(stream))
+    return _check(st, "tp_mlp_bwd_phase", check)
+
+
 def tp_attn_fwd(dims: tp_dims, rank: int, causal: bool, X, Wqkv_i, bqkv_i, Wo_i, QKV_i, O_i, lse_i, Z_i,
                 stream=None, dtype=None, check=True) -> int:
     st = lib.tp_attn_fwd(ctypes.byref(dims), int(rank), _dtype_code(X, dtype), 1 if causal else 0, _ptr(X),
@@ -216,9 +229,11 @@ class LaunchTimer:
     """Collects per-kernel HIP-event timings of every launch the library makes while armed.
 
     Usage: with LaunchTimer(capacity) as lt: ...calls...; then lt.results() -> [(kernel name, ms)] after a device
-    synchronisation.  Events are created with torch (hipEvent_t handles) and owned here."""
+    synchronisation.  Events are created with torch (hipEvent_t handles) and owned here.  only="prefix" records
+    just the launches whose kernel name starts with it."""
 
-    def __init__(self, capacity: int = 2048):
+    def __init__(self, capacity: int = 2048, only: Optional[str] = None):
+        self.only = only
         import torch
 
         self.capacity = capacity
@@ -234,6 +249,9 @@ class LaunchTimer:
         self.names = []
 
     def __enter__(self):
+        st = lib.tp_timing_filter(self.only.encode() if self.only else None)
+        if st != 0:
+            raise TpError(st, "tp_timing_filter")
         st = lib.tp_timing_begin(self._sa, self._so, self.capacity)
         if st != 0:
             raise TpError(st, "tp_timing_begin")
@@ -241,6 +259,7 @@ class LaunchTimer:
 
     def __exit__(self, *exc):
         self.n = lib.tp_timing_end()
+        lib.tp_timing_filter(None)
         self.names = [lib.tp_timing_kernel(i).decode() for i in range(self.n)]
         return False
 

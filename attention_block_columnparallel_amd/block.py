@@ -99,6 +99,79 @@ class MlpBlock:
         return self.reduce_backward(sp, stream)
 
 
+    # -- the same step with the reductions on a second stream (communication / computation overlap)
+    def forward_pipelined(self, X: torch.Tensor, out_rs: torch.Tensor, chunks: int = 2, comm=None, stream=None):
+        """Forward with the g-bar reduce-scatter pipelined along s: the block is run on `chunks` consecutive row
+        ranges of the sequence (the MLP is row-wise, so each range is an exact forward of its rows), and as soon
+        as every rank has finished range c, the reduce-scatter of the rank slices inside range c runs on `comm`
+        while range c + 1 computes ("Tensor Parallelism (TP) 与 Sequence Parallelism (SP)" §5: SP's g is a
+        reduce-scatter; the pages' tp_comm_overlap pipelines it with the GEMMs).  out_rs [t, s/t, b, h] receives
+        every rank's slice, bit for bit what reduce_forward(sp=True) gives.  Returns the event that marks the last
+        reduction on `comm`."""
+        L, t = self.L, self.t
+        if self.t % chunks != 0 or self.s % chunks != 0:
+            raise ValueError("chunks must divide t (and s)")
+        cur = torch.cuda.current_stream() if stream is None else stream
+        comm = self._comm(comm)
+        rows = (self.s // chunks) * self.b
+        dims_c = L.make_dims(s=self.s // chunks, b=self.b, h=self.h, ffn=self.ffn, t=t)
+        per = t // chunks
+        Xr = X.reshape(self.M, self.h)  # [s, b, h] as s-major rows
+        for c in range(chunks):
+            sl = slice(c * rows, (c + 1) * rows)
+            for r in range(t):
+                L.tp_mlp_fwd(dims_c, r, self.act, Xr[sl], self.A[r], None if self.a is None else self.a[r], self.B[r],
+                             self.U[r][sl], self.Y[r][sl], self.Zp[r][sl], cur)
+            ready = torch.cuda.Event()
+            ready.record(cur)
+            comm.wait_event(ready)
+            for j in range(c * per, (c + 1) * per):
+                L.tp_reduce_scatter_dim0(self.dims, j, self.Zp, self.c, out_rs[j], comm)
+        done = torch.cuda.Event()
+        done.record(comm)
+        return done
+
+    def backward_overlapped(self, X: torch.Tensor, dZ: torch.Tensor, out_rs: torch.Tensor, comm=None, stream=None):
+        """Backward with the dX reduction beside the weight gradients: every rank's dgrad half first (dU_i and the
+        dX_i partial), then the reduce-scatter of the dX partials on `comm` while every rank's wgrad half runs on
+        the compute stream ([ATLAS] §5: the dgrad reduction and the wgrad GEMMs are independent).  Each rank keeps
+        its own dU_i until its wgrad.  Outputs are bit for bit those of backward_ranks + reduce_backward(sp=True).
+        Returns the event that marks the reduction's end on `comm`."""
+        L, t = self.L, self.t
+        cur = torch.cuda.current_stream() if stream is None else stream
+        comm = self._comm(comm)
+        if getattr(self, "dUr", None) is None:
+            self.dUr = torch.empty((t, self.M, self.n1), dtype=self.dtype, device=self.A.device)
+        for r in range(t):
+            L.tp_mlp_bwd_phase(self.dims, r, self.act, "dgrad", None, self.A[r], self.B[r], self.U[r], None, dZ,
+                               self.dUr[r], None, None, None, self.dXp[r], cur)
+        ready = torch.cuda.Event()
+        ready.record(cur)
+        comm.wait_event(ready)
+        L.tp_reduce_scatter_dim0(self.dims, -1, self.dXp, None, out_rs, comm)
+        done = torch.cuda.Event()
+        done.record(comm)
+        for r in range(t):
+            L.tp_mlp_bwd_phase(self.dims, r, self.act, "wgrad", X, None, None, None, self.Y[r], dZ, self.dUr[r],
+                               self.dA[r], None if self.da is None else self.da[r], self.dB[r], None, cur)
+        return done
+
+    def step_overlapped(self, X: torch.Tensor, dZ: torch.Tensor, Z_rs: torch.Tensor, dX_rs: torch.Tensor,
+                        chunks: int = 2, comm=None, stream=None):
+        """forward_pipelined, then backward_overlapped; the compute stream waits for the last reduction."""
+        cur = torch.cuda.current_stream() if stream is None else stream
+        self.forward_pipelined(X, Z_rs, chunks, comm, cur)
+        done = self.backward_overlapped(X, dZ, dX_rs, comm, cur)
+        cur.wait_event(done)
+
+    def _comm(self, comm):
+        if comm is not None:
+            return comm
+        if getattr(self, "_comm_stream", None) is None:
+            self._comm_stream = torch.cuda.Stream(device=self.A.device)  # default priority
+        return self._comm_stream
+
+
 class AttnBlock:
     """All t shards of one attention block: QKV column-parallel by head, local causal attention, row-parallel
     output projection, partial sums reduced on the device."""

@@ -4,6 +4,7 @@
 // ("Tensor Parallelism (TP) 与 Sequence Parallelism (SP)" §1); output columns, input rows and heads must divide by
 // t, and h = a * d (Megatron-LM visual reading, divisibility rules; §1 of the same atlas page for h = a * d).
 #include <stdio.h>
+#include <string.h>
 
 #include "tp_common.h"
 
@@ -18,6 +19,7 @@ struct TimingLog {
   int n = 0;
   bool armed = false;
   bool open = false;  // a start was recorded for slot n
+  char only[64] = {0};  // when non-empty, only launches whose name starts with this are recorded
   const char* names[4096];
 };
 thread_local TimingLog g_timing;
@@ -66,10 +68,11 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;
 }  // namespace
 
 namespace tp {
-void timing_start(hipStream_t st) {
+void timing_start(hipStream_t st, const char* name) {
   TimingLog& T = g_timing;
   T.open = false;
   if (!T.armed || T.n >= T.cap) return;
+  if (T.only[0] != 0 && strncmp(name, T.only, strlen(T.only)) != 0) return;
   if (hipEventRecord(T.starts[T.n], st) == hipSuccess) T.open = true;
 }
 void timing_stop(hipStream_t st, const char* name) {
@@ -101,6 +104,18 @@ int tp_timing_begin(hipEvent_t* starts, hipEvent_t* stops, int capacity) {
 int tp_timing_end(void) {
   g_timing.armed = false;
   return g_timing.n;
+}
+
+int tp_timing_filter(const char* prefix) {
+  TimingLog& T = g_timing;
+  if (prefix == nullptr) {
+    T.only[0] = 0;
+    return TP_OK;
+  }
+  const size_t n = strlen(prefix);
+  if (n >= sizeof(T.only)) return TP_E_SHAPE;
+  memcpy(T.only, prefix, n + 1);
+  return TP_OK;
 }
 
 const char* tp_timing_kernel(int i) {
@@ -213,12 +228,14 @@ int tp_mlp_fwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const 
   return hip_status(e);
 }
 
-int tp_mlp_bwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const void* X, const void* A_i,
-               const void* B_i, const void* U_i, const void* Y_i, const void* dZ, void* dU_ws, void* dA_i,
-               void* da_i, void* dB_i, void* dX_i, hipStream_t stream) {
-  if (dims == nullptr || X == nullptr || A_i == nullptr || B_i == nullptr || U_i == nullptr || Y_i == nullptr ||
-      dZ == nullptr || dU_ws == nullptr || dA_i == nullptr || dB_i == nullptr || dX_i == nullptr)
-    return TP_E_NULL;
+int tp_mlp_bwd_phase(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, tp_bwd_phase phase, const void* X,
+                     const void* A_i, const void* B_i, const void* U_i, const void* Y_i, const void* dZ, void* dU_ws,
+                     void* dA_i, void* da_i, void* dB_i, void* dX_i, hipStream_t stream) {
+  const bool dgrad = phase == TP_BWD_ALL || phase == TP_BWD_DGRAD;
+  const bool wgrad = phase == TP_BWD_ALL || phase == TP_BWD_WGRAD;
+  if (dims == nullptr || dZ == nullptr || dU_ws == nullptr) return TP_E_NULL;
+  if (dgrad && (A_i == nullptr || B_i == nullptr || U_i == nullptr || dX_i == nullptr)) return TP_E_NULL;
+  if (wgrad && (X == nullptr || Y_i == nullptr || dA_i == nullptr || dB_i == nullptr)) return TP_E_NULL;
   const int64_t s = dims->s, b = dims->b, h = dims->h, ffn = dims->ffn, t = dims->t;
   if (s <= 0 || b <= 0 || h <= 0 || ffn <= 0 || t <= 0) return TP_E_SHAPE;
   if (s * b >= kMaxDim || h >= kMaxDim || ffn >= kMaxDim) return TP_E_SHAPE;
@@ -227,58 +244,81 @@ int tp_mlp_bwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const 
   if (bad_dtype(dtype)) return TP_E_DTYPE;
   if (act != TP_ACT_GELU && act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU && act != TP_ACT_RELU)
     return TP_E_UNSUPPORTED;
+  if (phase != TP_BWD_ALL && phase != TP_BWD_DGRAD && phase != TP_BWD_WGRAD) return TP_E_UNSUPPORTED;
   const int64_t M = s * b, f = ffn / t, n1 = act == TP_ACT_SWIGLU ? 2 * f : f, es = esize(dtype);
+  // a phase reads only its own operands; the others may be anything (they are not checked or touched)
+  const void* Xp = wgrad ? X : nullptr;
+  const void* Yp = wgrad ? Y_i : nullptr;
+  const void* Ap = dgrad ? A_i : nullptr;
+  const void* Bp = dgrad ? B_i : nullptr;
+  const void* Up = dgrad ? U_i : nullptr;
+  void* dAp = wgrad ? dA_i : nullptr;
+  void* dap = wgrad ? da_i : nullptr;
+  void* dBp = wgrad ? dB_i : nullptr;
+  void* dXp = dgrad ? dX_i : nullptr;
   if (dtype == TP_BF16 &&
-      (h % 8 != 0 || f % 8 != 0 || misaligned16({X, A_i, B_i, U_i, Y_i, dZ, dU_ws, dA_i, da_i, dB_i, dX_i})))
+      (h % 8 != 0 || f % 8 != 0 || misaligned16({Xp, Ap, Bp, Up, Yp, dZ, dU_ws, dAp, dap, dBp, dXp})))
     return TP_E_UNSUPPORTED;
-  const Buf outs[] = {{dU_ws, M * n1 * es}, {dA_i, h * n1 * es}, {da_i, n1 * es}, {dB_i, f * h * es},
-                      {dX_i, M * h * es}};
-  const Buf ins[] = {{X, M * h * es}, {A_i, h * n1 * es}, {B_i, f * h * es}, {U_i, M * n1 * es},
-                     {Y_i, M * f * es}, {dZ, M * h * es}};
-  if (any_alias(outs, 5, ins, 6)) return TP_E_ALIAS;
+  // dU_ws is an output of the dgrad phase and an input of the wgrad-only phase
+  const Buf dU = {dU_ws, M * n1 * es};
+  const Buf outs[] = {{dAp, h * n1 * es}, {dap, n1 * es}, {dBp, f * h * es}, {dXp, M * h * es},
+                      dgrad ? dU : Buf{nullptr, 0}};
+  const Buf ins[] = {{Xp, M * h * es}, {Ap, h * n1 * es}, {Bp, f * h * es}, {Up, M * n1 * es},
+                     {Yp, M * f * es}, {dZ, M * h * es}, dgrad ? Buf{nullptr, 0} : dU};
+  if (any_alias(outs, 5, ins, 7)) return TP_E_ALIAS;
 
   // dU = (dZ B_i^T) * act'(U):  A = dZ [M,h] K-major, B = B_i [f,h] read as rows n, K-major.
   tp::GemmParams gy = {};
   gy.A = dZ; gy.lda = h;
-  gy.B = B_i; gy.ldb = h;
+  gy.B = Bp; gy.ldb = h;
   gy.M = (int)M; gy.N = (int)f; gy.K = (int)h;
   gy.C = dU_ws; gy.ldc = n1;
-  gy.aux = U_i; gy.ldaux = n1;
+  gy.aux = Up; gy.ldaux = n1;
   gy.fhalf = (int)f;
   gy.act = (int)act;
   const int epiy = act == TP_ACT_SWIGLU ? tp::EPI_SWIGLU_BWD : tp::EPI_ACT_BWD;
   // dB = Y^T dZ: C [f,h], A(m=f, k=tok) = Y [tok,f] MN-major, B(n=h, k=tok) = dZ [tok,h] MN-major.
   tp::GemmParams gb = {};
-  gb.A = Y_i; gb.lda = f;
+  gb.A = Yp; gb.lda = f;
   gb.B = dZ; gb.ldb = h;
   gb.M = (int)f; gb.N = (int)h; gb.K = (int)M;
-  gb.C = dB_i; gb.ldc = h;
+  gb.C = dBp; gb.ldc = h;
   // dA = X^T dU: C [h,n1], A(m=h, k=tok) = X MN-major, B(n, k=tok) = dU MN-major.
   tp::GemmParams ga = {};
-  ga.A = X; ga.lda = h;
+  ga.A = Xp; ga.lda = h;
   ga.B = dU_ws; ga.ldb = n1;
   ga.M = (int)h; ga.N = (int)n1; ga.K = (int)M;
-  ga.C = dA_i; ga.ldc = n1;
+  ga.C = dAp; ga.ldc = n1;
   // dX = dU A^T: C [tok,h], A = dU [tok,n1] K-major, B(n=h, k=n1) = A_i [h,n1] K-major.
   tp::GemmParams gx = {};
   gx.A = dU_ws; gx.lda = n1;
-  gx.B = A_i; gx.ldb = n1;
+  gx.B = Ap; gx.ldb = n1;
   gx.M = (int)M; gx.N = (int)h; gx.K = (int)n1;
-  gx.C = dX_i; gx.ldc = h;
+  gx.C = dXp; gx.ldc = h;
 
+  // Order within one call: dU, then the weight gradients, then dX (the full backward keeps the launch order it
+  // always had; the split phases run dU + dX, or the weight gradients, alone).
   auto gemm = dtype == TP_BF16 ? tp::gemm_bf16 : tp::gemm_f32;
-  hipError_t e = gemm(gy, true, true, epiy, stream);
-  if (e == hipSuccess) {
+  hipError_t e = hipSuccess;
+  if (dgrad) e = gemm(gy, true, true, epiy, stream);
+  if (e == hipSuccess && wgrad) {
     if (dtype == TP_BF16) {
       e = tp::gemm_bf16_wgrad_pair(gb, ga, stream);
     } else {
       e = gemm(gb, false, false, tp::EPI_STORE, stream);
       if (e == hipSuccess) e = gemm(ga, false, false, tp::EPI_STORE, stream);
     }
+    if (e == hipSuccess && dap != nullptr) e = tp::colsum(dtype, dU_ws, M, n1, dap, stream);
   }
-  if (e == hipSuccess && da_i != nullptr) e = tp::colsum(dtype, dU_ws, M, n1, da_i, stream);
-  if (e == hipSuccess) e = gemm(gx, true, true, tp::EPI_STORE, stream);
+  if (e == hipSuccess && dgrad) e = gemm(gx, true, true, tp::EPI_STORE, stream);
   return hip_status(e);
+}
+
+int tp_mlp_bwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const void* X, const void* A_i,
+               const void* B_i, const void* U_i, const void* Y_i, const void* dZ, void* dU_ws, void* dA_i,
+               void* da_i, void* dB_i, void* dX_i, hipStream_t stream) {
+  return tp_mlp_bwd_phase(dims, rank, act, dtype, TP_BWD_ALL, X, A_i, B_i, U_i, Y_i, dZ, dU_ws, dA_i, da_i, dB_i,
+                          dX_i, stream);
 }
 
 int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const void* X, const void* Wqkv_i,

@@ -96,12 +96,12 @@ __device__ __forceinline__ float act_grad(int act, float x) {
 // Launch timing: when the calling thread is armed (tp_timing_begin), a LaunchTimer records the caller's start event
 // before a launch and its stop event after it, on the launch stream, and logs the kernel name.
 // ------------------------------------------------------------------------------------------------------------------
-void timing_start(hipStream_t st);
+void timing_start(hipStream_t st, const char* name);
 void timing_stop(hipStream_t st, const char* name);
 struct LaunchTimer {
   hipStream_t st;
   const char* name;
-  LaunchTimer(hipStream_t s, const char* n) : st(s), name(n) { timing_start(st); }
+  LaunchTimer(hipStream_t s, const char* n) : st(s), name(n) { timing_start(st, name); }
   ~LaunchTimer() { timing_stop(st, name); }
 };
 

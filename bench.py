@@ -8,12 +8,15 @@ for every rank the backward dgrad / wgrad GEMMs into dX partial i; the f reducti
 kernel).  Inputs and weights are resident in HBM before the timed region; the shards are packed once, before it.
 
 Prints ONE JSON line.  value = algorithmic GEMM flops of the step / wall time of the step (whole job, including
-both reductions), in TFLOP/s.  roofline = the kernel with the largest share of the step's time, its algorithmic
-flops per launch over its average HIP-event duration inside the timed region, against the dense bf16 MFMA peak.
-rs_dim0 = the reduce-scatter kernel against HBM bandwidth.  traffic = HBM bytes per launch from the committed
+both reductions), in TFLOP/s.  A census pass of K steps first brackets every library launch with HIP events (the
+"kernels" table and the step's dominant kernel); the timed region then runs K more steps with events around the
+dominant kernel's launches only, since every event pair adds launch latency.  roofline = that kernel's
+algorithmic flops per launch over its average HIP-event duration inside the timed region, against the dense bf16
+MFMA peak.  rs_dim0 = the reduce-scatter kernel (census pass) against HBM bandwidth.  traffic = HBM bytes per launch from the committed
 rocprofv3 counter summary under profiles/ (null once the kernel source differs from the one profiled).
-cpu_baseline = the fp64 oracle on a bounded sample.  attention_block, gather_dim0 and sp_region = the other rows
-of the hot path, timed after the step (not part of value): the attention block forward and backward at the
+cpu_baseline = the fp64 oracle on a bounded sample.  overlap, attention_block, gather_dim0 and sp_region = the
+other rows of the hot path, timed after the step (not part of value): the same step with its reductions on a
+second stream beside the GEMMs (serial vs overlapped ms/step), the attention block forward and backward at the
 22B-class shape, the dim-0 gather at the Llama-70B-sized SP shape, and the sequence-parallel region (dropout +
 residual + LayerNorm, forward and backward) on every rank's rows at that same shape.
 """
@@ -80,8 +83,9 @@ def attention_block_measure(L, steps: int, warmup: int) -> dict:
     """The attention block at the 22B-class shape (h=6144, 64 heads of 96, s=4096, t=8, causal).  Forward: for every
     rank the QKV GEMM, local causal attention and output projection into partial i, then the dim-0 reduce-scatter.
     Backward: for every rank tp_attn_bwd (dO GEMM, attention core backward, the weight-gradient pair, the dX GEMM),
-    then the reduce-scatter of the dX partials.  Per-kernel HIP-event durations; causal attention counts only
-    unmasked query-key pairs (forward 4 d, backward 10 d flops per pair)."""
+    then the reduce-scatter of the dX partials.  Per-kernel HIP-event durations from a pass with every launch
+    bracketed; the block times (ms_per_step, tflops_block) from a pass without those events.  Causal attention
+    counts only unmasked query-key pairs (forward 4 d, backward 10 d flops per pair)."""
     import numpy as np
     import torch
 
@@ -119,7 +123,18 @@ def attention_block_measure(L, steps: int, warmup: int) -> dict:
         role = "reduce_scatter" if j == 3 * w.t else ("qkv", "attention", "proj")[j % 3]
         r = roles.setdefault(role, {"kernel": name, "ms": []})
         r["ms"].append(ms)
-    out = {"workload": w.name, "ms_per_step": round(e0.elapsed_time(e1) / steps, 4), "kernels": {}}
+    def block_ms(fn):  # the block's own time, without per-launch events
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a0.record()
+        for _ in range(steps):
+            fn()
+        a1.record()
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / steps
+
+    out = {"workload": w.name, "ms_per_step": round(block_ms(lambda: blk.forward(X, sp=True)), 4),
+           "ms_per_step_with_launch_events": round(e0.elapsed_time(e1) / steps, 4), "kernels": {}}
     total_fl = w.t * sum(fl.values())
     out["tflops_block"] = round(total_fl / (out["ms_per_step"] * 1e-3) / 1e12, 1)
     for role, r in roles.items():
@@ -165,7 +180,8 @@ def attention_block_measure(L, steps: int, warmup: int) -> dict:
         r = roles.setdefault(role, {"kernels": {}, "ms": 0.0})
         r["ms"] += ms
         r["kernels"][name] = r["kernels"].get(name, 0.0) + ms
-    bwd = {"ms_per_step": round(e0.elapsed_time(e1) / steps, 4), "roles": {}}
+    bwd = {"ms_per_step": round(block_ms(lambda: blk.backward(X, dZ, sp=True)), 4),
+           "ms_per_step_with_launch_events": round(e0.elapsed_time(e1) / steps, 4), "roles": {}}
     bwd["tflops_block"] = round(w.t * sum(bfl.values()) / (bwd["ms_per_step"] * 1e-3) / 1e12, 1)
     for role, r in roles.items():
         per_rank_us = 1e3 * r["ms"] / steps / (1 if role == "reduce_scatter" else w.t)
@@ -179,6 +195,36 @@ def attention_block_measure(L, steps: int, warmup: int) -> dict:
     out["backward"] = bwd
     del blk, X, dZ
     return out
+
+
+def overlap_measure(blk, X, dZ, Z_rs, dX_rs, serial_step, steps: int, chunks: int = 2) -> dict:
+    """The same MLP step with the reductions on a second stream: forward on `chunks` row ranges with each range's
+    reduce-scatter beside the next range's GEMMs, and the backward's dX reduce-scatter beside every rank's wgrad
+    half.  Serial and overlapped steps alternate over three rounds; medians of the per-round ms/step."""
+    import torch
+
+    def overlapped():
+        blk.step_overlapped(X, dZ, Z_rs, dX_rs, chunks=chunks)
+
+    runs = {"serial": serial_step, "overlapped": overlapped}
+    for fn in runs.values():
+        fn()
+    torch.cuda.synchronize()
+    times = {k: [] for k in runs}
+    for _ in range(3):
+        for name, fn in runs.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times[name].append(e0.elapsed_time(e1) / steps)
+    med = {k: sorted(v)[len(v) // 2] for k, v in times.items()}
+    return {"chunks": chunks, "steps_per_round": steps, "serial_ms": round(med["serial"], 4),
+            "overlapped_ms": round(med["overlapped"], 4), "speedup": round(med["serial"] / med["overlapped"], 4),
+            "rounds_ms": {k: [round(x, 4) for x in v] for k, v in times.items()}}
 
 
 def gather_measure(L, reps: int) -> dict:
@@ -347,10 +393,44 @@ def main(argv=None) -> int:
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, bracketed by synchronisation; every library launch bracketed by HIP events
+    # kernel census: K steps with every library launch bracketed by HIP events (per-kernel durations; each event
+    # pair adds launch latency, so this pass is not the timed region)
     launches_per_step = 6 * w.t + 2
-    timer = L.LaunchTimer(capacity=args.steps * launches_per_step + 8)
+    census = L.LaunchTimer(capacity=args.steps * launches_per_step + 8)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    with census:
+        for _ in range(args.steps):
+            step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_census = e0.elapsed_time(e1) / args.steps
+
+    M, h, f, t = w.M, w.h, w.f_l, w.t
+    gemm_flops = 2.0 * M * h * f  # every GEMM of the step has this size
+    step_flops = 12.0 * M * h * f * t
+
+    kern = {}
+    for name, ms in census.results():
+        k = kern.setdefault(name, {"launches": 0, "total_ms": 0.0})
+        k["launches"] += 1
+        k["total_ms"] += ms
+    rs_name = next((n for n in kern if n.startswith("reduce_bf16") or n.startswith("reduce_f32")), None)
+    n_el = w.s * w.b * w.h
+    rs_bytes = (t + 1) * n_el * (2 if w.dtype == "bf16" else 4)
+    for name, k in kern.items():
+        k["avg_us"] = 1e3 * k["total_ms"] / k["launches"]
+        k["share"] = k["total_ms"] / (ms_census * args.steps)
+        if name.startswith("gemm"):
+            k["flops_per_launch"] = gemm_flops * (2 if "_pair_" in name else 1)
+            k["tflops"] = k["flops_per_launch"] / (k["avg_us"] * 1e-6) / 1e12
+        if name == rs_name:
+            k["gbps"] = rs_bytes / (k["avg_us"] * 1e-6) / 1e9
+    dom = max((n for n in kern if n.startswith("gemm")), key=lambda n: kern[n]["total_ms"])
+
+    # timed region: K steps bracketed by synchronisation; HIP events bracket only the dominant kernel's launches
+    timer = L.LaunchTimer(capacity=args.steps * launches_per_step + 8, only=dom)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
@@ -363,33 +443,14 @@ def main(argv=None) -> int:
     ms_per_step = e0.elapsed_time(e1) / args.steps
     ms_wall = wall * 1e3 / args.steps
     ms_step = max(ms_per_step, ms_wall)
-
-    M, h, f, t = w.M, w.h, w.f_l, w.t
-    gemm_flops = 2.0 * M * h * f  # every GEMM of the step has this size
-    step_flops = 12.0 * M * h * f * t
     value = step_flops / (ms_step * 1e-3) / 1e12
-
-    kern = {}
-    for name, ms in timer.results():
-        k = kern.setdefault(name, {"launches": 0, "total_ms": 0.0})
-        k["launches"] += 1
-        k["total_ms"] += ms
-    rs_name = next((n for n in kern if n.startswith("reduce_bf16") or n.startswith("reduce_f32")), None)
-    n_el = w.s * w.b * w.h
-    rs_bytes = (t + 1) * n_el * (2 if w.dtype == "bf16" else 4)
-    for name, k in kern.items():
-        k["avg_us"] = 1e3 * k["total_ms"] / k["launches"]
-        k["share"] = k["total_ms"] / (ms_per_step * args.steps)
-        if name.startswith("gemm"):
-            k["flops_per_launch"] = gemm_flops * (2 if "_pair_" in name else 1)
-            k["tflops"] = k["flops_per_launch"] / (k["avg_us"] * 1e-6) / 1e12
-        if name == rs_name:
-            k["gbps"] = rs_bytes / (k["avg_us"] * 1e-6) / 1e9
-    dom = max((n for n in kern if n.startswith("gemm")), key=lambda n: kern[n]["total_ms"])
-    ach = kern[dom]["tflops"]
+    dom_ms = [ms for name, ms in timer.results() if name == dom]
+    dom_us = 1e3 * sum(dom_ms) / len(dom_ms)
+    ach = kern[dom]["flops_per_launch"] / (dom_us * 1e-6) / 1e12
     roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": round(ach * 1e12 / PEAK_BF16_FLOPS, 4), "traffic": profiled_traffic(w.name, dom), "kernel": dom,
-                "flops_per_launch": kern[dom]["flops_per_launch"], "avg_us": round(kern[dom]["avg_us"], 2)}
+                "flops_per_launch": kern[dom]["flops_per_launch"], "avg_us": round(dom_us, 2),
+                "launches_timed": len(dom_ms)}
     gemm_ms = sum(k["total_ms"] for n, k in kern.items() if n.startswith("gemm")) / args.steps
     rs = kern[rs_name]
     out = {
@@ -414,6 +475,7 @@ def main(argv=None) -> int:
                     "bytes_per_launch": rs_bytes, "avg_us": round(rs["avg_us"], 2),
                     "traffic": profiled_traffic(w.name, rs_name)},
         "kernels": {n: {kk: (round(v, 4) if isinstance(v, float) else v) for kk, v in k.items()} for n, k in kern.items()},
+        "kernel_census_ms_per_step": round(ms_census, 4),
     }
     if args.calib_copy_mib > 0:
         nbytes = args.calib_copy_mib << 20
@@ -425,6 +487,8 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         (cname, cms), = ct.results()
         out["calib_copy"] = {"kernel": cname, "bytes_read": nbytes, "bytes_written": nbytes, "ms": round(cms, 4)}
+    if not args.no_extra:
+        out["overlap"] = overlap_measure(blk, X, dZ, Zrs, dXrs, step, max(3, args.steps // 2))
     del blk, X, dZ, Zrs, dXrs
     torch.cuda.empty_cache()
     if not args.no_extra:

@@ -112,6 +112,20 @@ int tp_mlp_bwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const 
                const void* B_i, const void* U_i, const void* Y_i, const void* dZ, void* dU_ws, void* dA_i,
                void* da_i, void* dB_i, void* dX_i, hipStream_t stream);
 
+/* The MLP backward split into its two independent halves ([ATLAS] §5: the dgrad's reduction and the wgrad GEMMs
+ * do not depend on each other, which is what lets the dX reduction run while the weight gradients compute):
+ *   TP_BWD_DGRAD: dU_ws = (dZ B_i^T) * act'(U_i) and dX_i = dU_ws A_i^T.  Reads dZ, B_i, U_i, A_i; X, Y_i, dA_i,
+ *                 da_i, dB_i are not used (may be NULL).
+ *   TP_BWD_WGRAD: dB_i = Y_i^T dZ, dA_i = X^T dU_ws, da_i = column sums of dU_ws, with dU_ws as left by this rank's
+ *                 TP_BWD_DGRAD call (an input here).  A_i, B_i, U_i, dX_i are not used (may be NULL).
+ *   TP_BWD_ALL:   both, exactly tp_mlp_bwd.
+ * The two phases of a rank, in that order, give bit-for-bit the outputs of tp_mlp_bwd (same kernels, same
+ * inputs).  A caller that runs every rank's dgrad first keeps one dU_ws per rank until that rank's wgrad. */
+typedef enum { TP_BWD_ALL = 0, TP_BWD_DGRAD = 1, TP_BWD_WGRAD = 2 } tp_bwd_phase;
+int tp_mlp_bwd_phase(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, tp_bwd_phase phase, const void* X,
+                     const void* A_i, const void* B_i, const void* U_i, const void* Y_i, const void* dZ, void* dU_ws,
+                     void* dA_i, void* da_i, void* dB_i, void* dX_i, hipStream_t stream);
+
 /* Attention forward of rank `rank` for its a/t local heads ([ATLAS] §3, [MEGA]: QKV column-parallel by head,
  * per-head softmax(Q K^T / sqrt d) V on the local heads, output projection row-parallel; [SPCP] CP step 3: the
  * online-softmax merge over key blocks):
@@ -212,6 +226,10 @@ int64_t tp_sp_ln_bwd_workspace(int64_t rows, int64_t h);
 int tp_timing_begin(hipEvent_t* starts, hipEvent_t* stops, int capacity);
 int tp_timing_end(void);
 const char* tp_timing_kernel(int i);
+/* Restrict the calling thread's log to launches whose kernel name starts with `prefix` (NULL: record all), so that
+ * a timed region can bracket only the kernels it reports (each recorded event pair costs launch latency).  Kept
+ * until changed; TP_E_SHAPE for a prefix of 64 characters or more. */
+int tp_timing_filter(const char* prefix);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
-    for n in ["tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd", "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce",
+    for n in ["tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_phase", "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce",
               "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd", "tp_sp_dropout_add_ln_bwd",
               "tp_sp_ln_bwd_workspace", "tp_status_str"]:
         assert n in names
@@ -200,3 +200,32 @@ def test_sp_region_validation(L):
     assert L.tp_sp_ln_bwd_workspace(2048, 4096) == 256 * 2 * 4096 * 4
     assert L.tp_sp_ln_bwd_workspace(3, 64) == 3 * 2 * 64 * 4
     assert L.tp_sp_ln_bwd_workspace(0, 64) == 0
+
+
+def test_mlp_bwd_phase_validation(L):
+    P = [addr(i) for i in range(11)]  # X, A_i, B_i, U_i, Y_i, dZ, dU_ws, dA_i, da_i, dB_i, dX_i
+    dims = L.make_dims(s=16, b=2, h=64, ffn=256, t=2)
+
+    def call(phase, p=P, dims=dims, rank=0):
+        return L.tp_mlp_bwd_phase(dims, rank, "gelu", phase, *p, stream=0, dtype=BF16, check=False)
+
+    # the dgrad half needs A_i, B_i, U_i, dX_i but not X, Y_i, dA_i, dB_i; the wgrad half the other way round
+    assert call("dgrad", [P[0]] + [None] + P[2:]) == -1
+    assert call("dgrad", P[:10] + [None]) == -1
+    assert call("wgrad", [None] + P[1:]) == -1
+    assert call("wgrad", P[:9] + [None, P[10]]) == -1
+    assert call("all", P[:4] + [None] + P[5:]) == -1
+    assert call(7) == -7                                                  # unknown phase
+    assert call("dgrad", dims=L.make_dims(s=16, b=2, h=64, ffn=255, t=2)) == -3
+    assert call("wgrad", rank=2) == -5
+    # unused operands are not checked: a misaligned X does not matter to the dgrad half, a misaligned dU does
+    assert call("dgrad", [P[0] + 2] + P[1:6] + [P[6] + 2] + P[7:]) == -7
+    # dU_ws is written by the dgrad half (may not alias an input) and only read by the wgrad half
+    assert call("dgrad", P[:6] + [P[5]] + P[7:]) == -6                    # dU_ws aliases dZ
+    assert call("wgrad", P[:9] + [P[6]] + P[10:]) == -6                   # dB_i aliases dU_ws (an input here)
+
+
+def test_timing_filter_arguments(L):
+    assert L.lib.tp_timing_filter(b"gemm_bf16_big_pair") == 0
+    assert L.lib.tp_timing_filter(b"x" * 64) == -2
+    assert L.lib.tp_timing_filter(None) == 0
