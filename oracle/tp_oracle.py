@@ -29,6 +29,9 @@ Readings where the pages are silent (each also listed in the design notes):
 The SP-region ops (LayerNorm, dropout + residual) are the plain per-row / per-element definitions; dropout takes
 its random words as an input (tp_inputs draws them), so both sides make the same keep decisions.
 
+Vocab-parallel cross entropy follows the pages' steps (per-rank max, all-reduce(max), per-rank sum of exponentials
+and target logit, all-reduce(sum)); a negative target marks an ignored row.
+
 The attention backward (core and block) follows the chain rule through the row softmax as written out in
 attention_core_backward; it is pinned by finite differences of the forward, torch's fp64 autograd, closed forms
 and softmax invariants (tests/test_oracle_attention_bwd.py).
@@ -667,6 +670,81 @@ def dropout_add_backward(dout: np.ndarray, bits: np.ndarray, p: float):
     keep = dropout_keep(bits, p)
     dout = np.asarray(dout, dtype=np.float64)
     return np.where(keep, dout / (1.0 - p), 0.0), dout
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# Vocab-parallel cross entropy ([ATLAS] §5 table: the vocab-parallel CE row, all-reduce(max) then all-reduce(sum),
+# backward local; [MEGA] embedding / logits remark: the column-parallel logits feed the loss directly, so only b*s
+# scalars per reduction cross ranks).  Targets are global vocab ids; a negative target marks an ignored row (loss 0,
+# no gradient).
+# ---------------------------------------------------------------------------------------------------------------
+
+
+def cross_entropy(logits: np.ndarray, targets: np.ndarray) -> np.ndarray:
+    """Unsharded per-row loss: log(sum_j exp(logits[i, j])) - logits[i, targets[i]]; 0 where targets[i] < 0."""
+    x = np.asarray(logits, dtype=np.float64)
+    tg = np.asarray(targets, dtype=np.int64)
+    m = x.max(axis=1)
+    lse = m + np.log(np.exp(x - m[:, None]).sum(axis=1))
+    keep = tg >= 0
+    loss = np.zeros(x.shape[0])
+    loss[keep] = lse[keep] - x[np.nonzero(keep)[0], tg[keep]]
+    return loss
+
+
+def cross_entropy_backward(logits: np.ndarray, targets: np.ndarray, dloss: np.ndarray) -> np.ndarray:
+    """Gradient of sum_i dloss[i] * loss[i]: (softmax(logits[i]) - onehot(targets[i])) * dloss[i]; 0 rows when
+    ignored."""
+    x = np.asarray(logits, dtype=np.float64)
+    tg = np.asarray(targets, dtype=np.int64)
+    e = np.exp(x - x.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)
+    keep = tg >= 0
+    rows = np.nonzero(keep)[0]
+    p[rows, tg[keep]] -= 1.0
+    p *= np.asarray(dloss, dtype=np.float64)[:, None]
+    p[~keep] = 0.0
+    return p
+
+
+def vocab_parallel_cross_entropy(logit_shards: Sequence[np.ndarray], targets: np.ndarray):
+    """The pages' sharded steps over t ranks, rank r holding vocab columns [r*v, (r+1)*v) of the logits:
+    1. each rank's row max, then all-reduce(max) -> m;
+    2. each rank's sum of exp(logits - m) and its target logit (0 when the target is not in its range), then
+       all-reduce(sum) of both -> S, target logit;
+    3. loss = log S + m - target logit (0 for ignored rows).  Returns loss and lse = m + log S per row."""
+    v = logit_shards[0].shape[1]
+    tg = np.asarray(targets, dtype=np.int64)
+    xs = [np.asarray(x, dtype=np.float64) for x in logit_shards]
+    m = np.max(np.stack([x.max(axis=1) for x in xs]), axis=0)                       # all-reduce(max)
+    sums, tls = [], []
+    for r, x in enumerate(xs):
+        sums.append(np.exp(x - m[:, None]).sum(axis=1))
+        local = tg - r * v
+        mine = (tg >= 0) & (local >= 0) & (local < v)
+        tl = np.zeros(x.shape[0])
+        tl[mine] = x[np.nonzero(mine)[0], local[mine]]
+        tls.append(tl)
+    S = np.sum(np.stack(sums), axis=0)                                               # all-reduce(sum)
+    tl = np.sum(np.stack(tls), axis=0)
+    lse = m + np.log(S)
+    loss = np.where(tg >= 0, lse - tl, 0.0)
+    return loss, lse
+
+
+def vocab_parallel_cross_entropy_backward(logits_r: np.ndarray, targets: np.ndarray, rank: int, lse: np.ndarray,
+                                          dloss: np.ndarray) -> np.ndarray:
+    """Rank-local backward: (exp(logits_r - lse) - [global column == target]) * dloss per row; 0 when ignored."""
+    x = np.asarray(logits_r, dtype=np.float64)
+    v = x.shape[1]
+    tg = np.asarray(targets, dtype=np.int64)
+    g = np.exp(x - np.asarray(lse, dtype=np.float64)[:, None])
+    local = tg - rank * v
+    mine = (tg >= 0) & (local >= 0) & (local < v)
+    g[np.nonzero(mine)[0], local[mine]] -= 1.0
+    g *= np.asarray(dloss, dtype=np.float64)[:, None]
+    g[tg < 0] = 0.0
+    return g
 
 
 # ---------------------------------------------------------------------------------------------------------------

@@ -1,0 +1,83 @@
+"""Pins of the oracle's cross entropy and its vocab-parallel form ("Tensor Parallelism (TP) 与 Sequence
+Parallelism (SP)" §5, the vocab-parallel CE row: all-reduce(max), all-reduce(sum), local backward).
+
+* the unsharded loss and gradient against torch's fp64 cross_entropy and autograd (an independent library
+  routine; a negative target -100 is torch's default ignored index);
+* closed forms: equal logits give log V; a target logit far above the rest gives a loss near 0;
+* shifting a row by a constant changes nothing; gradient rows sum to 0 and match finite differences;
+* the sharded steps equal the unsharded loss for t = 1, 2, 4, with targets in every shard, and stay finite for
+  logits of magnitude 1e4 (a plain exp would overflow).
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+
+
+def _case(seed, rows=9, V=24, scale=3.0):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((rows, V)) * scale
+    tg = r.integers(0, V, rows)
+    tg[2] = -100
+    return x, tg
+
+
+def test_against_torch_fp64():
+    torch = pytest.importorskip("torch")
+    x, tg = _case(1)
+    dl = np.random.default_rng(2).standard_normal(x.shape[0])
+    tx = torch.tensor(x, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(tx, torch.tensor(tg), reduction="none")
+    (loss * torch.tensor(dl)).sum().backward()
+    assert np.allclose(O.cross_entropy(x, tg), loss.detach().numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(O.cross_entropy_backward(x, tg, dl), tx.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_closed_forms_and_invariance():
+    V = 50
+    x = np.full((3, V), 2.5)
+    assert np.allclose(O.cross_entropy(x, np.array([0, 7, 49])), np.log(V))
+    y = np.zeros((1, V))
+    y[0, 3] = 60.0
+    assert O.cross_entropy(y, np.array([3]))[0] < 1e-20
+    x, tg = _case(3)
+    shift = np.random.default_rng(4).standard_normal(x.shape[0])[:, None] * 10
+    assert np.allclose(O.cross_entropy(x + shift, tg), O.cross_entropy(x, tg))
+
+
+def test_backward_finite_differences_and_row_sums():
+    x, tg = _case(5, rows=4, V=7)
+    dl = np.random.default_rng(6).standard_normal(4)
+    g = O.cross_entropy_backward(x, tg, dl)
+    fd = np.zeros_like(x)
+    for i in range(x.shape[0]):
+        for j in range(x.shape[1]):
+            xp, xm = x.copy(), x.copy()
+            xp[i, j] += 1e-6
+            xm[i, j] -= 1e-6
+            fd[i, j] = ((O.cross_entropy(xp, tg) - O.cross_entropy(xm, tg)) * dl).sum() / 2e-6
+    assert np.allclose(g, fd, rtol=1e-6, atol=1e-8)
+    assert np.allclose(g.sum(axis=1), 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("t", [1, 2, 4])
+def test_vocab_parallel_equals_unsharded(t):
+    x, tg = _case(7, rows=12, V=32)
+    tg[:4] = [0, 31, 8 * 1 + 3, 16]  # targets in the first, last and middle shards
+    tg[5] = -100
+    shards = [x[:, r * 32 // t:(r + 1) * 32 // t] for r in range(t)]
+    loss, lse = O.vocab_parallel_cross_entropy(shards, tg)
+    assert np.allclose(loss, O.cross_entropy(x, tg), rtol=1e-12, atol=1e-12)
+    m = x.max(axis=1)
+    assert np.allclose(lse, m + np.log(np.exp(x - m[:, None]).sum(axis=1)))
+    dl = np.random.default_rng(8).standard_normal(12)
+    g = np.concatenate([O.vocab_parallel_cross_entropy_backward(shards[r], tg, r, lse, dl) for r in range(t)], axis=1)
+    assert np.allclose(g, O.cross_entropy_backward(x, tg, dl), rtol=1e-12, atol=1e-12)
+    assert loss[5] == 0.0 and np.all(g[5] == 0.0)
+
+
+def test_large_logits_stay_finite():
+    x, tg = _case(9, rows=5, V=16, scale=1e4)
+    loss, lse = O.vocab_parallel_cross_entropy([x[:, :8], x[:, 8:]], tg)
+    assert np.all(np.isfinite(loss)) and np.all(np.isfinite(lse))
+    assert np.allclose(loss, O.cross_entropy(x, tg))

@@ -9,11 +9,14 @@ Recipe (one stream per tensor, so adding a tensor never shifts another):
   bf16 storage: round-to-nearest-even of those fp32 values (torch's CPU conversion); fp32 storage keeps them as is.
 
 Tensor ids: X=0, A (or Wqkv)=1, B (or Wo)=2, dZ=3, column bias=4, row bias=5, partial sums=7; the
-sequence-parallel region adds LayerNorm gamma=8, beta=9, residual=10, dropout random words=11, dy=12.
+sequence-parallel region adds LayerNorm gamma=8, beta=9, residual=10, dropout random words=11, dy=12; the
+vocab-parallel cross entropy logits=13, targets=14, per-row loss gradients=15.
 Distributions follow the workloads of the pages: activations and upstream gradients N(0,1), weights N(0, 0.02^2)
 (0.02 is the standard deviation, the GPT/Megatron init convention), biases N(0, 0.02^2); LayerNorm gamma
 1 + N(0, 0.1^2) and beta N(0, 0.1^2) (a trained-looking affine, not the identity, so a dropped gamma or beta
 shows).  Random words: rng.integers(0, 2^32) from the same per-tensor stream, one uint32 per element.
+Cross entropy: logits N(0, 2^2); targets uniform over the vocab, with one row in 64 (chosen by the same stream)
+set to -100, an ignored row; per-row loss gradients N(0, 1).
 """
 from __future__ import annotations
 
@@ -24,6 +27,8 @@ import numpy as np
 
 T_X, T_A, T_B, T_DZ, T_BIAS_COL, T_BIAS_ROW = 0, 1, 2, 3, 4, 5
 T_GAMMA, T_BETA, T_RESID, T_BITS, T_DY = 8, 9, 10, 11, 12
+T_LOGITS, T_TARGETS, T_DLOSS = 13, 14, 15
+LOGIT_STD = 2.0
 WEIGHT_STD = 0.02
 
 
@@ -162,6 +167,16 @@ def sp_region_inputs(rows: int, h: int, dtype: str = "bf16", seed: int = 0) -> d
         "dy": tensor(seed, T_DY, (rows, h), 1.0, dtype),
         "bits": random_words(seed, T_BITS, (rows, h)),
     }
+
+
+def vocab_ce_inputs(rows: int, vocab: int, dtype: str = "bf16", seed: int = 0) -> dict:
+    """Full logits [rows, vocab] (rank r's shard is columns [r*vocab/t, (r+1)*vocab/t)), int32 targets [rows] with
+    about 1/64 of the rows ignored (-100), and fp32 per-row loss gradients [rows]."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, T_TARGETS]))
+    targets = rng.integers(0, vocab, size=rows).astype(np.int32)
+    targets[rng.random(rows) < 1.0 / 64] = -100
+    return {"logits": tensor(seed, T_LOGITS, (rows, vocab), LOGIT_STD, dtype), "targets": targets,
+            "dloss": normal_f32(seed, T_DLOSS, (rows,))}
 
 
 def partials(seed: int, t: int, shape, dtype: str = "bf16", tensor_id: int = 7) -> np.ndarray:
