@@ -25,7 +25,8 @@ STATUS = {0: "TP_OK", -1: "TP_E_NULL", -2: "TP_E_SHAPE", -3: "TP_E_DIVISIBILITY"
 EXPORTED = ["tp_status_str", "tp_last_hip_error", "tp_abi_version", "tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd",
             "tp_mlp_bwd_phase",
             "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd",
-            "tp_sp_dropout_add_ln_bwd", "tp_sp_ln_bwd_workspace", "tp_timing_begin", "tp_timing_end",
+            "tp_sp_dropout_add_ln_bwd", "tp_sp_ln_bwd_workspace", "tp_vocab_ce_fwd_local", "tp_vocab_ce_combine",
+            "tp_vocab_ce_bwd", "tp_timing_begin", "tp_timing_end",
             "tp_timing_kernel", "tp_timing_filter"]
 
 
@@ -73,6 +74,9 @@ def _load() -> ctypes.CDLL:
         "tp_sp_dropout_add_ln_fwd": ([I64, I64, I, F64, F64, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_sp_dropout_add_ln_bwd": ([I64, I64, I, F64, P, P, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_sp_ln_bwd_workspace": ([I64, I64], I64),
+        "tp_vocab_ce_fwd_local": ([I64, I64, I, I, P, P, P, P], I),
+        "tp_vocab_ce_combine": ([I64, I, P, P, P, P, P], I),
+        "tp_vocab_ce_bwd": ([I64, I64, I, I, P, P, P, P, P, P], I),
         "tp_timing_begin": ([ctypes.POINTER(P), ctypes.POINTER(P), I], I),
         "tp_timing_end": ([], I),
         "tp_timing_kernel": ([I], ctypes.c_char_p),
@@ -223,6 +227,26 @@ def tp_sp_dropout_add_ln_bwd(rows: int, h: int, p: float, u, gamma, mean, rstd, 
 
 def tp_sp_ln_bwd_workspace(rows: int, h: int) -> int:
     return int(lib.tp_sp_ln_bwd_workspace(int(rows), int(h)))
+
+
+def tp_vocab_ce_fwd_local(rows: int, v_local: int, rank: int, logits_i, targets, stats_i, stream=None, dtype=None,
+                          check=True) -> int:
+    st = lib.tp_vocab_ce_fwd_local(int(rows), int(v_local), int(rank), _dtype_code(logits_i, dtype), _ptr(logits_i),
+                                   _ptr(targets), _ptr(stats_i), _stream(stream))
+    return _check(st, "tp_vocab_ce_fwd_local", check)
+
+
+def tp_vocab_ce_combine(rows: int, t: int, stats, targets, loss, lse, stream=None, check=True) -> int:
+    st = lib.tp_vocab_ce_combine(int(rows), int(t), _ptr(stats), _ptr(targets), _ptr(loss), _ptr(lse),
+                                 _stream(stream))
+    return _check(st, "tp_vocab_ce_combine", check)
+
+
+def tp_vocab_ce_bwd(rows: int, v_local: int, rank: int, logits_i, targets, lse, dloss, dlogits_i, stream=None,
+                    dtype=None, check=True) -> int:
+    st = lib.tp_vocab_ce_bwd(int(rows), int(v_local), int(rank), _dtype_code(logits_i, dtype), _ptr(logits_i),
+                             _ptr(targets), _ptr(lse), _ptr(dloss), _ptr(dlogits_i), _stream(stream))
+    return _check(st, "tp_vocab_ce_bwd", check)
 
 
 class LaunchTimer:

@@ -20,7 +20,7 @@ LIB_NAME = "libtpshard.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["tp_abi.hip", "comm_kernels.hip", "gemm_bf16.hip", "gemm_f32.hip", "attention.hip", "sp_region.hip"]
+SOURCES = ["tp_abi.hip", "comm_kernels.hip", "gemm_bf16.hip", "gemm_f32.hip", "attention.hip", "sp_region.hip", "vocab_ce.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -571,4 +571,54 @@ int tp_sp_dropout_add_ln_bwd(int64_t rows, int64_t h, tp_dtype dtype, double p, 
   return hip_status(tp::sp_dropout_add_ln_bwd(dtype, a, stream));
 }
 
+namespace {
+int ce_check(int64_t rows, int64_t v_local, int rank, tp_dtype dtype) {
+  if (rows <= 0 || v_local <= 0 || rows >= kMaxDim || v_local >= kMaxDim || rows * v_local >= ((int64_t)1 << 40))
+    return TP_E_SHAPE;
+  if (rank < 0) return TP_E_RANK;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  if (v_local % 8 != 0) return TP_E_UNSUPPORTED;
+  return TP_OK;
+}
+}  // namespace
+
+int tp_vocab_ce_fwd_local(int64_t rows, int64_t v_local, int rank, tp_dtype dtype, const void* logits_i,
+                          const int32_t* targets, float* stats_i, hipStream_t stream) {
+  if (logits_i == nullptr || targets == nullptr || stats_i == nullptr) return TP_E_NULL;
+  const int st = ce_check(rows, v_local, rank, dtype);
+  if (st != TP_OK) return st;
+  if (misaligned16({logits_i, (const void*)stats_i})) return TP_E_UNSUPPORTED;
+  const Buf outs[] = {{stats_i, rows * 16}};
+  const Buf ins[] = {{logits_i, rows * v_local * esize(dtype)}, {targets, rows * 4}};
+  if (any_alias(outs, 1, ins, 2)) return TP_E_ALIAS;
+  return hip_status(tp::vocab_ce_local(dtype, logits_i, targets, rows, (int)v_local, rank, stats_i, stream));
+}
+
+int tp_vocab_ce_combine(int64_t rows, int t, const float* stats, const int32_t* targets, float* loss, float* lse,
+                        hipStream_t stream) {
+  if (stats == nullptr || targets == nullptr || loss == nullptr) return TP_E_NULL;
+  if (rows <= 0 || t <= 0 || rows >= kMaxDim) return TP_E_SHAPE;
+  if (misaligned16({(const void*)stats})) return TP_E_UNSUPPORTED;
+  const Buf outs[] = {{loss, rows * 4}, {lse, rows * 4}};
+  const Buf ins[] = {{stats, (int64_t)t * rows * 16}, {targets, rows * 4}};
+  if (any_alias(outs, 2, ins, 2)) return TP_E_ALIAS;
+  return hip_status(tp::vocab_ce_combine(stats, t, rows, targets, loss, lse, stream));
+}
+
+int tp_vocab_ce_bwd(int64_t rows, int64_t v_local, int rank, tp_dtype dtype, const void* logits_i,
+                    const int32_t* targets, const float* lse, const float* dloss, void* dlogits_i,
+                    hipStream_t stream) {
+  if (logits_i == nullptr || targets == nullptr || lse == nullptr || dloss == nullptr || dlogits_i == nullptr)
+    return TP_E_NULL;
+  const int st = ce_check(rows, v_local, rank, dtype);
+  if (st != TP_OK) return st;
+  if (misaligned16({logits_i, (const void*)dlogits_i})) return TP_E_UNSUPPORTED;
+  const int64_t bytes = rows * v_local * esize(dtype);
+  const Buf outs[] = {{dlogits_i, bytes}};
+  const Buf ins[] = {{logits_i, bytes}, {targets, rows * 4}, {lse, rows * 4}, {dloss, rows * 4}};
+  if (any_alias(outs, 1, ins, 4)) return TP_E_ALIAS;
+  return hip_status(tp::vocab_ce_bwd(dtype, logits_i, targets, lse, dloss, rows, (int)v_local, rank, dlogits_i,
+                                     stream));
+}
+
 }  // extern "C"

@@ -221,4 +221,12 @@ int64_t sp_bwd_blocks(int64_t rows);
 hipError_t sp_dropout_add_ln_fwd(tp_dtype dt, const SpFwdArgs& a, hipStream_t st);
 hipError_t sp_dropout_add_ln_bwd(tp_dtype dt, const SpBwdArgs& a, hipStream_t st);
 
+// Vocab-parallel cross entropy.  stats: per row {max, sum of exp(x - max), target logit or 0, 0} as float4.
+hipError_t vocab_ce_local(tp_dtype dt, const void* logits, const int32_t* targets, int64_t rows, int v, int rank,
+                          float* stats, hipStream_t st);
+hipError_t vocab_ce_combine(const float* stats, int t, int64_t rows, const int32_t* targets, float* loss, float* lse,
+                            hipStream_t st);
+hipError_t vocab_ce_bwd(tp_dtype dt, const void* logits, const int32_t* targets, const float* lse,
+                        const float* dloss, int64_t rows, int v, int rank, void* dlogits, hipStream_t st);
+
 }  // namespace tp

@@ -217,6 +217,30 @@ int tp_sp_dropout_add_ln_bwd(int64_t rows, int64_t h, tp_dtype dtype, double p, 
  * workgroup of the row loop); <= 0 for non-positive sizes. */
 int64_t tp_sp_ln_bwd_workspace(int64_t rows, int64_t h);
 
+/* Vocab-parallel cross entropy ([ATLAS] §5 table, the vocab-parallel CE row: all-reduce(max), then all-reduce(sum),
+ * backward local; [MEGA] embedding remark: the column-parallel logits feed the loss directly, so only b*s scalars
+ * per reduction cross ranks).  Rank r holds logits_i [rows, v_local] for vocab columns [r*v_local, (r+1)*v_local)
+ * of every token row (rows = s*b).  targets: int32 [rows], global vocab ids in [0, t*v_local); a negative target
+ * marks an ignored row (loss 0, zero gradient).  A target >= t*v_local is in no rank's range (its logit counts 0).
+ *
+ * Local pass: stats_i float4 [rows] = {m_r, s_r, tl_r, 0} with m_r the row max of this rank's logits, s_r the sum of
+ * exp(x - m_r) over them, tl_r the target's logit when the target is one of this rank's columns, else 0. */
+int tp_vocab_ce_fwd_local(int64_t rows, int64_t v_local, int rank, tp_dtype dtype, const void* logits_i,
+                          const int32_t* targets, float* stats_i, hipStream_t stream);
+
+/* The two all-reduces, on one GPU over the t ranks' records stats [t][rows] float4 (rank order):
+ *   m = max_r m_r;  S = sum_r s_r exp(m_r - m);  lse = m + log S;  loss = lse - sum_r tl_r  (0 for ignored rows)
+ * loss: fp32 [rows]; lse: fp32 [rows] (nullable; the backward needs it).  stats 16-byte aligned. */
+int tp_vocab_ce_combine(int64_t rows, int t, const float* stats, const int32_t* targets, float* loss, float* lse,
+                        hipStream_t stream);
+
+/* Local backward: dlogits_i[i, j] = (exp(x[i, j] - lse[i]) - [r*v_local + j == target[i]]) * dloss[i], zero rows
+ * for ignored targets.  dloss fp32 [rows] (e.g. 1 / the number of counted rows for a mean loss).  logits_i and
+ * dlogits_i in dtype, 16-byte aligned; v_local % 8 == 0 for both calls on logits (else TP_E_UNSUPPORTED). */
+int tp_vocab_ce_bwd(int64_t rows, int64_t v_local, int rank, tp_dtype dtype, const void* logits_i,
+                    const int32_t* targets, const float* lse, const float* dloss, void* dlogits_i,
+                    hipStream_t stream);
+
 /* Launch timing, a profiling aid (not part of the block's arithmetic).  tp_timing_begin arms the calling thread:
  * every kernel launched by a later tp_* call on this thread is bracketed by hipEventRecord(starts[i], stream) and
  * hipEventRecord(stops[i], stream), for the first `capacity` launches (later ones run unrecorded).  The events are

@@ -30,7 +30,8 @@ def test_header_declares_the_expected_entry_points():
     names = declared_functions()
     for n in ["tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_phase", "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce",
               "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd", "tp_sp_dropout_add_ln_bwd",
-              "tp_sp_ln_bwd_workspace", "tp_status_str"]:
+              "tp_sp_ln_bwd_workspace", "tp_vocab_ce_fwd_local", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
+              "tp_status_str"]:
         assert n in names
 
 
@@ -229,3 +230,22 @@ def test_timing_filter_arguments(L):
     assert L.lib.tp_timing_filter(b"gemm_bf16_big_pair") == 0
     assert L.lib.tp_timing_filter(b"x" * 64) == -2
     assert L.lib.tp_timing_filter(None) == 0
+
+
+def test_vocab_ce_validation(L):
+    P = [addr(i) for i in range(6)]
+    assert L.tp_vocab_ce_fwd_local(16, 64, 0, None, P[1], P[2], stream=0, dtype=BF16, check=False) == -1
+    assert L.tp_vocab_ce_fwd_local(0, 64, 0, P[0], P[1], P[2], stream=0, dtype=BF16, check=False) == -2
+    assert L.tp_vocab_ce_fwd_local(16, 64, -1, P[0], P[1], P[2], stream=0, dtype=BF16, check=False) == -5
+    assert L.tp_vocab_ce_fwd_local(16, 64, 0, P[0], P[1], P[2], stream=0, dtype=4, check=False) == -4
+    assert L.tp_vocab_ce_fwd_local(16, 60, 0, P[0], P[1], P[2], stream=0, dtype=BF16, check=False) == -7
+    assert L.tp_vocab_ce_fwd_local(16, 64, 0, P[0], P[1], P[2] + 4, stream=0, dtype=BF16, check=False) == -7
+    assert L.tp_vocab_ce_fwd_local(16, 64, 0, P[0], P[1], P[0] + 64, stream=0, dtype=BF16, check=False) == -6
+    assert L.tp_vocab_ce_fwd_local(1 << 21, 1 << 20, 0, P[0], P[1], P[2], stream=0, dtype=BF16, check=False) == -2
+    assert L.tp_vocab_ce_combine(16, 0, P[0], P[1], P[2], P[3], stream=0, check=False) == -2
+    assert L.tp_vocab_ce_combine(16, 2, P[0], None, P[2], P[3], stream=0, check=False) == -1
+    assert L.tp_vocab_ce_combine(16, 2, P[0] + 8, P[1], P[2], P[3], stream=0, check=False) == -7
+    assert L.tp_vocab_ce_combine(16, 2, P[0], P[1], P[2], P[2] + 8, stream=0, check=False) == -6  # lse overlaps loss
+    assert L.tp_vocab_ce_bwd(16, 64, 0, P[0], P[1], P[2], None, P[4], stream=0, dtype=BF16, check=False) == -1
+    assert L.tp_vocab_ce_bwd(16, 64, 0, P[0], P[1], P[2], P[3], P[0] + 32, stream=0, dtype=BF16, check=False) == -6
+    assert L.tp_vocab_ce_bwd(16, 12, 0, P[0], P[1], P[2], P[3], P[4], stream=0, dtype="f32", check=False) == -7

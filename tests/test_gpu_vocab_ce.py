@@ -1,0 +1,110 @@
+"""Vocab-parallel cross entropy (tp_vocab_ce_fwd_local / _combine / _bwd) against the oracle, through the C ABI.
+
+Every rank's local pass on its vocab columns, the combine over the t ranks' records, every rank's backward:
+* the local records: the row max and the target logit are selections, so they must equal the oracle's bit for bit;
+  the local sum of exponentials within the fp32 bound;
+* loss and lse (fp32 outputs of fp32 arithmetic on exactly represented inputs): relative Frobenius <= 1e-5;
+* dlogits: the dtype's bound (bf16 1e-2 / 3e-2 unit scale, fp32 1e-5); ignored rows exactly zero;
+at small ragged sizes (vocab shards of 8 columns, shards whose chunk count leaves a partial pass, t = 1..8), at
+the pages' vocab 51200 with t = 8, at a 128256-entry vocab, and at the full 16384-row workload with sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import tp_inputs as TI
+from parity_utils import check_close, dev, empty, f64, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_block_columnparallel_amd as pkg
+
+    return pkg.load()
+
+
+def run(L, inp, rows, V, t, dtype):
+    v = V // t
+    logits = dev(inp["logits"], dtype)
+    shards = [logits[:, r * v:(r + 1) * v].contiguous() for r in range(t)]
+    tg = torch.from_numpy(inp["targets"]).cuda()
+    dl = torch.from_numpy(inp["dloss"]).cuda()
+    stats = torch.empty((t, rows, 4), dtype=torch.float32, device="cuda")
+    loss = torch.empty(rows, dtype=torch.float32, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    for r in range(t):
+        L.tp_vocab_ce_fwd_local(rows, v, r, shards[r], tg, stats[r], dtype=dtype)
+    L.tp_vocab_ce_combine(rows, t, stats, tg, loss, lse)
+    dlog = []
+    for r in range(t):
+        d = empty((rows, v), dtype)
+        L.tp_vocab_ce_bwd(rows, v, r, shards[r], tg, lse, dl, d, dtype=dtype)
+        dlog.append(d)
+    torch.cuda.synchronize()
+    return stats, loss, lse, dlog
+
+
+def check(inp, rows, V, t, dtype, stats, loss, lse, dlog, sample=None):
+    v = V // t
+    sel = np.arange(rows) if sample is None else sample
+    xs = O.as_f64(inp["logits"][sel], dtype).reshape(len(sel), V)
+    tgs, dls = inp["targets"][sel], inp["dloss"][sel].astype(np.float64)
+    sel_t = torch.from_numpy(sel).cuda()
+    shards = [xs[:, r * v:(r + 1) * v] for r in range(t)]
+    loss_ref, lse_ref = O.vocab_parallel_cross_entropy(shards, tgs)
+    st = stats.cpu().numpy()[:, sel]
+    for r in range(t):
+        m_r = shards[r].max(axis=1)
+        assert np.array_equal(st[r, :, 0].astype(np.float64), m_r), f"rank {r} row max"
+        local = tgs.astype(np.int64) - r * v
+        mine = (tgs >= 0) & (local >= 0) & (local < v)
+        tl = np.zeros(len(sel))
+        tl[mine] = shards[r][np.nonzero(mine)[0], local[mine]]
+        assert np.array_equal(st[r, :, 2].astype(np.float64), tl), f"rank {r} target logit"
+        check_close(st[r, :, 1], np.exp(shards[r] - m_r[:, None]).sum(axis=1), "f32", f"rank {r} local sum")
+    check_close(f64(loss[sel_t]), loss_ref, "f32", "loss")
+    check_close(f64(lse[sel_t]), lse_ref, "f32", "lse")
+    assert np.all(f64(loss[sel_t])[tgs < 0] == 0.0)
+    for r in range(t):
+        g_ref = O.vocab_parallel_cross_entropy_backward(shards[r], tgs, r, lse_ref, dls)
+        g = f64(dlog[r][sel_t])
+        check_close(g, g_ref, dtype, f"dlogits rank {r}")
+        assert np.all(g[tgs < 0] == 0.0)
+
+
+CASES = [  # rows, V, t, dtype
+    (1, 8, 1, "bf16"),
+    (37, 48, 2, "bf16"),
+    (19, 4112, 2, "bf16"),      # 257 chunks of 8 per shard: a second, nearly empty pass per thread
+    (33, 51200, 8, "bf16"),     # the pages' vocab, t = 8
+    (5, 128256, 8, "bf16"),     # 16032 columns per rank
+    (13, 96, 4, "f32"),
+    (9, 16384, 2, "f32"),
+]
+
+
+@pytest.mark.parametrize("rows,V,t,dtype", CASES)
+def test_vocab_parallel_ce_matches_oracle(L, rows, V, t, dtype):
+    say(f"vocab CE rows={rows} V={V} t={t} {dtype}")
+    inp = TI.vocab_ce_inputs(rows, V, dtype, seed=rows + t)
+    inp["targets"][0] = V - 1           # the last column of the last rank
+    if rows > 2:
+        inp["targets"][1] = -100        # an ignored row
+        inp["targets"][2] = (V // t) * (t // 2)  # the first column of a middle rank
+    stats, loss, lse, dlog = run(L, inp, rows, V, t, dtype)
+    check(inp, rows, V, t, dtype, stats, loss, lse, dlog)
+
+
+def test_full_workload_sampled_rows(L):
+    """16384 token rows (s=2048, b=8) over a 51200-entry vocab at t = 8; 192 rows checked against the oracle."""
+    rows, V, t = 16384, 51200, 8
+    say(f"vocab CE full workload rows={rows} V={V} t={t} bf16")
+    inp = TI.vocab_ce_inputs(rows, V, "bf16", seed=0)
+    stats, loss, lse, dlog = run(L, inp, rows, V, t, "bf16")
+    sample = np.sort(np.random.default_rng(1).choice(rows, 192, replace=False))
+    check(inp, rows, V, t, "bf16", stats, loss, lse, dlog, sample=sample)
