@@ -12,13 +12,16 @@ both reductions), in TFLOP/s.  A census pass of K steps first brackets every lib
 "kernels" table and the step's dominant kernel); the timed region then runs K more steps with events around the
 dominant kernel's launches only, since every event pair adds launch latency.  roofline = that kernel's
 algorithmic flops per launch over its average HIP-event duration inside the timed region, against the dense bf16
-MFMA peak.  rs_dim0 = the reduce-scatter kernel (census pass) against HBM bandwidth.  traffic = HBM bytes per launch from the committed
-rocprofv3 counter summary under profiles/ (null once the kernel source differs from the one profiled).
-cpu_baseline = the fp64 oracle on a bounded sample.  overlap, attention_block, gather_dim0 and sp_region = the
-other rows of the hot path, timed after the step (not part of value): the same step with its reductions on a
-second stream beside the GEMMs (serial vs overlapped ms/step), the attention block forward and backward at the
-22B-class shape, the dim-0 gather at the Llama-70B-sized SP shape, and the sequence-parallel region (dropout +
-residual + LayerNorm, forward and backward) on every rank's rows at that same shape.
+MFMA peak.  rs_dim0 = the reduce-scatter kernel (census pass) against HBM bandwidth.  traffic = HBM bytes per
+launch from the committed rocprofv3 counter summary under profiles/ (null once the kernel source differs from the
+one profiled).  cpu_baseline = the fp64 oracle on a bounded sample.
+
+overlap, attention_block, gather_dim0, sp_region and vocab_ce = the other rows of the hot path, timed after the
+step (not part of value): the same step with its reductions on a second stream beside the GEMMs (serial vs
+overlapped ms/step); the attention block forward and backward at the 22B-class shape; the dim-0 gather at the
+Llama-70B-sized SP shape; the sequence-parallel region (dropout + residual + LayerNorm, forward and backward) on
+every rank's rows at that same shape; the vocab-parallel cross entropy (local pass, combine, backward) at 16384
+token rows over a 51200-entry vocab.
 """
 from __future__ import annotations
 
@@ -41,7 +44,7 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default="mlp_h4096_ffn16384_t8_b8_s2048")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--no-extra", action="store_true", help="skip the attention-block, gather and SP-region measurements")
+    ap.add_argument("--no-extra", action="store_true", help="skip the overlap, attention-block, gather, SP-region and cross-entropy measurements")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one dim-0 gather (a plain copy) of this many MiB, for counter calibration")
     return ap.parse_args(argv)
@@ -315,6 +318,59 @@ def sp_region_measure(L, reps: int) -> dict:
     return out
 
 
+def vocab_ce_measure(L, reps: int) -> dict:
+    """Vocab-parallel cross entropy at s=2048, b=8 (16384 token rows) over a 51200-entry vocab, t=8, bf16 logits:
+    per step every rank's local pass (reads its [16384, 6400] logit shard once), the combine of the 8 ranks'
+    per-row records (the max and sum all-reduces), every rank's backward (reads the shard, writes its gradient)."""
+    import numpy as np
+    import torch
+
+    import tp_inputs as TI
+
+    rows, V, t = 16384, 51200, 8
+    v = V // t
+    inp = TI.vocab_ce_inputs(rows, V, "bf16", seed=0)
+    logits = torch.from_numpy(inp["logits"].view(np.int16)).view(torch.bfloat16).cuda()
+    del inp["logits"]
+    shards = [logits[:, r * v:(r + 1) * v].contiguous() for r in range(t)]
+    del logits
+    tg = torch.from_numpy(inp["targets"]).cuda()
+    dl = torch.from_numpy(inp["dloss"]).cuda()
+    stats = torch.empty((t, rows, 4), dtype=torch.float32, device="cuda")
+    loss = torch.empty(rows, dtype=torch.float32, device="cuda")
+    lse = torch.empty_like(loss)
+    dlog = [torch.empty_like(sh) for sh in shards]
+
+    def step():
+        for r in range(t):
+            L.tp_vocab_ce_fwd_local(rows, v, r, shards[r], tg, stats[r])
+        L.tp_vocab_ce_combine(rows, t, stats, tg, loss, lse)
+        for r in range(t):
+            L.tp_vocab_ce_bwd(rows, v, r, shards[r], tg, lse, dl, dlog[r])
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    with L.LaunchTimer(capacity=reps * (2 * t + 1) + 8) as lt:
+        for _ in range(reps):
+            step()
+    torch.cuda.synchronize()
+    alg = {"vocab_ce_local": rows * v * 2 + rows * 4 + rows * 16,
+           "vocab_ce_combine": t * rows * 16 + rows * 4 * 3,
+           "vocab_ce_bwd": rows * v * 2 * 2 + rows * 4 * 3}
+    kern = {}
+    for name, ms in lt.results():
+        kern.setdefault(name, []).append(ms)
+    out = {"workload": "vocab_ce_t8_s2048_b8_v51200", "rows": rows, "vocab": V, "kernels": {}}
+    for name, vv in kern.items():
+        med = 1e3 * float(np.median(vv))
+        out["kernels"][name] = {"launches_per_step": len(vv) // reps, "median_us": round(med, 2),
+                                "bytes_per_launch": alg[name], "gbps": round(alg[name] / (med * 1e-6) / 1e9, 1),
+                                "frac_hbm": round(alg[name] / (med * 1e-6) / PEAK_HBM_BYTES, 4)}
+    del shards, dlog
+    return out
+
+
 def cpu_baseline(w, inp, target_s: float) -> dict:
     """The oracle (fp64 NumPy, as it stands) on one rank's shard fwd + bwd over a sample of R token rows -- the
     same computation as the GPU's per-rank work for a batch of R tokens.  Reported in algorithmic TFLOP/s."""
@@ -495,6 +551,8 @@ def main(argv=None) -> int:
         out["attention_block"] = attention_block_measure(L, max(2, args.steps // 2), 2)
         out["gather_dim0"] = gather_measure(L, 20)
         out["sp_region"] = sp_region_measure(L, 10)
+        out["vocab_ce"] = vocab_ce_measure(L, 10)
+        torch.cuda.empty_cache()
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
