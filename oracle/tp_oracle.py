@@ -280,20 +280,30 @@ def local_head_ids(a: int, t: int, rank: int) -> List[int]:
     return list(range(rank * hl, (rank + 1) * hl))
 
 
-def qkv_shard_columns(a: int, d: int, t: int, rank: int) -> np.ndarray:
-    """Full-QKV column index of every column of rank r's grouped shard: for each local head j in order, the d
-    query columns of head j, then its d key columns, then its d value columns.  Full layout [Wq | Wk | Wv], each
-    a*d wide with head j at columns j*d .. j*d+d-1."""
+def qkv_shard_columns(a: int, d: int, t: int, rank: int, g: Optional[int] = None) -> np.ndarray:
+    """Full-QKV column index of every column of rank r's grouped shard.  Full layout [Wq | Wk | Wv]: a*d query
+    columns (head j at j*d .. j*d+d-1), then g*d key and g*d value columns (KV head, i.e. query group, j likewise).
+    g = None means g = a (multi-head attention).  Query head j belongs to group j // (a/g).  Rank r owns groups
+    r*g/t .. (r+1)*g/t - 1; per local group in order: the d columns of each of its a/g query heads, then its d key
+    columns, then its d value columns -- the interleave [q1 q2 k1 v1 | q3 q4 k2 v2 | ...] of [MEGA]'s QKV remark,
+    which for g = a is [q_j | k_j | v_j] per head."""
+    g = a if g is None else g
+    _need_div(a, g, "a (query heads) by g (KV heads)")
+    _need_div(g, t, "g (KV heads)")
+    G = a // g
+    gl = g // t
     cols = []
-    ad = a * d
-    for j in local_head_ids(a, t, rank):
-        for part in range(3):  # q, k, v
-            base = part * ad + j * d
+    for grp in range(rank * gl, (rank + 1) * gl):
+        for slot in range(G):
+            base = (grp * G + slot) * d
+            cols.extend(range(base, base + d))
+        for base in (a * d + grp * d, a * d + g * d + grp * d):
             cols.extend(range(base, base + d))
     return np.asarray(cols, dtype=np.int64)
 
 
-def shard_weight(kind: int, full: np.ndarray, t: int, rank: int, ffn: int = 0, a: int = 0, d: int = 0):
+def shard_weight(kind: int, full: np.ndarray, t: int, rank: int, ffn: int = 0, a: int = 0, d: int = 0,
+                 g: Optional[int] = None):
     """One rank's shard of a full weight or bias (any dtype; pure index selection)."""
     if kind == W_FC1:
         _need_div(full.shape[1], t, "ffn")
@@ -314,7 +324,7 @@ def shard_weight(kind: int, full: np.ndarray, t: int, rank: int, ffn: int = 0, a
         w = full.shape[0] // t
         return full[rank * w:(rank + 1) * w, :].copy()
     if kind in (W_QKV, B_QKV):
-        return np.take(full, qkv_shard_columns(a, d, t, rank), axis=-1).copy()
+        return np.take(full, qkv_shard_columns(a, d, t, rank, g), axis=-1).copy()
     if kind == W_PROJ:
         hl = len(local_head_ids(a, t, rank))
         return full[rank * hl * d:(rank + 1) * hl * d, :].copy()
@@ -484,11 +494,27 @@ def attention_core(Q: np.ndarray, K: np.ndarray, V: np.ndarray, causal: bool = T
     return O, lse
 
 
+def _kv_cols(a: int, d: int, g: int, j: int):
+    """Key and value column ranges of query head j in the full [Wq | Wk | Wv] layout (group j // (a/g))."""
+    grp = j // (a // g)
+    return slice(a * d + grp * d, a * d + (grp + 1) * d), slice(a * d + (g + grp) * d, a * d + (g + grp + 1) * d)
+
+
+def _local_cols(G: int, d: int, jj: int):
+    """Query, key and value column ranges of local query head jj in a grouped shard ([MEGA] interleave)."""
+    base = (jj // G) * (G + 2) * d
+    q0 = base + (jj % G) * d
+    return slice(q0, q0 + d), slice(base + G * d, base + (G + 1) * d), slice(base + (G + 1) * d, base + (G + 2) * d)
+
+
 def attention_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: int, b: int, a: int, d: int,
                       causal: bool = True, bqkv: Optional[np.ndarray] = None,
-                      c_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """Unsharded attention block.  X [M = s*b, h] rows s-major; Wqkv [h, 3ad] = [Wq|Wk|Wv]; Wo [ad, h].
-    Returns QKV [M, 3ad], O [M, ad] (head j at columns j*d..), lse [b, a, s], Z = O Wo + c."""
+                      c_bias: Optional[np.ndarray] = None, g: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Unsharded attention block.  X [M = s*b, h] rows s-major; Wqkv [h, (a + 2g)d] = [Wq|Wk|Wv] (g KV heads,
+    g = None for g = a); Wo [ad, h].  Query head j attends with key / value head j // (a/g) (grouped-query
+    attention; [MEGA] QKV remark).  Returns QKV, O [M, ad] (head j at columns j*d..), lse [b, a, s],
+    Z = O Wo + c."""
+    g = a if g is None else g
     QKV = X @ Wqkv
     if bqkv is not None:
         QKV = QKV + bqkv
@@ -498,9 +524,10 @@ def attention_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: int, b
     for bi in range(b):
         rows = np.arange(s) * b + bi
         for j in range(a):
+            ck, cv = _kv_cols(a, d, g, j)
             q = QKV[rows, j * d:(j + 1) * d]
-            k = QKV[rows, ad + j * d:ad + (j + 1) * d]
-            v = QKV[rows, 2 * ad + j * d:2 * ad + (j + 1) * d]
+            k = QKV[rows, ck]
+            v = QKV[rows, cv]
             o, l = attention_core(q, k, v, causal)
             O[rows, j * d:(j + 1) * d] = o
             lse[bi, j, :] = l
@@ -512,10 +539,13 @@ def attention_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: int, b
 
 def attention_shard_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: int, b: int, a: int, d: int,
                             t: int, rank: int, causal: bool = True,
-                            bqkv: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """Rank r's part: QKV_i in grouped [q_j k_j v_j] column order for its local heads, O_i = those heads' outputs
-    (head-major), lse_i [b, a/t, s], and the partial Z_i = O_i Wo[rows of its heads] (no row bias)."""
-    cols = qkv_shard_columns(a, d, t, rank)
+                            bqkv: Optional[np.ndarray] = None, g: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Rank r's part: QKV_i in the grouped column order of qkv_shard_columns for its local groups, O_i = its query
+    heads' outputs (head-major), lse_i [b, a/t, s], and the partial Z_i = O_i Wo[rows of its heads] (no row
+    bias)."""
+    g = a if g is None else g
+    G = a // g
+    cols = qkv_shard_columns(a, d, t, rank, g)
     QKVi = X @ Wqkv[:, cols]
     if bqkv is not None:
         QKVi = QKVi + bqkv[cols]
@@ -526,9 +556,8 @@ def attention_shard_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: 
     for bi in range(b):
         rows = np.arange(s) * b + bi
         for jj in range(hl):
-            base = jj * 3 * d
-            o, l = attention_core(QKVi[rows, base:base + d], QKVi[rows, base + d:base + 2 * d],
-                                  QKVi[rows, base + 2 * d:base + 3 * d], causal)
+            cq, ck, cv = _local_cols(G, d, jj)
+            o, l = attention_core(QKVi[rows, cq], QKVi[rows, ck], QKVi[rows, cv], causal)
             Oi[rows, jj * d:(jj + 1) * d] = o
             lsei[bi, jj, :] = l
     Zi = Oi @ Wo[rank * hl * d:(rank + 1) * hl * d, :]
@@ -536,9 +565,10 @@ def attention_shard_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: 
 
 
 def attention_rows(QKV_i: np.ndarray, s: int, b: int, hl: int, d: int, q_rows: Sequence[int],
-                   causal: bool = True) -> Dict[str, np.ndarray]:
-    """Attention outputs for selected token rows only (row index = s_idx*b + b_idx), from a rank's grouped QKV_i.
-    Each output row needs just its own query and the keys/values of its sequence, so sampling rows is exact."""
+                   causal: bool = True, G: int = 1) -> Dict[str, np.ndarray]:
+    """Attention outputs for selected token rows only (row index = s_idx*b + b_idx), from a rank's grouped QKV_i
+    (G query heads per KV head).  Each output row needs just its own query and the keys/values of its sequence,
+    so sampling rows is exact."""
     q_rows = np.asarray(q_rows, dtype=np.int64)
     O = np.zeros((len(q_rows), hl * d))
     lse = np.zeros((len(q_rows), hl))
@@ -547,10 +577,10 @@ def attention_rows(QKV_i: np.ndarray, s: int, b: int, hl: int, d: int, q_rows: S
         nk = si + 1 if causal else s
         krows = np.arange(nk) * b + bi
         for jj in range(hl):
-            base = jj * 3 * d
-            q = QKV_i[r, base:base + d]
-            k = QKV_i[krows, base + d:base + 2 * d]
-            v = QKV_i[krows, base + 2 * d:base + 3 * d]
+            cq, ck, cv = _local_cols(G, d, jj)
+            q = QKV_i[r, cq]
+            k = QKV_i[krows, ck]
+            v = QKV_i[krows, cv]
             sc = (k @ q) / math.sqrt(d)
             m = sc.max()
             e = np.exp(sc - m)
@@ -579,49 +609,54 @@ def attention_core_backward(Q: np.ndarray, K: np.ndarray, V: np.ndarray, dO: np.
 
 
 def attention_backward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, dZ: np.ndarray, s: int, b: int, a: int,
-                       d: int, causal: bool = True, bqkv: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                       d: int, causal: bool = True, bqkv: Optional[np.ndarray] = None,
+                       g: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Gradients of the unsharded attention block Z = O Wo + c for the upstream dZ [M, h]: dO = dZ Wo^T,
-    dWo = O^T dZ, dc = column sums of dZ; per (sequence, head) the core gradients into dQKV [M, 3ad] ([Wq|Wk|Wv]
-    column order); dWqkv = X^T dQKV, dbqkv = column sums of dQKV, dX = dQKV Wqkv^T."""
-    fw = attention_forward(X, Wqkv, Wo, s, b, a, d, causal, bqkv)
+    dWo = O^T dZ, dc = column sums of dZ; per (sequence, query head) the core gradients into dQKV ([Wq|Wk|Wv]
+    column order), a KV head's dK and dV summing over the query heads of its group; dWqkv = X^T dQKV,
+    dbqkv = column sums of dQKV, dX = dQKV Wqkv^T."""
+    g = a if g is None else g
+    fw = attention_forward(X, Wqkv, Wo, s, b, a, d, causal, bqkv, g=g)
     QKV, O = fw["QKV"], fw["O"]
-    ad = a * d
     dO = dZ @ Wo.T
     dQKV = np.zeros_like(QKV)
     for bi in range(b):
         rows = np.arange(s) * b + bi
         for j in range(a):
-            cq, ck, cv = (slice(j * d, (j + 1) * d), slice(ad + j * d, ad + (j + 1) * d),
-                          slice(2 * ad + j * d, 2 * ad + (j + 1) * d))
+            cq = slice(j * d, (j + 1) * d)
+            ck, cv = _kv_cols(a, d, g, j)
             gq, gk, gv = attention_core_backward(QKV[rows, cq], QKV[rows, ck], QKV[rows, cv], dO[rows, cq], causal)
-            dQKV[rows, cq], dQKV[rows, ck], dQKV[rows, cv] = gq, gk, gv
+            dQKV[rows, cq] = gq
+            dQKV[rows, ck] += gk
+            dQKV[rows, cv] += gv
     return {"dO": dO, "dWo": O.T @ dZ, "dc": dZ.sum(axis=0), "dQKV": dQKV, "dWqkv": X.T @ dQKV,
             "dbqkv": dQKV.sum(axis=0), "dX": dQKV @ Wqkv.T, "O": O, "QKV": QKV, "lse": fw["lse"]}
 
 
 def attention_shard_backward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, dZ: np.ndarray, s: int, b: int,
                              a: int, d: int, t: int, rank: int, causal: bool = True,
-                             bqkv: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                             bqkv: Optional[np.ndarray] = None, g: Optional[int] = None) -> Dict[str, np.ndarray]:
     """Rank r's part of the attention backward: its heads' dO_i = dZ Wo_i^T (Wo_i = the rows of its heads), the
     weight gradients dWo_i = O_i^T dZ, dQKV_i in the grouped [q_j k_j v_j] order, dWqkv_i = X^T dQKV_i,
     dbqkv_i, and the partial dX_i = dQKV_i Wqkv_i^T (the f reduction sums these over ranks)."""
-    fw = attention_shard_forward(X, Wqkv, Wo, s, b, a, d, t, rank, causal, bqkv)
+    g = a if g is None else g
+    G = a // g
+    fw = attention_shard_forward(X, Wqkv, Wo, s, b, a, d, t, rank, causal, bqkv, g=g)
     QKVi, Oi = fw["QKV"], fw["O"]
     hl = a // t
     Wo_i = Wo[rank * hl * d:(rank + 1) * hl * d, :]
-    Wqkv_i = Wqkv[:, qkv_shard_columns(a, d, t, rank)]
+    Wqkv_i = Wqkv[:, qkv_shard_columns(a, d, t, rank, g)]
     dOi = dZ @ Wo_i.T
     dQKVi = np.zeros_like(QKVi)
     for bi in range(b):
         rows = np.arange(s) * b + bi
         for jj in range(hl):
-            base = jj * 3 * d
-            gq, gk, gv = attention_core_backward(QKVi[rows, base:base + d], QKVi[rows, base + d:base + 2 * d],
-                                                 QKVi[rows, base + 2 * d:base + 3 * d],
+            cq, ck, cv = _local_cols(G, d, jj)
+            gq, gk, gv = attention_core_backward(QKVi[rows, cq], QKVi[rows, ck], QKVi[rows, cv],
                                                  dOi[rows, jj * d:(jj + 1) * d], causal)
-            dQKVi[rows, base:base + d] = gq
-            dQKVi[rows, base + d:base + 2 * d] = gk
-            dQKVi[rows, base + 2 * d:base + 3 * d] = gv
+            dQKVi[rows, cq] = gq
+            dQKVi[rows, ck] += gk
+            dQKVi[rows, cv] += gv
     return {"dO": dOi, "dWo": Oi.T @ dZ, "dQKV": dQKVi, "dWqkv": X.T @ dQKVi, "dbqkv": dQKVi.sum(axis=0),
             "dX": dQKVi @ Wqkv_i.T, "O": Oi, "QKV": QKVi, "lse": fw["lse"]}
 
