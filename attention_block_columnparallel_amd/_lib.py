@@ -40,11 +40,12 @@ class TpError(RuntimeError):
 
 
 class tp_dims(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_int64) for n in ("s", "b", "h", "ffn", "a", "d", "t")]
+    _fields_ = [(n, ctypes.c_int64) for n in ("s", "b", "h", "ffn", "a", "d", "t", "g")]
 
 
-def make_dims(s=0, b=0, h=0, ffn=0, a=0, d=0, t=1) -> tp_dims:
-    return tp_dims(int(s), int(b), int(h), int(ffn), int(a), int(d), int(t))
+def make_dims(s=0, b=0, h=0, ffn=0, a=0, d=0, t=1, g=0) -> tp_dims:
+    """g: KV heads (query groups) of grouped-query attention; 0 = a (multi-head)."""
+    return tp_dims(int(s), int(b), int(h), int(ffn), int(a), int(d), int(t), int(g))
 
 
 def _load() -> ctypes.CDLL:

@@ -178,26 +178,29 @@ class AttnBlock:
 
     def __init__(self, s: int, b: int, h: int, a: int, d: int, t: int, Wqkv_full: torch.Tensor,
                  Wo_full: torch.Tensor, bqkv_full: Optional[torch.Tensor] = None,
-                 c_full: Optional[torch.Tensor] = None, causal: bool = True, stream=None):
+                 c_full: Optional[torch.Tensor] = None, causal: bool = True, stream=None, g: int = 0):
+        """g: KV heads of grouped-query attention (0: g = a); Wqkv_full [h, (a + 2g)d] = [Wq | Wk | Wv]."""
         L = load()
         self.L = L
         self.s, self.b, self.h, self.a, self.d, self.t, self.causal = s, b, h, a, d, t, causal
-        self.dims = L.make_dims(s=s, b=b, h=h, a=a, d=d, t=t)
+        self.g = g or a
+        self.dims = L.make_dims(s=s, b=b, h=h, a=a, d=d, t=t, g=self.g)
         dev, dt = Wqkv_full.device, Wqkv_full.dtype
         hl = a // t
         self.hl = hl
+        self.nqkv = (hl + 2 * (self.g // t)) * d  # a rank's QKV columns
         M = s * b
         self.M = M
-        self.Wqkv = torch.empty((t, h, 3 * hl * d), dtype=dt, device=dev)
+        self.Wqkv = torch.empty((t, h, self.nqkv), dtype=dt, device=dev)
         self.Wo = torch.empty((t, hl * d, h), dtype=dt, device=dev)
-        self.bqkv = torch.empty((t, 3 * hl * d), dtype=dt, device=dev) if bqkv_full is not None else None
+        self.bqkv = torch.empty((t, self.nqkv), dtype=dt, device=dev) if bqkv_full is not None else None
         self.c = c_full
         for r in range(t):
             L.tp_shard_weights(self.dims, r, "qkv", Wqkv_full, self.Wqkv[r], stream)
             L.tp_shard_weights(self.dims, r, "proj", Wo_full, self.Wo[r], stream)
             if bqkv_full is not None:
                 L.tp_shard_weights(self.dims, r, "b_qkv", bqkv_full, self.bqkv[r], stream)
-        self.QKV = torch.empty((t, M, 3 * hl * d), dtype=dt, device=dev)
+        self.QKV = torch.empty((t, M, self.nqkv), dtype=dt, device=dev)
         self.O = torch.empty((t, M, hl * d), dtype=dt, device=dev)
         self.lse = torch.empty((t, b, hl, s), dtype=torch.float32, device=dev)
         self.Zp = torch.empty((t, M, h), dtype=dt, device=dev)
@@ -211,9 +214,9 @@ class AttnBlock:
         nqb = (self.s + 63) // 64
         self.dO = torch.empty((M, hl * d), dtype=dt, device=dev)  # workspace reused by every rank
         self.rec = torch.empty((self.b, hl, nqb, 256), dtype=torch.float32, device=dev)  # workspace
-        self.dQKV = torch.empty((t, M, 3 * hl * d), dtype=dt, device=dev)
-        self.dWqkv = torch.empty((t, h, 3 * hl * d), dtype=dt, device=dev)
-        self.dbqkv = torch.empty((t, 3 * hl * d), dtype=dt, device=dev) if self.bqkv is not None else None
+        self.dQKV = torch.empty((t, M, self.nqkv), dtype=dt, device=dev)
+        self.dWqkv = torch.empty((t, h, self.nqkv), dtype=dt, device=dev)
+        self.dbqkv = torch.empty((t, self.nqkv), dtype=dt, device=dev) if self.bqkv is not None else None
         self.dWo = torch.empty((t, hl * d, h), dtype=dt, device=dev)
         self.dXp = torch.empty((t, M, h), dtype=dt, device=dev)
         self.dX = torch.empty((M, h), dtype=dt, device=dev)

@@ -46,6 +46,24 @@ constexpr int NSTG = 3;
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// Columns of a rank's QKV rows (grouped-query attention, G query heads per KV head; G = 1 is multi-head): per
+// local KV group, the d columns of each of its G query heads, then the group's d key and d value columns (the
+// interleave of the fused QKV weight in the Megatron-LM visual reading).
+struct QkvCols {
+  int64_t ld;  // elements per token row
+  int64_t q;   // first column of query head jj
+  int64_t k;   // first key column of jj's group; its values follow at + d
+};
+__device__ __forceinline__ QkvCols qkv_cols(int hl, int G, int d, int jj) {
+  const int64_t gw = (int64_t)(G + 2) * d;
+  const int jg = jj / G;
+  QkvCols c;
+  c.ld = (int64_t)(hl / G) * gw;
+  c.q = jg * gw + (int64_t)(jj - jg * G) * d;
+  c.k = jg * gw + (int64_t)G * d;
+  return c;
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte address m0 + 16 l.  Inline
 // assembly, so that the compiler does not wait for these copies at every barrier; the kernel waits itself.
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
@@ -92,10 +110,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
   const int bh = (int)blockIdx.x % nbh;
   const int bidx = bh / p.hl, jj = bh % p.hl;
   const int d = p.d;
-  const int64_t ldq = (int64_t)p.hl * 3 * d;  // elements per token row of QKV
-  const int64_t tok_stride = ldq * p.b;        // consecutive sequence positions
-  const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
-  const uint16_t* __restrict__ kbase = qkv + d;  // V follows K at + d
+  const QkvCols cols = qkv_cols(p.hl, p.G, d, jj);
+  const int64_t ldq = cols.ld;           // elements per token row of QKV
+  const int64_t tok_stride = ldq * p.b;  // consecutive sequence positions
+  const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + cols.q;
+  const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + cols.k;  // V: + d
 
   // ---- this lane's query and its fragments (k = d: lane supplies d = 32u + 8g .. +8)
   const int q = qtile * QT + wave * 16 + l16;
@@ -279,24 +298,25 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams p) {
   const int bidx = bh / p.hl, jj = bh % p.hl;
   if (q >= p.s) return;
   const int d = p.d;
-  const int64_t ldq = (int64_t)p.hl * 3 * d;
+  const QkvCols cols = qkv_cols(p.hl, p.G, d, jj);
+  const int64_t ldq = cols.ld;
   const int64_t tok = ldq * p.b;
-  const float* qkv = static_cast<const float*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
-  const float* qv = qkv + (int64_t)q * tok;
+  const float* base = static_cast<const float*>(p.qkv) + (int64_t)bidx * ldq;
+  const float* qv = base + cols.q + (int64_t)q * tok;
   float o[DMAX];
   for (int e = 0; e < d; ++e) o[e] = 0.f;
   float m = -INFINITY, l = 0.f;
   const int nk = p.causal ? q + 1 : p.s;
   for (int k = 0; k < nk; ++k) {
-    const float* kv = qkv + (int64_t)k * tok;
+    const float* kv = base + cols.k + (int64_t)k * tok;  // K at kv, V at kv + d
     float sdot = 0.f;
-    for (int e = 0; e < d; ++e) sdot = fmaf(qv[e], kv[d + e], sdot);
+    for (int e = 0; e < d; ++e) sdot = fmaf(qv[e], kv[e], sdot);
     const float x = sdot * p.scale;
     const float mn = fmaxf(m, x);
     const float corr = expf(m - mn);
     const float pe = expf(x - mn);
     l = l * corr + pe;
-    for (int e = 0; e < d; ++e) o[e] = o[e] * corr + pe * kv[2 * d + e];
+    for (int e = 0; e < d; ++e) o[e] = o[e] * corr + pe * kv[d + e];
     m = mn;
   }
   float* out = static_cast<float*>(p.o) + ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jj * d;
@@ -367,17 +387,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int nqb = (p.s + 63) / 64;
-  const int nbh = p.b * p.hl;
+  const int gl = p.hl / p.G;  // local KV groups: one workgroup per (batch, group, 64-key block)
+  const int nbh = p.b * gl;
   const int ktile = (int)blockIdx.x / nbh;  // key block 0 sees the most queries: issued first
   const int bh = (int)blockIdx.x % nbh;
-  const int bidx = bh / p.hl, jj = bh % p.hl;
+  const int bidx = bh / gl, jg = bh % gl;
   const int d = p.d;
-  const int64_t ldq = (int64_t)p.hl * 3 * d;
+  const QkvCols kc = qkv_cols(p.hl, p.G, d, jg * p.G);
+  const int64_t ldq = kc.ld;
   const int64_t tok_stride = ldq * p.b;
   const int64_t ldo = (int64_t)p.hl * d * p.b;  // dO row stride (consecutive sequence positions)
-  const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
-  const uint16_t* __restrict__ dob = static_cast<const uint16_t*>(p.dout) + (int64_t)bidx * p.hl * d + (int64_t)jj * d;
-  const float* __restrict__ recb = p.rec + (int64_t)bh * nqb * 256;
+  const uint16_t* __restrict__ qkv0 = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq;
+  const uint16_t* __restrict__ kvb = qkv0 + kc.k;  // the group's K, V at + d
+  const uint16_t* __restrict__ dob0 = static_cast<const uint16_t*>(p.dout) + (int64_t)bidx * p.hl * d;
 
   // ---- this lane's key: K and V fragments (k = d: lane supplies d = 32u + 8g .. +8)
   const int key = ktile * 64 + wave * 16 + l16;
@@ -387,14 +409,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
     const int dd = 32 * u + 8 * g;
     uint4 a = make_uint4(0u, 0u, 0u, 0u), b = a;
     if (key < p.s && dd < d) {
-      a = *reinterpret_cast<const uint4*>(qkv + (int64_t)key * tok_stride + d + dd);
-      b = *reinterpret_cast<const uint4*>(qkv + (int64_t)key * tok_stride + 2 * d + dd);
+      a = *reinterpret_cast<const uint4*>(kvb + (int64_t)key * tok_stride + dd);
+      b = *reinterpret_cast<const uint4*>(kvb + (int64_t)key * tok_stride + d + dd);
     }
     kf[u] = __builtin_bit_cast(bf16x8_t, a);
     vf[u] = __builtin_bit_cast(bf16x8_t, b);
   }
   const int qb0 = p.causal ? ktile : 0;
   const int nblk = nqb - qb0;
+  const int ntot = p.G * nblk;  // (query head of the group, query block) steps, head by head
 
   // ---- copies (same chunk rotation as the forward's K / V tiles); wave 0 also copies the block's record
   int crow[CPW], ccol[CPW];
@@ -409,16 +432,21 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
   auto issue_tile = [&](int i, int st) {
-    const int qb = qb0 + min(i, nblk - 1);  // past the last block: a harmless re-copy of it
+    const int ii = min(i, ntot - 1);  // past the last step: a harmless re-copy of it
+    const int hs = ii / nblk, qb = qb0 + (ii - hs * nblk);
+    const int jh = jg * p.G + hs;  // the step's query head
+    const uint16_t* qsrc = qkv0 + qkv_cols(p.hl, p.G, d, jh).q;
+    const uint16_t* dsrc = dob0 + (int64_t)jh * d;
+    const float* rsrc = p.rec + ((int64_t)(bidx * p.hl + jh) * nqb + qb) * 256;
     const uint32_t sb = lds0 + st * STAGE_B;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int row = min(qb * 64 + crow[c], p.s - 1);
       const uint32_t dst = sb + (wave + 4 * c) * 1024;
-      dma16(qkv + (int64_t)row * tok_stride + ccol[c], __builtin_amdgcn_readfirstlane(dst));
-      dma16(dob + (int64_t)row * ldo + ccol[c], __builtin_amdgcn_readfirstlane(dst + TILE_B));
+      dma16(qsrc + (int64_t)row * tok_stride + ccol[c], __builtin_amdgcn_readfirstlane(dst));
+      dma16(dsrc + (int64_t)row * ldo + ccol[c], __builtin_amdgcn_readfirstlane(dst + TILE_B));
     }
-    if (wave == 0) dma16(recb + (int64_t)qb * 256 + 4 * lane, __builtin_amdgcn_readfirstlane(sb + 2 * TILE_B));
+    if (wave == 0) dma16(rsrc + 4 * lane, __builtin_amdgcn_readfirstlane(sb + 2 * TILE_B));
   };
   auto chunk_off = [&](int r, int c) { return r * CH * 16 + ((c + r) % CH) * 16; };
   int roff[4][NDS];  // A fragments of Q / dO rows (queries 16 qs + l16), d = 32u + 8g
@@ -455,12 +483,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   __syncthreads();
 
   int st_cur = 0, st_new = 2;
-  for (int i = 0; i < nblk; ++i) {
+  for (int i = 0; i < ntot; ++i) {
     issue_tile(i + 2, st_new);
     const char* Qt = &lds[st_cur * STAGE_B];
     const char* Dt = Qt + TILE_B;
     const float* R = reinterpret_cast<const float*>(Qt + 2 * TILE_B);
-    const int q0 = (qb0 + i) * 64;
+    const int qbi = qb0 + i % nblk;
+    const int q0 = qbi * 64;
 
     f32x4_t sc[4], dp[4];
 #pragma unroll
@@ -475,7 +504,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
       }
     }
     // P and dS for queries q0 + 16 qs + 4 g + e and this lane's key
-    const bool diag = p.causal && (qb0 + i) == ktile;
+    const bool diag = p.causal && qbi == ktile;
     const bool ragged = q0 + 64 > p.s;
     // P goes to the matrix cores as a bf16 pair hi + lo (lo = P - hi rounded again): with near-uniform weights
     // a single bf16 P carries 2^-9 relative error into every term of dV's sum over queries
@@ -541,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   wait_vmcnt<0>();
 
   if (key < p.s) {
-    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + ((int64_t)key * p.b + bidx) * ldq + (int64_t)jj * 3 * d;
+    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + ((int64_t)key * p.b + bidx) * ldq + kc.k;  // dK; dV at + d
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       const int dd = st * 16 + 4 * g;
@@ -549,10 +578,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
         uint2 w;
         w.x = f32_to_bf16_hw(dk[st][0] * p.scale) | (f32_to_bf16_hw(dk[st][1] * p.scale) << 16);
         w.y = f32_to_bf16_hw(dk[st][2] * p.scale) | (f32_to_bf16_hw(dk[st][3] * p.scale) << 16);
-        *reinterpret_cast<uint2*>(out + d + dd) = w;
+        *reinterpret_cast<uint2*>(out + dd) = w;
         w.x = f32_to_bf16_hw(dv[st][0]) | (f32_to_bf16_hw(dv[st][1]) << 16);
         w.y = f32_to_bf16_hw(dv[st][2]) | (f32_to_bf16_hw(dv[st][3]) << 16);
-        *reinterpret_cast<uint2*>(out + 2 * d + dd) = w;
+        *reinterpret_cast<uint2*>(out + d + dd) = w;
       }
     }
   }
@@ -578,10 +607,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
   const int bh = (int)blockIdx.x % nbh;
   const int bidx = bh / p.hl, jj = bh % p.hl;
   const int d = p.d;
-  const int64_t ldq = (int64_t)p.hl * 3 * d;
+  const QkvCols cols = qkv_cols(p.hl, p.G, d, jj);
+  const int64_t ldq = cols.ld;
   const int64_t tok_stride = ldq * p.b;
-  const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
-  const uint16_t* __restrict__ kbase = qkv + d;
+  const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + cols.q;
+  const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + cols.k;
 
   // ---- this lane's query: Q and dO fragments, lse (log2 units) and D
   const int q = qtile * QT + wave * 16 + l16;
@@ -730,7 +760,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
     return;
   }
   if (q < p.s) {
-    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + ((int64_t)q * p.b + bidx) * ldq + (int64_t)jj * 3 * d;
+    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + ((int64_t)q * p.b + bidx) * ldq + cols.q;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       const int dd = st * 16 + 4 * g;
@@ -752,9 +782,10 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(AttnBwdParams p) {
   const int bidx = bh / p.hl, jj = bh % p.hl;
   if (q >= p.s) return;
   const int d = p.d;
-  const int64_t ldq = (int64_t)p.hl * 3 * d, tok = ldq * p.b;
-  const float* qkv = static_cast<const float*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
-  const float* qv = qkv + (int64_t)q * tok;
+  const QkvCols cols = qkv_cols(p.hl, p.G, d, jj);
+  const int64_t ldq = cols.ld, tok = ldq * p.b;
+  const float* base = static_cast<const float*>(p.qkv) + (int64_t)bidx * ldq;
+  const float* qv = base + cols.q + (int64_t)q * tok;
   const float* dov = static_cast<const float*>(p.dout) + ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jj * d;
   const float lse = p.lse[(int64_t)bh * p.s + q];
   const float D = p.rec[((int64_t)bh * ((p.s + 63) / 64) + q / 64) * 256 + 64 + (q % 64)];
@@ -762,53 +793,60 @@ __global__ __launch_bounds__(64) void attn_bwd_dq_f32_kernel(AttnBwdParams p) {
   for (int e = 0; e < d; ++e) acc[e] = 0.f;
   const int nk = p.causal ? q + 1 : p.s;
   for (int k = 0; k < nk; ++k) {
-    const float* kv = qkv + (int64_t)k * tok;
+    const float* kv = base + cols.k + (int64_t)k * tok;  // K at kv, V at kv + d
     float sdot = 0.f, dpv = 0.f;
     for (int e = 0; e < d; ++e) {
-      sdot = fmaf(qv[e], kv[d + e], sdot);
-      dpv = fmaf(dov[e], kv[2 * d + e], dpv);
+      sdot = fmaf(qv[e], kv[e], sdot);
+      dpv = fmaf(dov[e], kv[d + e], dpv);
     }
     const float ds = expf(sdot * p.scale - lse) * (dpv - D);
-    for (int e = 0; e < d; ++e) acc[e] = fmaf(ds, kv[d + e], acc[e]);
+    for (int e = 0; e < d; ++e) acc[e] = fmaf(ds, kv[e], acc[e]);
   }
-  float* out = static_cast<float*>(p.dqkv) + ((int64_t)q * p.b + bidx) * ldq + (int64_t)jj * 3 * d;
+  float* out = static_cast<float*>(p.dqkv) + ((int64_t)q * p.b + bidx) * ldq + cols.q;
   for (int e = 0; e < d; ++e) out[e] = acc[e] * p.scale;
 }
 
 __global__ __launch_bounds__(64) void attn_bwd_dkv_f32_kernel(AttnBwdParams p) {
   constexpr int DMAX = 128;
   const int k = blockIdx.x * 64 + threadIdx.x;
+  const int gl = p.hl / p.G;  // one thread per (key, batch, local KV group); the group's query heads summed
   const int bh = blockIdx.y;
-  const int bidx = bh / p.hl, jj = bh % p.hl;
+  const int bidx = bh / gl, jg = bh % gl;
   if (k >= p.s) return;
   const int d = p.d;
-  const int64_t ldq = (int64_t)p.hl * 3 * d, tok = ldq * p.b;
-  const float* qkv = static_cast<const float*>(p.qkv) + (int64_t)bidx * ldq + (int64_t)jj * 3 * d;
-  const float* kv = qkv + (int64_t)k * tok;
+  const QkvCols kc = qkv_cols(p.hl, p.G, d, jg * p.G);
+  const int64_t ldq = kc.ld, tok = ldq * p.b;
+  const float* base = static_cast<const float*>(p.qkv) + (int64_t)bidx * ldq;
+  const float* kv = base + kc.k + (int64_t)k * tok;  // K at kv, V at kv + d
   const int nqb = (p.s + 63) / 64;
   float dk[DMAX], dv[DMAX];
   for (int e = 0; e < d; ++e) dk[e] = dv[e] = 0.f;
-  for (int q = p.causal ? k : 0; q < p.s; ++q) {
-    const float* qv = qkv + (int64_t)q * tok;
-    const float* dov = static_cast<const float*>(p.dout) + ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jj * d;
-    const float lse = p.lse[(int64_t)bh * p.s + q];
-    const float D = p.rec[((int64_t)bh * nqb + q / 64) * 256 + 64 + (q % 64)];
-    float sdot = 0.f, dpv = 0.f;
-    for (int e = 0; e < d; ++e) {
-      sdot = fmaf(qv[e], kv[d + e], sdot);
-      dpv = fmaf(dov[e], kv[2 * d + e], dpv);
-    }
-    const float pe = expf(sdot * p.scale - lse);
-    const float ds = pe * (dpv - D);
-    for (int e = 0; e < d; ++e) {
-      dv[e] = fmaf(pe, dov[e], dv[e]);
-      dk[e] = fmaf(ds, qv[e], dk[e]);
+  for (int hs = 0; hs < p.G; ++hs) {
+    const int jh = jg * p.G + hs;
+    const int64_t qcol = qkv_cols(p.hl, p.G, d, jh).q;
+    const int64_t hrow = (int64_t)bidx * p.hl + jh;
+    for (int q = p.causal ? k : 0; q < p.s; ++q) {
+      const float* qv = base + qcol + (int64_t)q * tok;
+      const float* dov = static_cast<const float*>(p.dout) + ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jh * d;
+      const float lse = p.lse[hrow * p.s + q];
+      const float D = p.rec[(hrow * nqb + q / 64) * 256 + 64 + (q % 64)];
+      float sdot = 0.f, dpv = 0.f;
+      for (int e = 0; e < d; ++e) {
+        sdot = fmaf(qv[e], kv[e], sdot);
+        dpv = fmaf(dov[e], kv[d + e], dpv);
+      }
+      const float pe = expf(sdot * p.scale - lse);
+      const float ds = pe * (dpv - D);
+      for (int e = 0; e < d; ++e) {
+        dv[e] = fmaf(pe, dov[e], dv[e]);
+        dk[e] = fmaf(ds, qv[e], dk[e]);
+      }
     }
   }
-  float* out = static_cast<float*>(p.dqkv) + ((int64_t)k * p.b + bidx) * ldq + (int64_t)jj * 3 * d;
+  float* out = static_cast<float*>(p.dqkv) + ((int64_t)k * p.b + bidx) * ldq + kc.k;
   for (int e = 0; e < d; ++e) {
-    out[d + e] = dk[e] * p.scale;
-    out[2 * d + e] = dv[e];
+    out[e] = dk[e] * p.scale;
+    out[d + e] = dv[e];
   }
 }
 
@@ -819,8 +857,9 @@ hipError_t launch_bwd_bf16(const AttnBwdParams& p, hipStream_t st) {
   static const std::string n0 = "attn_bwd_delta_bf16_d" + std::to_string(DP);
   static const std::string n1 = "attn_bwd_dkv_bf16_d" + std::to_string(DP);
   static const std::string n2 = "attn_bwd_dq_bf16_d" + std::to_string(DP);
+  const unsigned grid_kv = (unsigned)(nq * p.b * (p.hl / p.G));  // one workgroup per (64 keys, batch, KV group)
   hipError_t e = TP_LAUNCH(n0.c_str(), (attn_bwd_dq_bf16_kernel<DP, true>), dim3(grid), dim3(256), 0, st, p);
-  if (e == hipSuccess) e = TP_LAUNCH(n1.c_str(), (attn_bwd_dkv_bf16_kernel<DP>), dim3(grid), dim3(256), 0, st, p);
+  if (e == hipSuccess) e = TP_LAUNCH(n1.c_str(), (attn_bwd_dkv_bf16_kernel<DP>), dim3(grid_kv), dim3(256), 0, st, p);
   if (e == hipSuccess) e = TP_LAUNCH(n2.c_str(), (attn_bwd_dq_bf16_kernel<DP, false>), dim3(grid), dim3(256), 0, st, p);
   return e;
 }
@@ -859,7 +898,8 @@ hipError_t attention_bwd(tp_dtype dt, const AttnBwdParams& p, hipStream_t st) {
                 p);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((p.s + 63) / 64), (unsigned)(p.b * p.hl));
-  e = TP_LAUNCH("attn_bwd_dkv_f32", attn_bwd_dkv_f32_kernel, grid, dim3(64), 0, st, p);
+  const dim3 grid_kv((unsigned)((p.s + 63) / 64), (unsigned)(p.b * (p.hl / p.G)));
+  e = TP_LAUNCH("attn_bwd_dkv_f32", attn_bwd_dkv_f32_kernel, grid_kv, dim3(64), 0, st, p);
   if (e == hipSuccess) e = TP_LAUNCH("attn_bwd_dq_f32", attn_bwd_dq_f32_kernel, grid, dim3(64), 0, st, p);
   return e;
 }

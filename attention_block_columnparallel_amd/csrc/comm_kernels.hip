@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void copy1(const uint8_t* __restrict__ src, ui
 // Megatron-LM visual reading: fc1 split by output column, SwiGLU keeps gate and up columns of the same range,
 // QKV split by head with each local head's q, k, v columns kept together).
 __device__ __forceinline__ int64_t shard_src_col(int kind, int64_t c, int64_t f_l, int64_t ffn, int64_t rank,
-                                                 int64_t hl, int64_t d, int64_t ad) {
+                                                 int64_t hl, int64_t d, int64_t ad, int64_t G, int64_t gd) {
   switch (kind) {
     case TP_W_FC1:
     case TP_B_FC1:
@@ -202,10 +202,13 @@ __device__ __forceinline__ int64_t shard_src_col(int kind, int64_t c, int64_t f_
     case TP_W_FC1_GATE_UP:
     case TP_B_FC1_GATE_UP:
       return c < f_l ? rank * f_l + c : ffn + rank * f_l + (c - f_l);
-    default: {  // TP_W_QKV, TP_B_QKV
-      const int64_t jj = c / (3 * d), rem = c % (3 * d);
-      const int64_t part = rem / d, e = rem % d;
-      return part * ad + (rank * hl + jj) * d + e;
+    default: {  // TP_W_QKV, TP_B_QKV: per local KV group [its G query heads | k | v]; full [Wq | Wk | Wv]
+      const int64_t gw = (G + 2) * d;
+      const int64_t jg = c / gw, rem = c % gw;
+      const int64_t slot = rem / d, e = rem % d;
+      const int64_t grp = rank * (hl / G) + jg;
+      if (slot < G) return (grp * G + slot) * d + e;
+      return ad + (slot == G ? 0 : gd) + grp * d + e;
     }
   }
 }
@@ -216,12 +219,12 @@ template <typename V, int VEC, int ESZ>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ full, int64_t rows, int64_t full_cols,
                                                    uint8_t* __restrict__ shard, int64_t shard_cols, int kind,
                                                    int64_t f_l, int64_t ffn, int64_t rank, int64_t hl, int64_t d,
-                                                   int64_t ad) {
+                                                   int64_t ad, int64_t G, int64_t gd) {
   const int64_t groups = shard_cols / VEC;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (g >= rows * groups) return;
   const int64_t row = g / groups, c = (g % groups) * VEC;
-  const int64_t sc = shard_src_col(kind, c, f_l, ffn, rank, hl, d, ad);
+  const int64_t sc = shard_src_col(kind, c, f_l, ffn, rank, hl, d, ad, G, gd);
   const V* src = reinterpret_cast<const V*>(full + (row * full_cols + sc) * ESZ);
   V* dst = reinterpret_cast<V*>(shard + (row * shard_cols + c) * ESZ);
   *dst = *src;
@@ -326,7 +329,7 @@ hipError_t copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t st)
 
 hipError_t pack_columns(tp_dtype dt, const void* full, int64_t rows, int64_t full_cols, void* shard,
                         int64_t shard_cols, int kind, int64_t f_l, int64_t ffn, int64_t rank, int64_t hl, int64_t d,
-                        int64_t ad, hipStream_t st) {
+                        int64_t ad, int64_t G, int64_t gd, hipStream_t st) {
   const int esz = dt == TP_BF16 ? 2 : 4;
   // segment widths: f_l (FC kinds) or d (QKV kinds)
   const int64_t seg = (kind == TP_W_QKV || kind == TP_B_QKV) ? d : f_l;
@@ -340,17 +343,17 @@ hipError_t pack_columns(tp_dtype dt, const void* full, int64_t rows, int64_t ful
     const unsigned blocks = (unsigned)((n + 255) / 256);
     if (esz == 2)
       return TP_LAUNCH("pack_vec_bf16", (pack_kernel<uint4, 8, 2>), dim3(blocks), dim3(256), 0, st, F, rows, full_cols,
-                       S, shard_cols, kind, f_l, ffn, rank, hl, d, ad);
+                       S, shard_cols, kind, f_l, ffn, rank, hl, d, ad, G, gd);
     return TP_LAUNCH("pack_vec_f32", (pack_kernel<uint4, 4, 4>), dim3(blocks), dim3(256), 0, st, F, rows, full_cols, S,
-                     shard_cols, kind, f_l, ffn, rank, hl, d, ad);
+                     shard_cols, kind, f_l, ffn, rank, hl, d, ad, G, gd);
   } else {
     const int64_t n = rows * shard_cols;
     const unsigned blocks = (unsigned)((n + 255) / 256);
     if (esz == 2)
       return TP_LAUNCH("pack_elem_bf16", (pack_kernel<uint16_t, 1, 2>), dim3(blocks), dim3(256), 0, st, F, rows,
-                       full_cols, S, shard_cols, kind, f_l, ffn, rank, hl, d, ad);
+                       full_cols, S, shard_cols, kind, f_l, ffn, rank, hl, d, ad, G, gd);
     return TP_LAUNCH("pack_elem_f32", (pack_kernel<uint32_t, 1, 4>), dim3(blocks), dim3(256), 0, st, F, rows,
-                     full_cols, S, shard_cols, kind, f_l, ffn, rank, hl, d, ad);
+                     full_cols, S, shard_cols, kind, f_l, ffn, rank, hl, d, ad, G, gd);
   }
 }
 

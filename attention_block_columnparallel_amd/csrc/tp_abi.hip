@@ -146,28 +146,30 @@ int tp_shard_weights(const tp_dims* dims, int rank, tp_wkind kind, tp_dtype dtyp
                      hipStream_t stream) {
   if (dims == nullptr || full == nullptr || shard == nullptr) return TP_E_NULL;
   const int64_t h = dims->h, t = dims->t, ffn = dims->ffn, a = dims->a, d = dims->d;
+  const int64_t g = dims->g == 0 ? a : dims->g;  // KV heads (0: as many as query heads)
   const bool mlp = kind == TP_W_FC1 || kind == TP_W_FC1_GATE_UP || kind == TP_W_FC2 || kind == TP_B_FC1 ||
                    kind == TP_B_FC1_GATE_UP;
   const bool att = kind == TP_W_QKV || kind == TP_W_PROJ || kind == TP_B_QKV;
   if (!mlp && !att) return TP_E_UNSUPPORTED;
-  if (t <= 0 || h <= 0 || (mlp && ffn <= 0) || (att && (a <= 0 || d <= 0))) return TP_E_SHAPE;
+  if (t <= 0 || h <= 0 || (mlp && ffn <= 0) || (att && (a <= 0 || d <= 0 || g <= 0))) return TP_E_SHAPE;
   if (h >= kMaxDim || ffn >= kMaxDim) return TP_E_SHAPE;
   if (mlp && ffn % t != 0) return TP_E_DIVISIBILITY;
-  if (att && (a % t != 0 || h != a * d)) return TP_E_DIVISIBILITY;
+  if (att && (a % t != 0 || h != a * d || a % g != 0 || g % t != 0)) return TP_E_DIVISIBILITY;
   if (rank < 0 || rank >= t) return TP_E_RANK;
   if (bad_dtype(dtype)) return TP_E_DTYPE;
   const int64_t es = esize(dtype);
   const int64_t f_l = mlp ? ffn / t : 0, hl = att ? a / t : 0, ad = a * d;
+  const int64_t gl = att ? g / t : 0, G = att ? a / g : 1;  // local KV groups, query heads per group
   int64_t rows = 0, full_cols = 0, shard_cols = 0;
   switch (kind) {
     case TP_W_FC1: rows = h; full_cols = ffn; shard_cols = f_l; break;
     case TP_W_FC1_GATE_UP: rows = h; full_cols = 2 * ffn; shard_cols = 2 * f_l; break;
     case TP_W_FC2: rows = ffn; full_cols = h; shard_cols = h; break;
-    case TP_W_QKV: rows = h; full_cols = 3 * ad; shard_cols = 3 * hl * d; break;
+    case TP_W_QKV: rows = h; full_cols = ad + 2 * g * d; shard_cols = (hl + 2 * gl) * d; break;
     case TP_W_PROJ: rows = ad; full_cols = h; shard_cols = h; break;
     case TP_B_FC1: rows = 1; full_cols = ffn; shard_cols = f_l; break;
     case TP_B_FC1_GATE_UP: rows = 1; full_cols = 2 * ffn; shard_cols = 2 * f_l; break;
-    case TP_B_QKV: rows = 1; full_cols = 3 * ad; shard_cols = 3 * hl * d; break;
+    case TP_B_QKV: rows = 1; full_cols = ad + 2 * g * d; shard_cols = (hl + 2 * gl) * d; break;
   }
   const Buf out[] = {{shard, (kind == TP_W_FC2 ? f_l : kind == TP_W_PROJ ? hl * d : rows) * shard_cols * es}};
   const Buf in[] = {{full, rows * full_cols * es}};
@@ -179,7 +181,7 @@ int tp_shard_weights(const tp_dims* dims, int rank, tp_wkind kind, tp_dtype dtyp
     return hip_status(tp::copy_bytes(src, shard, rl * h * es, stream));
   }
   return hip_status(tp::pack_columns(dtype, full, rows, full_cols, shard, shard_cols, (int)kind, f_l, ffn, rank, hl,
-                                     d, ad, stream));
+                                     d, ad, G, g * d, stream));
 }
 
 int tp_mlp_fwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const void* X, const void* A_i,
@@ -328,13 +330,14 @@ int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
       O_i == nullptr || Z_i == nullptr)
     return TP_E_NULL;
   const int64_t s = dims->s, b = dims->b, h = dims->h, a = dims->a, d = dims->d, t = dims->t;
-  if (s <= 0 || b <= 0 || h <= 0 || a <= 0 || d <= 0 || t <= 0) return TP_E_SHAPE;
+  const int64_t g = dims->g == 0 ? a : dims->g;  // KV heads (0: as many as query heads)
+  if (s <= 0 || b <= 0 || h <= 0 || a <= 0 || d <= 0 || t <= 0 || g <= 0) return TP_E_SHAPE;
   if (s * b >= kMaxDim || h >= kMaxDim) return TP_E_SHAPE;
-  if (a % t != 0 || h != a * d) return TP_E_DIVISIBILITY;
+  if (a % t != 0 || h != a * d || a % g != 0 || g % t != 0) return TP_E_DIVISIBILITY;
   if (rank < 0 || rank >= t) return TP_E_RANK;
   if (bad_dtype(dtype)) return TP_E_DTYPE;
   if (d > 128) return TP_E_UNSUPPORTED;
-  const int64_t M = s * b, hl = a / t, n = 3 * hl * d, es = esize(dtype);
+  const int64_t M = s * b, hl = a / t, n = (hl + 2 * (g / t)) * d, es = esize(dtype);
   if (dtype == TP_BF16 && (h % 8 != 0 || d % 8 != 0 || misaligned16({X, Wqkv_i, bqkv_i, Wo_i, QKV_i, O_i, Z_i})))
     return TP_E_UNSUPPORTED;
   const Buf outs[] = {{QKV_i, M * n * es}, {O_i, M * hl * d * es}, {lse_i, b * hl * s * 4}, {Z_i, M * h * es}};
@@ -349,7 +352,7 @@ int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
   gq.bias = bqkv_i;
   tp::AttnParams ap = {};
   ap.qkv = QKV_i; ap.o = O_i; ap.lse = lse_i;
-  ap.s = (int)s; ap.b = (int)b; ap.hl = (int)hl; ap.d = (int)d;
+  ap.s = (int)s; ap.b = (int)b; ap.hl = (int)hl; ap.d = (int)d; ap.G = (int)(a / g);
   ap.causal = causal ? 1 : 0;
   ap.scale = (float)(1.0 / __builtin_sqrt((double)d));
   tp::GemmParams go = {};
@@ -379,13 +382,14 @@ int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
       dQKV_i == nullptr || dWqkv_i == nullptr || dWo_i == nullptr || dX_i == nullptr)
     return TP_E_NULL;
   const int64_t s = dims->s, b = dims->b, h = dims->h, a = dims->a, d = dims->d, t = dims->t;
-  if (s <= 0 || b <= 0 || h <= 0 || a <= 0 || d <= 0 || t <= 0) return TP_E_SHAPE;
+  const int64_t g = dims->g == 0 ? a : dims->g;  // KV heads (0: as many as query heads)
+  if (s <= 0 || b <= 0 || h <= 0 || a <= 0 || d <= 0 || t <= 0 || g <= 0) return TP_E_SHAPE;
   if (s * b >= kMaxDim || h >= kMaxDim) return TP_E_SHAPE;
-  if (a % t != 0 || h != a * d) return TP_E_DIVISIBILITY;
+  if (a % t != 0 || h != a * d || a % g != 0 || g % t != 0) return TP_E_DIVISIBILITY;
   if (rank < 0 || rank >= t) return TP_E_RANK;
   if (bad_dtype(dtype)) return TP_E_DTYPE;
   if (d > 128) return TP_E_UNSUPPORTED;
-  const int64_t M = s * b, hl = a / t, n = 3 * hl * d, es = esize(dtype), nqb = (s + 63) / 64;
+  const int64_t M = s * b, hl = a / t, n = (hl + 2 * (g / t)) * d, es = esize(dtype), nqb = (s + 63) / 64;
   if (dtype == TP_BF16 && (h % 8 != 0 || d % 8 != 0 ||
                            misaligned16({X, Wqkv_i, Wo_i, QKV_i, O_i, dZ, dO_ws, rec_ws, dQKV_i, dWqkv_i, dbqkv_i,
                                          dWo_i, dX_i})))
@@ -406,7 +410,7 @@ int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
   // attention core backward into dQKV_i
   tp::AttnBwdParams bp = {};
   bp.qkv = QKV_i; bp.o = O_i; bp.dout = dO_ws; bp.lse = lse_i; bp.rec = rec_ws; bp.dqkv = dQKV_i;
-  bp.s = (int)s; bp.b = (int)b; bp.hl = (int)hl; bp.d = (int)d;
+  bp.s = (int)s; bp.b = (int)b; bp.hl = (int)hl; bp.d = (int)d; bp.G = (int)(a / g);
   bp.causal = causal ? 1 : 0;
   bp.scale = (float)(1.0 / __builtin_sqrt((double)d));
   // weight gradients dWo_i = O_i^T dZ and dWqkv_i = X^T dQKV_i (both over K = s*b)

@@ -154,15 +154,17 @@ hipError_t colsum(tp_dtype dt, const void* x, int64_t rows, int64_t cols, void* 
 hipError_t reduce_partials(tp_dtype dt, const void* partials, int t, int64_t stride, int64_t in_off, int64_t count,
                            const void* bias, int64_t h, void* out, hipStream_t st);
 hipError_t copy_bytes(const void* src, void* dst, int64_t bytes, hipStream_t st);
+// QKV kinds: G query heads per KV head, gd = (KV heads) * d; other kinds ignore both.
 hipError_t pack_columns(tp_dtype dt, const void* full, int64_t rows, int64_t full_cols, void* shard,
                         int64_t shard_cols, int kind, int64_t f_l, int64_t ffn, int64_t rank, int64_t hl, int64_t d,
-                        int64_t ad, hipStream_t st);
+                        int64_t ad, int64_t G, int64_t gd, hipStream_t st);
 
 struct AttnParams {
-  const void* qkv;  // [s, b, hl*3d] grouped [q_j k_j v_j]
+  const void* qkv;  // [s, b, (hl + 2 hl/G) d]: per local KV group, its G query heads, then its K and V
   void* o;          // [s, b, hl*d]
   float* lse;       // [b, hl, s] or null
   int s, b, hl, d;
+  int G;            // query heads per KV head (1: multi-head)
   int causal;
   float scale;      // 1/sqrt(d)
 };
@@ -172,13 +174,14 @@ hipError_t attention_f32(const AttnParams& p, hipStream_t st);
 // Attention backward core.  rec: per (batch, head, 64-query block) one 256-float record [lse(64) | D(64) | 0(128)]
 // with D[q] = sum_e dO[q, e] O[q, e]; written by attention_bwd_prep, read by the dK/dV and dQ kernels.
 struct AttnBwdParams {
-  const void* qkv;   // [s, b, hl*3d] grouped [q_j k_j v_j]
+  const void* qkv;   // [s, b, (hl + 2 hl/G) d], grouped as in AttnParams
   const void* o;     // [s, b, hl*d]
   const void* dout;  // [s, b, hl*d]
   const float* lse;  // [b, hl, s]
   float* rec;        // [b, hl, ceil(s/64), 256]
-  void* dqkv;        // [s, b, hl*3d] grouped like qkv
+  void* dqkv;        // grouped like qkv; a KV head's dK / dV sum over its G query heads
   int s, b, hl, d;
+  int G;             // query heads per KV head (1: multi-head)
   int causal;
   float scale;       // 1/sqrt(d)
 };

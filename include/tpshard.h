@@ -36,12 +36,14 @@
 extern "C" {
 #endif
 
-#define TPSHARD_ABI_VERSION 1
+#define TPSHARD_ABI_VERSION 2
 
-/* Sizes in the pages' notation.  MLP calls read s, b, h, ffn, t; attention calls read s, b, h, a, d, t; the
- * reductions read s, b, h, t. */
+/* Sizes in the pages' notation.  MLP calls read s, b, h, ffn, t; attention calls read s, b, h, a, d, t and g; the
+ * reductions read s, b, h, t.  g is the number of KV heads (query groups) of grouped-query attention ([MEGA] QKV
+ * remark: the fused QKV weight is h + 2*hkv wide); 0 means g = a (multi-head attention).  Needs a % g == 0 and
+ * g % t == 0: each rank owns whole groups (with g < t a rank would need other ranks' KV heads). */
 typedef struct {
-  int64_t s, b, h, ffn, a, d, t;
+  int64_t s, b, h, ffn, a, d, t, g;
 } tp_dims;
 
 typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
@@ -56,11 +58,12 @@ typedef enum {
   TP_W_FC1 = 0,         /* full [h, ffn]            -> shard [h, ffn/t]  (column-parallel)                    */
   TP_W_FC1_GATE_UP = 1, /* full [h, 2ffn]=[Wg|Wu]   -> shard [h, 2ffn/t] = [Wg_i | Wu_i]                      */
   TP_W_FC2 = 2,         /* full [ffn, h]            -> shard [ffn/t, h]  (row-parallel)                       */
-  TP_W_QKV = 3,         /* full [h, 3ad]=[Wq|Wk|Wv] -> shard [h, (a/t)*3d], per local head j: [q_j | k_j | v_j] */
+  TP_W_QKV = 3,         /* full [h, (a+2g)d] = [Wq|Wk|Wv] -> shard [h, (a/t + 2g/t)d]: per local KV group its
+                           a/g query heads, then its k and v ([MEGA] interleave); g = a: [q_j | k_j | v_j]        */
   TP_W_PROJ = 4,        /* full [ad, h]             -> shard [(a/t)*d, h] (row-parallel)                      */
   TP_B_FC1 = 5,         /* full [ffn]               -> [ffn/t]                                                */
   TP_B_FC1_GATE_UP = 6, /* full [2ffn]=[bg|bu]      -> [2ffn/t] = [bg_i | bu_i]                               */
-  TP_B_QKV = 7          /* full [3ad]=[bq|bk|bv]    -> [(a/t)*3d] grouped per local head                      */
+  TP_B_QKV = 7          /* full [(a+2g)d] = [bq|bk|bv] -> [(a/t + 2g/t)d] grouped like TP_W_QKV              */
 } tp_wkind;
 
 enum {
@@ -126,31 +129,33 @@ int tp_mlp_bwd_phase(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, 
                      const void* A_i, const void* B_i, const void* U_i, const void* Y_i, const void* dZ, void* dU_ws,
                      void* dA_i, void* da_i, void* dB_i, void* dX_i, hipStream_t stream);
 
-/* Attention forward of rank `rank` for its a/t local heads ([ATLAS] §3, [MEGA]: QKV column-parallel by head,
- * per-head softmax(Q K^T / sqrt d) V on the local heads, output projection row-parallel; [SPCP] CP step 3: the
- * online-softmax merge over key blocks):
- *   QKV_i = X Wqkv_i (+ bqkv_i)     [s, b, (a/t)*3d], per local head j the columns [q_j | k_j | v_j]
- *   O_i   = per head softmax(Q_j K_j^T / sqrt(d), causal: key k visible to query q iff k <= q) V_j
- *                                   [s, b, (a/t)*d], head j at columns j*d .. j*d+d-1
+/* Attention forward of rank `rank` for its a/t local query heads and g/t local KV heads ([ATLAS] §3, [MEGA]: QKV
+ * column-parallel by head (by query group under GQA), per-head softmax(Q K^T / sqrt d) V on the local heads,
+ * output projection row-parallel; [SPCP] CP step 3: the online-softmax merge over key blocks).  n = (a/t + 2g/t)d:
+ *   QKV_i = X Wqkv_i (+ bqkv_i)     [s, b, n]: per local KV group, the d columns of each of its a/g query heads,
+ *                                   then its d key and d value columns (g = a: [q_j | k_j | v_j] per head)
+ *   O_i   = per query head j: softmax(Q_j K_j'^T / sqrt(d), causal: key k visible to query q iff k <= q) V_j'
+ *           with j' = j's KV head (its group)   [s, b, (a/t)*d], head j at columns j*d .. j*d+d-1
  *   lse_i = log sum_k exp(S[q, k]) per (b, local head, q), fp32 [b, a/t, s] (nullable)
  *   Z_i   = O_i Wo_i                [s, b, h], a partial sum (no row bias)
- * Wqkv_i [h, (a/t)*3d] and Wo_i [(a/t)*d, h] as produced by tp_shard_weights.  bf16 path: d % 8 == 0, d <= 128.
+ * Wqkv_i [h, n] and Wo_i [(a/t)*d, h] as produced by tp_shard_weights.  bf16 path: d % 8 == 0, d <= 128.
  * fp32 path: d <= 128. */
 int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const void* X, const void* Wqkv_i,
                 const void* bqkv_i, const void* Wo_i, void* QKV_i, void* O_i, float* lse_i, void* Z_i,
                 hipStream_t stream);
 
-/* Attention backward of rank `rank` for its a/t local heads, given the upstream gradient dZ of the block output
+/* Attention backward of rank `rank` for its a/t local query heads (g/t KV heads), given the upstream gradient dZ of the block output
  * ([ATLAS] §2 and §5: g's backward is the identity, so every rank receives the full dZ (gathered under SP); the
  * row-parallel projection's weight gradient and the column-parallel QKV's weight gradient stay local, the data
  * gradient dX is a partial that f sums over ranks; [SPLIT] backward of the column and row splits):
  *   dO_ws   = dZ Wo_i^T                          [s, b, (a/t)*d]    caller workspace (activation dtype)
  *   rec_ws  = per (b, local head, 64-query block) [lse(64) | D(64) | 0(128)], D[q] = sum_e dO[q,e] O[q,e]
  *                                                fp32 [b, a/t, ceil(s/64), 256], caller workspace
- *   dQKV_i  = per head dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO with P recomputed from lse_i
- *             (P = exp(S - lse)) and dS = P * (dO V^T - D)          [s, b, (a/t)*3d], grouped like QKV_i
- *   dWqkv_i = X^T dQKV_i                         [h, (a/t)*3d]     local weight gradient
- *   dbqkv_i = column sums of dQKV_i (nullable)   [(a/t)*3d]
+ *   dQKV_i  = per query head dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO with P recomputed from
+ *             lse_i (P = exp(S - lse)) and dS = P * (dO V^T - D); a KV head's dK, dV sum over the query heads
+ *             of its group                       [s, b, n], grouped like QKV_i
+ *   dWqkv_i = X^T dQKV_i                         [h, n]            local weight gradient
+ *   dbqkv_i = column sums of dQKV_i (nullable)   [n]
  *   dWo_i   = O_i^T dZ                           [(a/t)*d, h]      local weight gradient
  *   dX_i    = dQKV_i Wqkv_i^T                    [s, b, h]         a partial: f sums them over ranks
  * QKV_i, O_i and lse_i (not nullable here) are the forward's outputs for the same inputs and `causal`.  The

@@ -500,7 +500,7 @@ def _kv_cols(a: int, d: int, g: int, j: int):
     return slice(a * d + grp * d, a * d + (grp + 1) * d), slice(a * d + (g + grp) * d, a * d + (g + grp + 1) * d)
 
 
-def _local_cols(G: int, d: int, jj: int):
+def shard_head_columns(G: int, d: int, jj: int):
     """Query, key and value column ranges of local query head jj in a grouped shard ([MEGA] interleave)."""
     base = (jj // G) * (G + 2) * d
     q0 = base + (jj % G) * d
@@ -556,7 +556,7 @@ def attention_shard_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: 
     for bi in range(b):
         rows = np.arange(s) * b + bi
         for jj in range(hl):
-            cq, ck, cv = _local_cols(G, d, jj)
+            cq, ck, cv = shard_head_columns(G, d, jj)
             o, l = attention_core(QKVi[rows, cq], QKVi[rows, ck], QKVi[rows, cv], causal)
             Oi[rows, jj * d:(jj + 1) * d] = o
             lsei[bi, jj, :] = l
@@ -577,7 +577,7 @@ def attention_rows(QKV_i: np.ndarray, s: int, b: int, hl: int, d: int, q_rows: S
         nk = si + 1 if causal else s
         krows = np.arange(nk) * b + bi
         for jj in range(hl):
-            cq, ck, cv = _local_cols(G, d, jj)
+            cq, ck, cv = shard_head_columns(G, d, jj)
             q = QKV_i[r, cq]
             k = QKV_i[krows, ck]
             v = QKV_i[krows, cv]
@@ -651,7 +651,7 @@ def attention_shard_backward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, dZ
     for bi in range(b):
         rows = np.arange(s) * b + bi
         for jj in range(hl):
-            cq, ck, cv = _local_cols(G, d, jj)
+            cq, ck, cv = shard_head_columns(G, d, jj)
             gq, gk, gv = attention_core_backward(QKVi[rows, cq], QKVi[rows, ck], QKVi[rows, cv],
                                                  dOi[rows, jj * d:(jj + 1) * d], causal)
             dQKVi[rows, cq] = gq

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.lib.tp_abi_version() == 1
+    assert L.lib.tp_abi_version() == 2
     for code in range(0, -9, -1):
         s = L.status_str(code)
         assert isinstance(s, str) and s and s != "unknown status"
@@ -249,3 +249,24 @@ def test_vocab_ce_validation(L):
     assert L.tp_vocab_ce_bwd(16, 64, 0, P[0], P[1], P[2], None, P[4], stream=0, dtype=BF16, check=False) == -1
     assert L.tp_vocab_ce_bwd(16, 64, 0, P[0], P[1], P[2], P[3], P[0] + 32, stream=0, dtype=BF16, check=False) == -6
     assert L.tp_vocab_ce_bwd(16, 12, 0, P[0], P[1], P[2], P[3], P[4], stream=0, dtype="f32", check=False) == -7
+
+
+def test_gqa_dims_validation(L):
+    P = [addr(i) for i in range(8)]
+    ok = dict(s=16, b=2, h=64, a=8, d=8, t=2)
+
+    def fwd(**kw):
+        return L.tp_attn_fwd(L.make_dims(**{**ok, **kw}), 0, True, *P[:7], P[7], stream=0, dtype=BF16, check=False)
+
+    assert fwd(g=-2) == -2
+    assert fwd(g=3) == -3          # a % g
+    assert fwd(g=1) == -3          # g % t: a rank would not own a whole group
+    assert fwd(g=4, d=12, h=96) == -7   # valid groups; bf16 d % 8 decides
+    dims = L.make_dims(h=64, a=8, d=8, t=4, g=2)
+    assert L.tp_shard_weights(dims, 0, "qkv", P[0], P[1], stream=0, dtype=BF16, check=False) == -3
+    dims = L.make_dims(h=64, a=8, d=8, t=2, g=4)
+    assert L.tp_shard_weights(dims, 2, "b_qkv", P[0], P[1], stream=0, dtype=BF16, check=False) == -5
+    bw = L.tp_attn_bwd(L.make_dims(**{**ok, "g": 6}), 0, True, *P, P[0] + 0x800000, P[1] + 0x800000,
+                       P[2] + 0x800000, P[3] + 0x800000, P[4] + 0x800000, P[5] + 0x800000, stream=0, dtype=BF16,
+                       check=False)
+    assert bw == -3

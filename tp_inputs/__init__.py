@@ -74,6 +74,7 @@ class Workload:
     ffn: int = 0
     a: int = 0
     d: int = 0
+    g: int = 0  # KV heads of grouped-query attention (0: g = a, multi-head)
     act: str = "gelu"  # gelu | gelu_tanh | swiglu | relu
     dtype: str = "bf16"  # bf16 | f32
     causal: bool = True
@@ -107,7 +108,11 @@ MLP_SP_SWIGLU = Workload("sp_swiglu_h8192_ffn28672_t8_s4096", "mlp", s=4096, b=1
 ATTN_22B = Workload("attn_h6144_a64_d96_t8_s4096", "attn", s=4096, b=1, h=6144, a=64, d=96, t=8, causal=True,
                     sp=True)
 
-WORKLOADS = {w.name: w for w in (TINY, MLP_83B, MLP_CALC, MLP_SP_SWIGLU, ATTN_22B)}
+# Llama-70B-sized grouped-query attention ([ATLAS] §6: h 8192, 64 heads of 128, TP 8, s 4096, b 1; [SPCP] Table 4:
+# 8 KV heads of 128): per rank 8 query heads sharing one KV head
+ATTN_GQA_70B = Workload("attn_gqa_h8192_a64_g8_d128_t8_s4096", "attn", s=4096, b=1, h=8192, a=64, d=128, t=8, g=8,
+                        causal=True, sp=True)
+WORKLOADS = {w.name: w for w in (TINY, MLP_83B, MLP_CALC, MLP_SP_SWIGLU, ATTN_22B, ATTN_GQA_70B)}
 
 
 def mlp_inputs(w: Workload, with_bias: bool = False, seed: Optional[int] = None) -> dict:
@@ -129,20 +134,21 @@ def mlp_inputs(w: Workload, with_bias: bool = False, seed: Optional[int] = None)
 
 
 def attn_inputs(w: Workload, with_bias: bool = False, seed: Optional[int] = None) -> dict:
-    """Full attention inputs: X [s,b,h], Wqkv [h, 3ad] = [Wq|Wk|Wv] (head-major columns), Wo [ad, h], and the
-    upstream gradient dZ [s,b,h] for the backward."""
+    """Full attention inputs: X [s,b,h], Wqkv [h, (a + 2g)d] = [Wq|Wk|Wv] (head-major columns; g = a unless the
+    workload sets g), Wo [ad, h], and the upstream gradient dZ [s,b,h] for the backward."""
     sd = w.seed if seed is None else seed
     ad = w.a * w.d
+    nqkv = ad + 2 * (w.g or w.a) * w.d
     out = {
         "X": tensor(sd, T_X, (w.s, w.b, w.h), 1.0, w.dtype),
-        "Wqkv": tensor(sd, T_A, (w.h, 3 * ad), WEIGHT_STD, w.dtype),
+        "Wqkv": tensor(sd, T_A, (w.h, nqkv), WEIGHT_STD, w.dtype),
         "Wo": tensor(sd, T_B, (ad, w.h), WEIGHT_STD, w.dtype),
         "dZ": tensor(sd, T_DZ, (w.s, w.b, w.h), 1.0, w.dtype),
         "bqkv": None,
         "c": None,
     }
     if with_bias:
-        out["bqkv"] = tensor(sd, T_BIAS_COL, (3 * ad,), WEIGHT_STD, w.dtype)
+        out["bqkv"] = tensor(sd, T_BIAS_COL, (nqkv,), WEIGHT_STD, w.dtype)
         out["c"] = tensor(sd, T_BIAS_ROW, (w.h,), WEIGHT_STD, w.dtype)
     return out
 
