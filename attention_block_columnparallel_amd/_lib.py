@@ -24,7 +24,7 @@ STATUS = {0: "TP_OK", -1: "TP_E_NULL", -2: "TP_E_SHAPE", -3: "TP_E_DIVISIBILITY"
           -6: "TP_E_ALIAS", -7: "TP_E_UNSUPPORTED", -8: "TP_E_HIP"}
 EXPORTED = ["tp_status_str", "tp_last_hip_error", "tp_abi_version", "tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd",
             "tp_mlp_bwd_phase",
-            "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd",
+            "tp_attn_fwd", "tp_attn_bwd", "tp_attn_bwd_workspace", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd",
             "tp_sp_dropout_add_ln_bwd", "tp_sp_ln_bwd_workspace", "tp_vocab_ce_fwd_local", "tp_vocab_ce_combine",
             "tp_vocab_ce_bwd", "tp_timing_begin", "tp_timing_end",
             "tp_timing_kernel", "tp_timing_filter"]
@@ -69,6 +69,7 @@ def _load() -> ctypes.CDLL:
         "tp_mlp_bwd_phase": ([D, I, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_attn_fwd": ([D, I, I, I, P, P, P, P, P, P, P, P, P], I),
         "tp_attn_bwd": ([D, I, I, I, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P], I),
+        "tp_attn_bwd_workspace": ([D], I64),
         "tp_partial_reduce": ([I64, I64, I, I, P, P, P, P], I),
         "tp_reduce_scatter_dim0": ([D, I, I, P, P, P, P], I),
         "tp_gather_dim0": ([D, I, P, P, P], I),
@@ -190,6 +191,10 @@ def tp_attn_bwd(dims: tp_dims, rank: int, causal: bool, X, Wqkv_i, Wo_i, QKV_i, 
                          _ptr(rec_ws), _ptr(dQKV_i), _ptr(dWqkv_i), _ptr(dbqkv_i), _ptr(dWo_i), _ptr(dX_i),
                          _stream(stream))
     return _check(st, "tp_attn_bwd", check)
+
+
+def tp_attn_bwd_workspace(dims: tp_dims) -> int:
+    return int(lib.tp_attn_bwd_workspace(ctypes.byref(dims)))
 
 
 def tp_partial_reduce(n: int, h: int, t: int, partials, bias_c, out, stream=None, dtype=None, check=True) -> int:

@@ -213,7 +213,7 @@ class AttnBlock:
         dev, dt = self.Wqkv.device, self.Wqkv.dtype
         nqb = (self.s + 63) // 64
         self.dO = torch.empty((M, hl * d), dtype=dt, device=dev)  # workspace reused by every rank
-        self.rec = torch.empty((self.b, hl, nqb, 256), dtype=torch.float32, device=dev)  # workspace
+        self.rec = torch.empty(self.L.tp_attn_bwd_workspace(self.dims) // 4, dtype=torch.float32, device=dev)
         self.dQKV = torch.empty((t, M, self.nqkv), dtype=dt, device=dev)
         self.dWqkv = torch.empty((t, h, self.nqkv), dtype=dt, device=dev)
         self.dbqkv = torch.empty((t, self.nqkv), dtype=dt, device=dev) if self.bqkv is not None else None

@@ -387,11 +387,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int nqb = (p.s + 63) / 64;
-  const int gl = p.hl / p.G;  // local KV groups: one workgroup per (batch, group, 64-key block)
-  const int nbh = p.b * gl;
+  // one workgroup per (64-key block, batch, local KV group, head split): split sp walks query heads
+  // sp*HS .. sp*HS + HS - 1 of the group (HS = G / splits) and, with more than one split, writes fp32 partial dK / dV
+  // that attn_bwd_kv_sum_kernel adds up in split order
+  const int gl = p.hl / p.G;
+  const int splits = p.kvpart != nullptr ? p.G : 1;
+  const int HS = p.G / splits;
+  const int nbh = p.b * gl * splits;
   const int ktile = (int)blockIdx.x / nbh;  // key block 0 sees the most queries: issued first
   const int bh = (int)blockIdx.x % nbh;
-  const int bidx = bh / gl, jg = bh % gl;
+  const int sp = bh % splits;
+  const int bidx = bh / splits / gl, jg = bh / splits % gl;
   const int d = p.d;
   const QkvCols kc = qkv_cols(p.hl, p.G, d, jg * p.G);
   const int64_t ldq = kc.ld;
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   }
   const int qb0 = p.causal ? ktile : 0;
   const int nblk = nqb - qb0;
-  const int ntot = p.G * nblk;  // (query head of the group, query block) steps, head by head
+  const int ntot = HS * nblk;  // (query head of the split, query block) steps, head by head
 
   // ---- copies (same chunk rotation as the forward's K / V tiles); wave 0 also copies the block's record
   int crow[CPW], ccol[CPW];
@@ -434,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   auto issue_tile = [&](int i, int st) {
     const int ii = min(i, ntot - 1);  // past the last step: a harmless re-copy of it
     const int hs = ii / nblk, qb = qb0 + (ii - hs * nblk);
-    const int jh = jg * p.G + hs;  // the step's query head
+    const int jh = jg * p.G + sp * HS + hs;  // the step's query head
     const uint16_t* qsrc = qkv0 + qkv_cols(p.hl, p.G, d, jh).q;
     const uint16_t* dsrc = dob0 + (int64_t)jh * d;
     const float* rsrc = p.rec + ((int64_t)(bidx * p.hl + jh) * nqb + qb) * 256;
@@ -569,7 +575,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   }
   wait_vmcnt<0>();
 
-  if (key < p.s) {
+  if (key < p.s && splits > 1) {
+    // partial [split][token row][local group][dK (scaled) | dV], fp32
+    float* part = p.kvpart + (((int64_t)sp * p.s * p.b + (int64_t)key * p.b + bidx) * gl + jg) * 2 * d;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int dd = st * 16 + 4 * g;
+      if (dd < d) {
+        *reinterpret_cast<f32x4_t*>(part + dd) = f32x4_t{dk[st][0] * p.scale, dk[st][1] * p.scale,
+                                                          dk[st][2] * p.scale, dk[st][3] * p.scale};
+        *reinterpret_cast<f32x4_t*>(part + d + dd) = dv[st];
+      }
+    }
+  } else if (key < p.s) {
     uint16_t* out = static_cast<uint16_t*>(p.dqkv) + ((int64_t)key * p.b + bidx) * ldq + kc.k;  // dK; dV at + d
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
@@ -850,6 +868,35 @@ __global__ __launch_bounds__(64) void attn_bwd_dkv_f32_kernel(AttnBwdParams p) {
   }
 }
 
+// dK | dV of every (token row, local KV group) = the sum of the head splits' fp32 partials, in split order, rounded
+// once to bf16 into the group's key and value columns (adjacent in dQKV).  One thread per 4 columns.
+__global__ __launch_bounds__(256) void attn_bwd_kv_sum_kernel(AttnBwdParams p) {
+  const int gl = p.hl / p.G, d = p.d, w4 = d / 2;  // 2d columns per (row, group), in 4-column quads
+  const int64_t rows = (int64_t)p.s * p.b;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * gl * w4) return;
+  const int c4 = (int)(idx % w4);
+  const int64_t rg = idx / w4;  // token row * gl + group
+  const int jg = (int)(rg % gl);
+  const int64_t m = rg / gl;
+  const int64_t split_stride = rows * gl * 2 * d;
+  const float* part = p.kvpart + rg * 2 * d + 4 * c4;
+  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(part);
+  for (int sp = 1; sp < p.G; ++sp) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + sp * split_stride);
+    acc[0] += v[0];
+    acc[1] += v[1];
+    acc[2] += v[2];
+    acc[3] += v[3];
+  }
+  const QkvCols kc = qkv_cols(p.hl, p.G, d, jg * p.G);
+  uint16_t* out = static_cast<uint16_t*>(p.dqkv) + m * kc.ld + kc.k + 4 * c4;
+  uint2 w;
+  w.x = f32_to_bf16_hw(acc[0]) | (f32_to_bf16_hw(acc[1]) << 16);
+  w.y = f32_to_bf16_hw(acc[2]) | (f32_to_bf16_hw(acc[3]) << 16);
+  *reinterpret_cast<uint2*>(out) = w;
+}
+
 template <int DP>
 hipError_t launch_bwd_bf16(const AttnBwdParams& p, hipStream_t st) {
   const int nq = (p.s + 63) / 64;
@@ -857,9 +904,16 @@ hipError_t launch_bwd_bf16(const AttnBwdParams& p, hipStream_t st) {
   static const std::string n0 = "attn_bwd_delta_bf16_d" + std::to_string(DP);
   static const std::string n1 = "attn_bwd_dkv_bf16_d" + std::to_string(DP);
   static const std::string n2 = "attn_bwd_dq_bf16_d" + std::to_string(DP);
-  const unsigned grid_kv = (unsigned)(nq * p.b * (p.hl / p.G));  // one workgroup per (64 keys, batch, KV group)
+  const int splits = p.kvpart != nullptr ? p.G : 1;
+  // one workgroup per (64 keys, batch, KV group, head split)
+  const unsigned grid_kv = (unsigned)(nq * p.b * (p.hl / p.G) * splits);
   hipError_t e = TP_LAUNCH(n0.c_str(), (attn_bwd_dq_bf16_kernel<DP, true>), dim3(grid), dim3(256), 0, st, p);
   if (e == hipSuccess) e = TP_LAUNCH(n1.c_str(), (attn_bwd_dkv_bf16_kernel<DP>), dim3(grid_kv), dim3(256), 0, st, p);
+  if (e == hipSuccess && splits > 1) {
+    const int64_t n = (int64_t)p.s * p.b * (p.hl / p.G) * (p.d / 2);
+    e = TP_LAUNCH("attn_bwd_kv_sum_bf16", attn_bwd_kv_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                  st, p);
+  }
   if (e == hipSuccess) e = TP_LAUNCH(n2.c_str(), (attn_bwd_dq_bf16_kernel<DP, false>), dim3(grid), dim3(256), 0, st, p);
   return e;
 }

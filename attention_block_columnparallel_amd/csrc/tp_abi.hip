@@ -394,7 +394,9 @@ int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
                            misaligned16({X, Wqkv_i, Wo_i, QKV_i, O_i, dZ, dO_ws, rec_ws, dQKV_i, dWqkv_i, dbqkv_i,
                                          dWo_i, dX_i})))
     return TP_E_UNSUPPORTED;
-  const Buf outs[] = {{dO_ws, M * hl * d * es}, {rec_ws, b * hl * nqb * 256 * 4}, {dQKV_i, M * n * es},
+  const int64_t G = a / g, rec_floats = b * hl * nqb * 256;
+  const int64_t ws_floats = rec_floats + (G > 1 ? M * (g / t) * 2 * d * G : 0);
+  const Buf outs[] = {{dO_ws, M * hl * d * es}, {rec_ws, ws_floats * 4}, {dQKV_i, M * n * es},
                       {dWqkv_i, h * n * es},     {dbqkv_i, n * es},                  {dWo_i, hl * d * h * es},
                       {dX_i, M * h * es}};
   const Buf ins[] = {{X, M * h * es},     {Wqkv_i, h * n * es},     {Wo_i, hl * d * h * es}, {QKV_i, M * n * es},
@@ -410,7 +412,8 @@ int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
   // attention core backward into dQKV_i
   tp::AttnBwdParams bp = {};
   bp.qkv = QKV_i; bp.o = O_i; bp.dout = dO_ws; bp.lse = lse_i; bp.rec = rec_ws; bp.dqkv = dQKV_i;
-  bp.s = (int)s; bp.b = (int)b; bp.hl = (int)hl; bp.d = (int)d; bp.G = (int)(a / g);
+  bp.s = (int)s; bp.b = (int)b; bp.hl = (int)hl; bp.d = (int)d; bp.G = (int)G;
+  bp.kvpart = (G > 1 && dtype == TP_BF16) ? rec_ws + rec_floats : nullptr;
   bp.causal = causal ? 1 : 0;
   bp.scale = (float)(1.0 / __builtin_sqrt((double)d));
   // weight gradients dWo_i = O_i^T dZ and dWqkv_i = X^T dQKV_i (both over K = s*b)
@@ -445,6 +448,15 @@ int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
   if (e == hipSuccess && dbqkv_i != nullptr) e = tp::colsum(dtype, dQKV_i, M, n, dbqkv_i, stream);
   if (e == hipSuccess) e = gemm(gx, true, true, tp::EPI_STORE, stream);
   return hip_status(e);
+}
+
+int64_t tp_attn_bwd_workspace(const tp_dims* dims) {
+  if (dims == nullptr) return 0;
+  const int64_t s = dims->s, b = dims->b, a = dims->a, d = dims->d, t = dims->t;
+  const int64_t g = dims->g == 0 ? a : dims->g;
+  if (s <= 0 || b <= 0 || a <= 0 || d <= 0 || t <= 0 || g <= 0 || a % t != 0 || a % g != 0 || g % t != 0) return 0;
+  const int64_t hl = a / t, G = a / g, nqb = (s + 63) / 64;
+  return (b * hl * nqb * 256 + (G > 1 ? s * b * (g / t) * 2 * d * G : 0)) * 4;
 }
 
 int tp_partial_reduce(int64_t n, int64_t h, int t, tp_dtype dtype, const void* partials, const void* bias_c,

@@ -180,6 +180,7 @@ struct AttnBwdParams {
   const float* lse;  // [b, hl, s]
   float* rec;        // [b, hl, ceil(s/64), 256]
   void* dqkv;        // grouped like qkv; a KV head's dK / dV sum over its G query heads
+  float* kvpart;     // G > 1, bf16: fp32 [G][s*b][hl/G][2d] per-head partial dK | dV (null: one workgroup per group)
   int s, b, hl, d;
   int G;             // query heads per KV head (1: multi-head)
   int causal;

@@ -16,12 +16,12 @@ MFMA peak.  rs_dim0 = the reduce-scatter kernel (census pass) against HBM bandwi
 launch from the committed rocprofv3 counter summary under profiles/ (null once the kernel source differs from the
 one profiled).  cpu_baseline = the fp64 oracle on a bounded sample.
 
-overlap, attention_block, gather_dim0, sp_region and vocab_ce = the other rows of the hot path, timed after the
-step (not part of value): the same step with its reductions on a second stream beside the GEMMs (serial vs
-overlapped ms/step); the attention block forward and backward at the 22B-class shape; the dim-0 gather at the
-Llama-70B-sized SP shape; the sequence-parallel region (dropout + residual + LayerNorm, forward and backward) on
-every rank's rows at that same shape; the vocab-parallel cross entropy (local pass, combine, backward) at 16384
-token rows over a 51200-entry vocab.
+overlap, attention_block(_gqa), gather_dim0, sp_region and vocab_ce = the other rows of the hot path, timed after
+the step (not part of value): the same step with its reductions on a second stream beside the GEMMs (serial vs
+overlapped ms/step); the attention block forward and backward at the 22B-class shape and at the Llama-70B-sized
+grouped-query shape; the dim-0 gather at the Llama-70B-sized SP shape; the sequence-parallel region (dropout +
+residual + LayerNorm, forward and backward) on every rank's rows at that same shape; the vocab-parallel cross
+entropy (local pass, combine, backward) at 16384 token rows over a 51200-entry vocab.
 """
 from __future__ import annotations
 
@@ -82,8 +82,9 @@ def profiled_traffic(workload: str, kernel: str):
     return None
 
 
-def attention_block_measure(L, steps: int, warmup: int) -> dict:
-    """The attention block at the 22B-class shape (h=6144, 64 heads of 96, s=4096, t=8, causal).  Forward: for every
+def attention_block_measure(L, steps: int, warmup: int, w=None) -> dict:
+    """The attention block at the 22B-class shape (h=6144, 64 heads of 96, s=4096, t=8, causal), or the workload w
+    (the Llama-70B-sized grouped-query shape: 64 query and 8 KV heads of 128).  Forward: for every
     rank the QKV GEMM, local causal attention and output projection into partial i, then the dim-0 reduce-scatter.
     Backward: for every rank tp_attn_bwd (dO GEMM, attention core backward, the weight-gradient pair, the dX GEMM),
     then the reduce-scatter of the dX partials.  Per-kernel HIP-event durations from a pass with every launch
@@ -95,14 +96,14 @@ def attention_block_measure(L, steps: int, warmup: int) -> dict:
     import tp_inputs as TI
     from attention_block_columnparallel_amd.block import AttnBlock
 
-    w = TI.ATTN_22B
+    w = TI.ATTN_22B if w is None else w
 
     def dev(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
 
     inp = TI.attn_inputs(w)
     X = dev(inp["X"])
-    blk = AttnBlock(w.s, w.b, w.h, w.a, w.d, w.t, dev(inp["Wqkv"]), dev(inp["Wo"]), causal=True)
+    blk = AttnBlock(w.s, w.b, w.h, w.a, w.d, w.t, dev(inp["Wqkv"]), dev(inp["Wo"]), causal=True, g=w.g)
     for _ in range(warmup):
         blk.forward(X, sp=True)
     torch.cuda.synchronize()
@@ -115,7 +116,8 @@ def attention_block_measure(L, steps: int, warmup: int) -> dict:
     e1.record()
     torch.cuda.synchronize()
     hl, M = w.a // w.t, w.s * w.b
-    fl = {"qkv": 2.0 * M * w.h * 3 * hl * w.d, "attention": 4.0 * w.d * (w.s * (w.s + 1) / 2) * w.b * hl,
+    nqkv = blk.nqkv  # the rank's QKV columns: (a/t + 2 g/t) d
+    fl = {"qkv": 2.0 * M * w.h * nqkv, "attention": 4.0 * w.d * (w.s * (w.s + 1) / 2) * w.b * hl,
           "proj": 2.0 * M * hl * w.d * w.h}
     # launch order per step: for each rank QKV GEMM, attention, output projection; then the reduce-scatter
     res = timer.results()
@@ -167,7 +169,7 @@ def attention_block_measure(L, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     pairs = w.s * (w.s + 1) / 2 * w.b * hl
     bfl = {"dO_gemm": 2.0 * M * w.h * hl * w.d, "attention_core_bwd": 10.0 * w.d * pairs,
-           "wgrad_pair": 2.0 * M * hl * w.d * w.h + 2.0 * M * w.h * 3 * hl * w.d, "dX_gemm": 2.0 * M * 3 * hl * w.d * w.h}
+           "wgrad_pair": 2.0 * M * hl * w.d * w.h + 2.0 * M * w.h * nqkv, "dX_gemm": 2.0 * M * nqkv * w.h}
     roles = {}
     seq = []
     for name, ms in timer.results():
@@ -549,6 +551,8 @@ def main(argv=None) -> int:
     torch.cuda.empty_cache()
     if not args.no_extra:
         out["attention_block"] = attention_block_measure(L, max(2, args.steps // 2), 2)
+        torch.cuda.empty_cache()
+        out["attention_block_gqa"] = attention_block_measure(L, max(2, args.steps // 2), 2, TI.ATTN_GQA_70B)
         out["gather_dim0"] = gather_measure(L, 20)
         out["sp_region"] = sp_region_measure(L, 10)
         out["vocab_ce"] = vocab_ce_measure(L, 10)

@@ -150,7 +150,9 @@ int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
  * gradient dX is a partial that f sums over ranks; [SPLIT] backward of the column and row splits):
  *   dO_ws   = dZ Wo_i^T                          [s, b, (a/t)*d]    caller workspace (activation dtype)
  *   rec_ws  = per (b, local head, 64-query block) [lse(64) | D(64) | 0(128)], D[q] = sum_e dO[q,e] O[q,e]
- *                                                fp32 [b, a/t, ceil(s/64), 256], caller workspace
+ *                                                fp32 [b, a/t, ceil(s/64), 256], caller workspace; with g < a it
+ *             also holds the per-query-head partial dK | dV of each KV head (fp32 [a/g][s*b][g/t][2d]), summed in a
+ *             fixed order: size tp_attn_bwd_workspace(dims) bytes
  *   dQKV_i  = per query head dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO with P recomputed from
  *             lse_i (P = exp(S - lse)) and dS = P * (dO V^T - D); a KV head's dK, dV sum over the query heads
  *             of its group                       [s, b, n], grouped like QKV_i
@@ -164,6 +166,9 @@ int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
                 const void* Wo_i, const void* QKV_i, const void* O_i, const float* lse_i, const void* dZ, void* dO_ws,
                 float* rec_ws, void* dQKV_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i, void* dX_i,
                 hipStream_t stream);
+
+/* Bytes of the rec_ws workspace tp_attn_bwd needs for dims (0 for invalid dims). */
+int64_t tp_attn_bwd_workspace(const tp_dims* dims);
 
 /* g in forward / f in backward, all-reduce form ([ATLAS] §2; [SPLIT] row-parallel merge is a sum):
  *   out[e] = sum_{i=0}^{t-1} partials[i*n + e]  (+ bias_c[e % h])

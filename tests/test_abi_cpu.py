@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     names = declared_functions()
-    for n in ["tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_phase", "tp_attn_fwd", "tp_attn_bwd", "tp_partial_reduce",
+    for n in ["tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd", "tp_mlp_bwd_phase", "tp_attn_fwd", "tp_attn_bwd",
+              "tp_attn_bwd_workspace", "tp_partial_reduce",
               "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd", "tp_sp_dropout_add_ln_bwd",
               "tp_sp_ln_bwd_workspace", "tp_vocab_ce_fwd_local", "tp_vocab_ce_combine", "tp_vocab_ce_bwd",
               "tp_status_str"]:
@@ -270,3 +271,11 @@ def test_gqa_dims_validation(L):
                        P[2] + 0x800000, P[3] + 0x800000, P[4] + 0x800000, P[5] + 0x800000, stream=0, dtype=BF16,
                        check=False)
     assert bw == -3
+
+
+def test_attn_bwd_workspace_size(L):
+    # multi-head: the per-block records only; grouped-query: plus a/g partial dK | dV rows per KV head
+    assert L.tp_attn_bwd_workspace(L.make_dims(s=100, b=2, h=64, a=8, d=8, t=2)) == 2 * 4 * 2 * 256 * 4
+    g = L.make_dims(s=100, b=2, h=64, a=8, d=8, t=2, g=2)
+    assert L.tp_attn_bwd_workspace(g) == (2 * 4 * 2 * 256 + 100 * 2 * 1 * 16 * 4) * 4
+    assert L.tp_attn_bwd_workspace(L.make_dims(s=100, b=2, h=64, a=8, d=8, t=2, g=3)) == 0

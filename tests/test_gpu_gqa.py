@@ -51,7 +51,8 @@ def run_rank(L, w, inp, r, dtype, with_bias, causal, backward=True):
     if backward:
         nqb = (s + 63) // 64
         dO = empty((M, hl * d), dtype)
-        rec = torch.empty((b, hl, nqb, 256), dtype=torch.float32, device="cuda")
+        rec = torch.empty(L.tp_attn_bwd_workspace(dims) // 4, dtype=torch.float32, device="cuda")
+        assert rec.numel() == b * hl * nqb * 256 + (s * b * (g // t) * 2 * d * (a // g) if g < a else 0)
         dQKV, dWq, dWo, dX = empty((M, n), dtype), empty((h, n), dtype), empty((hl * d, h), dtype), empty((M, h), dtype)
         dbq = empty((n,), dtype) if with_bias else None
         L.tp_attn_bwd(dims, r, causal, X, Wq, Wo, QKV, Oo, lse, dZ, dO, rec, dQKV, dWq, dbq, dWo, dX)
