@@ -17,7 +17,7 @@
 //   * two LDS stages; the next K tile's global loads are issued into registers before the current tile's MFMAs
 //     and written to the other stage after them, with one barrier per K tile.
 // Both order tiles XCD-aware: the hardware deals workgroup i to XCD i % 8, so the launch index is remapped to give
-// each XCD a contiguous run of tiles, walked in groups of GROUP_M row tiles so the A rows and B columns an XCD
+// each XCD a contiguous run of tiles, walked in groups of a few row tiles so the A rows and B columns an XCD
 // touches stay in its own L2.
 #include <string>
 #include <type_traits>
@@ -638,11 +638,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   if (which) bid -= pp.tiles0;
   const int nbm = (p.M + BM - 1) / BM;
   const int nbn = SWIG ? (p.fhalf + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
-  const int group = bid / (GROUP_M * nbn);
-  const int first_m = group * GROUP_M;
-  const int gsz = min(nbm - first_m, GROUP_M);
-  const int tile_m = first_m + (bid % (GROUP_M * nbn)) % gsz;
-  const int tile_n = (bid % (GROUP_M * nbn)) / gsz;
+  // row-tile groups of 4 for a single GEMM, 8 for the weight-gradient pair (measured best for each)
+  const int gm = pp.tiles1 > 0 ? 8 : 4;
+  const int group = bid / (gm * nbn);
+  const int first_m = group * gm;
+  const int gsz = min(nbm - first_m, gm);
+  const int tile_m = first_m + (bid % (gm * nbn)) % gsz;
+  const int tile_n = (bid % (gm * nbn)) / gsz;
 
   Dma<AK, false> da;
   Dma<BKM, SWIG> db;
