@@ -333,8 +333,9 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams p) {
 //     copies into a 3-stage ring.  S = Q K^T and dP = dO V^T take Q / dO rows from LDS and the wave's K / V
 //     fragments from registers; dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T with transposing LDS reads
 //     whose row addresses follow the query order of the P / dS operand (the forward's V trick).
-//   * dQ: the forward's structure (64 queries per workgroup, K and V tiles in the ring): S^T = K Q^T,
-//     dP^T = V dO^T, dQ^T += K^T dS^T with K^T gathered by transposing reads.
+//   * dQ, run first: the forward's structure (64 queries per workgroup, K and V tiles in the ring): S^T = K Q^T,
+//     dP^T = V dO^T, and with K^T gathered by transposing reads A^T += K^T (P dP)^T, B^T += K^T P^T and
+//     D += sum_k P dP, so dQ = (A - D B) scale comes out of one walk over the keys; D is written to the record.
 // ================================================================================================================
 
 // Per (batch, head, 64-query block) record: [lse(64) | D(64) | 0(128)].
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdParams p) {
     rec[t] = q < p.s ? p.lse[(int64_t)bh * p.s + q] : 0.f;
   } else if (t < 128) {
     // fp32 path: D from the stored O (fp32, so as good as the row sum of P * dP); the bf16 path gets D from its
-    // own pass over the keys (attn_bwd_dq_bf16_kernel<DP, true>) and starts from zero here
+    // walk over the keys in the dQ kernel (attn_bwd_dq_bf16_kernel) and starts from zero here
     const int q = qb * 64 + (t - 64);
     float acc = 0.f;
     if (sizeof(T) == 4 && q < p.s) {
@@ -605,10 +606,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   }
 }
 
-// DPASS: instead of dQ, compute each query's D = sum_k P[q, k] dP[q, k] over all the keys it sees and write it into
-// the record (run before the dK / dV and dQ passes, which read it).  Taking D as the row sum of dO * O instead
-// would use the forward's bf16-rounded O, whose rounding reaches every element of dS = P * (dP - D).
-template <int DP, bool DPASS>
+// dQ without knowing D first: dQ = sum_k P (dP - D) K = A - D B with A = sum_k (P dP) K, B = sum_k P K and
+// D = sum_k P dP, all three gathered in the one walk over the keys (P dP and P reach the matrix cores as bf16
+// hi + lo pairs; with a single bf16 B the difference A - D B loses about 3e-2 of dQ's scale).  D goes into the
+// record for the dK / dV pass, which runs after this one.  Taking D as the row sum of dO * O instead would use the
+// forward's bf16-rounded O, whose rounding reaches every element of dS = P * (dP - D).
+template <int DP>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams p) {
   constexpr int CH = DP / 8;
   constexpr int TILE_B = KT * CH * 16;
@@ -648,7 +651,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
   }
   const float lse2 = q < p.s ? p.lse[(int64_t)bh * p.s + q] * 1.4426950408889634f : 0.f;
   float* const drec = p.rec + ((int64_t)bh * ((p.s + 63) / 64) + q / 64) * 256 + 64 + (q % 64);
-  const float Dq = (!DPASS && q < p.s) ? *drec : 0.f;
   float dsum = 0.f;
 
   const int nkt_all = (p.s + KT - 1) / KT;
@@ -696,9 +698,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
       }
 
   const float c2 = p.scale * 1.4426950408889634f;
-  f32x4_t dq[NST];
+  f32x4_t dq[NST], bq[NST];  // A^T and B^T
 #pragma unroll
-  for (int st = 0; st < NST; ++st) dq[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < NST; ++st) dq[st] = bq[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   issue_tile(0, 0);
   issue_tile(1, 1);
@@ -724,10 +726,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
       }
     }
     const bool need_mask = (p.causal && kt == qtile) || (kv0 + KT > p.s);
-    uint32_t dk2[4][2], dl2[4][2];  // dS as a hi + lo bf16 pair
+    uint32_t gh[4][2], gl[4][2], ph[4][2], pl[4][2];  // P dP and P as hi + lo bf16 pairs
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      float ds[4];
+      float gv[4], pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = fmaf(sc[ks][e], c2, -lse2);
@@ -735,34 +737,44 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
           const int kv = kv0 + ks * 16 + 4 * g + e;
           if (kv >= p.s || (p.causal && kv > q)) x = -INFINITY;
         }
-        const float pe = __builtin_amdgcn_exp2f(x);
-        if constexpr (DPASS) dsum = fmaf(pe, dp[ks][e], dsum);
-        ds[e] = pe * (dp[ks][e] - Dq);
+        pv[e] = __builtin_amdgcn_exp2f(x);
+        gv[e] = pv[e] * dp[ks][e];
+        dsum += gv[e];
       }
-      uint32_t hb[4];
-      float lo[4];
+      uint32_t hb[4], hp[4];
+      float lo[4], lp[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        hb[e] = f32_to_bf16_hw(ds[e]);
-        lo[e] = ds[e] - bf16_to_f32(hb[e]);
+        hb[e] = f32_to_bf16_hw(gv[e]);
+        lo[e] = gv[e] - bf16_to_f32(hb[e]);
+        hp[e] = f32_to_bf16_hw(pv[e]);
+        lp[e] = pv[e] - bf16_to_f32(hp[e]);
       }
-      dk2[ks][0] = hb[0] | (hb[1] << 16);
-      dk2[ks][1] = hb[2] | (hb[3] << 16);
-      dl2[ks][0] = f32_to_bf16_hw(lo[0]) | (f32_to_bf16_hw(lo[1]) << 16);
-      dl2[ks][1] = f32_to_bf16_hw(lo[2]) | (f32_to_bf16_hw(lo[3]) << 16);
+      gh[ks][0] = hb[0] | (hb[1] << 16);
+      gh[ks][1] = hb[2] | (hb[3] << 16);
+      gl[ks][0] = f32_to_bf16_hw(lo[0]) | (f32_to_bf16_hw(lo[1]) << 16);
+      gl[ks][1] = f32_to_bf16_hw(lo[2]) | (f32_to_bf16_hw(lo[3]) << 16);
+      ph[ks][0] = hp[0] | (hp[1] << 16);
+      ph[ks][1] = hp[2] | (hp[3] << 16);
+      pl[ks][0] = f32_to_bf16_hw(lp[0]) | (f32_to_bf16_hw(lp[1]) << 16);
+      pl[ks][1] = f32_to_bf16_hw(lp[2]) | (f32_to_bf16_hw(lp[3]) << 16);
     }
 #pragma unroll
-    for (int u = 0; u < (DPASS ? 0 : 2); ++u) {
-      const bf16x8_t sf = __builtin_bit_cast(bf16x8_t, make_uint4(dk2[2 * u][0], dk2[2 * u][1], dk2[2 * u + 1][0], dk2[2 * u + 1][1]));
-      const bf16x8_t slf = __builtin_bit_cast(bf16x8_t, make_uint4(dl2[2 * u][0], dl2[2 * u][1], dl2[2 * u + 1][0], dl2[2 * u + 1][1]));
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8_t gf = __builtin_bit_cast(bf16x8_t, make_uint4(gh[2 * u][0], gh[2 * u][1], gh[2 * u + 1][0], gh[2 * u + 1][1]));
+      const bf16x8_t glf = __builtin_bit_cast(bf16x8_t, make_uint4(gl[2 * u][0], gl[2 * u][1], gl[2 * u + 1][0], gl[2 * u + 1][1]));
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(ph[2 * u][0], ph[2 * u][1], ph[2 * u + 1][0], ph[2 * u + 1][1]));
+      const bf16x8_t plf = __builtin_bit_cast(bf16x8_t, make_uint4(pl[2 * u][0], pl[2 * u][1], pl[2 * u + 1][0], pl[2 * u + 1][1]));
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Kt + toff[u][st][0]));
         const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Kt + toff[u][st][1]));
         const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const bf16x8_t kt_ = __builtin_bit_cast(bf16x8_t, w);
-        dq[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt_, sf, dq[st], 0, 0, 0);
-        dq[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt_, slf, dq[st], 0, 0, 0);
+        dq[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt_, gf, dq[st], 0, 0, 0);
+        dq[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt_, glf, dq[st], 0, 0, 0);
+        bq[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt_, pf, bq[st], 0, 0, 0);
+        bq[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt_, plf, bq[st], 0, 0, 0);
       }
     }
     wait_vmcnt<NC>();
@@ -772,11 +784,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
   }
   wait_vmcnt<0>();
 
-  if constexpr (DPASS) {
-    dsum = sum_over_groups(dsum);
-    if (q < p.s && g == 0) *drec = dsum;
-    return;
-  }
+  dsum = sum_over_groups(dsum);  // D for this lane's query
+  if (q < p.s && g == 0) *drec = dsum;
+#pragma unroll
+  for (int st = 0; st < NST; ++st)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dq[st][e] = fmaf(-dsum, bq[st][e], dq[st][e]);  // A - D B
   if (q < p.s) {
     uint16_t* out = static_cast<uint16_t*>(p.dqkv) + ((int64_t)q * p.b + bidx) * ldq + cols.q;
 #pragma unroll
@@ -901,20 +914,20 @@ template <int DP>
 hipError_t launch_bwd_bf16(const AttnBwdParams& p, hipStream_t st) {
   const int nq = (p.s + 63) / 64;
   const unsigned grid = (unsigned)(nq * p.b * p.hl);
-  static const std::string n0 = "attn_bwd_delta_bf16_d" + std::to_string(DP);
   static const std::string n1 = "attn_bwd_dkv_bf16_d" + std::to_string(DP);
   static const std::string n2 = "attn_bwd_dq_bf16_d" + std::to_string(DP);
   const int splits = p.kvpart != nullptr ? p.G : 1;
   // one workgroup per (64 keys, batch, KV group, head split)
   const unsigned grid_kv = (unsigned)(nq * p.b * (p.hl / p.G) * splits);
-  hipError_t e = TP_LAUNCH(n0.c_str(), (attn_bwd_dq_bf16_kernel<DP, true>), dim3(grid), dim3(256), 0, st, p);
+  // dQ first: it also writes each query's D, which the dK / dV pass reads
+  hipError_t e = TP_LAUNCH(n2.c_str(), (attn_bwd_dq_bf16_kernel<DP>), dim3(grid), dim3(256), 0, st, p);
   if (e == hipSuccess) e = TP_LAUNCH(n1.c_str(), (attn_bwd_dkv_bf16_kernel<DP>), dim3(grid_kv), dim3(256), 0, st, p);
   if (e == hipSuccess && splits > 1) {
     const int64_t n = (int64_t)p.s * p.b * (p.hl / p.G) * (p.d / 2);
     e = TP_LAUNCH("attn_bwd_kv_sum_bf16", attn_bwd_kv_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                   st, p);
   }
-  if (e == hipSuccess) e = TP_LAUNCH(n2.c_str(), (attn_bwd_dq_bf16_kernel<DP, false>), dim3(grid), dim3(256), 0, st, p);
+
   return e;
 }
 
