@@ -100,14 +100,17 @@ class MlpBlock:
 
 
     # -- the same step with the reductions on a second stream (communication / computation overlap)
-    def forward_pipelined(self, X: torch.Tensor, out_rs: torch.Tensor, chunks: int = 2, comm=None, stream=None):
+    def forward_pipelined(self, X: torch.Tensor, out_rs: torch.Tensor, chunks: int = 2, comm=None, stream=None,
+                          slices: Optional[torch.Tensor] = None):
         """Forward with the g-bar reduce-scatter pipelined along s: the block is run on `chunks` consecutive row
         ranges of the sequence (the MLP is row-wise, so each range is an exact forward of its rows), and as soon
         as every rank has finished range c, the reduce-scatter of the rank slices inside range c runs on `comm`
         while range c + 1 computes ("Tensor Parallelism (TP) 与 Sequence Parallelism (SP)" §5: SP's g is a
         reduce-scatter; the pages' tp_comm_overlap pipelines it with the GEMMs).  out_rs [t, s/t, b, h] receives
-        every rank's slice, bit for bit what reduce_forward(sp=True) gives.  Returns the event that marks the last
-        reduction on `comm`."""
+        every rank's slice, bit for bit what reduce_forward(sp=True) gives.  With `slices` ([t, s/t, b, h], the
+        sequence-parallel input) the all-gather into X is pipelined too: range c's slices are gathered on `comm`
+        (the SP f: an all-gather along s) and range c's GEMMs start when they have landed, while range c + 1's
+        slices are still being gathered.  Returns the event that marks the last reduction on `comm`."""
         L, t = self.L, self.t
         if self.t % chunks != 0 or self.s % chunks != 0:
             raise ValueError("chunks must divide t (and s)")
@@ -117,8 +120,23 @@ class MlpBlock:
         dims_c = L.make_dims(s=self.s // chunks, b=self.b, h=self.h, ffn=self.ffn, t=t)
         per = t // chunks
         Xr = X.reshape(self.M, self.h)  # [s, b, h] as s-major rows
+        gathered = []
+        if slices is not None:
+            # every range's gather is queued on comm up front; range c's GEMMs wait for range c's event only
+            dims_g = L.make_dims(s=self.s // chunks, b=self.b, h=self.h, t=per)
+            src = slices.reshape(t, -1)
+            start = torch.cuda.Event()
+            start.record(cur)  # X may still be read by earlier work on the compute stream
+            comm.wait_event(start)
+            for c in range(chunks):
+                L.tp_gather_dim0(dims_g, src[c * per:(c + 1) * per], Xr[c * rows:(c + 1) * rows], comm)
+                ev = torch.cuda.Event()
+                ev.record(comm)
+                gathered.append(ev)
         for c in range(chunks):
             sl = slice(c * rows, (c + 1) * rows)
+            if gathered:
+                cur.wait_event(gathered[c])
             for r in range(t):
                 L.tp_mlp_fwd(dims_c, r, self.act, Xr[sl], self.A[r], None if self.a is None else self.a[r], self.B[r],
                              self.U[r][sl], self.Y[r][sl], self.Zp[r][sl], cur)

@@ -111,3 +111,35 @@ def test_phase_split_equals_full_backward(L):
         torch.cuda.synchronize()
         for x, y in zip(*outs):
             assert torch.equal(x, y)
+
+
+def test_pipelined_gather_equals_serial_gather(L):
+    """The SP entry all-gather pipelined with the forward (range c's slices gathered on the second stream while
+    range c - 1 computes) gives the serial gather + forward + reduce-scatter bit for bit."""
+    from attention_block_columnparallel_amd.block import MlpBlock
+
+    w = TI.Workload("ovl_ag", "mlp", s=64, b=3, h=136, ffn=4 * 104, t=4, act="gelu", dtype="bf16")
+    say(f"pipelined all-gather + forward (s={w.s} b={w.b} h={w.h} ffn={w.ffn} t={w.t}, 2 and 4 ranges)")
+    inp = TI.mlp_inputs(w, with_bias=True, seed=8)
+    blk = MlpBlock(w.s, w.b, w.h, w.ffn, w.t, w.act, dev(inp["A"], "bf16"), dev(inp["B"], "bf16"),
+                   dev(inp["a"], "bf16"), dev(inp["c"], "bf16"))
+    slices = dev(np.stack([O.split_dim0(inp["X"], w.t, r) for r in range(w.t)]), "bf16")
+    shape_rs = (w.t, w.s // w.t, w.b, w.h)
+    X = empty((w.s, w.b, w.h), "bf16")
+    L.tp_gather_dim0(blk.dims, slices, X)
+    Zs = empty(shape_rs, "bf16")
+    blk.forward_ranks(X)
+    blk.reduce_forward(sp=True, out=Zs)
+    torch.cuda.synchronize()
+    ref_Z, ref_U = _bits(Zs), _bits(blk.U)
+    assert torch.equal(_bits(X), _bits(dev(inp["X"], "bf16")))
+    for chunks in (2, 4):
+        X2 = torch.full((w.s, w.b, w.h), float("nan"), dtype=torch.bfloat16, device="cuda")
+        Zo = torch.full(shape_rs, float("nan"), dtype=torch.bfloat16, device="cuda")
+        blk.U.fill_(float("nan"))
+        done = blk.forward_pipelined(X2, Zo, chunks=chunks, slices=slices)
+        torch.cuda.current_stream().wait_event(done)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(X2), _bits(X)), chunks
+        assert torch.equal(_bits(Zo), ref_Z), chunks
+        assert torch.equal(_bits(blk.U), ref_U), chunks
