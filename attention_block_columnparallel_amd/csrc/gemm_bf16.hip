@@ -366,6 +366,8 @@ __device__ __forceinline__ void mfma_rows_t(f32x4_t (&acc)[TM][TN], const bf16x8
 struct GemmPair {
   GemmParams g[2];
   int tiles0, tiles1;
+  int ksplit;   // split-K launches: workgroup u takes tile u / ksplit and K range u % ksplit
+  float* part;  // split-K launches: fp32 partial tiles [ksplit][M][N]
 };
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -607,7 +609,7 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
 // run 3 k-tiles ahead of the MFMAs.  The MFMAs take the B fragment first, so each 16 x 16 accumulator block is the
 // transposed product: lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3 of the wave's sub-tile,
 // which the epilogue stages through LDS with one 16-byte write per block.
-template <bool AK, bool BKM, int EPI>
+template <bool AK, bool BKM, int EPI, bool SPLIT = false>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 8, TN = 8;
   constexpr int NSTAGE = 4;  // (a fifth 32 KB stage, filling the 160 KB LDS, measured slower)
@@ -633,6 +635,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
     const int xcd = bid % 8, idx = bid / 8;
     bid = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
   }
+  int split = 0;
+  if constexpr (SPLIT) {
+    split = bid % pp.ksplit;
+    bid /= pp.ksplit;
+  }
   const int which = bid < pp.tiles0 ? 0 : 1;
   const GemmParams& p = pp.g[which];
   if (which) bid -= pp.tiles0;
@@ -650,10 +657,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   Dma<BKM, SWIG> db;
   da.init(p.lda, tile_m, p.M, p.fhalf, wave, lane);
   db.init(p.ldb, tile_n, p.N, p.fhalf, wave, lane);
-  const uint16_t* const Ab = static_cast<const uint16_t*>(p.A);
-  const uint16_t* const Bb = static_cast<const uint16_t*>(p.B);
   const int64_t lda = p.lda, ldb = p.ldb;  // held in registers: no argument loads inside the K loop
-  const int nk = p.K / BK2;                // even, > D
+  // K range: all of K, or split `split` of pp.ksplit near-equal runs of 64-deep pairs of k-tiles
+  int kp0 = 0, kp1 = p.K / (2 * BK2);
+  if constexpr (SPLIT) {
+    const int np = kp1, base = np / pp.ksplit, rem = np % pp.ksplit;
+    kp0 = split * base + min(split, rem);
+    kp1 = kp0 + base + (split < rem ? 1 : 0);
+  }
+  const int64_t k0 = (int64_t)kp0 * 2 * BK2;
+  const uint16_t* const Ab = static_cast<const uint16_t*>(p.A) + (AK ? k0 : k0 * lda);
+  const uint16_t* const Bb = static_cast<const uint16_t*>(p.B) + (BKM ? k0 : k0 * ldb);
+  const int nk = (kp1 - kp0) * 2;  // even, > D
 
   const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
   auto stage_a = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B); };
@@ -761,6 +776,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
 #undef TP_GEMM_STEP
   wait_vmcnt0();
 
+  // (a run-time test on purpose: with the LDS epilogue below still compiled in, the kernel keeps the plain kernel's
+  // register allocation; as a compile-time branch the compiler spills around the partial-tile stores)
+  if (SPLIT && pp.ksplit > 1) {
+    // fp32 partial tile [split][M][N], straight from the accumulators: lane l holds row 16 tm + (l & 15) and the 4
+    // columns 16 tn + 4 (l >> 4) .. + 3 of the wave's sub-tile (N % 8 == 0: a 4-column group is in or out)
+    const int r0 = tile_m * BM + wm * WM + (lane & 15), c0 = tile_n * BN + wn * WN + 4 * (lane >> 4);
+    const float* const part = pp.part + (int64_t)split * p.M * p.N;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const int r = r0 + 16 * tm;
+      if (r < p.M) {
+        float* const row = const_cast<float*>(part) + (int64_t)r * p.N;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int c = c0 + 16 * tn;
+          if (c < p.N) *reinterpret_cast<f32x4_t*>(row + c) = acc[tm][tn];
+        }
+      }
+    }
+    return;
+  }
+
   // ---- epilogue, staged through LDS one 16-row chunk at a time: each wave writes the fp32 accumulators of its
   // rows 16 tm .. 16 tm + 15 (all 128 of its columns) to a padded buffer of its own, one 16-byte write per block,
   // then walks the chunk row by row with consecutive lanes on consecutive column pairs, so the math runs in a
@@ -816,6 +853,7 @@ constexpr Cfg kCfgs[] = {
     {64, 64, 2, 2, 0.25f},
 };
 constexpr int kNumCUs = 256;
+constexpr int kNumCUsBig = 256;  // workgroups of the large-tile kernel resident at once (one per CU)
 const char* const kEpiNames[] = {"store", "bias", "bias_act", "swiglu_fwd", "act_bwd", "swiglu_bwd"};
 
 int choose_cfg(int M, int ntiles_cols_of_bn256, int N, bool swig, int fhalf) {
@@ -864,6 +902,8 @@ hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st
   pp.g[1] = p1 ? *p1 : p0;
   pp.tiles0 = big_tiles(p0, EPI == EPI_SWIGLU_FWD);
   pp.tiles1 = p1 ? big_tiles(*p1, EPI == EPI_SWIGLU_FWD) : 0;
+  pp.ksplit = 1;
+  pp.part = nullptr;
   const int total = pp.tiles0 + pp.tiles1;
 
   static const std::string name = std::string("gemm_bf16_big_") + (AK ? "K" : "M") + (BKM ? "K" : "M") + "_" +
@@ -872,6 +912,74 @@ hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st
                                    kEpiNames[EPI];
   return TP_LAUNCH(p1 ? name2.c_str() : name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI>), dim3((unsigned)total),
                    dim3(256), 0, st, pp);
+}
+
+// Sum of the ksplit fp32 partial tiles in split order, then the epilogue (store, or bias + store), one rounding.
+// One thread per 4 consecutive columns.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(GemmParams p, const float* __restrict__ part, int ksplit) {
+  const int64_t nq = (int64_t)p.M * (p.N / 4);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nq) return;
+  const int64_t m = i / (p.N / 4);
+  const int c = (int)(i - m * (p.N / 4)) * 4;
+  const int64_t stride = (int64_t)p.M * p.N;
+  const float* src = part + m * p.N + c;
+  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(src);
+  for (int sp = 1; sp < ksplit; ++sp) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + sp * stride);
+    acc[0] += v[0];
+    acc[1] += v[1];
+    acc[2] += v[2];
+    acc[3] += v[3];
+  }
+  if constexpr (EPI == EPI_BIAS) {
+    if (p.bias != nullptr) {
+      const float2 b01 = ldg_bf16x2(p.bias, c), b23 = ldg_bf16x2(p.bias, c + 2);
+      acc[0] += b01.x;
+      acc[1] += b01.y;
+      acc[2] += b23.x;
+      acc[3] += b23.y;
+    }
+  }
+  uint2 w;
+  w.x = pack_bf16x2(acc[0], acc[1]);
+  w.y = pack_bf16x2(acc[2], acc[3]);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + m * p.ldc + c) = w;
+}
+
+// Split-K for a single GEMM whose 256 x 256 tiles fill few CUs: the number of K runs that brings tiles * runs
+// closest to one full round (at most 8 runs, each at least two 64-deep pairs of k-tiles, the partials fitting the
+// scratch); 1 when splitting does not pay.
+int choose_ksplit(const GemmParams& p, int tiles, int64_t part_floats) {
+  if (tiles * 4 >= kNumCUsBig * 3) return 1;
+  const int pairs = p.K / (2 * BK2);
+  int best = 1;
+  for (int sp = 2; sp <= 8; ++sp) {
+    if (tiles * sp > kNumCUsBig) break;
+    if (pairs / sp < 2) break;
+    if ((int64_t)sp * p.M * p.N > part_floats) break;
+    best = sp;
+  }
+  return best;
+}
+
+template <bool AK, bool BKM, int EPI>
+hipError_t launch_big_split(const GemmParams& p, int ksplit, float* part, hipStream_t st) {
+  GemmPair pp;
+  pp.g[0] = p;
+  pp.g[1] = p;
+  pp.tiles0 = big_tiles(p, false);
+  pp.tiles1 = 0;
+  pp.ksplit = ksplit;
+  pp.part = part;
+  static const std::string name = std::string("gemm_bf16_big_splitk_") + (AK ? "K" : "M") + (BKM ? "K" : "M");
+  hipError_t e = TP_LAUNCH(name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI_STORE, true>),
+                           dim3((unsigned)(pp.tiles0 * ksplit)), dim3(256), 0, st, pp);
+  if (e != hipSuccess) return e;
+  const int64_t nq = (int64_t)p.M * (p.N / 4);
+  return TP_LAUNCH("gemm_bf16_splitk_sum", splitk_sum_kernel<EPI>, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0,
+                   st, p, part, ksplit);
 }
 
 // The large-tile kernel needs an even number of 32-deep k-tiles, more than it keeps in flight (K >= 128), and
@@ -936,6 +1044,22 @@ hipError_t gemm_bf16_wgrad_pair(const GemmParams& p0, const GemmParams& p1, hipS
   hipError_t e = gemm_bf16(p0, false, false, EPI_STORE, st);
   if (e == hipSuccess) e = gemm_bf16(p1, false, false, EPI_STORE, st);
   return e;
+}
+
+hipError_t gemm_bf16_splitk(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, float* part,
+                            int64_t part_floats, hipStream_t st) {
+  if (part != nullptr && p.M > 0 && p.N > 0 && (epi == EPI_STORE || epi == EPI_BIAS) && a_kmajor &&
+      big_fits(p, a_kmajor, b_kmajor)) {
+    const int ks = choose_ksplit(p, big_tiles(p, false), part_floats);
+    if (ks > 1) {
+      if (b_kmajor)
+        return epi == EPI_STORE ? launch_big_split<true, true, EPI_STORE>(p, ks, part, st)
+                                : launch_big_split<true, true, EPI_BIAS>(p, ks, part, st);
+      return epi == EPI_STORE ? launch_big_split<true, false, EPI_STORE>(p, ks, part, st)
+                              : launch_big_split<true, false, EPI_BIAS>(p, ks, part, st);
+    }
+  }
+  return gemm_bf16(p, a_kmajor, b_kmajor, epi, st);
 }
 
 }  // namespace tp

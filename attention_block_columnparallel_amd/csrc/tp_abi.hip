@@ -362,7 +362,8 @@ int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
   go.C = Z_i; go.ldc = h;
   hipError_t e;
   if (dtype == TP_BF16) {
-    e = tp::gemm_bf16(gq, true, false, tp::EPI_BIAS, stream);
+    // Z_i is not written until the projection: it holds the QKV GEMM's split-K partials
+    e = tp::gemm_bf16_splitk(gq, true, false, tp::EPI_BIAS, static_cast<float*>(Z_i), M * h * es / 4, stream);
     if (e == hipSuccess) e = tp::attention_bf16(ap, stream);
     if (e == hipSuccess) e = tp::gemm_bf16(go, true, false, tp::EPI_STORE, stream);
   } else {
@@ -435,7 +436,10 @@ int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
   gx.C = dX_i; gx.ldc = h;
 
   auto gemm = dtype == TP_BF16 ? tp::gemm_bf16 : tp::gemm_f32;
-  hipError_t e = gemm(gd, true, true, tp::EPI_STORE, stream);
+  // dX_i is not written until the last GEMM: it holds the dO GEMM's split-K partials
+  hipError_t e = dtype == TP_BF16 ? tp::gemm_bf16_splitk(gd, true, true, tp::EPI_STORE, static_cast<float*>(dX_i),
+                                                         M * h * es / 4, stream)
+                                  : gemm(gd, true, true, tp::EPI_STORE, stream);
   if (e == hipSuccess) e = tp::attention_bwd(dtype, bp, stream);
   if (e == hipSuccess) {
     if (dtype == TP_BF16) {

@@ -148,6 +148,11 @@ struct GemmParams {
 // Launchers (return hipGetLastError after the launch).
 hipError_t gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, hipStream_t st);
 hipError_t gemm_bf16_wgrad_pair(const GemmParams& p0, const GemmParams& p1, hipStream_t st);
+// gemm_bf16 given fp32 scratch (part_floats elements): a GEMM with too few output tiles to fill the GPU (store or
+// bias epilogue, A K-major) splits K over several workgroups, writes fp32 partial tiles there and sums them in a
+// fixed order with the epilogue; any other GEMM runs as gemm_bf16 and leaves the scratch alone.
+hipError_t gemm_bf16_splitk(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, float* part,
+                            int64_t part_floats, hipStream_t st);
 hipError_t gemm_f32(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, hipStream_t st);
 hipError_t colsum(tp_dtype dt, const void* x, int64_t rows, int64_t cols, void* out, hipStream_t st);
 

@@ -139,7 +139,8 @@ int tp_mlp_bwd_phase(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, 
  *   lse_i = log sum_k exp(S[q, k]) per (b, local head, q), fp32 [b, a/t, s] (nullable)
  *   Z_i   = O_i Wo_i                [s, b, h], a partial sum (no row bias)
  * Wqkv_i [h, n] and Wo_i [(a/t)*d, h] as produced by tp_shard_weights.  bf16 path: d % 8 == 0, d <= 128.
- * fp32 path: d <= 128. */
+ * fp32 path: d <= 128.  The bf16 path may use Z_i as fp32 scratch for the QKV GEMM (split-K partials when that
+ * GEMM has too few output tiles to fill the GPU) before the projection writes it. */
 int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const void* X, const void* Wqkv_i,
                 const void* bqkv_i, const void* Wo_i, void* QKV_i, void* O_i, float* lse_i, void* Z_i,
                 hipStream_t stream);
@@ -161,7 +162,8 @@ int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
  *   dWo_i   = O_i^T dZ                           [(a/t)*d, h]      local weight gradient
  *   dX_i    = dQKV_i Wqkv_i^T                    [s, b, h]         a partial: f sums them over ranks
  * QKV_i, O_i and lse_i (not nullable here) are the forward's outputs for the same inputs and `causal`.  The
- * alignment and head-size rules of tp_attn_fwd apply; outputs and workspaces must not overlap the inputs. */
+ * alignment and head-size rules of tp_attn_fwd apply; outputs and workspaces must not overlap the inputs.  The
+ * bf16 path may use dX_i as fp32 scratch for the dO GEMM (split-K partials) before the last GEMM writes it. */
 int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const void* X, const void* Wqkv_i,
                 const void* Wo_i, const void* QKV_i, const void* O_i, const float* lse_i, const void* dZ, void* dO_ws,
                 float* rec_ws, void* dQKV_i, void* dWqkv_i, void* dbqkv_i, void* dWo_i, void* dX_i,

@@ -100,6 +100,8 @@ CASES = [  # a, g, d, t, dtype, causal
     (8, 4, 96, 2, "bf16", False),    # 2 per group, two groups per rank
     (4, 2, 128, 2, "bf16", True),
     (8, 2, 40, 2, "bf16", True),     # d = 40 in the 64 bucket
+    (16, 8, 32, 8, "bf16", True),    # t = 8: the QKV and dO GEMMs fill one tile, so K is split over workgroups
+    (8, 8, 64, 8, "bf16", False),    # g = a (plain multi-head), t = 8: split-K dO GEMM
     (4, 2, 16, 2, "f32", True),
     (6, 2, 8, 2, "f32", False),
 ]
@@ -135,6 +137,8 @@ def test_gqa_small_ragged(L, a, g, d, t, dtype, causal):
         check_close(Os, O.attention_rows(QKVs, w.s, w.b, hl, d, rows, causal, G=G)["O"], dtype, "O", row_unit=True)
         Wo_i = Wo[r * hl * d:(r + 1) * hl * d, :]
         Wq_i = Wqkv[:, O.qkv_shard_columns(a, d, t, r, g)]
+        qc = O.qkv_shard_columns(a, d, t, r, g)
+        check_close(QKVs, X @ Wq_i + bq[qc], dtype, "QKV")
         check_close(dOs, dZ @ Wo_i.T, dtype, "dO")
         check_close(f64(got["dQKV"]), core_grads_stored(QKVs, dOs, w.s, w.b, hl, G, d, causal), dtype, "dQKV")
         dQs = f64(got["dQKV"])
