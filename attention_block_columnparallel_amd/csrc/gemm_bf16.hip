@@ -366,9 +366,21 @@ __device__ __forceinline__ void mfma_rows_t(f32x4_t (&acc)[TM][TN], const bf16x8
 struct GemmPair {
   GemmParams g[2];
   int tiles0, tiles1;
-  int ksplit;   // split-K launches: workgroup u takes tile u / ksplit and K range u % ksplit
-  float* part;  // split-K launches: fp32 partial tiles [ksplit][M][N]
+  // Split-K launches: the first nfull workgroups take whole tiles 0 .. nfull-1; each later run of ksplit workgroups
+  // takes one of the remaining tiles, one K range each, and writes an fp32 partial tile to part: [ksplit][M][N]
+  // (A K-major: a single GEMM with every tile split), or 256 x 256 blocks [tile - nfull][ksplit] (A M-major: the
+  // tail tiles of a weight-gradient pair).
+  int ksplit, nfull;
+  float* part;
 };
+
+// XCD-aware order over nb workgroups: the hardware deals workgroup i to XCD i % 8; the result gives each XCD a
+// contiguous run of indices (a bijection on 0 .. nb-1).
+__device__ __forceinline__ int xcd_remap(int u, int nb) {
+  const int q = nb / 8, r = nb % 8;
+  const int xcd = u % 8, idx = u / 8;
+  return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -539,6 +551,18 @@ __device__ __forceinline__ float2 ldg_bf16x2(const void* p, int64_t i) {
   return make_float2(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
 }
 
+// One wave's 16 x 128 chunk of fp32 results in LDS (pitch ep_pitch) -> fp32 partial block of 256 x 256 (blk; the
+// tile's first row is m_tile).  Lane l owns columns 2l, 2l+1 of each row.
+__device__ __forceinline__ void partial_chunk(const GemmParams& p, const float* ep, int ep_pitch, int m0, int m_tile,
+                                              int tile_n, int wn, int lane, float* blk) {
+  const int col = tile_n * 256 + wn * 128 + 2 * lane;
+  if (col >= p.N) return;  // N % 8 == 0: a column pair is entirely in or out
+  const int rows = min(16, p.M - m0);
+  float* dst = blk + (int64_t)(m0 - m_tile) * 256 + wn * 128 + 2 * lane;
+  for (int r = 0; r < rows; ++r)
+    *reinterpret_cast<float2*>(dst + r * 256) = make_float2(ep[r * ep_pitch + 2 * lane], ep[r * ep_pitch + 2 * lane + 1]);
+}
+
 // One wave's 16 x 128 chunk of fp32 results in LDS (pitch ep_pitch) -> epilogue -> HBM.  Plain epilogues: lane l
 // owns columns 2l, 2l+1 of each row.  SwiGLU forward: the wave's 128 columns are 64 gate then 64 up columns of the
 // same 64 outputs j; lane l owns output j = l.
@@ -629,17 +653,19 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   // ---- problem and tile: XCD-aware remap over the whole launch (the hardware deals workgroup i to XCD i % 8;
   // each XCD gets a contiguous run of tiles), then split between the two problems of a pair
   int bid = blockIdx.x;
-  {
-    const int nb = gridDim.x;
-    const int q = nb / 8, r = nb % 8;
-    const int xcd = bid % 8, idx = bid / 8;
-    bid = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-  }
-  int split = 0;
+  int split = -1;  // -1: the whole K range
   if constexpr (SPLIT) {
-    split = bid % pp.ksplit;
-    bid /= pp.ksplit;
+    if (bid >= pp.nfull) {  // nfull is a multiple of 8, so each range starts on XCD 0
+      const int v = xcd_remap(bid - pp.nfull, (int)gridDim.x - pp.nfull);
+      split = v % pp.ksplit;
+      bid = pp.nfull + v / pp.ksplit;
+    } else {
+      bid = xcd_remap(bid, pp.nfull);
+    }
+  } else {
+    bid = xcd_remap(bid, (int)gridDim.x);
   }
+  const int tile_id = bid;
   const int which = bid < pp.tiles0 ? 0 : 1;
   const GemmParams& p = pp.g[which];
   if (which) bid -= pp.tiles0;
@@ -660,7 +686,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   const int64_t lda = p.lda, ldb = p.ldb;  // held in registers: no argument loads inside the K loop
   // K range: all of K, or split `split` of pp.ksplit near-equal runs of 64-deep pairs of k-tiles
   int kp0 = 0, kp1 = p.K / (2 * BK2);
-  if constexpr (SPLIT) {
+  if (SPLIT && split >= 0) {
     const int np = kp1, base = np / pp.ksplit, rem = np % pp.ksplit;
     kp0 = split * base + min(split, rem);
     kp1 = kp0 + base + (split < rem ? 1 : 0);
@@ -778,7 +804,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
 
   // (a run-time test on purpose: with the LDS epilogue below still compiled in, the kernel keeps the plain kernel's
   // register allocation; as a compile-time branch the compiler spills around the partial-tile stores)
-  if (SPLIT && pp.ksplit > 1) {
+  if (SPLIT && AK && split >= 0) {
     // fp32 partial tile [split][M][N], straight from the accumulators: lane l holds row 16 tm + (l & 15) and the 4
     // columns 16 tn + 4 (l >> 4) .. + 3 of the wave's sub-tile (N % 8 == 0: a 4-column group is in or out)
     const int r0 = tile_m * BM + wm * WM + (lane & 15), c0 = tile_n * BN + wn * WN + 4 * (lane >> 4);
@@ -830,7 +856,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    epilogue_chunk<EPI>(p, ep, EP, row0 + tm * 16, tile_n, wn, lane, ax);
+    if (SPLIT && !AK && split >= 0) {
+      // a weight-gradient pair's tail tile: the fp32 partial goes to its 256 x 256 block (the direct stores of the
+      // K-major case above cost this layout some 90 registers)
+      float* const blk = pp.part + ((int64_t)(tile_id - pp.nfull) * pp.ksplit + split) * (BM * BN);
+      partial_chunk(p, ep, EP, row0 + tm * 16, tile_m * BM, tile_n, wn, lane, blk);
+    } else {
+      epilogue_chunk<EPI>(p, ep, EP, row0 + tm * 16, tile_n, wn, lane, ax);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -903,6 +936,7 @@ hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st
   pp.tiles0 = big_tiles(p0, EPI == EPI_SWIGLU_FWD);
   pp.tiles1 = p1 ? big_tiles(*p1, EPI == EPI_SWIGLU_FWD) : 0;
   pp.ksplit = 1;
+  pp.nfull = 0;
   pp.part = nullptr;
   const int total = pp.tiles0 + pp.tiles1;
 
@@ -972,6 +1006,7 @@ hipError_t launch_big_split(const GemmParams& p, int ksplit, float* part, hipStr
   pp.tiles0 = big_tiles(p, false);
   pp.tiles1 = 0;
   pp.ksplit = ksplit;
+  pp.nfull = 0;
   pp.part = part;
   static const std::string name = std::string("gemm_bf16_big_splitk_") + (AK ? "K" : "M") + (BKM ? "K" : "M");
   hipError_t e = TP_LAUNCH(name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI_STORE, true>),
@@ -980,6 +1015,42 @@ hipError_t launch_big_split(const GemmParams& p, int ksplit, float* part, hipStr
   const int64_t nq = (int64_t)p.M * (p.N / 4);
   return TP_LAUNCH("gemm_bf16_splitk_sum", splitk_sum_kernel<EPI>, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0,
                    st, p, part, ksplit);
+}
+
+// Sum of the tail tiles' fp32 partial blocks (tile-block layout) in split order, stored as bf16 into the problem
+// each tile belongs to.  One thread per 4 consecutive columns of a 256 x 256 block; the tile decode is the large-tile
+// kernel's (row-tile groups of 8 for a pair).
+__global__ __launch_bounds__(256) void splitk_tail_sum_kernel(GemmPair pp, int ntail) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)ntail * (256 * 64)) return;
+  const int j = (int)(i >> 14);  // tail tile
+  const int e = (int)(i & 16383) * 4;
+  const int rl = e >> 8, cl = e & 255;
+  int u = pp.nfull + j;
+  const int which = u < pp.tiles0 ? 0 : 1;
+  const GemmParams& p = pp.g[which];
+  if (which) u -= pp.tiles0;
+  const int nbm = (p.M + 255) / 256, nbn = (p.N + 255) / 256;
+  const int gm = pp.tiles1 > 0 ? 8 : 4;
+  const int first_m = (u / (gm * nbn)) * gm;
+  const int gsz = min(nbm - first_m, gm);
+  const int tile_m = first_m + (u % (gm * nbn)) % gsz;
+  const int tile_n = (u % (gm * nbn)) / gsz;
+  const int r = tile_m * 256 + rl, c = tile_n * 256 + cl;
+  if (r >= p.M || c >= p.N) return;
+  const float* src = pp.part + (int64_t)j * pp.ksplit * 65536 + rl * 256 + cl;
+  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(src);
+  for (int sp = 1; sp < pp.ksplit; ++sp) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + (int64_t)sp * 65536);
+    acc[0] += v[0];
+    acc[1] += v[1];
+    acc[2] += v[2];
+    acc[3] += v[3];
+  }
+  uint2 w;
+  w.x = pack_bf16x2(acc[0], acc[1]);
+  w.y = pack_bf16x2(acc[2], acc[3]);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + (int64_t)r * p.ldc + c) = w;
 }
 
 // The large-tile kernel needs an even number of 32-deep k-tiles, more than it keeps in flight (K >= 128), and
@@ -1044,6 +1115,42 @@ hipError_t gemm_bf16_wgrad_pair(const GemmParams& p0, const GemmParams& p1, hipS
   hipError_t e = gemm_bf16(p0, false, false, EPI_STORE, st);
   if (e == hipSuccess) e = gemm_bf16(p1, false, false, EPI_STORE, st);
   return e;
+}
+
+// The pair's tile count past its last full round of one tile per CU (the tail): when the tail fills under three
+// quarters of the CUs and the scratch allows, the tail tiles split K over ksplit workgroups each.
+hipError_t gemm_bf16_wgrad_pair_splitk(const GemmParams& p0, const GemmParams& p1, float* part, int64_t part_floats,
+                                       hipStream_t st) {
+  if (part != nullptr && p0.M > 0 && p0.N > 0 && p1.M > 0 && p1.N > 0 && p0.K == p1.K && big_fits(p0, false, false) &&
+      big_fits(p1, false, false)) {
+    const int t = big_tiles(p0, false) + big_tiles(p1, false);
+    const int ntail = t % kNumCUsBig;
+    if (t > kNumCUsBig && ntail > 0 && ntail * 4 < kNumCUsBig * 3) {
+      const int pairs = p0.K / (2 * BK2);
+      int ks = 1;
+      for (int sp = 2; sp <= 8; ++sp) {
+        if (ntail * sp > kNumCUsBig || pairs / sp < 2 || (int64_t)ntail * sp * 65536 > part_floats) break;
+        ks = sp;
+      }
+      if (ks > 1) {
+        GemmPair pp;
+        pp.g[0] = p0;
+        pp.g[1] = p1;
+        pp.tiles0 = big_tiles(p0, false);
+        pp.tiles1 = big_tiles(p1, false);
+        pp.ksplit = ks;
+        pp.nfull = t - ntail;
+        pp.part = part;
+        hipError_t e = TP_LAUNCH("gemm_bf16_big_pair_splitk_MM", (gemm_bf16_big_kernel<false, false, EPI_STORE, true>),
+                                 dim3((unsigned)(pp.nfull + ntail * ks)), dim3(256), 0, st, pp);
+        if (e != hipSuccess) return e;
+        const int64_t nq = (int64_t)ntail * 16384;
+        return TP_LAUNCH("gemm_bf16_splitk_tail_sum", splitk_tail_sum_kernel, dim3((unsigned)((nq + 255) / 256)),
+                         dim3(256), 0, st, pp, ntail);
+      }
+    }
+  }
+  return gemm_bf16_wgrad_pair(p0, p1, st);
 }
 
 hipError_t gemm_bf16_splitk(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, float* part,

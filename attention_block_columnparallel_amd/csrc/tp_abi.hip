@@ -442,8 +442,8 @@ int tp_attn_bwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
                                   : gemm(gd, true, true, tp::EPI_STORE, stream);
   if (e == hipSuccess) e = tp::attention_bwd(dtype, bp, stream);
   if (e == hipSuccess) {
-    if (dtype == TP_BF16) {
-      e = tp::gemm_bf16_wgrad_pair(gwo, gwq, stream);
+    if (dtype == TP_BF16) {  // dX_i again lends its memory: split-K partials of the pair's tail tiles
+      e = tp::gemm_bf16_wgrad_pair_splitk(gwo, gwq, static_cast<float*>(dX_i), M * h * es / 4, stream);
     } else {
       e = gemm(gwo, false, false, tp::EPI_STORE, stream);
       if (e == hipSuccess) e = gemm(gwq, false, false, tp::EPI_STORE, stream);

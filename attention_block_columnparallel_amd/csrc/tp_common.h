@@ -153,6 +153,11 @@ hipError_t gemm_bf16_wgrad_pair(const GemmParams& p0, const GemmParams& p1, hipS
 // fixed order with the epilogue; any other GEMM runs as gemm_bf16 and leaves the scratch alone.
 hipError_t gemm_bf16_splitk(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, float* part,
                             int64_t part_floats, hipStream_t st);
+// gemm_bf16_wgrad_pair given fp32 scratch: when the pair's tiles overrun whole rounds of one tile per CU by a
+// short tail, the tail tiles split K over several workgroups (fp32 partial blocks of 256 x 256 in the scratch,
+// then a fixed-order sum); otherwise as gemm_bf16_wgrad_pair.
+hipError_t gemm_bf16_wgrad_pair_splitk(const GemmParams& p0, const GemmParams& p1, float* part, int64_t part_floats,
+                                       hipStream_t st);
 hipError_t gemm_f32(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, hipStream_t st);
 hipError_t colsum(tp_dtype dt, const void* x, int64_t rows, int64_t cols, void* out, hipStream_t st);
 

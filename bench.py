@@ -107,7 +107,7 @@ def attention_block_measure(L, steps: int, warmup: int, w=None) -> dict:
     for _ in range(warmup):
         blk.forward(X, sp=True)
     torch.cuda.synchronize()
-    timer = L.LaunchTimer(capacity=steps * (3 * w.t + 1) + 8)  # forward
+    timer = L.LaunchTimer(capacity=steps * (4 * w.t + 1) + 8)  # forward
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     with timer:
@@ -119,15 +119,24 @@ def attention_block_measure(L, steps: int, warmup: int, w=None) -> dict:
     nqkv = blk.nqkv  # the rank's QKV columns: (a/t + 2 g/t) d
     fl = {"qkv": 2.0 * M * w.h * nqkv, "attention": 4.0 * w.d * (w.s * (w.s + 1) / 2) * w.b * hl,
           "proj": 2.0 * M * hl * w.d * w.h}
-    # launch order per step: for each rank QKV GEMM, attention, output projection; then the reduce-scatter
-    res = timer.results()
-    per_step = 3 * w.t + 1
+    # launch order per step: for each rank the QKV GEMM (a split-K GEMM and its partial sum when the GEMM fills few
+    # CUs), attention, the output projection; then the reduce-scatter
     roles = {}
-    for i, (name, ms) in enumerate(res):
-        j = i % per_step
-        role = "reduce_scatter" if j == 3 * w.t else ("qkv", "attention", "proj")[j % 3]
-        r = roles.setdefault(role, {"kernel": name, "ms": []})
-        r["ms"].append(ms)
+    seq = []
+    for name, ms in timer.results():
+        if name.startswith("reduce"):
+            role = "reduce_scatter"
+        elif name.startswith("attn_fwd"):
+            role = "attention"
+        elif name == "gemm_bf16_splitk_sum":
+            role = seq[-1]
+        else:
+            role = "proj" if seq and seq[-1] == "attention" else "qkv"
+        seq.append(role)
+        r = roles.setdefault(role, {"kernels": {}, "ms": 0.0})
+        r["ms"] += ms
+        r["kernels"][name] = r["kernels"].get(name, 0.0) + ms
+
     def block_ms(fn):  # the block's own time, without per-launch events
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -138,22 +147,29 @@ def attention_block_measure(L, steps: int, warmup: int, w=None) -> dict:
         torch.cuda.synchronize()
         return a0.elapsed_time(a1) / steps
 
+    def role_fields(roles, flops, nbytes_rs):
+        out = {}
+        for role, r in roles.items():
+            per = 1 if role == "reduce_scatter" else w.t
+            us = 1e3 * r["ms"] / steps / per
+            k = {"us_per_rank" if per > 1 else "us_per_step": round(us, 2),
+                 "kernels_us_per_rank" if per > 1 else "kernels_us_per_step":
+                     {n: round(1e3 * v / steps / per, 2) for n, v in r["kernels"].items()}}
+            if role in flops:
+                k["tflops"] = round(flops[role] / (us * 1e-6) / 1e12, 1)
+                k["frac_bf16_peak"] = round(flops[role] / (us * 1e-6) / PEAK_BF16_FLOPS, 4)
+            else:
+                k["bytes"] = nbytes_rs
+                k["gbps"] = round(nbytes_rs / (us * 1e-6) / 1e9, 1)
+            out[role] = k
+        return out
+
     out = {"workload": w.name, "ms_per_step": round(block_ms(lambda: blk.forward(X, sp=True)), 4),
-           "ms_per_step_with_launch_events": round(e0.elapsed_time(e1) / steps, 4), "kernels": {}}
+           "ms_per_step_with_launch_events": round(e0.elapsed_time(e1) / steps, 4)}
     total_fl = w.t * sum(fl.values())
     out["tflops_block"] = round(total_fl / (out["ms_per_step"] * 1e-3) / 1e12, 1)
-    for role, r in roles.items():
-        avg = sum(r["ms"]) / len(r["ms"])
-        k = {"kernel": r["kernel"], "launches_per_step": len(r["ms"]) // steps, "avg_us": round(1e3 * avg, 2)}
-        if role in fl:
-            k["flops_per_launch"] = fl[role]
-            k["tflops"] = round(fl[role] / (avg * 1e-3) / 1e12, 1)
-            k["frac_bf16_peak"] = round(fl[role] / (avg * 1e-3) / PEAK_BF16_FLOPS, 4)
-        else:
-            nbytes = (w.t + 1) * M * w.h * 2
-            k["bytes_per_launch"] = nbytes
-            k["gbps"] = round(nbytes / (avg * 1e-3) / 1e9, 1)
-        out["kernels"][role] = k
+    rs_bytes = (w.t + 1) * M * w.h * 2
+    out["roles"] = role_fields(roles, fl, rs_bytes)
     # backward: every rank's tp_attn_bwd, then the f reduction of the dX partials (dim-0 reduce-scatter)
     dZ = dev(inp["dZ"])
     for _ in range(warmup):
@@ -179,24 +195,18 @@ def attention_block_measure(L, steps: int, warmup: int, w=None) -> dict:
             role = "attention_core_bwd"
         elif "_pair_" in name or name.endswith("MM_store"):
             role = "wgrad_pair"
-        else:  # the two data-gradient GEMMs of a rank: dO first, dX last
-            role = "dO_gemm" if not seq or seq[-1] in ("dX_gemm", "reduce_scatter") else "dX_gemm"
+        elif name == "gemm_bf16_splitk_sum":
+            role = seq[-1]
+        else:  # the two data-gradient GEMMs of a rank: dO first, dX after the weight gradients
+            role = "dX_gemm" if seq and seq[-1] == "wgrad_pair" else "dO_gemm"
         seq.append(role)
         r = roles.setdefault(role, {"kernels": {}, "ms": 0.0})
         r["ms"] += ms
         r["kernels"][name] = r["kernels"].get(name, 0.0) + ms
     bwd = {"ms_per_step": round(block_ms(lambda: blk.backward(X, dZ, sp=True)), 4),
-           "ms_per_step_with_launch_events": round(e0.elapsed_time(e1) / steps, 4), "roles": {}}
+           "ms_per_step_with_launch_events": round(e0.elapsed_time(e1) / steps, 4)}
     bwd["tflops_block"] = round(w.t * sum(bfl.values()) / (bwd["ms_per_step"] * 1e-3) / 1e12, 1)
-    for role, r in roles.items():
-        per_rank_us = 1e3 * r["ms"] / steps / (1 if role == "reduce_scatter" else w.t)
-        k = {"us_per_rank" if role != "reduce_scatter" else "us_per_step": round(per_rank_us, 2),
-             "kernels_us_per_rank": {n: round(1e3 * v / steps / (1 if role == "reduce_scatter" else w.t), 2)
-                                    for n, v in r["kernels"].items()}}
-        if role in bfl:
-            k["tflops"] = round(bfl[role] / (per_rank_us * 1e-6) / 1e12, 1)
-            k["frac_bf16_peak"] = round(bfl[role] / (per_rank_us * 1e-6) / PEAK_BF16_FLOPS, 4)
-        bwd["roles"][role] = k
+    bwd["roles"] = role_fields(roles, bfl, rs_bytes)
     out["backward"] = bwd
     del blk, X, dZ
     return out

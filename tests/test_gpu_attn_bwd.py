@@ -4,8 +4,8 @@
   with a QKV bias: dQKV_i, dWqkv_i, dbqkv_i, dWo_i and dX_i of every rank against the oracle's shard backward on
   the same stored inputs;
 * the 22B-width workload at full size for one rank (s = 4096, 8 local heads of 96, causal): the core gradients of
-  two heads in full against the oracle's core backward fed the QKV_i and dO the library stored (bf16), and sampled
-  rows of dX_i and sampled columns of the weight gradients against the oracle on the library's stored dQKV_i.
+  two heads in full against the oracle's core backward fed the QKV_i and dO the library stored (bf16), sampled
+  rows of dX_i and the weight gradients in full against the oracle on the library's stored dQKV_i.
 
 The bf16 path stores QKV_i, O_i and dO in bf16 and feeds P and dS to the matrix cores in bf16, so the exact fp64
 chain from X differs from it by storage rounding; as in the forward tests, the relative Frobenius bound is taken
@@ -107,7 +107,7 @@ def test_attention_backward_small_ragged(L, dtype, d, causal):
 def test_attention_backward_full_size_one_rank_sampled(L):
     w = TI.ATTN_22B
     r = 5
-    say("attention backward h=6144 a=64 d=96 s=4096 t=8 rank 5 (two heads in full, sampled rows / columns)")
+    say("attention backward h=6144 a=64 d=96 s=4096 t=8 rank 5 (two heads in full, sampled rows, full weight gradients)")
     inp = TI.attn_inputs(w, seed=0)
     got = run_rank(L, w, inp, r, "bf16", False, True)
     hl, d = w.a // w.t, w.d
@@ -128,7 +128,6 @@ def test_attention_backward_full_size_one_rank_sampled(L):
         for n, name in enumerate(("dQ", "dK", "dV")):
             check_close(dQs[:, base + n * d:base + (n + 1) * d], g[n], "bf16", f"{name} head {jj}")
     check_close(f64(got["dX"])[rows], dQs[rows] @ Wq_i.T, "bf16", "dX rows")
-    cols = np.sort(rng.choice(3 * hl * d, size=48, replace=False))
-    check_close(f64(got["dWqkv"])[:, cols], X.T @ dQs[:, cols], "bf16", "dWqkv columns")
-    cols = np.sort(rng.choice(w.h, size=48, replace=False))
-    check_close(f64(got["dWo"])[:, cols], Os.T @ dZ[:, cols], "bf16", "dWo columns")
+    # the weight gradients in full (the pair's tail tiles split K over workgroups)
+    check_close(f64(got["dWqkv"]), X.T @ dQs, "bf16", "dWqkv")
+    check_close(f64(got["dWo"]), Os.T @ dZ, "bf16", "dWo")
