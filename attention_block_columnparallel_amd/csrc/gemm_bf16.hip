@@ -571,6 +571,40 @@ __device__ __forceinline__ float2 lds_bf16x2(const uint16_t* ax, int i) {
   return make_float2(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
 }
 
+// The plain epilogues' rows of one chunk: lane l owns columns col, col + 1.  The activation is a template argument,
+// picked once per chunk: with the choice made per element, each of the kernel's 8 unrolled chunks carried the code
+// of every activation, and since a tile runs its epilogue once, that code ran mostly from instruction-cache misses
+// (the GeLU epilogues took 25-30 us longer per launch at h=4096, ffn/t=2048).  The row loop stays rolled for the
+// same reason.
+template <int EPI, int ACT>
+__device__ __forceinline__ void chunk_rows(const GemmParams& p, const float* ep, int ep_pitch, int m0, int col, int lane,
+                                           const uint16_t* ax, float b0, float b1, int rows) {
+  auto row = [&](int r) {
+    const float v0 = ep[r * ep_pitch + 2 * lane], v1 = ep[r * ep_pitch + 2 * lane + 1];
+    const int64_t m = m0 + r;
+    if constexpr (EPI == EPI_STORE) {
+      stg_bf16x2(p.C, m * p.ldc + col, v0, v1);
+    } else if constexpr (EPI == EPI_BIAS) {
+      stg_bf16x2(p.C, m * p.ldc + col, v0 + b0, v1 + b1);
+    } else if constexpr (EPI == EPI_BIAS_ACT) {
+      const float u0 = v0 + b0, u1 = v1 + b1;
+      stg_bf16x2(p.C, m * p.ldc + col, u0, u1);
+      stg_bf16x2(p.C2, m * p.ldc2 + col, act_apply(ACT, u0), act_apply(ACT, u1));
+    } else if constexpr (EPI == EPI_ACT_BWD) {
+      const float2 u = lds_bf16x2(ax, r * 128 + 2 * lane);
+      stg_bf16x2(p.C, m * p.ldc + col, v0 * act_grad(ACT, u.x), v1 * act_grad(ACT, u.y));
+    } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+      const float2 g = lds_bf16x2(ax, r * 128 + 2 * lane);
+      const float2 u = lds_bf16x2(ax, 2048 + r * 128 + 2 * lane);
+      const float s0 = act_sigmoid(g.x), s1 = act_sigmoid(g.y);
+      stg_bf16x2(p.C, m * p.ldc + col, v0 * u.x * s0 * (1.f + g.x * (1.f - s0)),
+                 v1 * u.y * s1 * (1.f + g.y * (1.f - s1)));
+      stg_bf16x2(p.C, m * p.ldc + p.fhalf + col, v0 * g.x * s0, v1 * g.y * s1);
+    }
+  };
+  for (int r = 0; r < rows; ++r) row(r);
+}
+
 // ax: this wave's 16 x 128 tile of the epilogue's auxiliary input (U for act', [gate | up] at +2048 for SwiGLU),
 // staged in LDS.
 template <int EPI>
@@ -602,28 +636,16 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
       }
     }
     const int rows = min(16, p.M - m0);
-    for (int r = 0; r < rows; ++r) {
-      const float v0 = ep[r * ep_pitch + 2 * lane], v1 = ep[r * ep_pitch + 2 * lane + 1];
-      const int64_t m = m0 + r;
-      if constexpr (EPI == EPI_STORE) {
-        stg_bf16x2(p.C, m * p.ldc + col, v0, v1);
-      } else if constexpr (EPI == EPI_BIAS) {
-        stg_bf16x2(p.C, m * p.ldc + col, v0 + b0, v1 + b1);
-      } else if constexpr (EPI == EPI_BIAS_ACT) {
-        const float u0 = v0 + b0, u1 = v1 + b1;
-        stg_bf16x2(p.C, m * p.ldc + col, u0, u1);
-        stg_bf16x2(p.C2, m * p.ldc2 + col, act_apply(p.act, u0), act_apply(p.act, u1));
-      } else if constexpr (EPI == EPI_ACT_BWD) {
-        const float2 u = lds_bf16x2(ax, r * 128 + 2 * lane);
-        stg_bf16x2(p.C, m * p.ldc + col, v0 * act_grad(p.act, u.x), v1 * act_grad(p.act, u.y));
-      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        const float2 g = lds_bf16x2(ax, r * 128 + 2 * lane);
-        const float2 u = lds_bf16x2(ax, 2048 + r * 128 + 2 * lane);
-        const float s0 = act_sigmoid(g.x), s1 = act_sigmoid(g.y);
-        stg_bf16x2(p.C, m * p.ldc + col, v0 * u.x * s0 * (1.f + g.x * (1.f - s0)),
-                   v1 * u.y * s1 * (1.f + g.y * (1.f - s1)));
-        stg_bf16x2(p.C, m * p.ldc + p.fhalf + col, v0 * g.x * s0, v1 * g.y * s1);
+    if constexpr (EPI == EPI_BIAS_ACT || EPI == EPI_ACT_BWD) {  // the activation chosen once per chunk
+      switch (p.act) {
+        case TP_ACT_GELU: chunk_rows<EPI, TP_ACT_GELU>(p, ep, ep_pitch, m0, col, lane, ax, b0, b1, rows); break;
+        case TP_ACT_GELU_TANH:
+          chunk_rows<EPI, TP_ACT_GELU_TANH>(p, ep, ep_pitch, m0, col, lane, ax, b0, b1, rows);
+          break;
+        default: chunk_rows<EPI, TP_ACT_RELU>(p, ep, ep_pitch, m0, col, lane, ax, b0, b1, rows); break;
       }
+    } else {
+      chunk_rows<EPI, TP_ACT_RELU>(p, ep, ep_pitch, m0, col, lane, ax, b0, b1, rows);
     }
   }
 }

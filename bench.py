@@ -128,7 +128,7 @@ def attention_block_measure(L, steps: int, warmup: int, w=None) -> dict:
             role = "reduce_scatter"
         elif name.startswith("attn_fwd"):
             role = "attention"
-        elif name == "gemm_bf16_splitk_sum":
+        elif name.startswith("gemm_bf16_splitk_"):  # the partial sum of a split-K GEMM
             role = seq[-1]
         else:
             role = "proj" if seq and seq[-1] == "attention" else "qkv"
@@ -195,7 +195,7 @@ def attention_block_measure(L, steps: int, warmup: int, w=None) -> dict:
             role = "attention_core_bwd"
         elif "_pair_" in name or name.endswith("MM_store"):
             role = "wgrad_pair"
-        elif name == "gemm_bf16_splitk_sum":
+        elif name.startswith("gemm_bf16_splitk_"):  # the partial sum of a split-K GEMM
             role = seq[-1]
         else:  # the two data-gradient GEMMs of a rank: dO first, dX after the weight gradients
             role = "dX_gemm" if seq and seq[-1] == "wgrad_pair" else "dO_gemm"
