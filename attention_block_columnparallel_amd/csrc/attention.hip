@@ -23,6 +23,8 @@
 //   * Query tiles are issued heaviest first over all heads (causal work grows with the tile index).
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
 #include <string>
 
 #include "tp_common.h"
@@ -86,6 +88,15 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Work rank (0 = the most work) of the causal tile a workgroup takes, from its launch-order index u over n tiles.
+// Heaviest first, so that workgroups dealt out as CUs free up balance greedily -- unless the whole grid is resident
+// at once (fold): then the first half of the launch takes ranks 0 .. h-1 and the second half ranks n-1 down to h,
+// so the two workgroups a CU receives (one from each half, in launch order) carry about the same total work.
+__device__ __forceinline__ int work_rank(int u, int n, int fold) {
+  const int h = (n + 1) / 2;
+  return (fold && u >= h) ? n - 1 - (u - h) : u;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -106,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int nq = (p.s + QT - 1) / QT;
   const int nbh = p.b * p.hl;
-  const int qtile = nq - 1 - (int)blockIdx.x / nbh;  // heaviest first over all (batch, head) pairs
+  const int qtile = nq - 1 - work_rank((int)blockIdx.x / nbh, nq, p.fold);  // over all (batch, head) pairs
   const int bh = (int)blockIdx.x % nbh;
   const int bidx = bh / p.hl, jj = bh % p.hl;
   const int d = p.d;
@@ -395,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   const int splits = p.kvpart != nullptr ? p.G : 1;
   const int HS = p.G / splits;
   const int nbh = p.b * gl * splits;
-  const int ktile = (int)blockIdx.x / nbh;  // key block 0 sees the most queries: issued first
+  const int ktile = work_rank((int)blockIdx.x / nbh, nqb, p.fold);  // key block 0 sees the most queries
   const int bh = (int)blockIdx.x % nbh;
   const int sp = bh % splits;
   const int bidx = bh / splits / gl, jg = bh / splits % gl;
@@ -624,7 +635,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int nq = (p.s + QT - 1) / QT;
   const int nbh = p.b * p.hl;
-  const int qtile = nq - 1 - (int)blockIdx.x / nbh;
+  const int qtile = nq - 1 - work_rank((int)blockIdx.x / nbh, nq, p.fold);
   const int bh = (int)blockIdx.x % nbh;
   const int bidx = bh / p.hl, jj = bh % p.hl;
   const int d = p.d;
@@ -910,8 +921,43 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_sum_kernel(AttnBwdParams p) {
   *reinterpret_cast<uint2*>(out) = w;
 }
 
+// Workgroups of Kernel (256 threads) resident on the current device at once; 0 when the runtime cannot say.  A
+// template on the kernel itself, so each kernel has its own cache (kernels of one signature share a type).
+template <auto Kernel>
+int64_t resident_limit() {
+  const void* const kernel = reinterpret_cast<const void*>(Kernel);
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int64_t> cache[kMaxDevices];  // 0: not yet asked
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    // the runtime's occupancy figure, capped by the LDS count (the runtime has reported 2 per CU for kernels of
+    // 96 KB of static LDS on a 160 KB CU)
+    int per_cu = 0, cus = 0, lds_cu = 0;
+    hipFuncAttributes fa;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+        hipFuncGetAttributes(&fa, kernel) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      per_cu = 0;
+    } else if (fa.sharedSizeBytes > 0) {
+      per_cu = std::min<int64_t>(per_cu, (int64_t)lds_cu / (int64_t)fa.sharedSizeBytes);
+    }
+    v = (int64_t)per_cu * cus + 1;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v - 1;
+}
+
+template <auto Kernel>
+int fold_for(unsigned grid, int causal) {
+  return causal && (int64_t)grid <= resident_limit<Kernel>() ? 1 : 0;
+}
+
 template <int DP>
-hipError_t launch_bwd_bf16(const AttnBwdParams& p, hipStream_t st) {
+hipError_t launch_bwd_bf16(const AttnBwdParams& p0, hipStream_t st) {
+  AttnBwdParams p = p0;
   const int nq = (p.s + 63) / 64;
   const unsigned grid = (unsigned)(nq * p.b * p.hl);
   static const std::string n1 = "attn_bwd_dkv_bf16_d" + std::to_string(DP);
@@ -920,7 +966,9 @@ hipError_t launch_bwd_bf16(const AttnBwdParams& p, hipStream_t st) {
   // one workgroup per (64 keys, batch, KV group, head split)
   const unsigned grid_kv = (unsigned)(nq * p.b * (p.hl / p.G) * splits);
   // dQ first: it also writes each query's D, which the dK / dV pass reads
+  p.fold = fold_for<attn_bwd_dq_bf16_kernel<DP>>(grid, p.causal);
   hipError_t e = TP_LAUNCH(n2.c_str(), (attn_bwd_dq_bf16_kernel<DP>), dim3(grid), dim3(256), 0, st, p);
+  p.fold = fold_for<attn_bwd_dkv_bf16_kernel<DP>>(grid_kv, p.causal);
   if (e == hipSuccess) e = TP_LAUNCH(n1.c_str(), (attn_bwd_dkv_bf16_kernel<DP>), dim3(grid_kv), dim3(256), 0, st, p);
   if (e == hipSuccess && splits > 1) {
     const int64_t n = (int64_t)p.s * p.b * (p.hl / p.G) * (p.d / 2);
@@ -932,10 +980,13 @@ hipError_t launch_bwd_bf16(const AttnBwdParams& p, hipStream_t st) {
 }
 
 template <int DP>
-hipError_t launch_bf16(const AttnParams& p, hipStream_t st) {
+hipError_t launch_bf16(const AttnParams& p0, hipStream_t st) {
+  AttnParams p = p0;
   const int nq = (p.s + QT - 1) / QT;
+  const unsigned grid = (unsigned)(nq * p.b * p.hl);
+  p.fold = fold_for<attn_fwd_bf16_kernel<DP>>(grid, p.causal);
   static const std::string name = "attn_fwd_bf16_d" + std::to_string(DP);
-  return TP_LAUNCH(name.c_str(), (attn_fwd_bf16_kernel<DP>), dim3((unsigned)(nq * p.b * p.hl)), dim3(256), 0, st, p);
+  return TP_LAUNCH(name.c_str(), (attn_fwd_bf16_kernel<DP>), dim3(grid), dim3(256), 0, st, p);
 }
 
 }  // namespace

@@ -177,6 +177,7 @@ struct AttnParams {
   int G;            // query heads per KV head (1: multi-head)
   int causal;
   float scale;      // 1/sqrt(d)
+  int fold;         // set by the launcher: tile order for a grid resident all at once (see work_rank)
 };
 hipError_t attention_bf16(const AttnParams& p, hipStream_t st);
 hipError_t attention_f32(const AttnParams& p, hipStream_t st);
@@ -195,6 +196,7 @@ struct AttnBwdParams {
   int G;             // query heads per KV head (1: multi-head)
   int causal;
   float scale;       // 1/sqrt(d)
+  int fold;          // set by the launcher, as in AttnParams
 };
 hipError_t attention_bwd(tp_dtype dt, const AttnBwdParams& p, hipStream_t st);
 
