@@ -50,6 +50,10 @@ constexpr int NSTG = 3;
 // (grouped-query shape, per rank: forward 116 -> 94 us, dQ 184 -> 176 us).
 template <int DP>
 constexpr int kv_stages() { return DP >= 128 ? 2 : NSTG_F; }
+// Stages of the dK / dV pass's Q / dO ring: likewise two at d = 128, where two workgroups then share a CU
+// (grouped-query shape: 204 -> 180 us per rank).
+template <int DP>
+constexpr int dkv_stages() { return DP >= 128 ? 2 : NSTG; }
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -401,7 +405,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   constexpr int STAGE_B = 2 * TILE_B + 1024;    // Q tile, dO tile, (lse, D) record
   constexpr int CPW = CH / 4;
   constexpr int NDS = DP / 32, NST = DP / 16;
-  __shared__ __attribute__((aligned(16))) char lds[NSTG * STAGE_B];
+  constexpr int NS = dkv_stages<DP>();
+  constexpr int D = NS - 1;  // query blocks in flight ahead of the one being used
+  __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_B];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int nqb = (p.s + 63) / 64;
@@ -501,14 +507,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
 #pragma unroll
   for (int st = 0; st < NST; ++st) dv[st] = dk[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  issue_tile(0, 0);
-  issue_tile(1, 1);
-  if (wave == 0) wait_vmcnt<2 * CPW + 1>(); else wait_vmcnt<2 * CPW>();
+#pragma unroll
+  for (int i = 0; i < D; ++i) issue_tile(i, i);
+  // step 0 has landed (wave 0 also copies the record: one more copy per step)
+  if (wave == 0) wait_vmcnt<(D - 1) * (2 * CPW + 1)>(); else wait_vmcnt<(D - 1) * 2 * CPW>();
   __syncthreads();
 
-  int st_cur = 0, st_new = 2;
+  int st_cur = 0, st_new = D;
   for (int i = 0; i < ntot; ++i) {
-    issue_tile(i + 2, st_new);
+    issue_tile(i + D, st_new);
     const char* Qt = &lds[st_cur * STAGE_B];
     const char* Dt = Qt + TILE_B;
     const float* R = reinterpret_cast<const float*>(Qt + 2 * TILE_B);
@@ -586,10 +593,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
         dk[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qt, slf, dk[st], 0, 0, 0);
       }
     }
-    if (wave == 0) wait_vmcnt<2 * CPW + 1>(); else wait_vmcnt<2 * CPW>();
+    if (wave == 0) wait_vmcnt<(D - 1) * (2 * CPW + 1)>(); else wait_vmcnt<(D - 1) * 2 * CPW>();
     __syncthreads();
-    st_cur = st_cur == NSTG - 1 ? 0 : st_cur + 1;
-    st_new = st_new == NSTG - 1 ? 0 : st_new + 1;
+    st_cur = st_cur == NS - 1 ? 0 : st_cur + 1;
+    st_new = st_new == NS - 1 ? 0 : st_new + 1;
   }
   wait_vmcnt<0>();
 
