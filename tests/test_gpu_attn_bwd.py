@@ -131,3 +131,18 @@ def test_attention_backward_full_size_one_rank_sampled(L):
     # the weight gradients in full (the pair's tail tiles split K over workgroups)
     check_close(f64(got["dWqkv"]), X.T @ dQs, "bf16", "dWqkv")
     check_close(f64(got["dWo"]), Os.T @ dZ, "bf16", "dWo")
+
+
+def test_attention_backward_ragged_pair_tail(L):
+    """A shape whose weight-gradient pair has ragged tiles and overruns one round of 256 tiles (dWo 800 x 6400 and
+    dWqkv 6400 x 2400: 350 tiles, a tail of 94 split over two K ranges): both weight gradients in full."""
+    w = TI.Workload("attn_ragged_tail", "attn", s=4096, b=1, h=6400, a=80, d=80, t=8, causal=True, dtype="bf16")
+    r = 3
+    say("attention backward h=6400 a=80 d=80 s=4096 t=8 rank 3 (ragged weight-gradient tiles, split tail)")
+    inp = TI.attn_inputs(w, seed=3)
+    got = run_rank(L, w, inp, r, "bf16", False, True)
+    X = O.as_f64(inp["X"], "bf16").reshape(w.M, w.h)
+    dZ = O.as_f64(inp["dZ"], "bf16").reshape(w.M, w.h)
+    Os, dQs = f64(got["O"]), f64(got["dQKV"])
+    check_close(f64(got["dWqkv"]), X.T @ dQs, "bf16", "dWqkv")
+    check_close(f64(got["dWo"]), Os.T @ dZ, "bf16", "dWo")
