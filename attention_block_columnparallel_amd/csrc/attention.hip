@@ -106,6 +106,15 @@ __device__ __forceinline__ int work_rank(int u, int n, int fold) {
   return (fold && u >= h) ? n - 1 - (u - h) : u;
 }
 
+// Four fp32 values -> bf16 hi pairs and bf16 lo pairs with x = hi + lo to about 2^-16 relative: hi = bf16(x), lo =
+// bf16(x - hi), the hi value read back from its packed bits.
+__device__ __forceinline__ void split_hi_lo(const float (&x)[4], uint32_t (&hi)[2], uint32_t (&lo)[2]) {
+  hi[0] = pack_bf16x2_hw(x[0], x[1]);
+  hi[1] = pack_bf16x2_hw(x[2], x[3]);
+  lo[0] = pack_bf16x2_hw(x[0] - __uint_as_float(hi[0] << 16), x[1] - __uint_as_float(hi[0] & 0xFFFF0000u));
+  lo[1] = pack_bf16x2_hw(x[2] - __uint_as_float(hi[1] << 16), x[3] - __uint_as_float(hi[1] & 0xFFFF0000u));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -273,8 +282,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
         pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[ks][e], c2, nm));
         psum += pe[e];
       }
-      pk[ks][0] = f32_to_bf16_hw(pe[0]) | (f32_to_bf16_hw(pe[1]) << 16);
-      pk[ks][1] = f32_to_bf16_hw(pe[2]) | (f32_to_bf16_hw(pe[3]) << 16);
+      pk[ks][0] = pack_bf16x2_hw(pe[0], pe[1]);
+      pk[ks][1] = pack_bf16x2_hw(pe[2], pe[3]);
     }
     l_part += psum;
 
@@ -301,8 +310,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
       const int dd = st * 16 + 4 * g;
       if (dd < d) {
         uint2 w;
-        w.x = f32_to_bf16_hw(acc_o[st][0] * inv) | (f32_to_bf16_hw(acc_o[st][1] * inv) << 16);
-        w.y = f32_to_bf16_hw(acc_o[st][2] * inv) | (f32_to_bf16_hw(acc_o[st][3] * inv) << 16);
+        w.x = pack_bf16x2_hw(acc_o[st][0] * inv, acc_o[st][1] * inv);
+        w.y = pack_bf16x2_hw(acc_o[st][2] * inv, acc_o[st][3] * inv);
         *reinterpret_cast<uint2*>(o + dd) = w;
       }
     }
@@ -555,26 +564,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
         pe[e] = __builtin_amdgcn_exp2f(x);
         ds[e] = pe[e] * (dp[qs][e] - D4[e]);
       }
-      uint32_t hb[4];
-      float lo[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hb[e] = f32_to_bf16_hw(pe[e]);
-        lo[e] = pe[e] - bf16_to_f32(hb[e]);
-      }
-      pp[qs][0] = hb[0] | (hb[1] << 16);
-      pp[qs][1] = hb[2] | (hb[3] << 16);
-      pl[qs][0] = f32_to_bf16_hw(lo[0]) | (f32_to_bf16_hw(lo[1]) << 16);
-      pl[qs][1] = f32_to_bf16_hw(lo[2]) | (f32_to_bf16_hw(lo[3]) << 16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hb[e] = f32_to_bf16_hw(ds[e]);
-        lo[e] = ds[e] - bf16_to_f32(hb[e]);
-      }
-      dd2[qs][0] = hb[0] | (hb[1] << 16);
-      dd2[qs][1] = hb[2] | (hb[3] << 16);
-      dl2[qs][0] = f32_to_bf16_hw(lo[0]) | (f32_to_bf16_hw(lo[1]) << 16);
-      dl2[qs][1] = f32_to_bf16_hw(lo[2]) | (f32_to_bf16_hw(lo[3]) << 16);
+      split_hi_lo(pe, pp[qs], pl[qs]);
+      split_hi_lo(ds, dd2[qs], dl2[qs]);
     }
     // dV^T += dO^T P, dK^T += Q^T dS over two 32-query steps (P and dS as hi + lo bf16 pairs)
 #pragma unroll
@@ -619,11 +610,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
       const int dd = st * 16 + 4 * g;
       if (dd < d) {
         uint2 w;
-        w.x = f32_to_bf16_hw(dk[st][0] * p.scale) | (f32_to_bf16_hw(dk[st][1] * p.scale) << 16);
-        w.y = f32_to_bf16_hw(dk[st][2] * p.scale) | (f32_to_bf16_hw(dk[st][3] * p.scale) << 16);
+        w.x = pack_bf16x2_hw(dk[st][0] * p.scale, dk[st][1] * p.scale);
+        w.y = pack_bf16x2_hw(dk[st][2] * p.scale, dk[st][3] * p.scale);
         *reinterpret_cast<uint2*>(out + dd) = w;
-        w.x = f32_to_bf16_hw(dv[st][0]) | (f32_to_bf16_hw(dv[st][1]) << 16);
-        w.y = f32_to_bf16_hw(dv[st][2]) | (f32_to_bf16_hw(dv[st][3]) << 16);
+        w.x = pack_bf16x2_hw(dv[st][0], dv[st][1]);
+        w.y = pack_bf16x2_hw(dv[st][2], dv[st][3]);
         *reinterpret_cast<uint2*>(out + d + dd) = w;
       }
     }
@@ -767,23 +758,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
         gv[e] = pv[e] * dp[ks][e];
         dsum += gv[e];
       }
-      uint32_t hb[4], hp[4];
-      float lo[4], lp[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        hb[e] = f32_to_bf16_hw(gv[e]);
-        lo[e] = gv[e] - bf16_to_f32(hb[e]);
-        hp[e] = f32_to_bf16_hw(pv[e]);
-        lp[e] = pv[e] - bf16_to_f32(hp[e]);
-      }
-      gh[ks][0] = hb[0] | (hb[1] << 16);
-      gh[ks][1] = hb[2] | (hb[3] << 16);
-      gl[ks][0] = f32_to_bf16_hw(lo[0]) | (f32_to_bf16_hw(lo[1]) << 16);
-      gl[ks][1] = f32_to_bf16_hw(lo[2]) | (f32_to_bf16_hw(lo[3]) << 16);
-      ph[ks][0] = hp[0] | (hp[1] << 16);
-      ph[ks][1] = hp[2] | (hp[3] << 16);
-      pl[ks][0] = f32_to_bf16_hw(lp[0]) | (f32_to_bf16_hw(lp[1]) << 16);
-      pl[ks][1] = f32_to_bf16_hw(lp[2]) | (f32_to_bf16_hw(lp[3]) << 16);
+      split_hi_lo(gv, gh[ks], gl[ks]);
+      split_hi_lo(pv, ph[ks], pl[ks]);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -823,8 +799,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
       const int dd = st * 16 + 4 * g;
       if (dd < d) {
         uint2 w;
-        w.x = f32_to_bf16_hw(dq[st][0] * p.scale) | (f32_to_bf16_hw(dq[st][1] * p.scale) << 16);
-        w.y = f32_to_bf16_hw(dq[st][2] * p.scale) | (f32_to_bf16_hw(dq[st][3] * p.scale) << 16);
+        w.x = pack_bf16x2_hw(dq[st][0] * p.scale, dq[st][1] * p.scale);
+        w.y = pack_bf16x2_hw(dq[st][2] * p.scale, dq[st][3] * p.scale);
         *reinterpret_cast<uint2*>(out + dd) = w;
       }
     }
@@ -931,8 +907,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_sum_kernel(AttnBwdParams p) {
   const QkvCols kc = qkv_cols(p.hl, p.G, d, jg * p.G);
   uint16_t* out = static_cast<uint16_t*>(p.dqkv) + m * kc.ld + kc.k + 4 * c4;
   uint2 w;
-  w.x = f32_to_bf16_hw(acc[0]) | (f32_to_bf16_hw(acc[1]) << 16);
-  w.y = f32_to_bf16_hw(acc[2]) | (f32_to_bf16_hw(acc[3]) << 16);
+  w.x = pack_bf16x2_hw(acc[0], acc[1]);
+  w.y = pack_bf16x2_hw(acc[2], acc[3]);
   *reinterpret_cast<uint2*>(out) = w;
 }
 

@@ -540,9 +540,7 @@ constexpr int seg_ds_count(int s) {
   return n;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_hw(lo) | (f32_to_bf16_hw(hi) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return pack_bf16x2_hw(lo, hi); }
 __device__ __forceinline__ void stg_bf16x2(void* p, int64_t i, float lo, float hi) {
   *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + i) = pack_bf16x2(lo, hi);
 }

@@ -54,10 +54,10 @@ struct Io<uint16_t> {
   }
   static __device__ __forceinline__ void store(void* base, int64_t e, const float* v) {
     uint4 o;
-    o.x = f32_to_bf16_hw(v[0]) | (f32_to_bf16_hw(v[1]) << 16);
-    o.y = f32_to_bf16_hw(v[2]) | (f32_to_bf16_hw(v[3]) << 16);
-    o.z = f32_to_bf16_hw(v[4]) | (f32_to_bf16_hw(v[5]) << 16);
-    o.w = f32_to_bf16_hw(v[6]) | (f32_to_bf16_hw(v[7]) << 16);
+    o.x = pack_bf16x2_hw(v[0], v[1]);
+    o.y = pack_bf16x2_hw(v[2], v[3]);
+    o.z = pack_bf16x2_hw(v[4], v[5]);
+    o.w = pack_bf16x2_hw(v[6], v[7]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + e) = o;
   }
   static __device__ __forceinline__ float round(float x) { return bf16_to_f32(f32_to_bf16_hw(x)); }

@@ -26,6 +26,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ uint32_t f32_to_bf16_hw(float f) {
   return (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f);
 }
+// Two floats -> a packed bf16 pair (lo in bits 0..15), nearest-even, as one v_cvt_pk_bf16_f32 (the two single
+// conversions plus shift and or took four instructions).
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  typedef float f32x2_pk_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_pk_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_pk_t){lo, hi}, bf16x2_pk_t));
+}
 
 // ------------------------------------------------------------------------------------------------------------------
 // Element-wise activations.
