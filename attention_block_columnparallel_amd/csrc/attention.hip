@@ -26,6 +26,7 @@
 #include <algorithm>
 #include <atomic>
 #include <string>
+#include <type_traits>
 
 #include "tp_common.h"
 
@@ -216,8 +217,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
   wait_vmcnt<(D - 1) * NC>();  // block 0 has landed (blocks 1 .. D-1 may still be in flight)
   __syncthreads();
 
-  int st_cur = 0, st_new = D;
-  for (int kt = 0; kt < nkt; ++kt) {
+  // one key block; the ring stage is a template constant, so the stage offsets fold into the LDS instructions'
+  // immediate offsets (the loop below is unrolled over the NS stages)
+  auto block = [&](int kt, auto stage) {
+    constexpr int st_cur = decltype(stage)::value;
+    constexpr int st_new = (st_cur + D) % NS;
     issue_tile(kt + D, st_new);
     const char* Kt = &lds[st_cur * STAGE_B];
     const char* Vt = Kt + TILE_B;
@@ -296,8 +300,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
     }
     wait_vmcnt<(D - 1) * NC>();  // block kt+1 has landed (blocks kt+2 .. kt+D may still be in flight)
     __syncthreads();   // publishes block kt+1; every wave is done with stage st_cur, refilled next iteration
-    st_cur = st_cur == NS - 1 ? 0 : st_cur + 1;
-    st_new = st_new == NS - 1 ? 0 : st_new + 1;
+  };
+  for (int kt = 0; kt < nkt; kt += NS) {
+    block(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nkt) block(kt + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS > 2) {
+      if (kt + 2 < nkt) block(kt + 2, std::integral_constant<int, 2 % NS>{});
+    }
   }
   wait_vmcnt<0>();
 
