@@ -531,8 +531,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   if (wave == 0) wait_vmcnt<(D - 1) * (2 * CPW + 1)>(); else wait_vmcnt<(D - 1) * 2 * CPW>();
   __syncthreads();
 
-  int st_cur = 0, st_new = D;
-  for (int i = 0; i < ntot; ++i) {
+  // one query block; the ring stage is a template constant, as in the forward
+  auto step = [&](int i, auto stage) {
+    constexpr int st_cur = decltype(stage)::value;
+    constexpr int st_new = (st_cur + D) % NS;
     issue_tile(i + D, st_new);
     const char* Qt = &lds[st_cur * STAGE_B];
     const char* Dt = Qt + TILE_B;
@@ -595,8 +597,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
     }
     if (wave == 0) wait_vmcnt<(D - 1) * (2 * CPW + 1)>(); else wait_vmcnt<(D - 1) * 2 * CPW>();
     __syncthreads();
-    st_cur = st_cur == NS - 1 ? 0 : st_cur + 1;
-    st_new = st_new == NS - 1 ? 0 : st_new + 1;
+  };
+  for (int i0 = 0; i0 < ntot; i0 += NS) {
+    step(i0, std::integral_constant<int, 0>{});
+    if (i0 + 1 < ntot) step(i0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS > 2) {
+      if (i0 + 2 < ntot) step(i0 + 2, std::integral_constant<int, 2 % NS>{});
+    }
   }
   wait_vmcnt<0>();
 
@@ -733,8 +740,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
   wait_vmcnt<(D - 1) * NC>();  // block 0 has landed
   __syncthreads();
 
-  int st_cur = 0, st_new = D;
-  for (int kt = 0; kt < nkt; ++kt) {
+  // one key block; the ring stage is a template constant, as in the forward
+  auto step = [&](int kt, auto stage) {
+    constexpr int st_cur = decltype(stage)::value;
+    constexpr int st_new = (st_cur + D) % NS;
     issue_tile(kt + D, st_new);
     const char* Kt = &lds[st_cur * STAGE_B];
     const char* Vt = Kt + TILE_B;
@@ -790,8 +799,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
     }
     wait_vmcnt<(D - 1) * NC>();  // block kt+1 has landed
     __syncthreads();
-    st_cur = st_cur == NS - 1 ? 0 : st_cur + 1;
-    st_new = st_new == NS - 1 ? 0 : st_new + 1;
+  };
+  for (int kt0 = 0; kt0 < nkt; kt0 += NS) {
+    step(kt0, std::integral_constant<int, 0>{});
+    if (kt0 + 1 < nkt) step(kt0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS > 2) {
+      if (kt0 + 2 < nkt) step(kt0 + 2, std::integral_constant<int, 2 % NS>{});
+    }
   }
   wait_vmcnt<0>();
 
