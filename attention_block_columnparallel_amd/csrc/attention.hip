@@ -554,9 +554,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
         dp[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[u], dp[qs], 0, 0, 0);
       }
     }
-    // P and dS for queries q0 + 16 qs + 4 g + e and this lane's key
+    // P and dS for queries q0 + 16 qs + 4 g + e and this lane's key; masked scores become -inf (P = 0), in a
+    // branch of their own that only the diagonal block and a ragged last block take
     const bool diag = p.causal && qbi == ktile;
     const bool ragged = q0 + 64 > p.s;
+    if (diag || ragged) {
+#pragma unroll
+      for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q = q0 + 16 * qs + 4 * g + e;
+          if (q >= p.s || (p.causal && key > q)) sc[qs][e] = -INFINITY;
+        }
+    }
     // P goes to the matrix cores as a bf16 pair hi + lo (lo = P - hi rounded again): with near-uniform weights
     // a single bf16 P carries 2^-9 relative error into every term of dV's sum over queries
     uint32_t pp[4][2], pl[4][2], dd2[4][2], dl2[4][2];
@@ -567,12 +577,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
       float pe[4], ds[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x = fmaf(sc[qs][e], c2, -lse4[e] * 1.4426950408889634f);
-        if (diag || ragged) {
-          const int q = q0 + 16 * qs + 4 * g + e;
-          if (q >= p.s || (p.causal && key > q)) x = -INFINITY;
-        }
-        pe[e] = __builtin_amdgcn_exp2f(x);
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[qs][e], c2, -lse4[e] * 1.4426950408889634f));
         ds[e] = pe[e] * (dp[qs][e] - D4[e]);
       }
       split_hi_lo(pe, pp[qs], pl[qs]);
@@ -760,19 +765,23 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
         dp[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, df[u], dp[ks], 0, 0, 0);
       }
     }
-    const bool need_mask = (p.causal && kt == qtile) || (kv0 + KT > p.s);
+    // masked scores become -inf (P = 0), in a branch of their own: the diagonal block and a ragged last block only
+    if ((p.causal && kt == qtile) || (kv0 + KT > p.s)) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kv = kv0 + ks * 16 + 4 * g + e;
+          if (kv >= p.s || (p.causal && kv > q)) sc[ks][e] = -INFINITY;
+        }
+    }
     uint32_t gh[4][2], gl[4][2], ph[4][2], pl[4][2];  // P dP and P as hi + lo bf16 pairs
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       float gv[4], pv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x = fmaf(sc[ks][e], c2, -lse2);
-        if (need_mask) {
-          const int kv = kv0 + ks * 16 + 4 * g + e;
-          if (kv >= p.s || (p.causal && kv > q)) x = -INFINITY;
-        }
-        pv[e] = __builtin_amdgcn_exp2f(x);
+        pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[ks][e], c2, -lse2));
         gv[e] = pv[e] * dp[ks][e];
         dsum += gv[e];
       }
