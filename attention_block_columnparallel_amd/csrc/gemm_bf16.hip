@@ -4,8 +4,8 @@
 // ("Tensor Parallelism (TP) 与 Sequence Parallelism (SP)" §2; the backward section of the 111qqz
 // "tensor-parallelism-matrix-split" post).
 //
-// Two kernels.  The large-tile kernel (gemm_bf16_big_kernel: 256 x 256 tiles, one wave per SIMD with 128 x 128
-// each, a 4-stage LDS ring fed by direct global -> LDS copies, transposing LDS reads for MN-major operands) runs
+// Two kernels.  The large-tile kernel (gemm_bf16_big_kernel: 256 x 256 tiles, 4 waves of 128 x 128 or 8 of 64 x 128,
+// a 4-stage LDS ring fed by direct global -> LDS copies, transposing LDS reads for MN-major operands) runs
 // every GEMM whose K is a multiple of 64 and whose tile count fills the GPU; its design is described above it.
 // The register-staged kernel (gemm_bf16_kernel) takes the rest:
 //   * one workgroup = one BM x BN output tile, NWM x NWN waves of 64 lanes, K stepped by 64;
@@ -317,8 +317,10 @@ __global__ __launch_bounds__(NWM* NWN * 64) void gemm_bf16_kernel(GemmParams p) 
 }
 
 // ------------------------------------------------------------------------------------------------------------------
-// Large-tile kernel: 256 x 256 output tile, 4 waves (2 x 2), each wave 128 x 128 = 8 x 8 MFMA subtiles whose 256
-// fp32 accumulators per lane live in the accumulation registers (one wave per SIMD, 512 registers).  Needs
+// Large-tile kernel: 256 x 256 output tile, either 4 waves (2 x 2), each wave 128 x 128 = 8 x 8 MFMA subtiles whose
+// 256 fp32 accumulators per lane live in the accumulation registers (one wave per SIMD, 512 registers), or 8 waves
+// (4 x 2) of 64 x 128 = 4 x 8 subtiles, 128 accumulators per lane (two waves per SIMD, 256 registers each), where
+// one wave's waits and epilogue overlap the other's MFMAs at the price of half again as many LDS reads.  Needs
 // K % 64 == 0 (an even number of 32-deep K tiles).  Out-of-range rows of either operand are clamped to the last valid row: they only feed output rows
 // or columns that are never stored, so no load needs a bounds branch.
 //
@@ -330,9 +332,9 @@ __global__ __launch_bounds__(NWM* NWN * 64) void gemm_bf16_kernel(GemmParams p) 
 //     columns n0 + 4 (k' % 4) .. +3, and lane i receives column n0 + i of rows k0 .. k0 + 3.
 // Both swizzles make the 16 lanes served together touch distinct bank groups.
 //
-// Pipeline per K tile kt (LDS stage kt & 1 holds tile kt, fragment set F holds its fragments, registers P hold
-// tile kt+1):  P -> stage (kt+1)&1;  global loads of tile kt+2 -> P;  barrier;  fragments of tile kt+1 -> F';
-// 64 MFMAs on F.  Every LDS read is issued one MFMA burst (1024 cycles) ahead of its use.
+// Pipeline per K tile kt (fragment set F holds its fragments): wait for the copies of tile kt+1, barrier; copies of
+// tile kt+3 into the stage tile kt-1 used; fragments of tile kt+1 -> F' interleaved with the MFMAs on F.  Every LDS
+// read is issued one MFMA burst (one k-tile of MFMAs) ahead of its use.
 // Two GEMMs of the same layout can share one launch (the two weight gradients): workgroups [0, tiles0) take the
 // first, the rest the second.
 // ------------------------------------------------------------------------------------------------------------------
@@ -386,6 +388,8 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 constexpr int BK2 = 32;
+// Waves of the large-tile kernel: 4 (2 x 2 waves of 128 x 128, one per SIMD) or 8 (4 x 2 waves of 64 x 128, two per
+// SIMD).  An operand tile is 16 copies of 1 KB, so a wave issues CPW = 16 / NW of them per operand and k-tile.
 
 __device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 3; }   // K-major tiles (4 chunks per row)
 __device__ __forceinline__ int swz_mn(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }  // MN-major tiles
@@ -401,34 +405,29 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
 }
 #pragma clang diagnostic pop
-__device__ __forceinline__ void wait_vmcnt16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void wait_vmcnt8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
-__device__ __forceinline__ void wait_vmcnt24() { asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); }
-// wait until at most T k-tiles' copies (8 per wave each) are still in flight
-template <int T>
+// wait until at most T k-tiles' copies (2 CPW per wave each) are still in flight
+template <int T, int CPW>
 __device__ __forceinline__ void wait_vmcnt_tiles() {
-  static_assert(T >= 1 && T <= 3, "k-tiles in flight");
-  if constexpr (T == 1) wait_vmcnt8();
-  else if constexpr (T == 2) wait_vmcnt16();
-  else wait_vmcnt24();
+  static_assert(T >= 0 && T <= 3, "k-tiles in flight");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(T * 2 * CPW) : "memory");
 }
 
 // One operand tile (256 rows or columns x 32 k) is 16 KB = 16 wave-wide copies of 1 KB; wave w issues copies
 // 4w .. 4w+3.  The source address of each lane is chosen so that the lane's fixed LDS slot receives the chunk the
 // swizzled layout puts there.
-template <bool KMAJ, bool SWIG>
+template <bool KMAJ, bool SWIG, int CPW>
 struct Dma;
 
 // Per-lane source positions are 32-bit element offsets from the operand's base (the launcher only takes this
 // kernel when every offset fits).
-template <bool SWIG>
-struct Dma<true, SWIG> {  // K-major: copy i holds rows 16 i .. 16 i + 15 (64 bytes each)
-  uint32_t off[4];
+template <bool SWIG, int CPW>
+struct Dma<true, SWIG, CPW> {  // K-major: copy i holds rows 16 i .. 16 i + 15 (64 bytes each)
+  uint32_t off[CPW];
   __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 16 * (4 * wave + q) + (lane >> 2);
+    for (int q = 0; q < CPW; ++q) {
+      const int r = 16 * (CPW * wave + q) + (lane >> 2);
       const int c = (lane & 3) ^ swz_k(r);
       const int row = min(tile * 256 + r, rows - 1);
       off[q] = (uint32_t)((int64_t)row * ld + c * 8);
@@ -436,22 +435,22 @@ struct Dma<true, SWIG> {  // K-major: copy i holds rows 16 i .. 16 i + 15 (64 by
   }
   __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, int k0, uint32_t lds_op, int wave) const {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      dma16(base + (off[q] + (uint32_t)k0), __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
+    for (int q = 0; q < CPW; ++q)
+      dma16(base + (off[q] + (uint32_t)k0), __builtin_amdgcn_readfirstlane(lds_op + (CPW * wave + q) * 1024));
   }
   // copy q only; koff = k0 (the k offset of the k-tile)
   __device__ __forceinline__ void issue1(int q, const uint16_t* base, uint32_t koff, uint32_t lds_op, int wave) const {
-    dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
+    dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (CPW * wave + q) * 1024));
   }
 };
 
-template <bool SWIG>
-struct Dma<false, SWIG> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 bytes each)
-  uint32_t off[4];
+template <bool SWIG, int CPW>
+struct Dma<false, SWIG, CPW> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 bytes each)
+  uint32_t off[CPW];
   __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = 2 * (4 * wave + q) + (lane >> 5);
+    for (int q = 0; q < CPW; ++q) {
+      const int k = 2 * (CPW * wave + q) + (lane >> 5);
       const int cl = 8 * ((lane & 31) ^ swz_mn(k));  // first logical column of the chunk this slot holds
       int col;
       if (SWIG) {
@@ -468,21 +467,21 @@ struct Dma<false, SWIG> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 by
   __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, int k0, uint32_t lds_op, int wave) const {
     const uint32_t koff = (uint32_t)((int64_t)k0 * ld);
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
+    for (int q = 0; q < CPW; ++q)
+      dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (CPW * wave + q) * 1024));
   }
   // copy q only; koff = k0 * ld (the element offset of the k-tile's first row)
   __device__ __forceinline__ void issue1(int q, const uint16_t* base, uint32_t koff, uint32_t lds_op, int wave) const {
-    dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (4 * wave + q) * 1024));
+    dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (CPW * wave + q) * 1024));
   }
 };
 
 // Fragments of one operand for a wave's 128 rows (8 subtiles of 16) over the tile's 32 k.
-template <bool KMAJ>
-__device__ __forceinline__ void frags2(const u32x4_t* lds, int rbase, int lane, bf16x8_t (&f)[8]) {
+template <bool KMAJ, int NFR>
+__device__ __forceinline__ void frags2(const u32x4_t* lds, int rbase, int lane, bf16x8_t (&f)[NFR]) {
   if constexpr (KMAJ) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NFR; ++i) {
       const int r = rbase + i * 16 + (lane & 15);
       f[i] = __builtin_bit_cast(bf16x8_t, lds[r * 4 + ((lane >> 4) ^ swz_k(r))]);
     }
@@ -492,7 +491,7 @@ __device__ __forceinline__ void frags2(const u32x4_t* lds, int rbase, int lane, 
     const int cq = 4 * (kq & 3);  // column offset of this lane's 4-element piece
     const char* base = reinterpret_cast<const char*>(lds);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NFR; ++i) {
       const int col = rbase + i * 16 + cq;
       const int ch = col >> 3, hf = (col >> 2) & 1;
       const int o1 = k1 * 512 + ((ch ^ swz_mn(k1)) << 4) + (hf << 3);
@@ -528,15 +527,19 @@ __device__ __forceinline__ void frag1(const u32x4_t* lds, int rbase, int lane, i
   }
 }
 
-// Fragment reads of one k-tile, spread over the first NSEGR of a step's 8 MFMA segments: fragments are taken in
-// the order A0 B0 A1 B1 ... A7 B7 and fragment f goes to segment f * NSEGR / 16.
-constexpr int NSEGR = 6;
-constexpr int frag_seg(int f) { return f * NSEGR / 16; }
-template <bool AK, bool BKM>
+// Fragment reads of one k-tile, spread over the first 3/4 of a step's TM MFMA segments: fragments are taken in
+// the order A0 B0 A1 B1 ... (then the B fragments past TM) and fragment f goes to segment f (3 TM / 4) / (TM + TN).
+template <int TM, int TN>
+constexpr int frag_seg(int f) { return f * (3 * TM / 4) / (TM + TN); }
+template <int TM>
+constexpr bool frag_is_a(int f) { return f < 2 * TM && f % 2 == 0; }
+template <int TM>
+constexpr int frag_idx(int f) { return f < 2 * TM ? f / 2 : f - TM; }
+template <bool AK, bool BKM, int TM, int TN>
 constexpr int seg_ds_count(int s) {
   int n = 0;
-  for (int f = 0; f < 16; ++f)
-    if (frag_seg(f) == s) n += (f % 2 == 0) ? (AK ? 1 : 2) : (BKM ? 1 : 2);
+  for (int f = 0; f < TM + TN; ++f)
+    if (frag_seg<TM, TN>(f) == s) n += frag_is_a<TM>(f) ? (AK ? 1 : 2) : (BKM ? 1 : 2);
   return n;
 }
 
@@ -653,9 +656,10 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
 // run 3 k-tiles ahead of the MFMAs.  The MFMAs take the B fragment first, so each 16 x 16 accumulator block is the
 // transposed product: lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3 of the wave's sub-tile,
 // which the epilogue stages through LDS with one 16-byte write per block.
-template <bool AK, bool BKM, int EPI, bool SPLIT = false>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
-  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TM = 8, TN = 8;
+template <bool AK, bool BKM, int EPI, bool SPLIT = false, int NW = 4>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) {
+  constexpr int CPW = 16 / NW;
+  constexpr int BM = 256, BN = 256, WM = 512 / NW, WN = 128, TM = WM / 16, TN = 8;
   constexpr int NSTAGE = 4;  // (a fifth 32 KB stage, filling the 160 KB LDS, measured slower)
   constexpr int D = NSTAGE - 1;                 // k-tiles in flight ahead of the one being multiplied
   constexpr int STAGE_B = (BM + BN) * BK2 * 2;  // bytes per stage (A tile then B tile)
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   constexpr int EP = 132;  // epilogue fp32 row pitch: 16-byte writes of 16 consecutive rows hit distinct banks
   constexpr int NAUX = EPI == EPI_SWIGLU_BWD ? 8 : EPI == EPI_ACT_BWD ? 4 : 0;  // 16-byte aux loads per lane
   constexpr int EPW = 16 * EP * 4 + NAUX * 1024;                                  // epilogue bytes per wave
-  constexpr int LDS_U4 = (NSTAGE * STAGE_B > 4 * EPW ? NSTAGE * STAGE_B : 4 * EPW) / 16;
+  constexpr int LDS_U4 = (NSTAGE * STAGE_B > NW * EPW ? NSTAGE * STAGE_B : NW * EPW) / 16;
   __shared__ u32x4_t lds[LDS_U4];
 
   const int tid = threadIdx.x;
@@ -699,8 +703,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   const int tile_m = first_m + (bid % (gm * nbn)) % gsz;
   const int tile_n = (bid % (gm * nbn)) / gsz;
 
-  Dma<AK, false> da;
-  Dma<BKM, SWIG> db;
+  Dma<AK, false, CPW> da;
+  Dma<BKM, SWIG, CPW> db;
   da.init(p.lda, tile_m, p.M, p.fhalf, wave, lane);
   db.init(p.ldb, tile_n, p.N, p.fhalf, wave, lane);
   const int64_t lda = p.lda, ldb = p.ldb;  // held in registers: no argument loads inside the K loop
@@ -726,11 +730,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
     da.issue(Ab, lda, d * BK2, lds0 + d * STAGE_B, wave);
     db.issue(Bb, ldb, d * BK2, lds0 + d * STAGE_B + BM * BK2 * 2, wave);
   }
-  wait_vmcnt_tiles<D - 1>();  // k-tile 0 has landed (D - 1 k-tiles, 8 copies each, may still be in flight)
+  wait_vmcnt_tiles<D - 1, CPW>();  // k-tile 0 has landed (D - 1 k-tiles may still be in flight)
   __syncthreads();
   bf16x8_t fa[TM], fb[TN], ga[TM], gb[TN];
-  frags2<AK>(stage_a(0), wm * WM, lane, fa);
-  frags2<BKM>(stage_b(0), wn * WN, lane, fb);
+  frags2<AK, TM>(stage_a(0), wm * WM, lane, fa);
+  frags2<BKM, TN>(stage_b(0), wn * WN, lane, fb);
 
   f32x4_t acc[TM][TN];
 #pragma unroll
@@ -744,17 +748,23 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   auto segment = [&](auto sc, bf16x8_t(&FCA)[TM], bf16x8_t(&FCB)[TN], bf16x8_t(&FNA)[TM], bf16x8_t(&FNB)[TN],
                      const u32x4_t* na, const u32x4_t* nb, uint32_t sb, uint32_t ka, uint32_t kb) {
     constexpr int S = decltype(sc)::value;
-    if constexpr (S < 4) da.issue1(S, Ab, ka, sb, wave);
-    else db.issue1(S - 4, Bb, kb, sb + BM * BK2 * 2, wave);
+    constexpr int NCP = 2 * CPW;  // copies per wave per k-tile, one per segment
 #pragma unroll
-    for (int f = 0; f < 16; ++f) {
-      if (frag_seg(f) == S) {
-        if (f % 2 == 0) frag1<AK>(na, wm * WM, lane, f / 2, FNA[f / 2]);
-        else frag1<BKM>(nb, wn * WN, lane, f / 2, FNB[f / 2]);
+    for (int q = 0; q < NCP; ++q) {
+      if (q * TM / NCP == S) {
+        if (q < CPW) da.issue1(q, Ab, ka, sb, wave);
+        else db.issue1(q - CPW, Bb, kb, sb + BM * BK2 * 2, wave);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < TM + TN; ++f) {
+      if (frag_seg<TM, TN>(f) == S) {
+        if (frag_is_a<TM>(f)) frag1<AK>(na, wm * WM, lane, frag_idx<TM>(f), FNA[frag_idx<TM>(f)]);
+        else frag1<BKM>(nb, wn * WN, lane, frag_idx<TM>(f), FNB[frag_idx<TM>(f)]);
       }
     }
     mfma_rows_t<S, S + 1, TN>(acc, FCA, FCB);
-    constexpr int nds = seg_ds_count<AK, BKM>(S);
+    constexpr int nds = seg_ds_count<AK, BKM, TM, TN>(S);
     if constexpr (nds > 0) {
 #pragma unroll
       for (int r = 0; r < nds; ++r) {
@@ -780,7 +790,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
 #define TP_GEMM_STEP(J, FCA, FCB, FNA, FNB)                                                      \
   {                                                                                              \
     const int j_ = (J);                                                                          \
-    wait_vmcnt_tiles<D - 2>();                                                                   \
+    wait_vmcnt_tiles<D - 2, CPW>();                                                                   \
     __syncthreads();                                                                             \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     const int kt_ = min(j_ + D, nk - 1);                                                         \
@@ -795,24 +805,26 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_big_kernel(GemmPair pp) {
       /* copies first and the 32 transposing reads one per MFMA over the first half */           \
       da.issue(Ab, lda, kt_ * BK2, sb_, wave);                                                   \
       db.issue(Bb, ldb, kt_ * BK2, sb_ + BM * BK2 * 2, wave);                                    \
-      frags2<AK>(na_, wm * WM, lane, FNA);                                                       \
-      frags2<BKM>(nb_, wn * WN, lane, FNB);                                                      \
+      frags2<AK, TM>(na_, wm * WM, lane, FNA);                                                   \
+      frags2<BKM, TN>(nb_, wn * WN, lane, FNB);                                                  \
       mfma_rows_t<0, TM, TN>(acc, FCA, FCB);                                                     \
-      _Pragma("unroll") for (int s_ = 0; s_ < 32; ++s_) {                                        \
+      _Pragma("unroll") for (int s_ = 0; s_ < 2 * (TM + TN); ++s_) {                             \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
       }                                                                                          \
-      __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);                                        \
+      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 2 * (TM + TN), 0);                   \
       __builtin_amdgcn_sched_barrier(0);                                                         \
     } else {                                                                                     \
     segment(I0{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
     segment(I1{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
     segment(I2{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
     segment(I3{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
-    segment(I4{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
-    segment(I5{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
-    segment(I6{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
-    segment(I7{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
+    if constexpr (TM == 8) {                                                                     \
+      segment(I4{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                \
+      segment(I5{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                \
+      segment(I6{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                \
+      segment(I7{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                \
+    }                                                                                            \
     }                                                                                            \
   }
   for (int kt = 0; kt < nk; kt += 2) {
@@ -964,8 +976,12 @@ hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st
                                   kEpiNames[EPI];
   static const std::string name2 = std::string("gemm_bf16_big_pair_") + (AK ? "K" : "M") + (BKM ? "K" : "M") + "_" +
                                    kEpiNames[EPI];
-  return TP_LAUNCH(p1 ? name2.c_str() : name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI>), dim3((unsigned)total),
-                   dim3(256), 0, st, pp);
+  // 8 waves (two per SIMD) where measured faster: a K-major A with an MN-major B, and the act' epilogues; 4 for the
+  // rest (h = 4096, ffn/t = 2048, per launch: column GEMM + GeLU 251 -> 241 us, row GEMM 240 -> 235, dY + GeLU'
+  // 267 -> 256; with 8 the dX GEMM 236 -> 241 and the weight-gradient pair 405 -> 412)
+  constexpr int NW = ((AK && !BKM) || EPI == EPI_ACT_BWD || EPI == EPI_SWIGLU_BWD) ? 8 : 4;
+  return TP_LAUNCH(p1 ? name2.c_str() : name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI, false, NW>),
+                   dim3((unsigned)total), dim3(NW * 64), 0, st, pp);
 }
 
 // Sum of the ksplit fp32 partial tiles in split order, then the epilogue (store, or bias + store), one rounding.
