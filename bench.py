@@ -21,7 +21,9 @@ the step (not part of value): the same step with its reductions on a second stre
 overlapped ms/step); the attention block forward and backward at the 22B-class shape and at the Llama-70B-sized
 grouped-query shape; the dim-0 gather at the Llama-70B-sized SP shape; the sequence-parallel region (dropout +
 residual + LayerNorm, forward and backward) on every rank's rows at that same shape; the vocab-parallel cross
-entropy (local pass, combine, backward) at 16384 token rows over a 51200-entry vocab.
+entropy (local pass, combine, backward) at 16384 token rows over a 51200-entry vocab.  vendor_gemm = the step's
+GEMMs at one rank's shapes through torch.matmul (the ROCm BLAS libraries), beside this library's census times: a
+comparison point only, never on the path.
 """
 from __future__ import annotations
 
@@ -240,6 +242,44 @@ def overlap_measure(blk, X, dZ, Z_rs, dX_rs, serial_step, steps: int, chunks: in
     return {"chunks": chunks, "steps_per_round": steps, "serial_ms": round(med["serial"], 4),
             "overlapped_ms": round(med["overlapped"], 4), "speedup": round(med["serial"] / med["overlapped"], 4),
             "rounds_ms": {k: [round(x, 4) for x in v] for k, v in times.items()}}
+
+
+def vendor_gemm_measure(w, kernels: dict, reps: int = 20) -> dict:
+    """The step's GEMMs through torch.matmul (the ROCm BLAS libraries) at one rank's shapes, beside this library's
+    census times of the same products.  A comparison point only: nothing of it is on the path or in value."""
+    import torch
+
+    M, h, fl = w.M, w.h, w.f_l
+    dev = "cuda"
+    X, A, B = (torch.randn(r, c, device=dev).to(torch.bfloat16) for r, c in ((M, h), (h, fl), (fl, h)))
+    Y, dZ, dU = (torch.randn(r, c, device=dev).to(torch.bfloat16) for r, c in ((M, fl), (M, h), (M, fl)))
+    cases = [  # name, product, flops, this library's kernel for it (its launch also runs the epilogue named)
+        ("column X.A_i", lambda: X @ A, 2 * M * fl * h, "gemm_bf16_big_KM_bias_act"),
+        ("row Y_i.B_i", lambda: Y @ B, 2 * M * h * fl, "gemm_bf16_big_KM_store"),
+        ("dY = dZ.B_i^T", lambda: dZ @ B.t(), 2 * M * fl * h, "gemm_bf16_big_KK_act_bwd"),
+        ("dX_i = dU_i.A_i^T", lambda: dU @ A.t(), 2 * M * h * fl, "gemm_bf16_big_KK_store"),
+        ("dB_i = Y_i^T.dZ then dA_i = X^T.dU_i", lambda: (Y.t() @ dZ, X.t() @ dU), 4 * M * h * fl,
+         "gemm_bf16_big_pair_MM_store"),
+    ]
+    out = {}
+    for name, fn, flops, ours in cases:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        med = sorted(ts)[len(ts) // 2]
+        k = kernels.get(ours, {})
+        out[name] = {"library_median_us": round(med, 2), "library_tflops": round(flops / med / 1e6, 1),
+                     "ours_kernel": ours, "ours_avg_us": round(k["avg_us"], 2) if k else None}
+    del X, A, B, Y, dZ, dU
+    return {"library": "torch.matmul (ROCm BLAS), bf16 in / bf16 out, no epilogue", "per_rank_gemms": out}
 
 
 def gather_measure(L, reps: int) -> dict:
@@ -579,6 +619,9 @@ def main(argv=None) -> int:
         out["sp_region"] = sp_region_measure(L, 10)
         out["vocab_ce"] = vocab_ce_measure(L, 10)
         torch.cuda.empty_cache()
+        if w.dtype == "bf16":
+            out["vendor_gemm"] = vendor_gemm_measure(w, out["kernels"])
+            torch.cuda.empty_cache()
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
