@@ -23,7 +23,8 @@ grouped-query shape; the dim-0 gather at the Llama-70B-sized SP shape; the seque
 residual + LayerNorm, forward and backward) on every rank's rows at that same shape; the vocab-parallel cross
 entropy (local pass, combine, backward) at 16384 token rows over a 51200-entry vocab.  vendor_gemm = the step's
 GEMMs at one rank's shapes through torch.matmul (the ROCm BLAS libraries), beside this library's census times: a
-comparison point only, never on the path.
+comparison point only, never on the path; vendor_sdpa = the same for one rank's causal attention through torch's
+fused scaled_dot_product_attention, beside this library's attention kernels.
 """
 from __future__ import annotations
 
@@ -280,6 +281,55 @@ def vendor_gemm_measure(w, kernels: dict, reps: int = 20) -> dict:
                      "ours_kernel": ours, "ours_avg_us": round(k["avg_us"], 2) if k else None}
     del X, A, B, Y, dZ, dU
     return {"library": "torch.matmul (ROCm BLAS), bf16 in / bf16 out, no epilogue", "per_rank_gemms": out}
+
+
+def vendor_sdpa_measure(blocks: dict, reps: int = 10) -> dict:
+    """Causal attention of one rank's heads through torch's fused scaled_dot_product_attention (flash and
+    memory-efficient backends only; a backend that cannot take the shape is reported, never replaced by the math
+    path), forward and backward, beside this library's attention kernels from the attention-block legs.  A
+    comparison point only."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    out = {}
+    for key, (hq, d) in (("attention_block", (8, 96)), ("attention_block_gqa", (8, 128))):
+        s = 4096
+        q, k, v = (torch.randn(1, hq, s, d, device="cuda", dtype=torch.bfloat16) for _ in range(3))
+        res = {}
+        for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+            try:
+                with sdpa_kernel([be]):
+                    qq, kk, vv = (x.clone().requires_grad_(True) for x in (q, k, v))
+                    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True)
+                    go = torch.randn_like(o)
+
+                    def timed(fn):
+                        for _ in range(2):
+                            fn()
+                        torch.cuda.synchronize()
+                        ts = []
+                        for _ in range(reps):
+                            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                            e0.record()
+                            fn()
+                            e1.record()
+                            torch.cuda.synchronize()
+                            ts.append(e0.elapsed_time(e1) * 1e3)
+                        return round(sorted(ts)[len(ts) // 2], 2)
+
+                    fwd = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True))
+                    bwd = timed(lambda: o.backward(go, retain_graph=True))
+                    res[be.name] = {"fwd_median_us": fwd, "bwd_median_us": bwd}
+                    del qq, kk, vv, o, go
+            except Exception as e:  # the backend does not take this shape: say so
+                res[be.name] = {"error": str(e)[:160]}
+        b = blocks.get(key, {})
+        ours_f = b.get("roles", {}).get("attention", {}).get("us_per_rank")
+        ours_b = b.get("backward", {}).get("roles", {}).get("attention_core_bwd", {}).get("us_per_rank")
+        out[key] = {"shape": f"b=1, {hq} heads, s={s}, d={d}, causal", "torch_sdpa": res,
+                    "ours_fwd_us": ours_f, "ours_bwd_us": ours_b}
+        del q, k, v
+    return out
 
 
 def gather_measure(L, reps: int) -> dict:
@@ -621,6 +671,8 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
         if w.dtype == "bf16":
             out["vendor_gemm"] = vendor_gemm_measure(w, out["kernels"])
+            torch.cuda.empty_cache()
+            out["vendor_sdpa"] = vendor_sdpa_measure(out)
             torch.cuda.empty_cache()
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
