@@ -6,8 +6,8 @@
 // bf16 kernel, one workgroup = 64 queries of one (batch, head), 4 waves x 16 queries, key blocks of 64:
 //   * K and V tiles are copied as they sit in HBM (direct global -> LDS copies, 16 bytes per lane) into a ring of
 //     3 LDS stages, so the copies of block kt+2 are in flight while block kt is multiplied.  Within a row the
-//     16-byte chunks are rotated by the row index, so the 16 rows one fragment read touches fall in different
-//     banks.
+//     16-byte chunks are permuted by a per-row XOR pattern (tile_chunk), so both the 16-byte fragment reads and
+//     the transposing reads of a pass fall in distinct banks.
 //   * S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): K fragments are 16-byte LDS reads, the wave's
 //     16 queries sit in registers for the whole kernel.  In the transposed product every lane owns one query
 //     (lane & 15), so the row statistics need only a max over the 4 lane groups that share it.
@@ -98,6 +98,24 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Physical 16-byte chunk of logical chunk c of row r in a K / V (forward, dQ) or Q / dO (dK / dV) tile of CH
+// chunks per row: c XOR z(r mod 8).  The LDS serves a 16-byte fragment read 8 lanes (128 bytes, 32 banks) per pass
+// and a transposing 8-byte read 32 lanes (256 bytes, 64 banks) per pass -- the widths under which the large-tile
+// GEMM's reads, which the bank-conflict counter reports free, are conflict-free, and which account for the counts
+// measured here.  The two reads of these tiles touch 8 consecutive rows at one chunk (16-byte reads) and 8
+// consecutive rows at an even-odd chunk pair (transposing reads); z makes both hit distinct banks:
+//   CH = 4, 12 (rows start 0 or 4 chunks into a 128-byte window): z = r / 2;
+//   CH = 8: z = r;  CH = 16: z = 2 r + r / 4.
+// Each z keeps c ^ z a chunk of the row.  A rotation by the row index doubled the passes of the transposing reads
+// at every head size and of the 16-byte reads at d = 96.
+template <int CH>
+__device__ __forceinline__ int tile_chunk(int r, int c) {
+  static_assert(CH == 4 || CH == 8 || CH == 12 || CH == 16, "chunks per row");
+  const int b = r & 7;
+  const int z = (CH == 8) ? b : (CH == 16) ? 2 * b + (b >> 2) : (b >> 1);
+  return c ^ z;
+}
+
 // Work rank (0 = the most work) of the causal tile a workgroup takes, from its launch-order index u over n tiles.
 // Heaviest first, so that workgroups dealt out as CUs free up balance greedily -- unless the whole grid is resident
 // at once (fold): then the first half of the launch takes ranks 0 .. h-1 and the second half ranks n-1 down to h,
@@ -163,14 +181,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
   const int klim = p.causal ? min(q, p.s - 1) : p.s - 1;  // last key this lane's query sees
 
   // ---- copies: copy c (0 .. CH-1) of a tile fills LDS chunks 64 c .. 64 c + 63; wave w issues copies w + 4 i.
-  // LDS chunk position P = r CH + slot holds chunk (slot - r) mod CH of row r (chunks past d repeat chunk 0).
+  // LDS chunk position P = r CH + slot holds chunk tile_chunk(r, slot) of row r (the map is its own inverse;
+  // chunks past d repeat chunk 0).
   int crow[CPW], ccol[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int P = (wave + 4 * i) * 64 + lane;
     const int r = P / CH, slot = P % CH;
-    int c = slot - r % CH;
-    if (c < 0) c += CH;
+    const int c = tile_chunk<CH>(r, slot);
     crow[i] = r;
     ccol[i] = (c * 8 < d) ? c * 8 : 0;
   }
@@ -188,7 +206,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
     }
   };
   // ---- fragment read offsets (bytes within a tile), loop invariant
-  auto chunk_off = [&](int r, int c) { return r * CH * 16 + ((c + r) % CH) * 16; };
+  auto chunk_off = [&](int r, int c) { return r * CH * 16 + tile_chunk<CH>(r, c) * 16; };
   int koff[4][NDS];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -467,14 +485,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   const int nblk = nqb - qb0;
   const int ntot = HS * nblk;  // (query head of the split, query block) steps, head by head
 
-  // ---- copies (same chunk rotation as the forward's K / V tiles); wave 0 also copies the block's record
+  // ---- copies (same chunk layout as the forward's K / V tiles); wave 0 also copies the block's record
   int crow[CPW], ccol[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int P = (wave + 4 * i) * 64 + lane;
     const int r = P / CH, slot = P % CH;
-    int c = slot - r % CH;
-    if (c < 0) c += CH;
+    const int c = tile_chunk<CH>(r, slot);
     crow[i] = r;
     ccol[i] = (c * 8 < d) ? c * 8 : 0;
   }
@@ -496,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
     }
     if (wave == 0) dma16(rsrc + 4 * lane, __builtin_amdgcn_readfirstlane(sb + 2 * TILE_B));
   };
-  auto chunk_off = [&](int r, int c) { return r * CH * 16 + ((c + r) % CH) * 16; };
+  auto chunk_off = [&](int r, int c) { return r * CH * 16 + tile_chunk<CH>(r, c) * 16; };
   int roff[4][NDS];  // A fragments of Q / dO rows (queries 16 qs + l16), d = 32u + 8g
 #pragma unroll
   for (int qs = 0; qs < 4; ++qs)
@@ -699,8 +716,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
   for (int i = 0; i < CPW; ++i) {
     const int P = (wave + 4 * i) * 64 + lane;
     const int r = P / CH, slot = P % CH;
-    int c = slot - r % CH;
-    if (c < 0) c += CH;
+    const int c = tile_chunk<CH>(r, slot);
     crow[i] = r;
     ccol[i] = (c * 8 < d) ? c * 8 : 0;
   }
@@ -717,7 +733,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
       dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
     }
   };
-  auto chunk_off = [&](int r, int c) { return r * CH * 16 + ((c + r) % CH) * 16; };
+  auto chunk_off = [&](int r, int c) { return r * CH * 16 + tile_chunk<CH>(r, c) * 16; };
   int koff[4][NDS];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
