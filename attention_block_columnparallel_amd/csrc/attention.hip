@@ -116,6 +116,15 @@ __device__ __forceinline__ int tile_chunk(int r, int c) {
   return c ^ z;
 }
 
+// Complete a wave's register-resident fragments (ordinary global loads) before its key or query loop: left to the
+// compiler, the wait for them lands at their first use inside the loop as vmcnt(0) -- the compiler does not count
+// the direct copies -- and drains the copies of the next blocks once per unrolled iteration.
+template <typename T, int N>
+__device__ __forceinline__ void settle(const T (&f)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(f[i]));
+}
+
 // Work rank (0 = the most work) of the causal tile a workgroup takes, from its launch-order index u over n tiles.
 // Heaviest first, so that workgroups dealt out as CUs free up balance greedily -- unless the whole grid is resident
 // at once (fold): then the first half of the launch takes ranks 0 .. h-1 and the second half ranks n-1 down to h,
@@ -175,6 +184,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
     if (q < p.s && dd < d) v = *reinterpret_cast<const uint4*>(qkv + (int64_t)q * tok_stride + dd);
     qf[u] = __builtin_bit_cast(bf16x8_t, v);
   }
+  settle(qf);
 
   const int nkt_all = (p.s + KT - 1) / KT;
   const int nkt = p.causal ? min(nkt_all, qtile + 1) : nkt_all;
@@ -481,6 +491,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
     kf[u] = __builtin_bit_cast(bf16x8_t, a);
     vf[u] = __builtin_bit_cast(bf16x8_t, b);
   }
+  settle(kf);
+  settle(vf);
   const int qb0 = p.causal ? ktile : 0;
   const int nblk = nqb - qb0;
   const int ntot = HS * nblk;  // (query head of the split, query block) steps, head by head
@@ -705,6 +717,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
     df[u] = __builtin_bit_cast(bf16x8_t, b);
   }
   const float lse2 = q < p.s ? p.lse[(int64_t)bh * p.s + q] * 1.4426950408889634f : 0.f;
+  settle(qf);
+  settle(df);
+  asm volatile("" ::"v"(lse2));
   float* const drec = p.rec + ((int64_t)bh * ((p.s + 63) / 64) + q / 64) * 256 + 64 + (q % 64);
   float dsum = 0.f;
 
