@@ -357,6 +357,225 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
   }
 }
 
+// Key-split variant of the forward: 8 waves, wave = 4 kh + qw.  Wave (kh, qw) takes queries 16 qw .. 16 qw + 15 of
+// the tile and keys 32 kh .. 32 kh + 31 of every block, with running statistics of its own; the two halves of each
+// query group merge through LDS at the end (m = max(m0, m1), l = l0 2^(m0-m) + l1 2^(m1-m), likewise O).  Each
+// wave reads half of each K / V tile and does half the MFMAs and softmax work of the 4-wave kernel, so a SIMD holds
+// twice the waves over the same tiles.  Only the kh = 0 waves issue the copies (their waits count them); a key half
+// that is entirely masked (the diagonal block's upper half for the tile's first 32 queries) keeps m = -inf, and its
+// probabilities are taken as 0, not exp2(-inf + inf).
+template <int DP>
+__global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) {
+  constexpr int CH = DP / 8;
+  constexpr int TILE_B = KT * CH * 16;
+  constexpr int STAGE_B = 2 * TILE_B;
+  constexpr int CPW = CH / 4;   // copies per copying wave per tile and operand
+  constexpr int NC = 2 * CPW;   // copies per copying wave per block
+  constexpr int NDS = DP / 32;
+  constexpr int NST = DP / 16;
+  constexpr int NS = kv_stages<DP>();
+  constexpr int MREC = NST * 4 + 2;  // merge record per lane: O (NST x 4), m, l
+  static_assert(4 * 64 * MREC * 4 <= NS * STAGE_B, "merge records fit in the ring");
+  __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_B];
+  constexpr int D = NS - 1;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int qw = wave & 3, kh = wave >> 2;
+  const int nq = (p.s + QT - 1) / QT;
+  const int nbh = p.b * p.hl;
+  const int qtile = nq - 1 - work_rank((int)blockIdx.x / nbh, nq, p.fold);
+  const int bh = (int)blockIdx.x % nbh;
+  const int bidx = bh / p.hl, jj = bh % p.hl;
+  const int d = p.d;
+  const QkvCols cols = qkv_cols(p.hl, p.G, d, jj);
+  const int64_t ldq = cols.ld;
+  const int64_t tok_stride = ldq * p.b;
+  const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + cols.q;
+  const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + cols.k;
+
+  const int q = qtile * QT + qw * 16 + l16;
+  bf16x8_t qf[NDS];
+#pragma unroll
+  for (int u = 0; u < NDS; ++u) {
+    const int dd = 32 * u + 8 * g;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (q < p.s && dd < d) v = *reinterpret_cast<const uint4*>(qkv + (int64_t)q * tok_stride + dd);
+    qf[u] = __builtin_bit_cast(bf16x8_t, v);
+  }
+  settle(qf);
+
+  const int nkt_all = (p.s + KT - 1) / KT;
+  const int nkt = p.causal ? min(nkt_all, qtile + 1) : nkt_all;
+  const int klim = p.causal ? min(q, p.s - 1) : p.s - 1;
+
+  // copies (kh = 0 waves): copy c of a tile fills LDS chunks 64 c .. 64 c + 63; wave qw issues copies qw + 4 i
+  int crow[CPW], ccol[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int P = (qw + 4 * i) * 64 + lane;
+    const int r = P / CH, slot = P % CH;
+    const int c = tile_chunk<CH>(r, slot);
+    crow[i] = r;
+    ccol[i] = (c * 8 < d) ? c * 8 : 0;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
+  auto issue_tile = [&](int kt, int st) {
+    if (kh != 0) return;
+    const int kv0 = min(kt, nkt - 1) * KT;
+    const uint32_t sb = lds0 + st * STAGE_B;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const int row = min(kv0 + crow[i], p.s - 1);
+      const uint16_t* src = kbase + (int64_t)row * tok_stride + ccol[i];
+      const uint32_t dst = sb + (qw + 4 * i) * 1024;
+      dma16(src, __builtin_amdgcn_readfirstlane(dst));
+      dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
+    }
+  };
+  auto chunk_off = [&](int r, int c) { return r * CH * 16 + tile_chunk<CH>(r, c) * 16; };
+  int koff[2][NDS];  // this wave's two 16-key subtiles 2 kh, 2 kh + 1
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int u = 0; u < NDS; ++u) koff[i][u] = chunk_off(16 * (2 * kh + i) + l16, 4 * u + g);
+  int voff[NST][2];  // V^T fragments of this wave's 32-key step
+#pragma unroll
+  for (int st = 0; st < NST; ++st)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int R = 32 * kh + 16 * hh + 4 * g + (l16 >> 2);
+      const int dc = 16 * st + 4 * (l16 & 3);
+      voff[st][hh] = chunk_off(R, dc >> 3) + ((dc >> 2) & 1) * 8;
+    }
+
+  const float c2 = p.scale * 1.4426950408889634f;
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x4_t acc_o[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) acc_o[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int i = 0; i < D; ++i) issue_tile(i, i);
+  wait_vmcnt<(D - 1) * NC>();
+  __syncthreads();
+
+  auto block = [&](int kt, auto stage) {
+    constexpr int st_cur = decltype(stage)::value;
+    constexpr int st_new = (st_cur + D) % NS;
+    issue_tile(kt + D, st_new);
+    const char* Kt = &lds[st_cur * STAGE_B];
+    const char* Vt = Kt + TILE_B;
+    const int kv0 = kt * KT + 32 * kh;  // this wave's first key
+
+    bf16x8_t kfr[2][NDS];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int u = 0; u < NDS; ++u) kfr[i][u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Kt + koff[i][u]));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t sc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      sc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NDS; ++u) sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[i][u], qf[u], sc[i], 0, 0, 0);
+    }
+    bf16x8_t vfr[NST];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[st][0]));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[st][1]));
+      const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      vfr[st] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if ((p.causal && kt == qtile) || (kt * KT + KT > p.s)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[i][e] = (kv0 + i * 16 + 4 * g + e > klim) ? -INFINITY : sc[i][e];
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[i][e]);
+    mx = max_over_groups(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (__any(m_new > m_run)) {
+      const float corr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
+      l_part *= corr;
+#pragma unroll
+      for (int st = 0; st < NST; ++st) acc_o[st] *= corr;
+      m_run = m_new;
+    }
+    const float nm = m_run == -INFINITY ? 0.f : -m_run * c2;  // a fully masked half: every p is exp2(-inf) = 0
+    float psum = 0.f;
+    uint32_t pk[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      float pe[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[i][e], c2, nm));
+        psum += pe[e];
+      }
+      pk[i][0] = pack_bf16x2_hw(pe[0], pe[1]);
+      pk[i][1] = pack_bf16x2_hw(pe[2], pe[3]);
+    }
+    l_part += psum;
+    const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
+#pragma unroll
+    for (int st = 0; st < NST; ++st) acc_o[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[st], pf, acc_o[st], 0, 0, 0);
+    wait_vmcnt<(D - 1) * NC>();
+    __syncthreads();
+  };
+  for (int kt = 0; kt < nkt; kt += NS) {
+    block(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nkt) block(kt + 1, std::integral_constant<int, 1>{});
+    if constexpr (NS > 2) {
+      if (kt + 2 < nkt) block(kt + 2, std::integral_constant<int, 2 % NS>{});
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every copy has landed and every read of the ring is done: it holds the merge records now
+
+  float* rec = reinterpret_cast<float*>(lds) + (qw * 64 + lane) * MREC;
+  if (kh == 1) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rec[st * 4 + e] = acc_o[st][e];
+    rec[NST * 4] = m_run;
+    rec[NST * 4 + 1] = l_part;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float m1 = rec[NST * 4], l1 = rec[NST * 4 + 1];
+  const float m = fmaxf(m_run, m1);  // m_run is finite: key 0 is visible to every query in block 0
+  const float f0 = __builtin_amdgcn_exp2f((m_run - m) * c2), f1 = __builtin_amdgcn_exp2f((m1 - m) * c2);
+  const float l_tot = sum_over_groups(l_part * f0 + l1 * f1);
+  if (q < p.s) {
+    const float inv = 1.f / l_tot;
+    uint16_t* o = static_cast<uint16_t*>(p.o) + ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jj * d;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int dd = st * 16 + 4 * g;
+      if (dd < d) {
+        float ov[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (acc_o[st][e] * f0 + rec[st * 4 + e] * f1) * inv;
+        uint2 w;
+        w.x = pack_bf16x2_hw(ov[0], ov[1]);
+        w.y = pack_bf16x2_hw(ov[2], ov[3]);
+        *reinterpret_cast<uint2*>(o + dd) = w;
+      }
+    }
+    if (p.lse != nullptr && g == 0)
+      p.lse[((int64_t)bidx * p.hl + jj) * p.s + q] = (m * c2 + log2f(l_tot)) * 0.69314718055994531f;
+  }
+}
+
 // fp32: one thread per query, keys visited one at a time with the same online merge.
 __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams p) {
   constexpr int DMAX = 128;
@@ -977,7 +1196,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_sum_kernel(AttnBwdParams p) {
 
 // Workgroups of Kernel (256 threads) resident on the current device at once; 0 when the runtime cannot say.  A
 // template on the kernel itself, so each kernel has its own cache (kernels of one signature share a type).
-template <auto Kernel>
+template <auto Kernel, int NT = 256>
 int64_t resident_limit() {
   const void* const kernel = reinterpret_cast<const void*>(Kernel);
   constexpr int kMaxDevices = 64;
@@ -990,7 +1209,7 @@ int64_t resident_limit() {
     // 96 KB of static LDS on a 160 KB CU)
     int per_cu = 0, cus = 0, lds_cu = 0;
     hipFuncAttributes fa;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NT, 0) != hipSuccess ||
         hipFuncGetAttributes(&fa, kernel) != hipSuccess ||
         hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
@@ -1004,9 +1223,9 @@ int64_t resident_limit() {
   return v - 1;
 }
 
-template <auto Kernel>
+template <auto Kernel, int NT = 256>
 int fold_for(unsigned grid, int causal) {
-  return causal && (int64_t)grid <= resident_limit<Kernel>() ? 1 : 0;
+  return causal && (int64_t)grid <= resident_limit<Kernel, NT>() ? 1 : 0;
 }
 
 template <int DP>
@@ -1038,8 +1257,15 @@ hipError_t launch_bf16(const AttnParams& p0, hipStream_t st) {
   AttnParams p = p0;
   const int nq = (p.s + QT - 1) / QT;
   const unsigned grid = (unsigned)(nq * p.b * p.hl);
-  p.fold = fold_for<attn_fwd_bf16_kernel<DP>>(grid, p.causal);
   static const std::string name = "attn_fwd_bf16_d" + std::to_string(DP);
+#ifndef TP_ATTN_KS
+#define TP_ATTN_KS 1
+#endif
+  if constexpr (TP_ATTN_KS) {
+    p.fold = fold_for<attn_fwd_bf16_ks_kernel<DP>, 512>(grid, p.causal);
+    return TP_LAUNCH(name.c_str(), (attn_fwd_bf16_ks_kernel<DP>), dim3(grid), dim3(512), 0, st, p);
+  }
+  p.fold = fold_for<attn_fwd_bf16_kernel<DP>>(grid, p.causal);
   return TP_LAUNCH(name.c_str(), (attn_fwd_bf16_kernel<DP>), dim3(grid), dim3(256), 0, st, p);
 }
 
