@@ -61,6 +61,27 @@ def test_attention_small_ragged(L, dtype, d, causal):
         assert np.max(np.abs(lse - ref["lse"])) < (1e-4 if dtype == "f32" else 2e-2)
 
 
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_short_sequence_masked_key_half(L, d, causal):
+    # s < 32: the forward splits each 64-key block between two waves of the same queries, and here the upper half
+    # (keys 32..63) holds no key at all, so that half's running max stays -inf up to the merge
+    a, t, s = 4, 2, 20
+    w = TI.Workload("attn_short", "attn", s=s, b=3, h=a * d, a=a, d=d, t=t, causal=causal, dtype="bf16")
+    say(f"attention s={s} b=3 a=4 d={d} t=2 causal={causal} bf16")
+    inp = TI.attn_inputs(w, with_bias=False, seed=100 + d)
+    X = O.as_f64(inp["X"], "bf16").reshape(w.M, w.h)
+    Wqkv, Wo = O.as_f64(inp["Wqkv"], "bf16"), O.as_f64(inp["Wo"], "bf16")
+    for r in range(t):
+        got = run_rank(L, w, inp, r, "bf16", False, causal)
+        ref = O.attention_shard_forward(X, Wqkv, Wo, w.s, w.b, a, d, t, r, causal, None)
+        assert torch.isfinite(got["O"].float()).all() and torch.isfinite(got["lse"]).all()
+        check_close(f64(got["O"]), ref["O"], "bf16", "O", row_unit=True)
+        check_close(f64(got["Z"]), ref["Z"], "bf16", "Z", row_unit=True)
+        lse = got["lse"].cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(lse - ref["lse"])) < 2e-2
+
+
 def test_attention_full_size_one_rank_sampled(L):
     w = TI.ATTN_22B
     r = 3
