@@ -3,23 +3,22 @@
 // (TP) 与 Sequence Parallelism (SP)" §3 and the Megatron-LM visual reading: heads are independent, each is local
 // to its rank; "Sequence Parallel 与 Context Parallel", CP step 3: block statistics merged by online softmax).
 //
-// bf16 kernel, one workgroup = 64 queries of one (batch, head), 4 waves x 16 queries, key blocks of 64:
+// bf16 kernel, one workgroup = 64 queries of one (batch, head), key blocks of 64, 8 waves: wave (kh, qw) takes 16
+// queries (qw) and one 32-key half (kh) of every block, with statistics of its own, merged at the end:
 //   * K and V tiles are copied as they sit in HBM (direct global -> LDS copies, 16 bytes per lane) into a ring of
-//     3 LDS stages, so the copies of block kt+2 are in flight while block kt is multiplied.  Within a row the
-//     16-byte chunks are permuted by a per-row XOR pattern (tile_chunk), so both the 16-byte fragment reads and
-//     the transposing reads of a pass fall in distinct banks.
+//     LDS stages (3 at d <= 96, 2 at d = 128), so the copies of the next blocks are in flight while one block is
+//     multiplied.  Within a row the 16-byte chunks are permuted by a per-row XOR pattern (tile_chunk), so both the
+//     16-byte fragment reads and the transposing reads of a pass fall in distinct banks.
 //   * S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): K fragments are 16-byte LDS reads, the wave's
 //     16 queries sit in registers for the whole kernel.  In the transposed product every lane owns one query
 //     (lane & 15), so the row statistics need only a max over the 4 lane groups that share it.
 //   * O^T = V^T P^T: the probabilities never leave registers.  A lane holds scores for keys 4g..4g+3 and
-//     16+4g..16+4g+3 of each 32-key step (g = lane >> 4); the V^T fragment is gathered from the untransposed V
-//     tile by two transposing LDS reads (ds_read_b64_tr_b16) whose row addresses follow the same key order, so the
-//     pair of operands agree on k.
-//   * Each block reads all its K fragments before the S^T MFMAs and all its V^T fragments right after them, so
-//     the read latency overlaps the MFMAs and the softmax arithmetic; the causal mask is one select per score.
+//     16+4g..16+4g+3 of its 32-key half (g = lane >> 4); the V^T fragment is gathered from the untransposed V tile
+//     by two transposing LDS reads (ds_read_b64_tr_b16) whose row addresses follow the same key order, so the pair
+//     of operands agree on k.
 //   * Softmax in base 2 with the scale folded into one FMA per score (exp2(s c - m c), c = scale log2 e) and the
 //     hardware exp2; row statistics combine the 4 lane groups with the gfx950 lane swaps; the running output is
-//     rescaled only in blocks where some query's maximum rose.
+//     rescaled only in blocks where some query's maximum rose; the causal mask is one select per score.
 //   * Query tiles are issued heaviest first over all heads (causal work grows with the tile index).
 #include <math.h>
 
@@ -148,222 +147,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int DP>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnParams p) {
-  constexpr int CH = DP / 8;            // 16-byte chunks per K or V row in LDS
-  constexpr int TILE_B = KT * CH * 16;  // bytes of one K (or V) tile
-  constexpr int STAGE_B = 2 * TILE_B;   // K tile then V tile
-  constexpr int CPW = CH / 4;           // copies of 64 lanes per wave per tile and operand
-  constexpr int NC = 2 * CPW;           // copies per wave per block (K and V)
-  constexpr int NDS = DP / 32;          // 32-wide d steps of S^T
-  constexpr int NST = DP / 16;          // 16-row d subtiles of O^T
-  constexpr int NS = kv_stages<DP>();
-  __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_B];
-  constexpr int D = NS - 1;  // blocks in flight ahead of the one being multiplied
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int nq = (p.s + QT - 1) / QT;
-  const int nbh = p.b * p.hl;
-  const int qtile = nq - 1 - work_rank((int)blockIdx.x / nbh, nq, p.fold);  // over all (batch, head) pairs
-  const int bh = (int)blockIdx.x % nbh;
-  const int bidx = bh / p.hl, jj = bh % p.hl;
-  const int d = p.d;
-  const QkvCols cols = qkv_cols(p.hl, p.G, d, jj);
-  const int64_t ldq = cols.ld;           // elements per token row of QKV
-  const int64_t tok_stride = ldq * p.b;  // consecutive sequence positions
-  const uint16_t* __restrict__ qkv = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + cols.q;
-  const uint16_t* __restrict__ kbase = static_cast<const uint16_t*>(p.qkv) + (int64_t)bidx * ldq + cols.k;  // V: + d
-
-  // ---- this lane's query and its fragments (k = d: lane supplies d = 32u + 8g .. +8)
-  const int q = qtile * QT + wave * 16 + l16;
-  bf16x8_t qf[NDS];
-#pragma unroll
-  for (int u = 0; u < NDS; ++u) {
-    const int dd = 32 * u + 8 * g;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (q < p.s && dd < d) v = *reinterpret_cast<const uint4*>(qkv + (int64_t)q * tok_stride + dd);
-    qf[u] = __builtin_bit_cast(bf16x8_t, v);
-  }
-  settle(qf);
-
-  const int nkt_all = (p.s + KT - 1) / KT;
-  const int nkt = p.causal ? min(nkt_all, qtile + 1) : nkt_all;
-  const int klim = p.causal ? min(q, p.s - 1) : p.s - 1;  // last key this lane's query sees
-
-  // ---- copies: copy c (0 .. CH-1) of a tile fills LDS chunks 64 c .. 64 c + 63; wave w issues copies w + 4 i.
-  // LDS chunk position P = r CH + slot holds chunk tile_chunk(r, slot) of row r (the map is its own inverse;
-  // chunks past d repeat chunk 0).
-  int crow[CPW], ccol[CPW];
-#pragma unroll
-  for (int i = 0; i < CPW; ++i) {
-    const int P = (wave + 4 * i) * 64 + lane;
-    const int r = P / CH, slot = P % CH;
-    const int c = tile_chunk<CH>(r, slot);
-    crow[i] = r;
-    ccol[i] = (c * 8 < d) ? c * 8 : 0;
-  }
-  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
-  auto issue_tile = [&](int kt, int st) {
-    const int kv0 = min(kt, nkt - 1) * KT;  // past the last block: a harmless re-copy of it
-    const uint32_t sb = lds0 + st * STAGE_B;
-#pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int row = min(kv0 + crow[i], p.s - 1);
-      const uint16_t* src = kbase + (int64_t)row * tok_stride + ccol[i];
-      const uint32_t dst = sb + (wave + 4 * i) * 1024;
-      dma16(src, __builtin_amdgcn_readfirstlane(dst));
-      dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
-    }
-  };
-  // ---- fragment read offsets (bytes within a tile), loop invariant
-  auto chunk_off = [&](int r, int c) { return r * CH * 16 + tile_chunk<CH>(r, c) * 16; };
-  int koff[4][NDS];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int u = 0; u < NDS; ++u) koff[ks][u] = chunk_off(16 * ks + l16, 4 * u + g);
-  int voff[2][NST][2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int st = 0; st < NST; ++st)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int R = 32 * u + 16 * hh + 4 * g + (l16 >> 2);
-        const int dc = 16 * st + 4 * (l16 & 3);
-        voff[u][st][hh] = chunk_off(R, dc >> 3) + ((dc >> 2) & 1) * 8;
-      }
-
-  const float c2 = p.scale * 1.4426950408889634f;  // scores -> log2 units
-  float m_run = -INFINITY, l_part = 0.f;
-  f32x4_t acc_o[NST];
-#pragma unroll
-  for (int st = 0; st < NST; ++st) acc_o[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int i = 0; i < D; ++i) issue_tile(i, i);
-  wait_vmcnt<(D - 1) * NC>();  // block 0 has landed (blocks 1 .. D-1 may still be in flight)
-  __syncthreads();
-
-  // one key block; the ring stage is a template constant, so the stage offsets fold into the LDS instructions'
-  // immediate offsets (the loop below is unrolled over the NS stages)
-  auto block = [&](int kt, auto stage) {
-    constexpr int st_cur = decltype(stage)::value;
-    constexpr int st_new = (st_cur + D) % NS;
-    issue_tile(kt + D, st_new);
-    const char* Kt = &lds[st_cur * STAGE_B];
-    const char* Vt = Kt + TILE_B;
-    const int kv0 = kt * KT;
-
-    // all K fragment reads of the block first, then the S^T MFMAs (each finds its operand landed)
-    bf16x8_t kfr[4][NDS];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int u = 0; u < NDS; ++u) kfr[ks][u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Kt + koff[ks][u]));
-    __builtin_amdgcn_sched_barrier(0);
-    // S^T [64 keys x 16 queries] in 4 subtiles of 16 keys
-    f32x4_t sc[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      sc[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < NDS; ++u) sc[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[ks][u], qf[u], sc[ks], 0, 0, 0);
-    }
-    // V^T fragments for the PV step, read now so their latency overlaps the softmax arithmetic
-    bf16x8_t vfr[2][NST];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[u][st][0]));
-        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(Vt + voff[u][st][1]));
-        const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        vfr[u][st] = __builtin_bit_cast(bf16x8_t, w);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    // mask (diagonal and ragged blocks only): key kv is visible iff kv <= klim; block max of the raw scores
-    if ((p.causal && kt == qtile) || (kv0 + KT > p.s)) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sc[ks][e] = (kv0 + ks * 16 + 4 * g + e > klim) ? -INFINITY : sc[ks][e];
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[ks][e]);
-    mx = max_over_groups(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (__any(m_new > m_run)) {  // some query's maximum rose: rescale (corr = 1 where it did not)
-      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * c2);
-      l_part *= corr;
-#pragma unroll
-      for (int st = 0; st < NST; ++st) acc_o[st] *= corr;
-      m_run = m_new;
-    }
-    const float nm = -m_run * c2;
-    float psum = 0.f;
-    uint32_t pk[4][2];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float pe[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[ks][e], c2, nm));
-        psum += pe[e];
-      }
-      pk[ks][0] = pack_bf16x2_hw(pe[0], pe[1]);
-      pk[ks][1] = pack_bf16x2_hw(pe[2], pe[3]);
-    }
-    l_part += psum;
-
-    // O^T [d x 16 queries] += V^T P^T, two 32-key steps
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pk[2 * u][0], pk[2 * u][1], pk[2 * u + 1][0], pk[2 * u + 1][1]));
-#pragma unroll
-      for (int st = 0; st < NST; ++st) acc_o[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[u][st], pf, acc_o[st], 0, 0, 0);
-    }
-    wait_vmcnt<(D - 1) * NC>();  // block kt+1 has landed (blocks kt+2 .. kt+D may still be in flight)
-    __syncthreads();   // publishes block kt+1; every wave is done with stage st_cur, refilled next iteration
-  };
-  for (int kt = 0; kt < nkt; kt += NS) {
-    block(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < nkt) block(kt + 1, std::integral_constant<int, 1>{});
-    if constexpr (NS > 2) {
-      if (kt + 2 < nkt) block(kt + 2, std::integral_constant<int, 2 % NS>{});
-    }
-  }
-  wait_vmcnt<0>();
-
-  const float l_tot = sum_over_groups(l_part);
-  if (q < p.s) {
-    const float inv = 1.f / l_tot;
-    uint16_t* o = static_cast<uint16_t*>(p.o) + ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * d) + (int64_t)jj * d;
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      const int dd = st * 16 + 4 * g;
-      if (dd < d) {
-        uint2 w;
-        w.x = pack_bf16x2_hw(acc_o[st][0] * inv, acc_o[st][1] * inv);
-        w.y = pack_bf16x2_hw(acc_o[st][2] * inv, acc_o[st][3] * inv);
-        *reinterpret_cast<uint2*>(o + dd) = w;
-      }
-    }
-    if (p.lse != nullptr && g == 0)
-      p.lse[((int64_t)bidx * p.hl + jj) * p.s + q] = (m_run * c2 + log2f(l_tot)) * 0.69314718055994531f;
-  }
-}
-
-// Key-split variant of the forward: 8 waves, wave = 4 kh + qw.  Wave (kh, qw) takes queries 16 qw .. 16 qw + 15 of
-// the tile and keys 32 kh .. 32 kh + 31 of every block, with running statistics of its own; the two halves of each
-// query group merge through LDS at the end (m = max(m0, m1), l = l0 2^(m0-m) + l1 2^(m1-m), likewise O).  Each
-// wave reads half of each K / V tile and does half the MFMAs and softmax work of the 4-wave kernel, so a SIMD holds
-// twice the waves over the same tiles.  Only the kh = 0 waves issue the copies (their waits count them); a key half
-// that is entirely masked (the diagonal block's upper half for the tile's first 32 queries) keeps m = -inf, and its
-// probabilities are taken as 0, not exp2(-inf + inf).
+// The forward kernel.  Wave (kh, qw) of the 8 takes queries 16 qw .. 16 qw + 15 of the tile and keys
+// 32 kh .. 32 kh + 31 of every block, with running statistics of its own; the two halves of each query group merge
+// through LDS at the end (m = max(m0, m1), l = l0 2^(m0-m) + l1 2^(m1-m), likewise O).  Splitting the keys rather
+// than giving each wave all 64 keys of a block (4 waves of 16 queries; about 5% slower at d = 96 and 128) lets a
+// SIMD hold four waves over the same K / V tiles instead of two.  Only the kh = 0 waves issue the copies (their
+// waits count them); a key half that is entirely masked (the diagonal block's upper half for the tile's first 32
+// queries, every block when s <= 32) keeps m = -inf, and its probabilities are taken as 0, not exp2(-inf + inf).
 template <int DP>
 __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) {
   constexpr int CH = DP / 8;
@@ -619,7 +409,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams p) {
 //     copies into a 3-stage ring.  S = Q K^T and dP = dO V^T take Q / dO rows from LDS and the wave's K / V
 //     fragments from registers; dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T with transposing LDS reads
 //     whose row addresses follow the query order of the P / dS operand (the forward's V trick).
-//   * dQ, run first: the forward's structure (64 queries per workgroup, K and V tiles in the ring): S^T = K Q^T,
+//   * dQ, run first: 64 queries per workgroup, 4 waves x 16, K and V tiles in the ring: S^T = K Q^T,
 //     dP^T = V dO^T, and with K^T gathered by transposing reads A^T += K^T (P dP)^T, B^T += K^T P^T and
 //     D += sum_k P dP, so dQ = (A - D B) scale comes out of one walk over the keys; D is written to the record.
 // ================================================================================================================
@@ -1258,15 +1048,8 @@ hipError_t launch_bf16(const AttnParams& p0, hipStream_t st) {
   const int nq = (p.s + QT - 1) / QT;
   const unsigned grid = (unsigned)(nq * p.b * p.hl);
   static const std::string name = "attn_fwd_bf16_d" + std::to_string(DP);
-  // the key-split kernel; the 4-wave one (the layout the dQ kernel follows) measured about 5% slower at d = 96 and
-  // d = 128 and stays for comparison
-  constexpr bool kKeySplit = true;
-  if constexpr (kKeySplit) {
-    p.fold = fold_for<attn_fwd_bf16_ks_kernel<DP>, 512>(grid, p.causal);
-    return TP_LAUNCH(name.c_str(), (attn_fwd_bf16_ks_kernel<DP>), dim3(grid), dim3(512), 0, st, p);
-  }
-  p.fold = fold_for<attn_fwd_bf16_kernel<DP>>(grid, p.causal);
-  return TP_LAUNCH(name.c_str(), (attn_fwd_bf16_kernel<DP>), dim3(grid), dim3(256), 0, st, p);
+  p.fold = fold_for<attn_fwd_bf16_ks_kernel<DP>, 512>(grid, p.causal);
+  return TP_LAUNCH(name.c_str(), (attn_fwd_bf16_ks_kernel<DP>), dim3(grid), dim3(512), 0, st, p);
 }
 
 }  // namespace
