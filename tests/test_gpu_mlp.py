@@ -155,10 +155,27 @@ def test_bf16_large_ragged_k_sampled(L):
 
 @pytest.mark.parametrize("act", ["gelu", "swiglu"])
 def test_bf16_large_ragged_mn_sampled(L, act):
-    # K % 32 == 0 everywhere (the large-tile kernel) with ragged M = 16352 and N in {1056, 2080, 2 x 2080}
+    # ragged M = 16352 and N in {1056, 2080, 2 x 2080}; K in {1056, 2080} is not a multiple of 64, so these GEMMs take
+    # the register-staged kernel (SwiGLU's dX, K = 4160, the large-tile one)
     w = TI.Workload("large_ragged_mn", "mlp", s=2044, b=8, h=1056, ffn=2 * 2080, t=2, act=act, dtype="bf16")
     say(f"bf16 MLP large ragged M=16352 h=1056 f_l=2080 act={act} (sampled)")
     _sampled_check(L, w, 0, with_bias=True, seed=8)
+
+
+@pytest.mark.parametrize("act", ["gelu", "swiglu"])
+def test_bf16_large_tile_kernels_ragged_sampled(L, act):
+    # every K a multiple of 64 (h = 3136, f_l = 2112, M = 16320) and enough tiles for the pair (over 3/4 of the
+    # CUs), so every GEMM of the rank takes the large-tile kernel -- the 8-wave column, row and dY GEMMs, the 4-wave
+    # dX GEMM and weight-gradient pair -- while M, h and f_l are not multiples of 256: ragged last row and column
+    # tiles in every one of them
+    w = TI.Workload("large_tile_ragged", "mlp", s=2040, b=8, h=3136, ffn=2 * 2112, t=2, act=act, dtype="bf16")
+    say(f"bf16 MLP large-tile kernels ragged M=16320 h=3136 f_l=2112 act={act} (sampled)")
+    with L.LaunchTimer(256, only="gemm_bf16") as lt:
+        _sampled_check(L, w, 1, with_bias=True, seed=11)
+    fwd_epi, bwd_epi = ("swiglu_fwd", "swiglu_bwd") if act == "swiglu" else ("bias_act", "act_bwd")
+    want = {f"gemm_bf16_big_KM_{fwd_epi}", "gemm_bf16_big_KM_store", f"gemm_bf16_big_KK_{bwd_epi}",
+            "gemm_bf16_big_KK_store", "gemm_bf16_big_pair_MM_store"}
+    assert want <= set(lt.names), (want - set(lt.names), lt.names)
 
 
 @pytest.mark.parametrize("name,rank", [("mlp_h3072_ffn12288_t8_b8_s1024", 5),
