@@ -696,7 +696,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   const int nbm = (p.M + BM - 1) / BM;
   const int nbn = SWIG ? (p.fhalf + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
   // row-tile groups of 4 for a single GEMM, 8 for the weight-gradient pair (measured best for each)
-  const int gm = pp.tiles1 > 0 ? 8 : 4;
+  // row-tile groups: 8 for the weight-gradient pair and the act' epilogues, 2 for the plain K-major x MN-major
+  // GEMM, 4 otherwise (measured best for each at h = 4096, ffn/t = 2048)
+  constexpr int GM1 = (EPI == EPI_ACT_BWD || EPI == EPI_SWIGLU_BWD) ? 8 : (AK && !BKM && EPI == EPI_STORE) ? 2 : 4;
+  const int gm = pp.tiles1 > 0 ? 8 : GM1;
   const int group = bid / (gm * nbn);
   const int first_m = group * gm;
   const int gsz = min(nbm - first_m, gm);
@@ -1067,7 +1070,7 @@ __global__ __launch_bounds__(256) void splitk_tail_sum_kernel(GemmPair pp, int n
   const GemmParams& p = pp.g[which];
   if (which) u -= pp.tiles0;
   const int nbm = (p.M + 255) / 256, nbn = (p.N + 255) / 256;
-  const int gm = pp.tiles1 > 0 ? 8 : 4;
+  const int gm = pp.tiles1 > 0 ? 8 : 4;  // the large-tile kernel's grouping for this layout (K- and MN-major A / B)
   const int first_m = (u / (gm * nbn)) * gm;
   const int gsz = min(nbm - first_m, gm);
   const int tile_m = first_m + (u % (gm * nbn)) % gsz;
