@@ -115,21 +115,29 @@ __global__ __launch_bounds__(CE_THREADS) void ce_local_kernel(const void* __rest
       const int c = c0 + k * CE_THREADS;
       if (c < nch) ch[k].load(logits, base + 8 * c);
     }
+    // the four chunks' max first, then their exponentials against it and one merge into the running pair
+    float x[4][8];
+    float cm = -INFINITY;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = c0 + k * CE_THREADS;
       if (c < nch) {
-        float x[8];
-        ch[k].get(x);
-        float cm = x[0];
+        ch[k].get(x[k]);
 #pragma unroll
-        for (int i = 1; i < 8; ++i) cm = fmaxf(cm, x[i]);
-        float cs = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cs += __builtin_amdgcn_exp2f((x[i] - cm) * LOG2E);
-        merge(m, s, cm, cs);
+        for (int i = 0; i < 8; ++i) cm = fmaxf(cm, x[k][i]);
       }
     }
+    const float nb = -cm * LOG2E;
+    float cs = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + k * CE_THREADS;
+      if (c < nch) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cs += __builtin_amdgcn_exp2f(fmaf(x[k][i], LOG2E, nb));
+      }
+    }
+    if (cm > -INFINITY) merge(m, s, cm, cs);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
