@@ -186,31 +186,44 @@ __global__ __launch_bounds__(CE_THREADS) void ce_bwd_kernel(const void* __restri
                                                             const float* __restrict__ lse,
                                                             const float* __restrict__ dloss, int64_t rows, int v,
                                                             int rank, void* __restrict__ dlogits) {
+  // one workgroup per row: the row's target, lse and dloss are read once, and each thread keeps four 16-byte
+  // chunks of logits in flight
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
   const int nch = v >> 3;
-  const int64_t idx = (int64_t)blockIdx.x * CE_THREADS + threadIdx.x;
-  if (idx >= rows * nch) return;
-  const int64_t row = idx / nch;
-  const int c = (int)(idx - row * nch);
-  const int64_t e = row * v + 8 * c;
-  Chunk8<T> ch;
-  ch.load(logits, e);
+  const int64_t base = row * v;
   const int tg = targets[row];
-  float g[8];
-  if (tg < 0) {
+  const float l = lse[row], dl = dloss[row];
+  const int64_t tloc = (int64_t)tg - (int64_t)rank * v;  // the target's column in this shard (if it is one)
+  for (int c0 = tid; c0 < nch; c0 += 4 * CE_THREADS) {
+    Chunk8<T> ch[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) g[i] = 0.0f;
-  } else {
-    const float l = lse[row], dl = dloss[row];
-    const int64_t local = (int64_t)tg - (int64_t)rank * v - 8 * c;  // target's position within this chunk
-    float x[8];
-    ch.get(x);
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + k * CE_THREADS;
+      if (c < nch && tg >= 0) ch[k].load(logits, base + 8 * c);
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = __builtin_amdgcn_exp2f((x[i] - l) * LOG2E);
-      g[i] = (local == i ? p - 1.0f : p) * dl;
+    for (int k = 0; k < 4; ++k) {
+      const int c = c0 + k * CE_THREADS;
+      if (c < nch) {
+        float g[8];
+        if (tg < 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) g[i] = 0.0f;
+        } else {
+          float x[8];
+          ch[k].get(x);
+          const int64_t local = tloc - 8 * c;  // the target's position within this chunk
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float p = __builtin_amdgcn_exp2f((x[i] - l) * LOG2E);
+            g[i] = (local == i ? p - 1.0f : p) * dl;
+          }
+        }
+        Chunk8<T>::store(dlogits, base + 8 * c, g);
+      }
     }
   }
-  Chunk8<T>::store(dlogits, e, g);
 }
 
 }  // namespace
@@ -234,8 +247,7 @@ hipError_t vocab_ce_combine(const float* stats, int t, int64_t rows, const int32
 
 hipError_t vocab_ce_bwd(tp_dtype dt, const void* logits, const int32_t* targets, const float* lse,
                         const float* dloss, int64_t rows, int v, int rank, void* dlogits, hipStream_t st) {
-  const int64_t n = rows * (v / 8);
-  const unsigned blocks = (unsigned)((n + CE_THREADS - 1) / CE_THREADS);
+  const unsigned blocks = (unsigned)rows;  // one workgroup per row
   if (dt == TP_BF16)
     return TP_LAUNCH("vocab_ce_bwd", ce_bwd_kernel<uint16_t>, dim3(blocks), dim3(CE_THREADS), 0, st, logits,
                      targets, lse, dloss, rows, v, rank, dlogits);
