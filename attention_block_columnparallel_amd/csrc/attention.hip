@@ -580,17 +580,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
     const int qbi = qb0 + i % nblk;
     const int q0 = qbi * 64;
 
+    // S and dP in two halves of 32 queries, each half's Q and dO fragments read before its MFMAs (as in dQ)
     f32x4_t sc[4], dp[4];
 #pragma unroll
-    for (int qs = 0; qs < 4; ++qs) {
-      sc[qs] = dp[qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int hq = 0; hq < 2; ++hq) {
+      bf16x8_t qa[2][NDS], da[2][NDS];
 #pragma unroll
-      for (int u = 0; u < NDS; ++u) {
-        const bf16x8_t qa = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Qt + roff[qs][u]));
-        const bf16x8_t da = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Dt + roff[qs][u]));
-        sc[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[u], sc[qs], 0, 0, 0);
-        dp[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da, vf[u], dp[qs], 0, 0, 0);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int u = 0; u < NDS; ++u) {
+          qa[i][u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Qt + roff[2 * hq + i][u]));
+          da[i][u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Dt + roff[2 * hq + i][u]));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int qs = 2 * hq + i;
+        sc[qs] = dp[qs] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NDS; ++u) {
+          sc[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i][u], kf[u], sc[qs], 0, 0, 0);
+          dp[qs] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[i][u], vf[u], dp[qs], 0, 0, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // P and dS for queries q0 + 16 qs + 4 g + e and this lane's key; masked scores become -inf (P = 0), in a
     // branch of their own that only the diagonal block and a ragged last block take
@@ -793,17 +806,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
     const char* Kt = &lds[st_cur * STAGE_B];
     const char* Vt = Kt + TILE_B;
     const int kv0 = kt * KT;
+    // S^T and dP^T in two halves of 32 keys: the half's K and V fragments are all read before its MFMAs, so only
+    // the first MFMA waits on LDS (read one by one, each MFMA waited on the read just before it)
     f32x4_t sc[4], dp[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      sc[ks] = dp[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int hk = 0; hk < 2; ++hk) {
+      bf16x8_t ka[2][NDS], va[2][NDS];
 #pragma unroll
-      for (int u = 0; u < NDS; ++u) {
-        const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Kt + koff[ks][u]));
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Vt + koff[ks][u]));
-        sc[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[u], sc[ks], 0, 0, 0);
-        dp[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, df[u], dp[ks], 0, 0, 0);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int u = 0; u < NDS; ++u) {
+          ka[i][u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Kt + koff[2 * hk + i][u]));
+          va[i][u] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(Vt + koff[2 * hk + i][u]));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ks = 2 * hk + i;
+        sc[ks] = dp[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < NDS; ++u) {
+          sc[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[i][u], qf[u], sc[ks], 0, 0, 0);
+          dp[ks] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i][u], df[u], dp[ks], 0, 0, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // masked scores become -inf (P = 0), in a branch of their own: the diagonal block and a ragged last block only
     if ((p.causal && kt == qtile) || (kv0 + KT > p.s)) {
