@@ -83,6 +83,11 @@ def stored(x: np.ndarray, dtype: str) -> np.ndarray:
     return x32.astype(np.float64)
 
 
+def _keep(x: np.ndarray, store: Optional[str]) -> np.ndarray:
+    """x as the block stores it between two steps: unchanged for store=None (the exact chain), else stored(x)."""
+    return x if store is None else stored(x, store)
+
+
 def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     """Storage form (uint16 bf16 patterns or float32) to float64."""
     if dtype == "bf16":
@@ -393,9 +398,14 @@ def mlp_shard_columns(ffn: int, t: int, rank: int, act: str) -> np.ndarray:
 
 
 def mlp_shard_forward(X: np.ndarray, A: np.ndarray, B: np.ndarray, t: int, rank: int, act: str = "gelu",
-                      a_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                      a_bias: Optional[np.ndarray] = None, store: Optional[str] = None) -> Dict[str, np.ndarray]:
     """Rank r's part of the forward, by slicing the unsharded operands: U_i = X A[:, C_i] + a[C_i], Y_i = act(U_i),
-    Z_i = Y_i B[R_i, :] is a partial sum of full shape (no row bias)."""
+    Z_i = Y_i B[R_i, :] is a partial sum of full shape (no row bias).
+
+    store = None is the exact chain.  store = "bf16" follows the block's data flow with 16-bit activations ([MEGA]
+    calculator and [ATLAS] §5 size every activation at 2 bytes): Y_i is stored before the row GEMM reads it, and
+    U_i is kept stored for the backward.  Each returned entry is the exact value of the step that produces it from
+    its (stored) inputs, before that step's own rounding."""
     ffn = B.shape[0]
     cols = mlp_shard_columns(ffn, t, rank, act)
     w = ffn // t
@@ -403,33 +413,38 @@ def mlp_shard_forward(X: np.ndarray, A: np.ndarray, B: np.ndarray, t: int, rank:
     if a_bias is not None:
         Ui = Ui + a_bias[cols]
     Yi = _act_fwd(Ui, act)
-    Zi = Yi @ B[rank * w:(rank + 1) * w, :]
+    Zi = _keep(Yi, store) @ B[rank * w:(rank + 1) * w, :]
     return {"U": Ui, "Y": Yi, "Z": Zi}
 
 
 def mlp_shard_backward(X: np.ndarray, A: np.ndarray, B: np.ndarray, dZ: np.ndarray, t: int, rank: int,
-                       act: str = "gelu", a_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                       act: str = "gelu", a_bias: Optional[np.ndarray] = None,
+                       store: Optional[str] = None) -> Dict[str, np.ndarray]:
     """Rank r's part of the backward ([SPLIT] backward section): row layer dY_i = dZ B_i^T (no sum) and
     dB_i = Y_i^T dZ; local act' step; column layer dA_i = X^T dU_i (local) and the partial dX_i = dU_i A_i^T, whose
-    sum over ranks is dX."""
+    sum over ranks is dX.  store as in mlp_shard_forward: the saved U_i and Y_i are the stored ones, and dU_i is
+    stored before the two GEMMs (and the column sum) that read it."""
     ffn = B.shape[0]
     cols = mlp_shard_columns(ffn, t, rank, act)
     w = ffn // t
     fw = mlp_shard_forward(X, A, B, t, rank, act, a_bias)
     Bi = B[rank * w:(rank + 1) * w, :]
     dYi = dZ @ Bi.T
-    dBi = fw["Y"].T @ dZ
-    dUi = _act_bwd(fw["U"], dYi, act)
-    dAi = X.T @ dUi
-    dai = dUi.sum(axis=0)
-    dXi = dUi @ A[:, cols].T
+    dBi = _keep(fw["Y"], store).T @ dZ
+    dUi = _act_bwd(_keep(fw["U"], store), dYi, act)
+    dUs = _keep(dUi, store)
+    dAi = X.T @ dUs
+    dai = dUs.sum(axis=0)
+    dXi = dUs @ A[:, cols].T
     return {"dY": dYi, "dB": dBi, "dU": dUi, "dA": dAi, "da": dai, "dX": dXi}
 
 
 def mlp_shard_rows(X_rows: np.ndarray, dZ_rows: np.ndarray, A: np.ndarray, B: np.ndarray, t: int, rank: int,
-                   act: str = "gelu", a_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                   act: str = "gelu", a_bias: Optional[np.ndarray] = None,
+                   store: Optional[str] = None) -> Dict[str, np.ndarray]:
     """Rank r's per-token results for a subset of token rows.  Every row of U_i, Y_i, Z_i, dU_i and dX_i depends
-    only on the same row of X (and of dZ), so computing them for sampled rows is exact."""
+    only on the same row of X (and of dZ), so computing them for sampled rows is exact.  store as in
+    mlp_shard_backward."""
     ffn = B.shape[0]
     cols = mlp_shard_columns(ffn, t, rank, act)
     w = ffn // t
@@ -439,20 +454,21 @@ def mlp_shard_rows(X_rows: np.ndarray, dZ_rows: np.ndarray, A: np.ndarray, B: np
     if a_bias is not None:
         U = U + a_bias[cols]
     Y = _act_fwd(U, act)
-    Z = Y @ Bi
+    Z = _keep(Y, store) @ Bi
     dY = dZ_rows @ Bi.T
-    dU = _act_bwd(U, dY, act)
-    dX = dU @ Ai.T
+    dU = _act_bwd(_keep(U, store), dY, act)
+    dX = _keep(dU, store) @ Ai.T
     return {"U": U, "Y": Y, "Z": Z, "dU": dU, "dX": dX}
 
 
 def mlp_shard_weight_grad_cols(X: np.ndarray, dZ: np.ndarray, A: np.ndarray, B: np.ndarray, t: int, rank: int,
                                j_cols: Sequence[int], act: str = "gelu",
-                               a_bias: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                               a_bias: Optional[np.ndarray] = None,
+                               store: Optional[str] = None) -> Dict[str, np.ndarray]:
     """Rank r's weight gradients restricted to shard columns j of the GeLU/ReLU output (for SwiGLU: j indexes the
     f/t output columns and both the gate column j and the up column f/t + j of dA_i are returned).
     dB_i[j, :] = Y_i[:, j]^T dZ and dA_i[:, j] = X^T dU_i[:, j] each need only column j of the activations, over
-    all token rows, so sampling columns is exact."""
+    all token rows, so sampling columns is exact.  store as in mlp_shard_backward."""
     ffn = B.shape[0]
     w = ffn // t
     j = np.asarray(j_cols, dtype=np.int64)
@@ -468,8 +484,8 @@ def mlp_shard_weight_grad_cols(X: np.ndarray, dZ: np.ndarray, A: np.ndarray, B: 
         U = U + a_bias[cols]
     Y = _act_fwd(U, act)                          # [M, len(j)]
     dY = dZ @ Bj.T
-    dU = _act_bwd(U, dY, act)                     # [M, len(sel)]
-    return {"dB_rows": Y.T @ dZ, "dA_cols": X.T @ dU, "da_cols": dU.sum(axis=0), "sel": sel}
+    dU = _keep(_act_bwd(_keep(U, store), dY, act), store)  # [M, len(sel)]
+    return {"dB_rows": _keep(Y, store).T @ dZ, "dA_cols": X.T @ dU, "da_cols": dU.sum(axis=0), "sel": sel}
 
 
 # ---------------------------------------------------------------------------------------------------------------
@@ -539,16 +555,19 @@ def attention_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: int, b
 
 def attention_shard_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: int, b: int, a: int, d: int,
                             t: int, rank: int, causal: bool = True,
-                            bqkv: Optional[np.ndarray] = None, g: Optional[int] = None) -> Dict[str, np.ndarray]:
+                            bqkv: Optional[np.ndarray] = None, g: Optional[int] = None,
+                            store: Optional[str] = None) -> Dict[str, np.ndarray]:
     """Rank r's part: QKV_i in the grouped column order of qkv_shard_columns for its local groups, O_i = its query
     heads' outputs (head-major), lse_i [b, a/t, s], and the partial Z_i = O_i Wo[rows of its heads] (no row
-    bias)."""
+    bias).  store = "bf16": QKV_i is stored before the attention reads it and O_i before the projection reads it
+    (16-bit activations, as in mlp_shard_forward); each entry is the exact value of its step from stored inputs."""
     g = a if g is None else g
     G = a // g
     cols = qkv_shard_columns(a, d, t, rank, g)
     QKVi = X @ Wqkv[:, cols]
     if bqkv is not None:
         QKVi = QKVi + bqkv[cols]
+    QKVk = _keep(QKVi, store)
     heads = local_head_ids(a, t, rank)
     hl = len(heads)
     Oi = np.zeros((s * b, hl * d))
@@ -557,10 +576,10 @@ def attention_shard_forward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, s: 
         rows = np.arange(s) * b + bi
         for jj in range(hl):
             cq, ck, cv = shard_head_columns(G, d, jj)
-            o, l = attention_core(QKVi[rows, cq], QKVi[rows, ck], QKVi[rows, cv], causal)
+            o, l = attention_core(QKVk[rows, cq], QKVk[rows, ck], QKVk[rows, cv], causal)
             Oi[rows, jj * d:(jj + 1) * d] = o
             lsei[bi, jj, :] = l
-    Zi = Oi @ Wo[rank * hl * d:(rank + 1) * hl * d, :]
+    Zi = _keep(Oi, store) @ Wo[rank * hl * d:(rank + 1) * hl * d, :]
     return {"QKV": QKVi, "O": Oi, "lse": lsei, "Z": Zi}
 
 
@@ -635,30 +654,35 @@ def attention_backward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, dZ: np.n
 
 def attention_shard_backward(X: np.ndarray, Wqkv: np.ndarray, Wo: np.ndarray, dZ: np.ndarray, s: int, b: int,
                              a: int, d: int, t: int, rank: int, causal: bool = True,
-                             bqkv: Optional[np.ndarray] = None, g: Optional[int] = None) -> Dict[str, np.ndarray]:
+                             bqkv: Optional[np.ndarray] = None, g: Optional[int] = None,
+                             store: Optional[str] = None) -> Dict[str, np.ndarray]:
     """Rank r's part of the attention backward: its heads' dO_i = dZ Wo_i^T (Wo_i = the rows of its heads), the
     weight gradients dWo_i = O_i^T dZ, dQKV_i in the grouped [q_j k_j v_j] order, dWqkv_i = X^T dQKV_i,
-    dbqkv_i, and the partial dX_i = dQKV_i Wqkv_i^T (the f reduction sums these over ranks)."""
+    dbqkv_i, and the partial dX_i = dQKV_i Wqkv_i^T (the f reduction sums these over ranks).  store = "bf16": the
+    forward's QKV_i and O_i are the stored ones (attention_shard_forward), dO_i is stored before the core
+    backward reads it and dQKV_i before the two GEMMs (and the column sum) that read it."""
     g = a if g is None else g
     G = a // g
-    fw = attention_shard_forward(X, Wqkv, Wo, s, b, a, d, t, rank, causal, bqkv, g=g)
-    QKVi, Oi = fw["QKV"], fw["O"]
+    fw = attention_shard_forward(X, Wqkv, Wo, s, b, a, d, t, rank, causal, bqkv, g=g, store=store)
+    QKVi, Oi = _keep(fw["QKV"], store), _keep(fw["O"], store)
     hl = a // t
     Wo_i = Wo[rank * hl * d:(rank + 1) * hl * d, :]
     Wqkv_i = Wqkv[:, qkv_shard_columns(a, d, t, rank, g)]
     dOi = dZ @ Wo_i.T
+    dOk = _keep(dOi, store)
     dQKVi = np.zeros_like(QKVi)
     for bi in range(b):
         rows = np.arange(s) * b + bi
         for jj in range(hl):
             cq, ck, cv = shard_head_columns(G, d, jj)
             gq, gk, gv = attention_core_backward(QKVi[rows, cq], QKVi[rows, ck], QKVi[rows, cv],
-                                                 dOi[rows, jj * d:(jj + 1) * d], causal)
+                                                 dOk[rows, jj * d:(jj + 1) * d], causal)
             dQKVi[rows, cq] = gq
             dQKVi[rows, ck] += gk
             dQKVi[rows, cv] += gv
-    return {"dO": dOi, "dWo": Oi.T @ dZ, "dQKV": dQKVi, "dWqkv": X.T @ dQKVi, "dbqkv": dQKVi.sum(axis=0),
-            "dX": dQKVi @ Wqkv_i.T, "O": Oi, "QKV": QKVi, "lse": fw["lse"]}
+    dQk = _keep(dQKVi, store)
+    return {"dO": dOi, "dWo": Oi.T @ dZ, "dQKV": dQKVi, "dWqkv": X.T @ dQk, "dbqkv": dQk.sum(axis=0),
+            "dX": dQk @ Wqkv_i.T, "O": fw["O"], "QKV": fw["QKV"], "lse": fw["lse"], "Z": fw["Z"]}
 
 
 # ---------------------------------------------------------------------------------------------------------------
@@ -821,12 +845,3 @@ def rel_frobenius(got: np.ndarray, ref: np.ndarray) -> float:
     ref = np.asarray(ref, dtype=np.float64)
     den = np.linalg.norm(ref.ravel())
     return float(np.linalg.norm((got - ref).ravel()) / (den if den > 0 else 1.0))
-
-
-def max_abs_unit(got: np.ndarray, ref: np.ndarray) -> float:
-    """Max absolute error after scaling both by the RMS of the reference (outputs brought to unit scale)."""
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 1.0
-    rms = rms if rms > 0 else 1.0
-    return float(np.max(np.abs(got - ref))) / rms if ref.size else 0.0

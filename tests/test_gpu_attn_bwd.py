@@ -1,15 +1,17 @@
 """GPU parity of the per-rank attention backward (tp_attn_bwd) against the fp64 oracle, through the C ABI.
 
 * small shapes with ragged 64-row tiles (s = 100), every supported head-dim bucket, causal and not, fp32 and bf16,
-  with a QKV bias: dQKV_i, dWqkv_i, dbqkv_i, dWo_i and dX_i of every rank against the oracle's shard backward on
-  the same stored inputs;
-* the 22B-width workload at full size for one rank (s = 4096, 8 local heads of 96, causal): the core gradients of
-  two heads in full against the oracle's core backward fed the QKV_i and dO the library stored (bf16), sampled
-  rows of dX_i and the weight gradients in full against the oracle on the library's stored dQKV_i.
+  with a QKV bias: dO, dQKV_i, dWqkv_i, dbqkv_i, dWo_i and dX_i of every rank;
+* the 22B-width workload at full size for one rank (s = 4096, 8 local heads of 96, causal): two heads' dQ, dK, dV
+  in full, sampled rows of dO and dX_i, and both weight gradients in full.
 
-The bf16 path stores QKV_i, O_i and dO in bf16 and feeds P and dS to the matrix cores in bf16, so the exact fp64
-chain from X differs from it by storage rounding; as in the forward tests, the relative Frobenius bound is taken
-against the exact chain and the element bound against the oracle fed the stored intermediates.
+Every expected value comes from the oracle alone, from the seeded inputs.  The bf16 path keeps QKV_i, O_i, dO and
+dQKV_i in bf16 between its steps, so each bf16 output meets relative Frobenius 1e-2 against the exact fp64 chain
+from X, and the unit-scale element bound against the oracle's chain with those four rounded to bf16 where the
+block stores them (store="bf16").  For that element check the backward reads the oracle's stored forward outputs
+(oracle_saved); the library's own forward into its backward is checked against the exact chain as well.  Against the exact chain the element error of dQ, dK, dV at full size is set by
+that storage rounding alone (exact arithmetic on the rounded QKV_i and dO shows the same figure), so no kernel
+could meet the element bound there.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,7 @@ import torch
 
 import oracle as O
 import tp_inputs as TI
-from parity_utils import check_close, dev, empty, f64, say
+from parity_utils import check_close, dev, empty, f64, say, storage
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +33,16 @@ def L():
     return pkg.load()
 
 
-def run_rank(L, w, inp, r, dtype, with_bias, causal):
+def oracle_saved(st, dtype):
+    """The forward outputs the backward reads (QKV_i, O_i, lse_i), from the oracle's bf16 data-flow forward, in
+    storage form.  Feeding these to tp_attn_bwd, rather than the library's own forward outputs, lets the element
+    check compare like with like: where a QKV_i value sits on a rounding boundary, the library's fp32-accumulated
+    value and the oracle's exact one may round to neighbouring bf16 values, and the softmax backward magnifies such
+    a step."""
+    return {"QKV": storage(st["QKV"], dtype), "O": storage(st["O"], dtype), "lse": st["lse"].astype(np.float32)}
+
+
+def run_rank(L, w, inp, r, dtype, with_bias, causal, saved=None):
     s, b, h, a, d, t = w.s, w.b, w.h, w.a, w.d, w.t
     hl = a // t
     M = s * b
@@ -53,9 +64,17 @@ def run_rank(L, w, inp, r, dtype, with_bias, causal):
     dQKV, dWq, dWo, dX = empty((M, 3 * hl * d), dtype), empty((h, 3 * hl * d), dtype), empty((hl * d, h), dtype), \
         empty((M, h), dtype)
     dbq = empty((3 * hl * d,), dtype) if with_bias else None
+    if saved is not None:
+        QKV, Oo = dev(saved["QKV"], dtype), dev(saved["O"], dtype)
+        lse = torch.from_numpy(np.ascontiguousarray(saved["lse"], dtype=np.float32)).cuda()
     L.tp_attn_bwd(dims, r, causal, X, Wq, Wo, QKV, Oo, lse, dZ, dO, rec, dQKV, dWq, dbq, dWo, dX)
     torch.cuda.synchronize()
     return dict(QKV=QKV, O=Oo, lse=lse, dO=dO, dQKV=dQKV, dWqkv=dWq, dbqkv=dbq, dWo=dWo, dX=dX, rec=rec)
+
+
+def _rel_frob(got, ref, what):
+    rf = O.rel_frobenius(got, ref)
+    assert rf <= 1e-2, f"{what}: rel Frobenius {rf:.3e} > 1e-2"
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -69,39 +88,20 @@ def test_attention_backward_small_ragged(L, dtype, d, causal):
     X = O.as_f64(inp["X"], dtype).reshape(w.M, w.h)
     dZ = O.as_f64(inp["dZ"], dtype).reshape(w.M, w.h)
     Wqkv, Wo, bq = O.as_f64(inp["Wqkv"], dtype), O.as_f64(inp["Wo"], dtype), O.as_f64(inp["bqkv"], dtype)
-    hl = a // t
     for r in range(t):
-        got = run_rank(L, w, inp, r, dtype, True, causal)
         ref = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, a, d, t, r, causal, bq)
-        if dtype == "f32":
-            for k in ("dO", "dQKV", "dWqkv", "dbqkv", "dWo", "dX"):
-                check_close(f64(got[k]), ref[k], dtype, k)
-            continue
-        # exact chain: relative Frobenius
+        rst = ref if dtype == "f32" else O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, a, d, t, r, causal,
+                                                                    bq, store="bf16")
+        got = run_rank(L, w, inp, r, dtype, True, causal, saved=oracle_saved(rst, dtype))
         for k in ("dO", "dQKV", "dWqkv", "dbqkv", "dWo", "dX"):
-            rf = O.rel_frobenius(f64(got[k]), ref[k])
-            assert rf <= 1e-2, f"{k}: rel Frobenius {rf:.3e}"
-        # element bounds against the oracle fed the stored intermediates (QKV_i, O_i, dO in bf16)
-        QKVs, Os, dOs = f64(got["QKV"]), f64(got["O"]), f64(got["dO"])
-        Wo_i = Wo[r * hl * d:(r + 1) * hl * d, :]
-        Wq_i = Wqkv[:, O.qkv_shard_columns(a, d, t, r)]
-        check_close(f64(got["dO"]), dZ @ Wo_i.T, dtype, "dO")
-        dQKV = np.zeros_like(QKVs)
-        for bi in range(w.b):
-            rows = np.arange(w.s) * w.b + bi
-            for jj in range(hl):
-                base = jj * 3 * d
-                g = O.attention_core_backward(QKVs[rows, base:base + d], QKVs[rows, base + d:base + 2 * d],
-                                              QKVs[rows, base + 2 * d:base + 3 * d], dOs[rows, jj * d:(jj + 1) * d],
-                                              causal)
-                for n, gg in enumerate(g):
-                    dQKV[rows, base + n * d:base + (n + 1) * d] = gg
-        check_close(f64(got["dQKV"]), dQKV, dtype, "dQKV")
-        dQs = f64(got["dQKV"])
-        check_close(f64(got["dWqkv"]), X.T @ dQs, dtype, "dWqkv")
-        check_close(f64(got["dbqkv"]), dQs.sum(axis=0), dtype, "dbqkv")
-        check_close(f64(got["dWo"]), Os.T @ dZ, dtype, "dWo")
-        check_close(f64(got["dX"]), dQs @ Wq_i.T, dtype, "dX")
+            check_close(f64(got[k]), ref[k], dtype, k, elem_ref=rst[k])
+        # the library's own forward into its backward: against the exact chain
+        nat = run_rank(L, w, inp, r, dtype, True, causal)
+        for k in ("dQKV", "dWqkv", "dWo", "dX"):
+            if dtype == "f32":
+                check_close(f64(nat[k]), ref[k], dtype, f"{k} (own forward)")
+            else:
+                _rel_frob(f64(nat[k]), ref[k], f"{k} (own forward)")
 
 
 def test_attention_backward_full_size_one_rank_sampled(L):
@@ -109,28 +109,32 @@ def test_attention_backward_full_size_one_rank_sampled(L):
     r = 5
     say("attention backward h=6144 a=64 d=96 s=4096 t=8 rank 5 (two heads in full, sampled rows, full weight gradients)")
     inp = TI.attn_inputs(w, seed=0)
-    got = run_rank(L, w, inp, r, "bf16", False, True)
     hl, d = w.a // w.t, w.d
     X = O.as_f64(inp["X"], "bf16").reshape(w.M, w.h)
     dZ = O.as_f64(inp["dZ"], "bf16").reshape(w.M, w.h)
     Wqkv, Wo = O.as_f64(inp["Wqkv"], "bf16"), O.as_f64(inp["Wo"], "bf16")
-    Wo_i = Wo[r * hl * d:(r + 1) * hl * d, :]
-    Wq_i = Wqkv[:, O.qkv_shard_columns(w.a, d, w.t, r)]
-    QKVs, Os, dOs, dQs = f64(got["QKV"]), f64(got["O"]), f64(got["dO"]), f64(got["dQKV"])
+    say("attention backward h=6144 rank 5: oracle, exact chain and bf16 data flow")
+    ref = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, w.a, d, w.t, r, True)
+    rst = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, w.a, d, w.t, r, True, store="bf16")
+    say("attention backward h=6144 rank 5: library forward into backward, then backward from the oracle's forward")
+    nat = run_rank(L, w, inp, r, "bf16", False, True)
+    for k in ("dQKV", "dWqkv", "dWo", "dX"):
+        _rel_frob(f64(nat[k]), ref[k], f"{k} (own forward)")
+    got = run_rank(L, w, inp, r, "bf16", False, True, saved=oracle_saved(rst, "bf16"))
+    dQs = f64(got["dQKV"])
     rng = np.random.default_rng(11)
     rows = np.sort(rng.choice(w.M, size=64, replace=False))
     rows[0], rows[-1] = 0, w.M - 1
-    check_close(dOs[rows], dZ[rows] @ Wo_i.T, "bf16", "dO rows")
+    check_close(f64(got["dO"])[rows], ref["dO"][rows], "bf16", "dO rows", elem_ref=rst["dO"][rows])
     for jj in (0, hl - 1):  # two heads in full (b = 1: every row is one sequence position)
         base = jj * 3 * d
-        g = O.attention_core_backward(QKVs[:, base:base + d], QKVs[:, base + d:base + 2 * d],
-                                      QKVs[:, base + 2 * d:base + 3 * d], dOs[:, jj * d:(jj + 1) * d], True)
         for n, name in enumerate(("dQ", "dK", "dV")):
-            check_close(dQs[:, base + n * d:base + (n + 1) * d], g[n], "bf16", f"{name} head {jj}")
-    check_close(f64(got["dX"])[rows], dQs[rows] @ Wq_i.T, "bf16", "dX rows")
+            c = slice(base + n * d, base + (n + 1) * d)
+            check_close(dQs[:, c], ref["dQKV"][:, c], "bf16", f"{name} head {jj}", elem_ref=rst["dQKV"][:, c])
+    check_close(f64(got["dX"])[rows], ref["dX"][rows], "bf16", "dX rows", elem_ref=rst["dX"][rows])
     # the weight gradients in full (the pair's tail tiles split K over workgroups)
-    check_close(f64(got["dWqkv"]), X.T @ dQs, "bf16", "dWqkv")
-    check_close(f64(got["dWo"]), Os.T @ dZ, "bf16", "dWo")
+    check_close(f64(got["dWqkv"]), ref["dWqkv"], "bf16", "dWqkv", elem_ref=rst["dWqkv"])
+    check_close(f64(got["dWo"]), ref["dWo"], "bf16", "dWo", elem_ref=rst["dWo"])
 
 
 def test_attention_backward_ragged_pair_tail(L):
@@ -140,9 +144,12 @@ def test_attention_backward_ragged_pair_tail(L):
     r = 3
     say("attention backward h=6400 a=80 d=80 s=4096 t=8 rank 3 (ragged weight-gradient tiles, split tail)")
     inp = TI.attn_inputs(w, seed=3)
-    got = run_rank(L, w, inp, r, "bf16", False, True)
     X = O.as_f64(inp["X"], "bf16").reshape(w.M, w.h)
     dZ = O.as_f64(inp["dZ"], "bf16").reshape(w.M, w.h)
-    Os, dQs = f64(got["O"]), f64(got["dQKV"])
-    check_close(f64(got["dWqkv"]), X.T @ dQs, "bf16", "dWqkv")
-    check_close(f64(got["dWo"]), Os.T @ dZ, "bf16", "dWo")
+    Wqkv, Wo = O.as_f64(inp["Wqkv"], "bf16"), O.as_f64(inp["Wo"], "bf16")
+    say("attention backward h=6400 rank 3: oracle, exact chain and bf16 data flow")
+    ref = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, w.a, w.d, w.t, r, True)
+    rst = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, w.a, w.d, w.t, r, True, store="bf16")
+    got = run_rank(L, w, inp, r, "bf16", False, True, saved=oracle_saved(rst, "bf16"))
+    check_close(f64(got["dWqkv"]), ref["dWqkv"], "bf16", "dWqkv", elem_ref=rst["dWqkv"])
+    check_close(f64(got["dWo"]), ref["dWo"], "bf16", "dWo", elem_ref=rst["dWo"])

@@ -9,7 +9,10 @@
   dQ in full, sampled rows of dX_i and both weight gradients in full.
 
 Tolerances as in the multi-head tests: fp32 relative Frobenius 1e-5; bf16 relative Frobenius 1e-2 against the
-exact chain and the unit-scale element bound against the oracle fed the intermediates the library stored.
+exact fp64 chain from X and the unit-scale element bound against the oracle's chain along the block's bf16 data
+flow (QKV_i, O_i, dO and dQKV_i rounded where the block stores them).  Every expected value is the oracle's.  For
+the element check the backward reads the oracle's stored forward outputs; the library's own forward into its
+backward is checked against the exact chain too.
 """
 import numpy as np
 import pytest
@@ -17,7 +20,7 @@ import torch
 
 import oracle as O
 import tp_inputs as TI
-from parity_utils import check_close, dev, empty, f64, say
+from parity_utils import check_close, dev, empty, f64, say, storage
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +34,13 @@ def L():
     return pkg.load()
 
 
-def run_rank(L, w, inp, r, dtype, with_bias, causal, backward=True):
+def oracle_saved(st, dtype):
+    """The forward outputs the backward reads (QKV_i, O_i, lse_i) from the oracle's bf16 data-flow forward, in
+    storage form (so that the backward's element check compares like with like; as in the multi-head tests)."""
+    return {"QKV": storage(st["QKV"], dtype), "O": storage(st["O"], dtype), "lse": st["lse"].astype(np.float32)}
+
+
+def run_rank(L, w, inp, r, dtype, with_bias, causal, backward=True, saved=None):
     s, b, h, a, d, t, g = w.s, w.b, w.h, w.a, w.d, w.t, w.g
     hl, n = a // t, (a // t + 2 * (g // t)) * d
     M = s * b
@@ -55,25 +64,14 @@ def run_rank(L, w, inp, r, dtype, with_bias, causal, backward=True):
         assert rec.numel() == b * hl * nqb * 256 + (s * b * (g // t) * 2 * d * (a // g) if g < a else 0)
         dQKV, dWq, dWo, dX = empty((M, n), dtype), empty((h, n), dtype), empty((hl * d, h), dtype), empty((M, h), dtype)
         dbq = empty((n,), dtype) if with_bias else None
-        L.tp_attn_bwd(dims, r, causal, X, Wq, Wo, QKV, Oo, lse, dZ, dO, rec, dQKV, dWq, dbq, dWo, dX)
+        Qb, Ob, lb = QKV, Oo, lse
+        if saved is not None:
+            Qb, Ob = dev(saved["QKV"], dtype), dev(saved["O"], dtype)
+            lb = torch.from_numpy(np.ascontiguousarray(saved["lse"], dtype=np.float32)).cuda()
+        L.tp_attn_bwd(dims, r, causal, X, Wq, Wo, Qb, Ob, lb, dZ, dO, rec, dQKV, dWq, dbq, dWo, dX)
         out.update(dO=dO, dQKV=dQKV, dWqkv=dWq, dbqkv=dbq, dWo=dWo, dX=dX)
     torch.cuda.synchronize()
     return out
-
-
-def core_grads_stored(QKVs, dOs, s, b, hl, G, d, causal):
-    """dQKV_i from the stored QKV_i and dO by the oracle's per-head core backward, dK / dV summed per group."""
-    dQKV = np.zeros_like(QKVs)
-    for bi in range(b):
-        rows = np.arange(s) * b + bi
-        for jj in range(hl):
-            cq, ck, cv = O.shard_head_columns(G, d, jj)
-            gq, gk, gv = O.attention_core_backward(QKVs[rows, cq], QKVs[rows, ck], QKVs[rows, cv],
-                                                   dOs[rows, jj * d:(jj + 1) * d], causal)
-            dQKV[rows, cq] = gq
-            dQKV[rows, ck] += gk
-            dQKV[rows, cv] += gv
-    return dQKV
 
 
 def test_qkv_packer_with_groups(L):
@@ -115,37 +113,24 @@ def test_gqa_small_ragged(L, a, g, d, t, dtype, causal):
     X = O.as_f64(inp["X"], dtype).reshape(w.M, w.h)
     dZ = O.as_f64(inp["dZ"], dtype).reshape(w.M, w.h)
     Wqkv, Wo, bq = O.as_f64(inp["Wqkv"], dtype), O.as_f64(inp["Wo"], dtype), O.as_f64(inp["bqkv"], dtype)
-    hl, G = a // t, a // g
+    store = None if dtype == "f32" else "bf16"
     for r in range(t):
-        got = run_rank(L, w, inp, r, dtype, True, causal)
-        fw = O.attention_shard_forward(X, Wqkv, Wo, w.s, w.b, a, d, t, r, causal, bq, g=g)
         ref = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, a, d, t, r, causal, bq, g=g)
-        if dtype == "f32":
-            for k in ("QKV", "O", "Z"):
-                check_close(f64(got[k]), fw[k], dtype, k)
-            check_close(f64(got["lse"]), fw["lse"], dtype, "lse")
-            for k in ("dO", "dQKV", "dWqkv", "dbqkv", "dWo", "dX"):
-                check_close(f64(got[k]), ref[k], dtype, k)
-            continue
-        for k in ("O", "Z", "dO", "dQKV", "dWqkv", "dbqkv", "dWo", "dX"):
-            want = fw[k] if k in ("O", "Z") else ref[k]
-            rf = O.rel_frobenius(f64(got[k]), want)
-            assert rf <= 1e-2, f"rank {r} {k}: rel Frobenius {rf:.3e}"
-        QKVs, Os, dOs = f64(got["QKV"]), f64(got["O"]), f64(got["dO"])
-        # forward element bound: the oracle's attention on the stored QKV_i
-        rows = np.arange(w.M)
-        check_close(Os, O.attention_rows(QKVs, w.s, w.b, hl, d, rows, causal, G=G)["O"], dtype, "O", row_unit=True)
-        Wo_i = Wo[r * hl * d:(r + 1) * hl * d, :]
-        Wq_i = Wqkv[:, O.qkv_shard_columns(a, d, t, r, g)]
-        qc = O.qkv_shard_columns(a, d, t, r, g)
-        check_close(QKVs, X @ Wq_i + bq[qc], dtype, "QKV")
-        check_close(dOs, dZ @ Wo_i.T, dtype, "dO")
-        check_close(f64(got["dQKV"]), core_grads_stored(QKVs, dOs, w.s, w.b, hl, G, d, causal), dtype, "dQKV")
-        dQs = f64(got["dQKV"])
-        check_close(f64(got["dWqkv"]), X.T @ dQs, dtype, "dWqkv")
-        check_close(f64(got["dbqkv"]), dQs.sum(axis=0), dtype, "dbqkv")
-        check_close(f64(got["dWo"]), Os.T @ dZ, dtype, "dWo")
-        check_close(f64(got["dX"]), dQs @ Wq_i.T, dtype, "dX")
+        rst = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, a, d, t, r, causal, bq, g=g, store=store)
+        # forward outputs from the library's forward; the backward from the oracle's stored forward outputs
+        got = run_rank(L, w, inp, r, dtype, True, causal, saved=oracle_saved(rst, dtype))
+        for k in ("QKV", "O", "Z", "lse", "dO", "dQKV", "dWqkv", "dbqkv", "dWo", "dX"):
+            # attention rows average different numbers of value rows: their unit is the row's RMS
+            check_close(f64(got[k]).reshape(ref[k].shape), ref[k], dtype, f"rank {r} {k}",
+                        row_unit=k in ("O", "Z"), elem_ref=rst[k])
+        # the library's own forward into its backward
+        nat = run_rank(L, w, inp, r, dtype, True, causal)
+        for k in ("dQKV", "dWqkv", "dWo", "dX"):
+            if dtype == "f32":
+                check_close(f64(nat[k]), ref[k], dtype, f"rank {r} {k} (own forward)")
+            else:
+                rf = O.rel_frobenius(f64(nat[k]), ref[k])
+                assert rf <= 1e-2, f"rank {r} {k} (own forward): rel Frobenius {rf:.3e}"
 
 
 def test_gqa_llama70b_shape_one_rank(L):
@@ -153,36 +138,36 @@ def test_gqa_llama70b_shape_one_rank(L):
     r = 3
     say("GQA h=8192 a=64 g=8 d=128 s=4096 t=8 rank 3 (one group of 8 query heads)")
     inp = TI.attn_inputs(w, seed=0)
-    got = run_rank(L, w, inp, r, "bf16", False, True)
     hl, d, G = w.a // w.t, w.d, w.a // w.g
     X = O.as_f64(inp["X"], "bf16").reshape(w.M, w.h)
     dZ = O.as_f64(inp["dZ"], "bf16").reshape(w.M, w.h)
     Wqkv, Wo = O.as_f64(inp["Wqkv"], "bf16"), O.as_f64(inp["Wo"], "bf16")
-    cols_i = O.qkv_shard_columns(w.a, d, w.t, r, w.g)
-    Wq_i, Wo_i = Wqkv[:, cols_i], Wo[r * hl * d:(r + 1) * hl * d, :]
-    QKVs, Os, dOs, dQs = f64(got["QKV"]), f64(got["O"]), f64(got["dO"]), f64(got["dQKV"])
+    say("GQA rank 3: oracle, exact chain and bf16 data flow")
+    ref = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, w.a, d, w.t, r, True, g=w.g)
+    rst = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, w.a, d, w.t, r, True, g=w.g, store="bf16")
+    say("GQA rank 3: library forward into backward, then backward from the oracle's forward")
+    nat = run_rank(L, w, inp, r, "bf16", False, True)
+    for k in ("dQKV", "dWqkv", "dWo", "dX"):
+        rf = O.rel_frobenius(f64(nat[k]), ref[k])
+        assert rf <= 1e-2, f"{k} (own forward): rel Frobenius {rf:.3e}"
+    got = run_rank(L, w, inp, r, "bf16", False, True, saved=oracle_saved(rst, "bf16"))
+    QKVs, Os, dQs = f64(got["QKV"]), f64(got["O"]), f64(got["dQKV"])
     rng = np.random.default_rng(5)
     rows = np.sort(rng.choice(w.M, size=48, replace=False))
     rows[0], rows[-1] = 0, w.M - 1
-    check_close(QKVs[rows], X[rows] @ Wq_i, "bf16", "QKV rows")
-    check_close(Os[rows], O.attention_rows(QKVs, w.s, w.b, hl, d, rows, True, G=G)["O"], "bf16", "O rows",
-                row_unit=True)
-    check_close(dOs[rows], dZ[rows] @ Wo_i.T, "bf16", "dO rows")
-    # the group's dK and dV in full (sum over its 8 query heads), two heads' dQ in full
-    dK = np.zeros((w.M, d))
-    dV = np.zeros((w.M, d))
-    for jj in range(hl):
-        cq, ck, cv = O.shard_head_columns(G, d, jj)
-        gq, gk, gv = O.attention_core_backward(QKVs[:, cq], QKVs[:, ck], QKVs[:, cv], dOs[:, jj * d:(jj + 1) * d], True)
-        dK += gk
-        dV += gv
-        if jj in (0, hl - 1):
-            check_close(dQs[:, cq], gq, "bf16", f"dQ head {jj}")
+    # the QKV GEMM splits K over workgroups: in full
+    check_close(QKVs, ref["QKV"], "bf16", "QKV", elem_ref=rst["QKV"])
+    check_close(Os[rows], ref["O"][rows], "bf16", "O rows", row_unit=True, elem_ref=rst["O"][rows])
+    check_close(f64(got["Z"])[rows], ref["Z"][rows], "bf16", "Z rows", row_unit=True, elem_ref=rst["Z"][rows])
+    check_close(f64(got["dO"])[rows], ref["dO"][rows], "bf16", "dO rows", elem_ref=rst["dO"][rows])
+    # the group's dK and dV in full (sums over its 8 query heads), two heads' dQ in full
+    for jj in (0, hl - 1):
+        cq, _, _ = O.shard_head_columns(G, d, jj)
+        check_close(dQs[:, cq], ref["dQKV"][:, cq], "bf16", f"dQ head {jj}", elem_ref=rst["dQKV"][:, cq])
     _, ck, cv = O.shard_head_columns(G, d, 0)
-    check_close(dQs[:, ck], dK, "bf16", "dK (group)")
-    check_close(dQs[:, cv], dV, "bf16", "dV (group)")
-    check_close(f64(got["dX"])[rows], dQs[rows] @ Wq_i.T, "bf16", "dX rows")
-    # the GEMMs that split K over workgroups (the QKV GEMM in full, the weight-gradient pair's tail tiles) in full
-    check_close(QKVs, X @ Wq_i, "bf16", "QKV")
-    check_close(f64(got["dWqkv"]), X.T @ dQs, "bf16", "dWqkv")
-    check_close(f64(got["dWo"]), Os.T @ dZ, "bf16", "dWo")
+    check_close(dQs[:, ck], ref["dQKV"][:, ck], "bf16", "dK (group)", elem_ref=rst["dQKV"][:, ck])
+    check_close(dQs[:, cv], ref["dQKV"][:, cv], "bf16", "dV (group)", elem_ref=rst["dQKV"][:, cv])
+    check_close(f64(got["dX"])[rows], ref["dX"][rows], "bf16", "dX rows", elem_ref=rst["dX"][rows])
+    # the weight-gradient pair's tail tiles split K over workgroups: both in full
+    check_close(f64(got["dWqkv"]), ref["dWqkv"], "bf16", "dWqkv", elem_ref=rst["dWqkv"])
+    check_close(f64(got["dWo"]), ref["dWo"], "bf16", "dWo", elem_ref=rst["dWo"])

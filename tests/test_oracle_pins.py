@@ -144,11 +144,8 @@ def test_gelu_against_math_erf_and_tanh():
     assert np.max(np.abs(O.gelu(xs) - O.gelu_tanh(xs))) > 1e-4
 
 
-@pytest.mark.parametrize("f,df", [(O.gelu, O.gelu_grad), (O.gelu_tanh, O.gelu_tanh_grad), (O.silu, O.silu_grad),
-                                  (O.sigmoid, None)])
+@pytest.mark.parametrize("f,df", [(O.gelu, O.gelu_grad), (O.gelu_tanh, O.gelu_tanh_grad), (O.silu, O.silu_grad)])
 def test_activation_derivatives_by_central_differences(f, df):
-    if df is None:
-        return
     xs = np.linspace(-6, 6, 241) + 0.013
     h = 1e-5
     fd = (f(xs + h) - f(xs - h)) / (2 * h)
