@@ -21,11 +21,11 @@ BWD_PHASES = {"all": 0, "dgrad": 1, "wgrad": 2}
 WKINDS = {"fc1": TP_W_FC1, "fc1_gate_up": TP_W_FC1_GATE_UP, "fc2": TP_W_FC2, "qkv": TP_W_QKV, "proj": TP_W_PROJ,
           "b_fc1": TP_B_FC1, "b_fc1_gate_up": TP_B_FC1_GATE_UP, "b_qkv": TP_B_QKV}
 STATUS = {0: "TP_OK", -1: "TP_E_NULL", -2: "TP_E_SHAPE", -3: "TP_E_DIVISIBILITY", -4: "TP_E_DTYPE", -5: "TP_E_RANK",
-          -6: "TP_E_ALIAS", -7: "TP_E_UNSUPPORTED", -8: "TP_E_HIP"}
+          -6: "TP_E_ALIAS", -7: "TP_E_UNSUPPORTED", -8: "TP_E_HIP", -9: "TP_E_SCRATCH"}
 EXPORTED = ["tp_status_str", "tp_last_hip_error", "tp_abi_version", "tp_shard_weights", "tp_mlp_fwd", "tp_mlp_bwd",
             "tp_mlp_bwd_phase",
             "tp_attn_fwd", "tp_attn_bwd", "tp_attn_bwd_workspace", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd",
-            "tp_sp_dropout_add_ln_bwd", "tp_sp_ln_bwd_workspace", "tp_vocab_ce_fwd_local", "tp_vocab_ce_combine",
+            "tp_sp_dropout_add_ln_bwd", "tp_sp_dropout_add_ln_bwd_noalloc", "tp_sp_ln_bwd_workspace", "tp_vocab_ce_fwd_local", "tp_vocab_ce_combine",
             "tp_vocab_ce_bwd", "tp_timing_begin", "tp_timing_end",
             "tp_timing_kernel", "tp_timing_filter"]
 
@@ -75,6 +75,7 @@ def _load() -> ctypes.CDLL:
         "tp_gather_dim0": ([D, I, P, P, P], I),
         "tp_sp_dropout_add_ln_fwd": ([I64, I64, I, F64, F64, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_sp_dropout_add_ln_bwd": ([I64, I64, I, F64, P, P, P, P, P, P, P, P, P, P, P, P, P], I),
+        "tp_sp_dropout_add_ln_bwd_noalloc": ([I64, I64, I, F64, P, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_sp_ln_bwd_workspace": ([I64, I64], I64),
         "tp_vocab_ce_fwd_local": ([I64, I64, I, I, P, P, P, P], I),
         "tp_vocab_ce_combine": ([I64, I, P, P, P, P, P], I),
@@ -229,6 +230,15 @@ def tp_sp_dropout_add_ln_bwd(rows: int, h: int, p: float, u, gamma, mean, rstd, 
                                       _ptr(mean), _ptr(rstd), _ptr(dy), _ptr(dres_in), _ptr(mask), _ptr(dres),
                                       _ptr(dz), _ptr(dgamma), _ptr(dbeta), _ptr(ws), _stream(stream))
     return _check(st, "tp_sp_dropout_add_ln_bwd", check)
+
+
+def tp_sp_dropout_add_ln_bwd_noalloc(rows: int, h: int, p: float, u, gamma, mean, rstd, dy, dres_in, mask, dres, dz,
+                                     dgamma, dbeta, stream=None, dtype=None, check=True) -> int:
+    st = lib.tp_sp_dropout_add_ln_bwd_noalloc(int(rows), int(h), _dtype_code(u, dtype), float(p), _ptr(u),
+                                              _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dy), _ptr(dres_in),
+                                              _ptr(mask), _ptr(dres), _ptr(dz), _ptr(dgamma), _ptr(dbeta),
+                                              _stream(stream))
+    return _check(st, "tp_sp_dropout_add_ln_bwd_noalloc", check)
 
 
 def tp_sp_ln_bwd_workspace(rows: int, h: int) -> int:

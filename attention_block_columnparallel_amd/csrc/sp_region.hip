@@ -26,7 +26,38 @@
 // one, and writes one fp32 partial row [dgamma | dbeta]; a second kernel sums the partials in a fixed order.
 #include "tp_common.h"
 
+#include <mutex>
+
+// Scratch of the backward's entry point that allocates nothing: the partial [dgamma | dbeta] rows live here instead
+// of in a caller workspace.  Each GPU holds its own copy until the process ends.  In host code this name is only a
+// stand-in for the symbol; the device address comes from hipGetSymbolAddress (sp_noalloc_scratch).
+static __device__ __align__(256) float scratch[tp::SP_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
 namespace tp {
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kScratchDevices] = {};
+}  // namespace
+
+// The address of `scratch` on the current device, looked up once per device (with that device current) and kept.
+hipError_t sp_noalloc_scratch(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 namespace {
 

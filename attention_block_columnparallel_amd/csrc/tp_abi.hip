@@ -134,6 +134,7 @@ const char* tp_status_str(int status) {
     case TP_E_ALIAS: return "an output buffer overlaps an input buffer";
     case TP_E_UNSUPPORTED: return "unsupported combination (activation/dtype, alignment or head dim)";
     case TP_E_HIP: return "HIP launch failed";
+    case TP_E_SCRATCH: return "the call needs more scratch than the library's fixed no-allocation buffer holds";
     default: return "unknown status";
   }
 }
@@ -553,18 +554,22 @@ int tp_sp_dropout_add_ln_fwd(int64_t rows, int64_t h, tp_dtype dtype, double p, 
   return hip_status(tp::sp_dropout_add_ln_fwd(dtype, a, stream));
 }
 
-int tp_sp_dropout_add_ln_bwd(int64_t rows, int64_t h, tp_dtype dtype, double p, const void* u, const void* gamma,
-                             const float* mean, const float* rstd, const void* dy, const void* dres_in,
-                             const uint8_t* mask, void* dres, void* dz, float* dgamma, float* dbeta, float* ws,
-                             hipStream_t stream) {
+namespace {
+// The backward's checks and launch, shared by the workspace and the no-allocation entry points.  noalloc: ws is
+// ignored (may be NULL) and the library's fixed scratch takes its place.
+int sp_bwd_entry(int64_t rows, int64_t h, tp_dtype dtype, double p, const void* u, const void* gamma,
+                 const float* mean, const float* rstd, const void* dy, const void* dres_in, const uint8_t* mask,
+                 void* dres, void* dz, float* dgamma, float* dbeta, float* ws, bool noalloc, hipStream_t stream) {
   if (u == nullptr || gamma == nullptr || mean == nullptr || rstd == nullptr || dy == nullptr ||
-      dgamma == nullptr || dbeta == nullptr || ws == nullptr)
+      dgamma == nullptr || dbeta == nullptr || (!noalloc && ws == nullptr))
     return TP_E_NULL;
   if (p > 0.0 && mask == nullptr) return TP_E_NULL;
   int st = sp_check_sizes(rows, h, dtype, p);
   if (st != TP_OK) return st;
+  if (noalloc) ws = nullptr;
   if (misaligned16({u, gamma, dy, dres_in, dres, dz, (const void*)dgamma, (const void*)dbeta, (const void*)ws}))
     return TP_E_UNSUPPORTED;
+  if (noalloc && tp_sp_ln_bwd_workspace(rows, h) > tp::SP_NOALLOC_SCRATCH_BYTES) return TP_E_SCRATCH;
   const uint8_t* mask_used = p > 0.0 ? mask : nullptr;
   const int64_t es = esize(dtype), n = rows * h;
   const Buf outs[] = {{dres, n * es}, {dz, n * es}, {dgamma, h * 4}, {dbeta, h * 4},
@@ -572,6 +577,10 @@ int tp_sp_dropout_add_ln_bwd(int64_t rows, int64_t h, tp_dtype dtype, double p, 
   const Buf ins[] = {{u, n * es}, {gamma, h * es}, {mean, rows * 4}, {rstd, rows * 4}, {dy, n * es},
                      {dres_in, n * es}, {mask_used, n / 8}};
   if (any_alias(outs, 5, ins, 7)) return TP_E_ALIAS;
+  if (noalloc) {
+    const hipError_t e = tp::sp_noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e);
+  }
   tp::SpBwdArgs a;
   a.u = u;
   a.gamma = gamma;
@@ -589,6 +598,23 @@ int tp_sp_dropout_add_ln_bwd(int64_t rows, int64_t h, tp_dtype dtype, double p, 
   a.h = h;
   a.p = p;
   return hip_status(tp::sp_dropout_add_ln_bwd(dtype, a, stream));
+}
+}  // namespace
+
+int tp_sp_dropout_add_ln_bwd(int64_t rows, int64_t h, tp_dtype dtype, double p, const void* u, const void* gamma,
+                             const float* mean, const float* rstd, const void* dy, const void* dres_in,
+                             const uint8_t* mask, void* dres, void* dz, float* dgamma, float* dbeta, float* ws,
+                             hipStream_t stream) {
+  return sp_bwd_entry(rows, h, dtype, p, u, gamma, mean, rstd, dy, dres_in, mask, dres, dz, dgamma, dbeta, ws, false,
+                      stream);
+}
+
+int tp_sp_dropout_add_ln_bwd_noalloc(int64_t rows, int64_t h, tp_dtype dtype, double p, const void* u,
+                                     const void* gamma, const float* mean, const float* rstd, const void* dy,
+                                     const void* dres_in, const uint8_t* mask, void* dres, void* dz, float* dgamma,
+                                     float* dbeta, hipStream_t stream) {
+  return sp_bwd_entry(rows, h, dtype, p, u, gamma, mean, rstd, dy, dres_in, mask, dres, dz, dgamma, dbeta, nullptr,
+                      true, stream);
 }
 
 namespace {

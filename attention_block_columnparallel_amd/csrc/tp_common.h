@@ -241,6 +241,10 @@ struct SpBwdArgs {
 constexpr int64_t SP_MAX_H = 12288;
 constexpr int64_t SP_BWD_MAX_BLOCKS = 256;
 int64_t sp_bwd_blocks(int64_t rows);
+// The fixed device buffer that stands in for ws in the entry point that allocates nothing: 16 MiB, the partial
+// rows of 256 workgroups at h = 8192.  sp_noalloc_scratch gives its address on the current device.
+constexpr int64_t SP_NOALLOC_SCRATCH_BYTES = (int64_t)16 << 20;
+hipError_t sp_noalloc_scratch(float** out);
 hipError_t sp_dropout_add_ln_fwd(tp_dtype dt, const SpFwdArgs& a, hipStream_t st);
 hipError_t sp_dropout_add_ln_bwd(tp_dtype dt, const SpBwdArgs& a, hipStream_t st);
 

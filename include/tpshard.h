@@ -14,8 +14,8 @@
  *
  * Conventions shared by every entry point:
  *   - Tensors are caller-owned, device-resident, dense row-major.  The library allocates nothing, frees nothing
- *     and keeps no state between calls (apart from the opt-in, thread-local launch-timing log below); code objects
- *     are linked into the shared object.
+ *     and keeps no state between calls (apart from the opt-in, thread-local launch-timing log below, and the fixed
+ *     per-GPU scratch of tp_sp_dropout_add_ln_bwd_noalloc); code objects are linked into the shared object.
  *   - bf16 (TP_BF16) tensors hold bfloat16 values; the bf16 path needs every row length that is a GEMM K or N
  *     dimension (h, ffn/t, d, 3*(a/t)*d) to be a multiple of 8 and every pointer 16-byte aligned.  fp32 (TP_F32)
  *     tensors hold IEEE binary32 and have no alignment rule.
@@ -75,7 +75,8 @@ enum {
   TP_E_RANK = -5,         /* rank outside [0, t) (or -1 where not allowed)                         */
   TP_E_ALIAS = -6,        /* an output buffer overlaps an input buffer                            */
   TP_E_UNSUPPORTED = -7,  /* valid but not built: activation/dtype combination, alignment, d range  */
-  TP_E_HIP = -8           /* a HIP launch failed; tp_last_hip_error() names it                      */
+  TP_E_HIP = -8,          /* a HIP launch failed; tp_last_hip_error() names it                      */
+  TP_E_SCRATCH = -9       /* needs more scratch than the fixed no-allocation buffer holds          */
 };
 
 /* Text of a status code (static storage). */
@@ -228,6 +229,20 @@ int tp_sp_dropout_add_ln_bwd(int64_t rows, int64_t h, tp_dtype dtype, double p, 
 /* Bytes of fp32 scratch tp_sp_dropout_add_ln_bwd needs for rows x h (one partial [dgamma | dbeta] row per
  * workgroup of the row loop); <= 0 for non-positive sizes. */
 int64_t tp_sp_ln_bwd_workspace(int64_t rows, int64_t h);
+
+/* tp_sp_dropout_add_ln_bwd for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation and kernels, bit for bit, with no ws
+ * argument.  The partial rows go to a fixed 16 MiB buffer inside the library instead, one per GPU, held until the
+ * process ends (looked up on a device's first call, with that device current).  Calls that need more than that,
+ * tp_sp_ln_bwd_workspace(rows, h) > 16 MiB (e.g. h > 8192 with 256 or more rows), return TP_E_SCRATCH before any
+ * HIP call.  The call allocates and frees nothing.  Every call on one GPU shares that GPU's buffer: calls that
+ * overlap on one GPU (on different streams, or from different threads) race and must be serialised by the
+ * caller.  `stream` must belong to the current device.  Other arguments, rules and errors as in
+ * tp_sp_dropout_add_ln_bwd. */
+int tp_sp_dropout_add_ln_bwd_noalloc(int64_t rows, int64_t h, tp_dtype dtype, double p, const void* u,
+                                     const void* gamma, const float* mean, const float* rstd, const void* dy,
+                                     const void* dres_in, const uint8_t* mask, void* dres, void* dz, float* dgamma,
+                                     float* dbeta, hipStream_t stream);
 
 /* Vocab-parallel cross entropy ([ATLAS] §5 table, the vocab-parallel CE row: all-reduce(max), then all-reduce(sum),
  * backward local; [MEGA] embedding remark: the column-parallel logits feed the loss directly, so only b*s scalars

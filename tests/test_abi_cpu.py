@@ -199,6 +199,22 @@ def test_sp_region_validation(L):
     assert bwd(ptrs=P[:11] + [P[11] + 4]) == -7              # misaligned workspace
     assert bwd(ptrs=P[:8] + [P[4]] + P[9:12]) == -6          # dz aliases dy
     assert bwd(ptrs=P[:11] + [P[9] + 16]) == -6              # workspace overlaps dgamma
+    # the no-allocation variant: same checks without the workspace, and sizes beyond its fixed 16 MiB scratch
+    # refused (TP_E_SCRATCH) before any HIP call
+    def bwd_na(rows=rows, h=h, p=0.1, dt=BF16, ptrs=None):
+        q = ptrs or P[:11]
+        return L.tp_sp_dropout_add_ln_bwd_noalloc(rows, h, p, *q, stream=0, dtype=dt, check=False)
+
+    for i in (0, 1, 2, 3, 4, 9, 10):
+        assert bwd_na(ptrs=P[:i] + [None] + P[i + 1:11]) == -1, i
+    assert bwd_na(h=20) == -7
+    assert bwd_na(ptrs=P[:8] + [P[4]] + P[9:11]) == -6
+    assert bwd_na(rows=512, h=12288) == -9                   # 256 x 2 x 12288 fp32 = 24 MiB
+    assert bwd_na(rows=171, h=12288) == -9                   # 171 x 2 x 12288 x 4 B > 16 MiB
+    assert bwd_na(rows=171, h=12288, ptrs=P[:8] + [P[4]] + P[9:11]) == -9  # the size check comes first
+    assert bwd_na(rows=170, h=12288, ptrs=P[:8] + [P[4]] + P[9:11]) == -6  # 170 rows fit: on to the alias check
+    assert L.tp_sp_ln_bwd_workspace(512, 8192) == 16 << 20     # the largest that fits: the SP workload's rows
+    assert L.status_str(-9).startswith("the call needs more scratch")
     assert L.tp_sp_ln_bwd_workspace(2048, 4096) == 256 * 2 * 4096 * 4
     assert L.tp_sp_ln_bwd_workspace(3, 64) == 3 * 2 * 64 * 4
     assert L.tp_sp_ln_bwd_workspace(0, 64) == 0
