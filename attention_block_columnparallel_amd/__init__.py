@@ -7,18 +7,18 @@ library every entry point raises.
 """
 from __future__ import annotations
 
-import os
-
-from .build import LIB_PATH, build  # noqa: F401
+from .build import LIB_PATH, build, is_current  # noqa: F401
 
 _BINDING = None
 
 
 def load():
-    """The ctypes binding module; builds the library first if no built copy exists."""
+    """The ctypes binding module.  Builds the library first when there is no built copy, or when the copy was built
+    from other sources or flags than the ones in the tree (a hash recorded at build time), so a stale binary is
+    never used."""
     global _BINDING
     if _BINDING is None:
-        if not os.path.exists(LIB_PATH):
+        if not is_current():
             build()
         from . import _lib
 

@@ -6,6 +6,7 @@ next to this file.  Run as `python -m attention_block_columnparallel_amd.build` 
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -18,6 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libtpshard.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# sha256 of the sources and flags a library was built from, written next to it by build()
+HASH_PATH = LIB_PATH + ".srchash"
 ARCH = "gfx950"
 
 SOURCES = ["tp_abi.hip", "comm_kernels.hip", "gemm_bf16.hip", "gemm_f32.hip", "attention.hip", "sp_region.hip", "vocab_ce.hip"]
@@ -33,6 +36,32 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
+
+
+def source_hash(extra_flags=()) -> str:
+    """sha256 over every file under csrc/, the C header, the source list and the compile flags."""
+    h = hashlib.sha256()
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if not f.startswith("."))
+    for path in files + [os.path.join(INCLUDE, "tpshard.h")]:
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    h.update("\0".join(SOURCES + COMMON_FLAGS + list(extra_flags)).encode())
+    return h.hexdigest()
+
+
+def built_hash() -> str:
+    """The source hash recorded by the build that made the current library ("" if none)."""
+    try:
+        with open(HASH_PATH) as fh:
+            return fh.read().strip()
+    except OSError:
+        return ""
+
+
+def is_current() -> bool:
+    """True when the built library exists and was built from the sources and flags as they are now."""
+    return os.path.exists(LIB_PATH) and built_hash() == source_hash()
 
 
 def _hipcc() -> str:
@@ -71,6 +100,9 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    with open(HASH_PATH + ".tmp", "w") as fh:
+        fh.write(source_hash(extra_flags) + "\n")
+    os.replace(HASH_PATH + ".tmp", HASH_PATH)
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH

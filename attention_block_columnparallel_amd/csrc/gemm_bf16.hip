@@ -24,6 +24,8 @@
 
 #include "tp_common.h"
 
+#include <atomic>
+
 namespace tp {
 
 namespace {
@@ -651,6 +653,14 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
   }
 }
 
+// Row tiles per group of the large-tile kernel's walk over its tiles (each XCD walks its tiles a group of row tiles
+// at a time, column by column): 8 for a two-GEMM (pair) launch and for the act' epilogues, 2 for the plain K-major A
+// x MN-major B store (the row GEMM), 4 otherwise -- measured best for each at h = 4096, ffn/t = 2048.  The split-K
+// tail sum decodes tiles with the same rule.
+__host__ __device__ constexpr int big_row_group(bool pair, int epi, bool ak, bool bkm) {
+  return pair ? 8 : (epi == EPI_ACT_BWD || epi == EPI_SWIGLU_BWD) ? 8 : (ak && !bkm && epi == EPI_STORE) ? 2 : 4;
+}
+
 // Large-tile kernel: one 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (one wave per SIMD, fp32
 // accumulators in AGPRs), K in steps of 32 through a ring of 4 LDS stages fed by direct global -> LDS copies that
 // run 3 k-tiles ahead of the MFMAs.  The MFMAs take the B fragment first, so each 16 x 16 accumulator block is the
@@ -695,11 +705,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   if (which) bid -= pp.tiles0;
   const int nbm = (p.M + BM - 1) / BM;
   const int nbn = SWIG ? (p.fhalf + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
-  // row-tile groups of 4 for a single GEMM, 8 for the weight-gradient pair (measured best for each)
-  // row-tile groups: 8 for the weight-gradient pair and the act' epilogues, 2 for the plain K-major x MN-major
-  // GEMM, 4 otherwise (measured best for each at h = 4096, ffn/t = 2048)
-  constexpr int GM1 = (EPI == EPI_ACT_BWD || EPI == EPI_SWIGLU_BWD) ? 8 : (AK && !BKM && EPI == EPI_STORE) ? 2 : 4;
-  const int gm = pp.tiles1 > 0 ? 8 : GM1;
+  const int gm = big_row_group(pp.tiles1 > 0, EPI, AK, BKM);
   const int group = bid / (gm * nbn);
   const int first_m = group * gm;
   const int gsz = min(nbm - first_m, gm);
@@ -911,7 +917,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
 // ------------------------------------------------------------------------------------------------------------------
 struct Cfg {
   int bm, bn, nwm, nwn;
-  float eff;  // relative per-tile efficiency used to trade tile size against filling 256 CUs
+  float eff;  // relative per-tile efficiency used to trade tile size against filling the CUs
 };
 // eff: measured throughput of a full wave of tiles relative to the large-tile kernel (at K in the thousands)
 constexpr Cfg kCfgs[] = {
@@ -920,12 +926,25 @@ constexpr Cfg kCfgs[] = {
     {128, 128, 2, 2, 0.50f},
     {64, 64, 2, 2, 0.25f},
 };
-constexpr int kNumCUs = 256;
-constexpr int kNumCUsBig = 256;  // workgroups of the large-tile kernel resident at once (one per CU)
+// Compute units of the current device (256 on an MI355X), asked once per device.  The large-tile kernel holds one
+// workgroup per CU, so this is also how many of its tiles run at once (one round).
+int num_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];  // 0: not yet asked
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 const char* const kEpiNames[] = {"store", "bias", "bias_act", "swiglu_fwd", "act_bwd", "swiglu_bwd"};
 
 int choose_cfg(int M, int ntiles_cols_of_bn256, int N, bool swig, int fhalf) {
   (void)ntiles_cols_of_bn256;
+  const int ncu = num_cus();
   int best = 0;
   float best_score = -1.f;
   for (int i = 0; i < (int)(sizeof(kCfgs) / sizeof(kCfgs[0])); ++i) {
@@ -933,11 +952,11 @@ int choose_cfg(int M, int ntiles_cols_of_bn256, int N, bool swig, int fhalf) {
     const long nbm = (M + c.bm - 1) / c.bm;
     const long nbn = swig ? (fhalf + c.bn / 2 - 1) / (c.bn / 2) : (N + c.bn - 1) / c.bn;
     const long tiles = nbm * nbn;
-    const long waves = (tiles + kNumCUs - 1) / kNumCUs;
+    const long waves = (tiles + ncu - 1) / ncu;
     // useful fraction of the computed tile area (ragged edges) times the fill of the last wave
     const double rows_used = (double)M / (double)(nbm * c.bm);
     const double cols_used = swig ? (double)fhalf / (double)(nbn * c.bn / 2) : (double)N / (double)(nbn * c.bn);
-    const double fill = (double)tiles / (double)(waves * kNumCUs);
+    const double fill = (double)tiles / (double)(waves * ncu);
     const float score = (float)(fill * rows_used * cols_used * c.eff);
     if (score > best_score + 1e-6f) {
       best_score = score;
@@ -1025,11 +1044,12 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(GemmParams p, const flo
 // closest to one full round (at most 8 runs, each at least two 64-deep pairs of k-tiles, the partials fitting the
 // scratch); 1 when splitting does not pay.
 int choose_ksplit(const GemmParams& p, int tiles, int64_t part_floats) {
-  if (tiles * 4 >= kNumCUsBig * 3) return 1;
+  const int ncu = num_cus();
+  if (tiles * 4 >= ncu * 3) return 1;
   const int pairs = p.K / (2 * BK2);
   int best = 1;
   for (int sp = 2; sp <= 8; ++sp) {
-    if (tiles * sp > kNumCUsBig) break;
+    if (tiles * sp > ncu) break;
     if (pairs / sp < 2) break;
     if ((int64_t)sp * p.M * p.N > part_floats) break;
     best = sp;
@@ -1058,7 +1078,7 @@ hipError_t launch_big_split(const GemmParams& p, int ksplit, float* part, hipStr
 
 // Sum of the tail tiles' fp32 partial blocks (tile-block layout) in split order, stored as bf16 into the problem
 // each tile belongs to.  One thread per 4 consecutive columns of a 256 x 256 block; the tile decode is the large-tile
-// kernel's (row-tile groups of 8 for a pair).
+// kernel's (big_row_group).
 __global__ __launch_bounds__(256) void splitk_tail_sum_kernel(GemmPair pp, int ntail) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)ntail * (256 * 64)) return;
@@ -1070,7 +1090,7 @@ __global__ __launch_bounds__(256) void splitk_tail_sum_kernel(GemmPair pp, int n
   const GemmParams& p = pp.g[which];
   if (which) u -= pp.tiles0;
   const int nbm = (p.M + 255) / 256, nbn = (p.N + 255) / 256;
-  const int gm = pp.tiles1 > 0 ? 8 : 4;  // the large-tile kernel's grouping for this layout (K- and MN-major A / B)
+  const int gm = big_row_group(pp.tiles1 > 0, EPI_STORE, false, false);  // the kernel's own walk (MN x MN, store)
   const int first_m = (u / (gm * nbn)) * gm;
   const int gsz = min(nbm - first_m, gm);
   const int tile_m = first_m + (u % (gm * nbn)) % gsz;
@@ -1149,7 +1169,7 @@ hipError_t gemm_bf16_wgrad_pair(const GemmParams& p0, const GemmParams& p1, hipS
       big_fits(p1, false, false)) {
     const int t = big_tiles(p0, false) + big_tiles(p1, false);
     const int c0 = choose_cfg(p0.M, 0, p0.N, false, 0), c1 = choose_cfg(p1.M, 0, p1.N, false, 0);
-    if (t >= kNumCUs * 3 / 4 || (c0 == 0 && c1 == 0)) return launch_big<false, false, EPI_STORE>(p0, &p1, st);
+    if (t >= num_cus() * 3 / 4 || (c0 == 0 && c1 == 0)) return launch_big<false, false, EPI_STORE>(p0, &p1, st);
   }
   hipError_t e = gemm_bf16(p0, false, false, EPI_STORE, st);
   if (e == hipSuccess) e = gemm_bf16(p1, false, false, EPI_STORE, st);
@@ -1163,12 +1183,13 @@ hipError_t gemm_bf16_wgrad_pair_splitk(const GemmParams& p0, const GemmParams& p
   if (part != nullptr && p0.M > 0 && p0.N > 0 && p1.M > 0 && p1.N > 0 && p0.K == p1.K && big_fits(p0, false, false) &&
       big_fits(p1, false, false)) {
     const int t = big_tiles(p0, false) + big_tiles(p1, false);
-    const int ntail = t % kNumCUsBig;
-    if (t > kNumCUsBig && ntail > 0 && ntail * 4 < kNumCUsBig * 3) {
+    const int ncu = num_cus();
+    const int ntail = t % ncu;
+    if (t > ncu && ntail > 0 && ntail * 4 < ncu * 3) {
       const int pairs = p0.K / (2 * BK2);
       int ks = 1;
       for (int sp = 2; sp <= 8; ++sp) {
-        if (ntail * sp > kNumCUsBig || pairs / sp < 2 || (int64_t)ntail * sp * 65536 > part_floats) break;
+        if (ntail * sp > ncu || pairs / sp < 2 || (int64_t)ntail * sp * 65536 > part_floats) break;
         ks = sp;
       }
       if (ks > 1) {

@@ -9,7 +9,8 @@
 //                           m = max_r m_r,  S = sum_r s_r exp(m_r - m),  lse = m + log S,  loss = lse - sum_r tl_r
 //   backward (per rank):    dx[i, j] = (exp(x[i, j] - lse[i]) - [j is the target]) * dloss[i]
 //
-// A negative target marks an ignored row: loss 0 and a zero gradient row.
+// A negative target marks an ignored row: loss 0 and a zero gradient row.  A target in no rank's columns gives NaN
+// loss and lse (and so NaN gradients); a row whose logits are all -inf gives lse = -inf and a NaN loss.
 //
 // The local pass reads the logits once: each thread keeps a running (max, sum) over its chunks, rescaling the sum
 // when the max rises, and the workgroup merges the (max, sum) pairs.  The max all-reduce then rescales each rank's
@@ -155,8 +156,9 @@ __global__ __launch_bounds__(CE_THREADS) void ce_local_kernel(const void* __rest
 #pragma unroll
     for (int w = 1; w < CE_THREADS / 64; ++w) merge(M, S, red[0][w], red[1][w]);
     const int64_t local = (int64_t)targets[row] - (int64_t)rank * v;
-    const float tl = (targets[row] >= 0 && local >= 0 && local < v) ? Chunk8<T>::one(logits, base + local) : 0.0f;
-    stats[row] = make_float4(M, S, tl, 0.0f);
+    const bool mine = targets[row] >= 0 && local >= 0 && local < v;
+    const float tl = mine ? Chunk8<T>::one(logits, base + local) : 0.0f;
+    stats[row] = make_float4(M, S, tl, mine ? 1.0f : 0.0f);
   }
 }
 
@@ -168,15 +170,20 @@ __global__ __launch_bounds__(CE_THREADS) void ce_combine_kernel(const float4* __
   if (row >= rows) return;
   float m = -INFINITY;
   for (int r = 0; r < t; ++r) m = fmaxf(m, stats[(int64_t)r * rows + row].x);
-  float S = 0.0f, tl = 0.0f;
+  float S = 0.0f, tl = 0.0f, owners = 0.0f;
   for (int r = 0; r < t; ++r) {
     const float4 st = stats[(int64_t)r * rows + row];
-    S += st.y * __builtin_amdgcn_exp2f((st.x - m) * LOG2E);
+    if (m > -INFINITY) S += st.y * __builtin_amdgcn_exp2f((st.x - m) * LOG2E);
     tl += st.z;
+    owners += st.w;
   }
-  const float l = m + __builtin_amdgcn_logf(S) * LN2;
+  const int tg = targets[row];
+  // a row of -inf logits has lse = -inf (its loss, -inf - (-inf), is NaN); a target in no rank's columns (at or past
+  // t * v) is flagged with NaN in lse and loss, so the backward's exp(x - lse) turns NaN as well
+  float l = m > -INFINITY ? m + __builtin_amdgcn_logf(S) * LN2 : -INFINITY;
+  if (tg >= 0 && owners == 0.0f) l = __builtin_nanf("");
   if (lse != nullptr) lse[row] = l;
-  loss[row] = targets[row] >= 0 ? l - tl : 0.0f;
+  loss[row] = tg >= 0 ? l - tl : 0.0f;
 }
 
 // One thread per 8-column chunk of the rank's [rows, v] logits.

@@ -248,15 +248,19 @@ int tp_sp_dropout_add_ln_bwd_noalloc(int64_t rows, int64_t h, tp_dtype dtype, do
  * backward local; [MEGA] embedding remark: the column-parallel logits feed the loss directly, so only b*s scalars
  * per reduction cross ranks).  Rank r holds logits_i [rows, v_local] for vocab columns [r*v_local, (r+1)*v_local)
  * of every token row (rows = s*b).  targets: int32 [rows], global vocab ids in [0, t*v_local); a negative target
- * marks an ignored row (loss 0, zero gradient).  A target >= t*v_local is in no rank's range (its logit counts 0).
+ * marks an ignored row (loss 0, zero gradient).  A target >= t*v_local is in no rank's range: combine writes NaN to
+ * that row's loss and lse, so the backward's gradient row is NaN too (never a silently wrong value).
  *
- * Local pass: stats_i float4 [rows] = {m_r, s_r, tl_r, 0} with m_r the row max of this rank's logits, s_r the sum of
- * exp(x - m_r) over them, tl_r the target's logit when the target is one of this rank's columns, else 0. */
+ * Local pass: stats_i float4 [rows] = {m_r, s_r, tl_r, o_r} with m_r the row max of this rank's logits, s_r the sum
+ * of exp(x - m_r) over them, tl_r the target's logit when the target is one of this rank's columns, else 0, and
+ * o_r = 1 when it is, else 0. */
 int tp_vocab_ce_fwd_local(int64_t rows, int64_t v_local, int rank, tp_dtype dtype, const void* logits_i,
                           const int32_t* targets, float* stats_i, hipStream_t stream);
 
 /* The two all-reduces, on one GPU over the t ranks' records stats [t][rows] float4 (rank order):
  *   m = max_r m_r;  S = sum_r s_r exp(m_r - m);  lse = m + log S;  loss = lse - sum_r tl_r  (0 for ignored rows)
+ * A row whose logits are all -inf gets lse = -inf and loss NaN; a counted row that no rank owns (sum_r o_r = 0)
+ * gets NaN in both. 
  * loss: fp32 [rows]; lse: fp32 [rows] (nullable; the backward needs it).  stats 16-byte aligned. */
 int tp_vocab_ce_combine(int64_t rows, int t, const float* stats, const int32_t* targets, float* loss, float* lse,
                         hipStream_t stream);

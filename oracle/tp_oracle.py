@@ -740,14 +740,20 @@ def dropout_add_backward(dout: np.ndarray, bits: np.ndarray, p: float):
 
 
 def cross_entropy(logits: np.ndarray, targets: np.ndarray) -> np.ndarray:
-    """Unsharded per-row loss: log(sum_j exp(logits[i, j])) - logits[i, targets[i]]; 0 where targets[i] < 0."""
+    """Unsharded per-row loss: log(sum_j exp(logits[i, j])) - logits[i, targets[i]]; 0 where targets[i] < 0.
+
+    Rows the definition leaves undefined give NaN, so they cannot pass for a loss: a target at or beyond the vocab
+    size (no such logit), and a row whose logits are all -inf (log 0 - (-inf))."""
     x = np.asarray(logits, dtype=np.float64)
     tg = np.asarray(targets, dtype=np.int64)
     m = x.max(axis=1)
-    lse = m + np.log(np.exp(x - m[:, None]).sum(axis=1))
-    keep = tg >= 0
-    loss = np.zeros(x.shape[0])
-    loss[keep] = lse[keep] - x[np.nonzero(keep)[0], tg[keep]]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        lse = np.where(np.isneginf(m), -np.inf, m + np.log(np.exp(x - m[:, None]).sum(axis=1)))
+        keep = tg >= 0
+        inside = keep & (tg < x.shape[1])
+        loss = np.zeros(x.shape[0])
+        loss[keep] = np.nan
+        loss[inside] = lse[inside] - x[np.nonzero(inside)[0], tg[inside]]
     return loss
 
 
@@ -771,23 +777,28 @@ def vocab_parallel_cross_entropy(logit_shards: Sequence[np.ndarray], targets: np
     1. each rank's row max, then all-reduce(max) -> m;
     2. each rank's sum of exp(logits - m) and its target logit (0 when the target is not in its range), then
        all-reduce(sum) of both -> S, target logit;
-    3. loss = log S + m - target logit (0 for ignored rows).  Returns loss and lse = m + log S per row."""
+    3. loss = log S + m - target logit (0 for ignored rows).  Returns loss and lse = m + log S per row.
+    A target that no rank's range holds gives NaN for both loss and lse (the backward then gives NaN too); a row
+    whose logits are all -inf gives lse = -inf and loss NaN, as in cross_entropy."""
     v = logit_shards[0].shape[1]
     tg = np.asarray(targets, dtype=np.int64)
     xs = [np.asarray(x, dtype=np.float64) for x in logit_shards]
     m = np.max(np.stack([x.max(axis=1) for x in xs]), axis=0)                       # all-reduce(max)
-    sums, tls = [], []
-    for r, x in enumerate(xs):
-        sums.append(np.exp(x - m[:, None]).sum(axis=1))
-        local = tg - r * v
-        mine = (tg >= 0) & (local >= 0) & (local < v)
-        tl = np.zeros(x.shape[0])
-        tl[mine] = x[np.nonzero(mine)[0], local[mine]]
-        tls.append(tl)
-    S = np.sum(np.stack(sums), axis=0)                                               # all-reduce(sum)
-    tl = np.sum(np.stack(tls), axis=0)
-    lse = m + np.log(S)
-    loss = np.where(tg >= 0, lse - tl, 0.0)
+    sums, tls, owned = [], [], np.zeros(len(tg), dtype=bool)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        for r, x in enumerate(xs):
+            sums.append(np.where(np.isneginf(m), 0.0, np.exp(x - m[:, None]).sum(axis=1)))
+            local = tg - r * v
+            mine = (tg >= 0) & (local >= 0) & (local < v)
+            owned |= mine
+            tl = np.zeros(x.shape[0])
+            tl[mine] = x[np.nonzero(mine)[0], local[mine]]
+            tls.append(tl)
+        S = np.sum(np.stack(sums), axis=0)                                           # all-reduce(sum)
+        tl = np.sum(np.stack(tls), axis=0)
+        lse = np.where(np.isneginf(m), -np.inf, m + np.log(S))
+        lse = np.where((tg >= 0) & ~owned, np.nan, lse)
+        loss = np.where(tg >= 0, lse - tl, 0.0)
     return loss, lse
 
 

@@ -295,3 +295,44 @@ def test_attn_bwd_workspace_size(L):
     g = L.make_dims(s=100, b=2, h=64, a=8, d=8, t=2, g=2)
     assert L.tp_attn_bwd_workspace(g) == (2 * 4 * 2 * 256 + 100 * 2 * 1 * 16 * 4) * 4
     assert L.tp_attn_bwd_workspace(L.make_dims(s=100, b=2, h=64, a=8, d=8, t=2, g=3)) == 0
+
+
+def test_binding_checks_tensor_extents_before_the_call(L):
+    """The binding refuses a view that is not contiguous, a buffer shorter than the extent the call works out from
+    its sizes, and a tensor that is not on a GPU -- with ValueError, before the library runs (its kernels trust
+    the extents)."""
+    import torch
+
+    dims = L.make_dims(s=16, b=2, h=64, t=2)
+    n = 16 * 2 * 64
+    full = torch.zeros(n, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="not contiguous"):
+        L.tp_gather_dim0(dims, torch.zeros(64, 2 * n // 64, dtype=torch.bfloat16).t(), addr(1), stream=0)
+    with pytest.raises(ValueError, match="the call needs"):
+        L.tp_gather_dim0(dims, full[: n - 8], addr(1), stream=0)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        L.tp_gather_dim0(dims, full, addr(1), stream=0)
+    # the extent follows the call's own sizes: rank r's reduce-scatter slice is n / t, every slice n
+    part = torch.zeros(2 * n, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out: 2048 bytes, the call needs 4096"):
+        L.tp_reduce_scatter_dim0(dims, -1, addr(0), None, torch.zeros(n // 2, dtype=torch.bfloat16), stream=0,
+                                 dtype=BF16)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        L.tp_reduce_scatter_dim0(dims, 1, addr(0), None, torch.zeros(n // 2, dtype=torch.bfloat16), stream=0,
+                                 dtype=BF16)
+    with pytest.raises(ValueError, match="partials: 4096 bytes, the call needs 8192"):
+        L.tp_reduce_scatter_dim0(dims, 1, part[:n], None, addr(1), stream=0)
+    # SwiGLU doubles the column shard: A_i of [64, 128] is short for ffn = 256, t = 2
+    md = L.make_dims(s=16, b=2, h=64, ffn=256, t=2)
+    with pytest.raises(ValueError, match="A_i"):
+        L.tp_mlp_fwd(md, 0, "swiglu", addr(0), torch.zeros(64 * 128, dtype=torch.bfloat16), None, addr(2), addr(3),
+                     addr(4), addr(5), stream=0, dtype=BF16)
+
+
+def test_built_library_matches_the_sources():
+    """build() records a hash of the sources and flags next to the library; load() rebuilds when it no longer
+    matches, so a library built from other sources is never used."""
+    from attention_block_columnparallel_amd.build import built_hash, is_current, source_hash
+
+    assert is_current() and built_hash() == source_hash()
+    assert source_hash(("-DSOMETHING_ELSE",)) != source_hash()

@@ -108,3 +108,29 @@ def test_full_workload_sampled_rows(L):
     stats, loss, lse, dlog = run(L, inp, rows, V, t, "bf16")
     sample = np.sort(np.random.default_rng(1).choice(rows, 192, replace=False))
     check(inp, rows, V, t, "bf16", stats, loss, lse, dlog, sample=sample)
+
+
+def test_undefined_rows_are_flagged(L):
+    """A target past the vocab and a row of -inf logits have no defined loss: the library writes NaN (and lse NaN
+    for the unowned target, -inf for the -inf row), like the oracle; ignored and ordinary rows are unaffected."""
+    rows, V, t = 6, 64, 2
+    say(f"vocab CE undefined rows rows={rows} V={V} t={t} bf16")
+    inp = TI.vocab_ce_inputs(rows, V, "bf16", seed=5)
+    inp["logits"] = inp["logits"].copy()
+    inp["logits"].reshape(rows, V)[2, :] = 0xFF80          # bf16 -inf
+    inp["targets"][[0, 2, 3, 5]] = [0, 3, 40, 63]
+    inp["targets"][1] = V                                   # no rank owns it
+    inp["targets"][4] = -100
+    stats, loss, lse, dlog = run(L, inp, rows, V, t, "bf16")
+    x = O.as_f64(inp["logits"], "bf16").reshape(rows, V)
+    loss_ref, lse_ref = O.vocab_parallel_cross_entropy([x[:, :V // t], x[:, V // t:]], inp["targets"])
+    got_l, got_s = f64(loss), f64(lse)
+    assert np.isnan(got_l[1]) and np.isnan(got_s[1]) and np.isnan(loss_ref[1])
+    assert np.isnan(got_l[2]) and np.isneginf(got_s[2]) and np.isneginf(lse_ref[2])
+    assert got_l[4] == 0.0
+    ok = [0, 3, 5]
+    check_close(got_l[ok], loss_ref[ok], "f32", "loss (defined rows)")
+    for r in range(t):
+        g = f64(dlog[r])
+        assert np.all(np.isnan(g[1])), f"rank {r}: the unowned target's gradient row is not NaN"
+        assert np.all(g[4] == 0.0)

@@ -81,3 +81,25 @@ def test_large_logits_stay_finite():
     loss, lse = O.vocab_parallel_cross_entropy([x[:, :8], x[:, 8:]], tg)
     assert np.all(np.isfinite(loss)) and np.all(np.isfinite(lse))
     assert np.allclose(loss, O.cross_entropy(x, tg))
+
+
+def test_undefined_rows_are_nan_not_a_number_that_passes():
+    """A target past the vocab (no such logit) and a row of -inf logits have no defined loss: both give NaN, in the
+    unsharded definition and in the sharded steps; ignored rows stay 0; the other rows are unaffected."""
+    x, tg = _case(11, rows=6, V=16)
+    x[2, :] = -np.inf            # every logit of row 2 is -inf
+    tg[[0, 2, 3, 5]] = [0, 3, 9, 15]
+    tg[1] = 16                   # past the vocab: no rank of t = 2 (8 columns each) owns it
+    tg[4] = -100                 # ignored
+    loss = O.cross_entropy(x, tg)
+    assert np.isnan(loss[1]) and np.isnan(loss[2]) and loss[4] == 0.0
+    ok = [0, 3, 5]
+    m = x[ok].max(axis=1)
+    ref = m + np.log(np.exp(x[ok] - m[:, None]).sum(axis=1)) - x[ok, tg[ok]]
+    assert np.allclose(loss[ok], ref, rtol=1e-14)
+    lv, lse = O.vocab_parallel_cross_entropy([x[:, :8], x[:, 8:]], tg)
+    assert np.isnan(lv[1]) and np.isnan(lse[1])          # the backward's exp(x - lse) turns NaN too
+    assert np.isnan(lv[2]) and np.isneginf(lse[2])
+    assert lv[4] == 0.0 and np.allclose(lv[ok], loss[ok], rtol=1e-12)
+    g = O.vocab_parallel_cross_entropy_backward(x[:, :8], tg, 0, lse, np.ones(6))
+    assert np.all(np.isnan(g[1])) and np.all(g[4] == 0.0)

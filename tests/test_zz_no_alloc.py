@@ -64,9 +64,11 @@ def test_noalloc_fp32_no_dropout_twice(L):
 
 def test_noalloc_rejects_oversize_before_any_launch(L):
     # 256 workgroups x 2 x 12288 fp32 = 24 MiB > 16 MiB: rejected by the host check, no kernel runs
+    # (raw addresses: the library refuses the size before it would touch any of them, and the binding's own extent
+    # check applies to tensors only)
     rows, h = 512, 12288
-    t = torch.empty(8, dtype=torch.bfloat16, device="cuda")
-    f = torch.empty(8, device="cuda")
+    t = torch.empty(8, dtype=torch.bfloat16, device="cuda").data_ptr()
+    f = torch.empty(8, device="cuda").data_ptr()
     st = L.tp_sp_dropout_add_ln_bwd_noalloc(rows, h, 0.0, t, t, f, f, t, None, None, None, t, f, f, dtype="bf16",
                                             check=False)
     assert st == -9 and L.STATUS[st] == "TP_E_SCRATCH"
