@@ -26,7 +26,7 @@ EXPORTED = ["tp_status_str", "tp_last_hip_error", "tp_abi_version", "tp_shard_we
             "tp_mlp_bwd_phase",
             "tp_attn_fwd", "tp_attn_bwd", "tp_attn_bwd_workspace", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd",
             "tp_sp_dropout_add_ln_bwd", "tp_sp_dropout_add_ln_bwd_noalloc", "tp_sp_ln_bwd_workspace", "tp_vocab_ce_fwd_local", "tp_vocab_ce_combine",
-            "tp_vocab_ce_bwd", "tp_timing_begin", "tp_timing_end",
+            "tp_vocab_ce_bwd", "tp_vocab_logits_fwd", "tp_vocab_logits_bwd", "tp_timing_begin", "tp_timing_end",
             "tp_timing_kernel", "tp_timing_filter"]
 
 
@@ -80,6 +80,8 @@ def _load() -> ctypes.CDLL:
         "tp_vocab_ce_fwd_local": ([I64, I64, I, I, P, P, P, P], I),
         "tp_vocab_ce_combine": ([I64, I, P, P, P, P, P], I),
         "tp_vocab_ce_bwd": ([I64, I64, I, I, P, P, P, P, P, P], I),
+        "tp_vocab_logits_fwd": ([I64, I64, I64, I, P, P, P, P], I),
+        "tp_vocab_logits_bwd": ([I64, I64, I64, I, P, P, P, P, P, P], I),
         "tp_timing_begin": ([ctypes.POINTER(P), ctypes.POINTER(P), I], I),
         "tp_timing_end": ([], I),
         "tp_timing_kernel": ([I], ctypes.c_char_p),
@@ -380,6 +382,28 @@ def tp_vocab_ce_bwd(rows: int, v_local: int, rank: int, logits_i, targets, lse, 
                              _ptr(dloss, rows * 4 if ok else 0, "dloss"), _ptr(dlogits_i, nb, "dlogits_i"),
                              _stream(stream))
     return _check(st, "tp_vocab_ce_bwd", check)
+
+
+def tp_vocab_logits_fwd(rows: int, h: int, v_local: int, X, E_i, logits_i, stream=None, dtype=None,
+                        check=True) -> int:
+    dt = _dtype_code(X, dtype)
+    es, ok = _es(dt), _pos(rows, h, v_local)
+    st = lib.tp_vocab_logits_fwd(int(rows), int(h), int(v_local), dt, _ptr(X, rows * h * es if ok else 0, "X"),
+                                 _ptr(E_i, v_local * h * es if ok else 0, "E_i"),
+                                 _ptr(logits_i, rows * v_local * es if ok else 0, "logits_i"), _stream(stream))
+    return _check(st, "tp_vocab_logits_fwd", check)
+
+
+def tp_vocab_logits_bwd(rows: int, h: int, v_local: int, X, E_i, dlogits_i, dX_i, dE_i, stream=None, dtype=None,
+                        check=True) -> int:
+    dt = _dtype_code(dlogits_i, dtype)
+    es, ok = _es(dt), _pos(rows, h, v_local)
+    st = lib.tp_vocab_logits_bwd(int(rows), int(h), int(v_local), dt, _ptr(X, rows * h * es if ok else 0, "X"),
+                                 _ptr(E_i, v_local * h * es if ok else 0, "E_i"),
+                                 _ptr(dlogits_i, rows * v_local * es if ok else 0, "dlogits_i"),
+                                 _ptr(dX_i, rows * h * es if ok else 0, "dX_i"),
+                                 _ptr(dE_i, v_local * h * es if ok else 0, "dE_i"), _stream(stream))
+    return _check(st, "tp_vocab_logits_bwd", check)
 
 
 class LaunchTimer:

@@ -667,4 +667,71 @@ int tp_vocab_ce_bwd(int64_t rows, int64_t v_local, int rank, tp_dtype dtype, con
                                      stream));
 }
 
+namespace {
+int logits_check(int64_t rows, int64_t h, int64_t v_local, tp_dtype dtype) {
+  if (rows <= 0 || h <= 0 || v_local <= 0 || rows >= kMaxDim || h >= kMaxDim || v_local >= kMaxDim)
+    return TP_E_SHAPE;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  if (dtype == TP_BF16 && (h % 8 != 0 || v_local % 8 != 0)) return TP_E_UNSUPPORTED;
+  return TP_OK;
+}
+}  // namespace
+
+int tp_vocab_logits_fwd(int64_t rows, int64_t h, int64_t v_local, tp_dtype dtype, const void* X, const void* E_i,
+                        void* logits_i, hipStream_t stream) {
+  if (X == nullptr || E_i == nullptr || logits_i == nullptr) return TP_E_NULL;
+  const int st = logits_check(rows, h, v_local, dtype);
+  if (st != TP_OK) return st;
+  if (dtype == TP_BF16 && misaligned16({X, E_i, logits_i})) return TP_E_UNSUPPORTED;
+  const int64_t es = esize(dtype);
+  const Buf outs[] = {{logits_i, rows * v_local * es}};
+  const Buf ins[] = {{X, rows * h * es}, {E_i, v_local * h * es}};
+  if (any_alias(outs, 1, ins, 2)) return TP_E_ALIAS;
+  // logits = X E_i^T: A = X [rows, h] K-major; B(n = vocab row, k) = E_i [v_local, h] K-major
+  tp::GemmParams g = {};
+  g.A = X; g.lda = h;
+  g.B = E_i; g.ldb = h;
+  g.M = (int)rows; g.N = (int)v_local; g.K = (int)h;
+  g.C = logits_i; g.ldc = v_local;
+  auto gemm = dtype == TP_BF16 ? tp::gemm_bf16 : tp::gemm_f32;
+  return hip_status(gemm(g, true, true, tp::EPI_STORE, stream));
+}
+
+int tp_vocab_logits_bwd(int64_t rows, int64_t h, int64_t v_local, tp_dtype dtype, const void* X, const void* E_i,
+                        const void* dlogits_i, void* dX_i, void* dE_i, hipStream_t stream) {
+  if (dlogits_i == nullptr || (dX_i == nullptr && dE_i == nullptr)) return TP_E_NULL;
+  if (dX_i != nullptr && E_i == nullptr) return TP_E_NULL;
+  if (dE_i != nullptr && X == nullptr) return TP_E_NULL;
+  const int st = logits_check(rows, h, v_local, dtype);
+  if (st != TP_OK) return st;
+  const void* Xp = dE_i != nullptr ? X : nullptr;    // each output reads only its own operands
+  const void* Ep = dX_i != nullptr ? E_i : nullptr;
+  if (dtype == TP_BF16 && misaligned16({Xp, Ep, dlogits_i, dX_i, dE_i})) return TP_E_UNSUPPORTED;
+  const int64_t es = esize(dtype);
+  const Buf outs[] = {{dX_i, rows * h * es}, {dE_i, v_local * h * es}};
+  const Buf ins[] = {{Xp, rows * h * es}, {Ep, v_local * h * es}, {dlogits_i, rows * v_local * es}};
+  if (any_alias(outs, 2, ins, 3)) return TP_E_ALIAS;
+  auto gemm = dtype == TP_BF16 ? tp::gemm_bf16 : tp::gemm_f32;
+  hipError_t e = hipSuccess;
+  if (dE_i != nullptr) {
+    // dE_i = dlogits^T X: C [v_local, h]; A(m = vocab row, k = token) = dlogits MN-major; B(n, k) = X MN-major
+    tp::GemmParams g = {};
+    g.A = dlogits_i; g.lda = v_local;
+    g.B = Xp; g.ldb = h;
+    g.M = (int)v_local; g.N = (int)h; g.K = (int)rows;
+    g.C = dE_i; g.ldc = h;
+    e = gemm(g, false, false, tp::EPI_STORE, stream);
+  }
+  if (e == hipSuccess && dX_i != nullptr) {
+    // dX_i = dlogits E_i: A = dlogits [rows, v_local] K-major; B(n = h, k = vocab row) = E_i [v_local, h] MN-major
+    tp::GemmParams g = {};
+    g.A = dlogits_i; g.lda = v_local;
+    g.B = Ep; g.ldb = h;
+    g.M = (int)rows; g.N = (int)h; g.K = (int)v_local;
+    g.C = dX_i; g.ldc = h;
+    e = gemm(g, true, false, tp::EPI_STORE, stream);
+  }
+  return hip_status(e);
+}
+
 }  // extern "C"

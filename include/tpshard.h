@@ -272,6 +272,23 @@ int tp_vocab_ce_bwd(int64_t rows, int64_t v_local, int rank, tp_dtype dtype, con
                     const int32_t* targets, const float* lse, const float* dloss, void* dlogits_i,
                     hipStream_t stream);
 
+/* Vocab-parallel output layer ([MEGA] output-logits remark: the output (embedding) weight E [V, h] is split by
+ * vocab rows, so each rank's GEMM gives its own logit columns and feeds the cross entropy above directly, with only
+ * per-row scalars crossing ranks; [ATLAS] §5 table, the vocab-parallel CE row; [SPLIT] "Column Parallel" and its
+ * backward).  Rank r holds E_i = E[r*v_local : (r+1)*v_local] [v_local, h], row-major (one row per vocab entry):
+ *   forward:  logits_i = X E_i^T        [rows, v_local]  (rows = s*b token rows of X [rows, h])
+ *   backward: dE_i     = dlogits_i^T X  [v_local, h]     local weight gradient
+ *             dX_i     = dlogits_i E_i  [rows, h]        a partial: the input gradient is its sum over the t ranks
+ *                                                        (tp_partial_reduce)
+ * logits_i is what tp_vocab_ce_fwd_local / tp_vocab_ce_bwd read, and dlogits_i what tp_vocab_ce_bwd writes.  In the
+ * backward either output may be NULL (not computed; its operand X or E_i may then be NULL too), not both.  bf16:
+ * h and v_local multiples of 8, pointers 16-byte aligned (else TP_E_UNSUPPORTED).  Outputs must not overlap
+ * inputs. */
+int tp_vocab_logits_fwd(int64_t rows, int64_t h, int64_t v_local, tp_dtype dtype, const void* X, const void* E_i,
+                        void* logits_i, hipStream_t stream);
+int tp_vocab_logits_bwd(int64_t rows, int64_t h, int64_t v_local, tp_dtype dtype, const void* X, const void* E_i,
+                        const void* dlogits_i, void* dX_i, void* dE_i, hipStream_t stream);
+
 /* Launch timing, a profiling aid (not part of the block's arithmetic).  tp_timing_begin arms the calling thread:
  * every kernel launched by a later tp_* call on this thread is bracketed by hipEventRecord(starts[i], stream) and
  * hipEventRecord(stops[i], stream), for the first `capacity` launches (later ones run unrecorded).  The events are

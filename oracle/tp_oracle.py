@@ -802,6 +802,30 @@ def vocab_parallel_cross_entropy(logit_shards: Sequence[np.ndarray], targets: np
     return loss, lse
 
 
+def vocab_parallel_logits(X: np.ndarray, E: np.ndarray, t: int, rank: int) -> np.ndarray:
+    """Rank r's logits of the vocab-sharded output layer ([MEGA] output-logits remark; [ATLAS] §5 vocab-parallel
+    row): the output weight E [V, h] (one row per vocab entry, the embedding table's layout) is split by vocab rows,
+    rank r holding E_r = E[r*V/t : (r+1)*V/t]; its logits are X E_r^T [rows, V/t], the columns
+    [r*V/t, (r+1)*V/t) of the full X E^T."""
+    V = E.shape[0]
+    _need_div(V, t, "vocab")
+    v = V // t
+    return np.asarray(X, dtype=np.float64) @ np.asarray(E[rank * v:(rank + 1) * v], dtype=np.float64).T
+
+
+def vocab_parallel_logits_backward(X: np.ndarray, E: np.ndarray, dlogits_r: np.ndarray, t: int, rank: int):
+    """Gradients of rank r's logits X E_r^T for the upstream gradient dlogits_r [rows, V/t]: the local weight
+    gradient dE_r = dlogits_r^T X [V/t, h], and the partial input gradient dX_r = dlogits_r E_r [rows, h], whose sum
+    over the t ranks is the input gradient (the backward of a column-parallel layer, [SPLIT] "Column Parallel"
+    backward)."""
+    V = E.shape[0]
+    _need_div(V, t, "vocab")
+    v = V // t
+    d = np.asarray(dlogits_r, dtype=np.float64)
+    Er = np.asarray(E[rank * v:(rank + 1) * v], dtype=np.float64)
+    return {"dX": d @ Er, "dE": d.T @ np.asarray(X, dtype=np.float64)}
+
+
 def vocab_parallel_cross_entropy_backward(logits_r: np.ndarray, targets: np.ndarray, rank: int, lse: np.ndarray,
                                           dloss: np.ndarray) -> np.ndarray:
     """Rank-local backward: (exp(logits_r - lse) - [global column == target]) * dloss per row; 0 when ignored."""

@@ -336,3 +336,28 @@ def test_built_library_matches_the_sources():
 
     assert is_current() and built_hash() == source_hash()
     assert source_hash(("-DSOMETHING_ELSE",)) != source_hash()
+
+
+def test_vocab_logits_validation(L):
+    P = [addr(i) for i in range(6)]
+
+    def fwd(rows=64, h=32, v=48, dt=BF16, ptrs=None):
+        q = ptrs or P[:3]  # X, E_i, logits_i
+        return L.tp_vocab_logits_fwd(rows, h, v, *q, stream=0, dtype=dt, check=False)
+
+    def bwd(rows=64, h=32, v=48, dt=BF16, ptrs=None):
+        q = ptrs or P[:5]  # X, E_i, dlogits_i, dX_i, dE_i
+        return L.tp_vocab_logits_bwd(rows, h, v, *q, stream=0, dtype=dt, check=False)
+
+    for i in range(3):
+        assert fwd(ptrs=P[:i] + [None] + P[i + 1:3]) == -1, i
+    assert fwd(rows=0) == -2 and fwd(v=-8) == -2
+    assert fwd(dt=5) == -4
+    assert fwd(v=44) == -7 and fwd(h=30) == -7                        # bf16 rows of 8
+    assert fwd(ptrs=[P[0], P[1] + 2, P[2]]) == -7                      # misaligned E_i
+    assert fwd(ptrs=[P[0], P[1], P[0]]) == -6                          # logits over X
+    assert bwd(ptrs=[P[0], P[1], P[2], None, None]) == -1              # no output
+    assert bwd(ptrs=[P[0], None, P[2], P[3], None]) == -1              # dX needs E_i
+    assert bwd(ptrs=[None, P[1], P[2], None, P[4]]) == -1              # dE needs X
+    assert bwd(ptrs=[P[0], P[1], P[2], P[2], P[4]]) == -6              # dX over dlogits
+    assert bwd(v=12) == -7

@@ -6,7 +6,10 @@ Parallelism (SP)" §5, the vocab-parallel CE row: all-reduce(max), all-reduce(su
 * closed forms: equal logits give log V; a target logit far above the rest gives a loss near 0;
 * shifting a row by a constant changes nothing; gradient rows sum to 0 and match finite differences;
 * the sharded steps equal the unsharded loss for t = 1, 2, 4, with targets in every shard, and stay finite for
-  logits of magnitude 1e4 (a plain exp would overflow).
+  logits of magnitude 1e4 (a plain exp would overflow);
+* undefined rows (a target past the vocab, a row of -inf logits) give NaN;
+* the vocab-sharded logits X E_r^T against a triple loop, and their backward (dX_r summed over ranks, dE_r
+  stacked) against central differences of the whole output-layer loss.
 """
 import numpy as np
 import pytest
@@ -103,3 +106,65 @@ def test_undefined_rows_are_nan_not_a_number_that_passes():
     assert lv[4] == 0.0 and np.allclose(lv[ok], loss[ok], rtol=1e-12)
     g = O.vocab_parallel_cross_entropy_backward(x[:, :8], tg, 0, lse, np.ones(6))
     assert np.all(np.isnan(g[1])) and np.all(g[4] == 0.0)
+
+
+def test_vocab_parallel_logits_brute_force_and_concat():
+    """Rank r's logits are columns [r V/t, (r+1) V/t) of X E^T: against a triple loop on a tiny case, and the t
+    shards concatenated give the unsharded logits."""
+    rng = np.random.default_rng(21)
+    rows, h, V, t = 3, 5, 8, 2
+    X, E = rng.standard_normal((rows, h)), rng.standard_normal((V, h))
+    full = np.zeros((rows, V))
+    for i in range(rows):
+        for j in range(V):
+            for k in range(h):
+                full[i, j] += X[i, k] * E[j, k]
+    shards = [O.vocab_parallel_logits(X, E, t, r) for r in range(t)]
+    assert np.allclose(np.concatenate(shards, axis=1), full, rtol=1e-14, atol=1e-14)
+    assert np.allclose(shards[1], full[:, 4:], rtol=1e-14, atol=1e-14)
+    with pytest.raises(ValueError):
+        O.vocab_parallel_logits(X, E[:7], 2, 0)
+
+
+def test_vocab_parallel_logits_backward_by_finite_differences():
+    """The loss sum_i dloss_i CE(X E^T)_i: its gradients by central differences equal the sum over ranks of dX_r
+    and the stacked dE_r, with dlogits the cross entropy's own backward (the whole output-layer chain)."""
+    rng = np.random.default_rng(22)
+    rows, h, V, t = 4, 6, 12, 3
+    X, E = rng.standard_normal((rows, h)), rng.standard_normal((V, h)) * 0.5
+    tg = rng.integers(0, V, rows)
+    tg[1] = -100
+    dl = rng.standard_normal(rows)
+
+    def loss(Xv, Ev):
+        return float((O.cross_entropy(Xv @ Ev.T, tg) * dl).sum())
+
+    shards = [O.vocab_parallel_logits(X, E, t, r) for r in range(t)]
+    _, lse = O.vocab_parallel_cross_entropy(shards, tg)
+    dX = np.zeros_like(X)
+    dE = []
+    for r in range(t):
+        g = O.vocab_parallel_cross_entropy_backward(shards[r], tg, r, lse, dl)
+        b = O.vocab_parallel_logits_backward(X, E, g, t, r)
+        dX += b["dX"]
+        dE.append(b["dE"])
+    dE = np.concatenate(dE, axis=0)
+    eps = 1e-6
+    for M, G in ((X, dX), (E, dE)):
+        fd = np.zeros_like(M)
+        for idx in np.ndindex(M.shape):
+            keep = M[idx]
+            M[idx] = keep + eps
+            lp = loss(X, E)
+            M[idx] = keep - eps
+            lm = loss(X, E)
+            M[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert np.allclose(G, fd, rtol=1e-6, atol=1e-8)
+    # a mistake in the backward's operands shows: dE from X^T dlogits (transposed) has the wrong shape / values
+    assert not np.allclose(dX, dlogits_all(shards, tg, lse, dl, t) @ E[::-1])
+
+
+def dlogits_all(shards, tg, lse, dl, t):
+    return np.concatenate([O.vocab_parallel_cross_entropy_backward(shards[r], tg, r, lse, dl) for r in range(t)],
+                          axis=1)

@@ -10,7 +10,8 @@ Recipe (one stream per tensor, so adding a tensor never shifts another):
 
 Tensor ids: X=0, A (or Wqkv)=1, B (or Wo)=2, dZ=3, column bias=4, row bias=5, partial sums=7; the
 sequence-parallel region adds LayerNorm gamma=8, beta=9, residual=10, dropout random words=11, dy=12; the
-vocab-parallel cross entropy logits=13, targets=14, per-row loss gradients=15.
+vocab-parallel cross entropy logits=13, targets=14, per-row loss gradients=15; the vocab-parallel output layer's
+weight E [V, h] = 16 and a synthetic upstream logit gradient = 17.
 Distributions follow the workloads of the pages: activations and upstream gradients N(0,1), weights N(0, 0.02^2)
 (0.02 is the standard deviation, the GPT/Megatron init convention), biases N(0, 0.02^2); LayerNorm gamma
 1 + N(0, 0.1^2) and beta N(0, 0.1^2) (a trained-looking affine, not the identity, so a dropped gamma or beta
@@ -28,6 +29,7 @@ import numpy as np
 T_X, T_A, T_B, T_DZ, T_BIAS_COL, T_BIAS_ROW = 0, 1, 2, 3, 4, 5
 T_GAMMA, T_BETA, T_RESID, T_BITS, T_DY = 8, 9, 10, 11, 12
 T_LOGITS, T_TARGETS, T_DLOSS = 13, 14, 15
+T_EMBED, T_DLOGITS = 16, 17
 LOGIT_STD = 2.0
 WEIGHT_STD = 0.02
 
@@ -183,6 +185,17 @@ def vocab_ce_inputs(rows: int, vocab: int, dtype: str = "bf16", seed: int = 0) -
     targets[rng.random(rows) < 1.0 / 64] = -100
     return {"logits": tensor(seed, T_LOGITS, (rows, vocab), LOGIT_STD, dtype), "targets": targets,
             "dloss": normal_f32(seed, T_DLOSS, (rows,))}
+
+
+def vocab_logits_inputs(rows: int, h: int, vocab: int, dtype: str = "bf16", seed: int = 0) -> dict:
+    """The vocab-parallel output layer: token activations X [rows, h] N(0, 1), the output weight E [vocab, h]
+    N(0, 0.02^2) (one row per vocab entry; rank r's shard is rows [r*vocab/t, (r+1)*vocab/t)), targets and per-row
+    loss gradients as in vocab_ce_inputs, and a synthetic upstream logit gradient dlogits [rows, vocab] N(0, 1) for
+    testing the backward GEMMs on their own."""
+    ce = vocab_ce_inputs(rows, vocab, dtype, seed)
+    return {"X": tensor(seed, T_X, (rows, h), 1.0, dtype), "E": tensor(seed, T_EMBED, (vocab, h), WEIGHT_STD, dtype),
+            "targets": ce["targets"], "dloss": ce["dloss"],
+            "dlogits": tensor(seed, T_DLOGITS, (rows, vocab), 1.0, dtype)}
 
 
 def partials(seed: int, t: int, shape, dtype: str = "bf16", tensor_id: int = 7) -> np.ndarray:
