@@ -16,15 +16,15 @@ MFMA peak.  rs_dim0 = the reduce-scatter kernel (census pass) against HBM bandwi
 launch from the committed rocprofv3 counter summary under profiles/ (null once the kernel source differs from the
 one profiled).  cpu_baseline = the fp64 oracle on a bounded sample.
 
-overlap, attention_block(_gqa), gather_dim0, sp_region and vocab_ce = the other rows of the hot path, timed after
-the step (not part of value): the same step with its reductions on a second stream beside the GEMMs (serial vs
-overlapped ms/step); the attention block forward and backward at the 22B-class shape and at the Llama-70B-sized
-grouped-query shape; the dim-0 gather at the Llama-70B-sized SP shape; the sequence-parallel region (dropout +
-residual + LayerNorm, forward and backward) on every rank's rows at that same shape; the vocab-parallel cross
-entropy (local pass, combine, backward) at 16384 token rows over a 51200-entry vocab.  vendor_gemm = the step's
-GEMMs at one rank's shapes through torch.matmul (the ROCm BLAS libraries), beside this library's census times: a
-comparison point only, never on the path; vendor_sdpa = the same for one rank's causal attention through torch's
-fused scaled_dot_product_attention, beside this library's attention kernels.
+overlap, attention_block(_gqa), gather_dim0, sp_region, output_layer and the two other MLP workloads = the other
+rows of the hot path, timed after the step (not part of value): the same step with its reductions on a second
+stream beside the GEMMs (serial vs overlapped ms/step); the attention block forward and backward at the 22B-class
+shape and at the Llama-70B-sized grouped-query shape; the dim-0 gather at the Llama-70B-sized SP shape (rotating
+over buffer sets larger than the Infinity Cache); the sequence-parallel region (dropout + residual + LayerNorm,
+forward and backward) on every rank's rows at that same shape; the vocab-parallel output layer (logits GEMM, cross
+entropy, backward GEMMs, dX all-reduce) at 16384 token rows, h=4096 and a 51200-entry vocab; the 8.3B-width MLP
+(h=3072, ffn=12288, s=1024, b=8; all-reduce form) and the sequence-parallel SwiGLU MLP (h=8192, ffn=28672,
+s=4096, b=1; all-gather in, reduce-scatter out), each a whole fwd+bwd step with per-kernel rates.
 """
 from __future__ import annotations
 
@@ -47,7 +47,8 @@ def parse_args(argv=None):
     ap.add_argument("--workload", default="mlp_h4096_ffn16384_t8_b8_s2048")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--no-extra", action="store_true", help="skip the overlap, attention-block, gather, SP-region and cross-entropy measurements")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the overlap, attention-block, gather, SP-region, output-layer and other-MLP legs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one dim-0 gather (a plain copy) of this many MiB, for counter calibration")
     return ap.parse_args(argv)
@@ -245,113 +246,220 @@ def overlap_measure(blk, X, dZ, Z_rs, dX_rs, serial_step, steps: int, chunks: in
             "rounds_ms": {k: [round(x, 4) for x in v] for k, v in times.items()}}
 
 
-def vendor_gemm_measure(w, kernels: dict, reps: int = 20) -> dict:
-    """The step's GEMMs through torch.matmul (the ROCm BLAS libraries) at one rank's shapes, beside this library's
-    census times of the same products.  A comparison point only: nothing of it is on the path or in value."""
-    import torch
-
-    M, h, fl = w.M, w.h, w.f_l
-    dev = "cuda"
-    X, A, B = (torch.randn(r, c, device=dev).to(torch.bfloat16) for r, c in ((M, h), (h, fl), (fl, h)))
-    Y, dZ, dU = (torch.randn(r, c, device=dev).to(torch.bfloat16) for r, c in ((M, fl), (M, h), (M, fl)))
-    cases = [  # name, product, flops, this library's kernel for it (its launch also runs the epilogue named)
-        ("column X.A_i", lambda: X @ A, 2 * M * fl * h, "gemm_bf16_big_KM_bias_act"),
-        ("row Y_i.B_i", lambda: Y @ B, 2 * M * h * fl, "gemm_bf16_big_KM_store"),
-        ("dY = dZ.B_i^T", lambda: dZ @ B.t(), 2 * M * fl * h, "gemm_bf16_big_KK_act_bwd"),
-        ("dX_i = dU_i.A_i^T", lambda: dU @ A.t(), 2 * M * h * fl, "gemm_bf16_big_KK_store"),
-        ("dB_i = Y_i^T.dZ then dA_i = X^T.dU_i", lambda: (Y.t() @ dZ, X.t() @ dU), 4 * M * h * fl,
-         "gemm_bf16_big_pair_MM_store"),
-    ]
-    out = {}
-    for name, fn, flops, ours in cases:
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        med = sorted(ts)[len(ts) // 2]
-        k = kernels.get(ours, {})
-        out[name] = {"library_median_us": round(med, 2), "library_tflops": round(flops / med / 1e6, 1),
-                     "ours_kernel": ours, "ours_avg_us": round(k["avg_us"], 2) if k else None}
-    del X, A, B, Y, dZ, dU
-    return {"library": "torch.matmul (ROCm BLAS), bf16 in / bf16 out, no epilogue", "per_rank_gemms": out}
-
-
-def vendor_sdpa_measure(blocks: dict, reps: int = 10) -> dict:
-    """Causal attention of one rank's heads through torch's fused scaled_dot_product_attention (flash and
-    memory-efficient backends only; a backend that cannot take the shape is reported, never replaced by the math
-    path), forward and backward, beside this library's attention kernels from the attention-block legs.  A
-    comparison point only."""
-    import torch
-    from torch.nn.attention import SDPBackend, sdpa_kernel
-
-    out = {}
-    for key, (hq, d) in (("attention_block", (8, 96)), ("attention_block_gqa", (8, 128))):
-        s = 4096
-        q, k, v = (torch.randn(1, hq, s, d, device="cuda", dtype=torch.bfloat16) for _ in range(3))
-        res = {}
-        for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
-            try:
-                with sdpa_kernel([be]):
-                    qq, kk, vv = (x.clone().requires_grad_(True) for x in (q, k, v))
-                    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True)
-                    go = torch.randn_like(o)
-
-                    def timed(fn):
-                        for _ in range(2):
-                            fn()
-                        torch.cuda.synchronize()
-                        ts = []
-                        for _ in range(reps):
-                            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                            e0.record()
-                            fn()
-                            e1.record()
-                            torch.cuda.synchronize()
-                            ts.append(e0.elapsed_time(e1) * 1e3)
-                        return round(sorted(ts)[len(ts) // 2], 2)
-
-                    fwd = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True))
-                    bwd = timed(lambda: o.backward(go, retain_graph=True))
-                    res[be.name] = {"fwd_median_us": fwd, "bwd_median_us": bwd}
-                    del qq, kk, vv, o, go
-            except Exception as e:  # the backend does not take this shape: say so
-                res[be.name] = {"error": str(e)[:160]}
-        b = blocks.get(key, {})
-        ours_f = b.get("roles", {}).get("attention", {}).get("us_per_rank")
-        ours_b = b.get("backward", {}).get("roles", {}).get("attention_core_bwd", {}).get("us_per_rank")
-        out[key] = {"shape": f"b=1, {hq} heads, s={s}, d={d}, causal", "torch_sdpa": res,
-                    "ours_fwd_us": ours_f, "ours_bwd_us": ours_b}
-        del q, k, v
-    return out
-
-
-def gather_measure(L, reps: int) -> dict:
+def gather_measure(L, reps: int, sets: int = 6) -> dict:
     """The sequence-parallel entry gather: t = 8 slices [s/t, b, h] -> [s, b, h] at the Llama-70B-sized SP shape
-    (s=4096, b=1, h=8192, bf16): reads and writes 64 MiB."""
+    (s=4096, b=1, h=8192, bf16): reads and writes 64 MiB.  The launches rotate over `sets` source / destination
+    pairs (768 MiB for 6), more than the 256 MB Infinity Cache holds, so each launch streams from HBM."""
     import torch
 
     t, s, b, h = 8, 4096, 1, 8192
-    sl = torch.randn((t, s // t, b, h), device="cuda").to(torch.bfloat16)
-    out = torch.empty((s, b, h), dtype=torch.bfloat16, device="cuda")
+    srcs = [torch.randn((t, s // t, b, h), device="cuda").to(torch.bfloat16) for _ in range(sets)]
+    outs = [torch.empty((s, b, h), dtype=torch.bfloat16, device="cuda") for _ in range(sets)]
     dims = L.make_dims(s=s, b=b, h=h, t=t)
-    L.tp_gather_dim0(dims, sl, out)
+    for i in range(sets):
+        L.tp_gather_dim0(dims, srcs[i], outs[i])
     torch.cuda.synchronize()
     with L.LaunchTimer(capacity=reps + 2) as lt:
-        for _ in range(reps):
-            L.tp_gather_dim0(dims, sl, out)
+        for i in range(reps):
+            L.tp_gather_dim0(dims, srcs[i % sets], outs[i % sets])
     torch.cuda.synchronize()
     ms = sorted(m for _, m in lt.results())
     med = ms[len(ms) // 2]
     nbytes = 2 * s * b * h * 2
-    return {"workload": "gather_dim0_t8_s4096_b1_h8192", "bytes_per_launch": nbytes, "median_us": round(1e3 * med, 2),
-            "gbps": round(nbytes / (med * 1e-3) / 1e9, 1), "frac_hbm": round(nbytes / (med * 1e-3) / PEAK_HBM_BYTES, 4)}
+    del srcs, outs
+    return {"workload": "gather_dim0_t8_s4096_b1_h8192", "buffer_sets": sets, "bytes_per_launch": nbytes,
+            "median_us": round(1e3 * med, 2), "gbps": round(nbytes / (med * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (med * 1e-3) / PEAK_HBM_BYTES, 4)}
+
+
+def mlp_gemm_flops(w, name: str) -> float:
+    """Algorithmic flops of one launch of an MLP GEMM kernel at workload w (2 M N K per product)."""
+    M, h, fl = w.M, w.h, w.f_l
+    n1 = 2 * fl if w.act == "swiglu" else fl
+    if "_pair_" in name:
+        return 2.0 * M * h * (fl + n1)                       # dB_i and dA_i
+    if name.endswith("swiglu_fwd") or name.endswith("bias_act") or name.endswith("KM_bias"):
+        return 2.0 * M * h * n1                              # column GEMM
+    if name.endswith("KM_store"):
+        return 2.0 * M * fl * h                              # row GEMM
+    if name.endswith("act_bwd") or name.endswith("swiglu_bwd"):
+        return 2.0 * M * h * fl                              # dY = dZ B_i^T (+ act')
+    if name.endswith("KK_store"):
+        return 2.0 * M * n1 * h                              # dX_i = dU A_i^T
+    return 0.0
+
+
+def mlp_leg(L, w, steps: int, warmup: int = 2) -> dict:
+    """Another MLP workload's whole step, all t ranks on the one GPU.  The 8.3B-width GeLU MLP (h=3072,
+    ffn=12288, s=1024, b=8): every rank's forward, the all-reduce of the partials, every rank's backward, the
+    all-reduce of the dX partials.  The sequence-parallel SwiGLU MLP (h=8192, ffn=28672, s=4096, b=1): the dim-0
+    all-gather of the input's 512-token slices, every rank's forward, the reduce-scatter back to slices; then the
+    all-gather of the upstream gradient's slices, every rank's backward, the reduce-scatter of the dX partials.
+    Per-kernel HIP-event durations from a pass with every launch bracketed; ms_per_step and tflops_step from a pass
+    without those events."""
+    import numpy as np
+    import torch
+
+    import tp_inputs as TI
+    from attention_block_columnparallel_amd.block import MlpBlock
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    sp = w.name.startswith("sp_")
+    inp = TI.mlp_inputs(w)
+    blk = MlpBlock(w.s, w.b, w.h, w.ffn, w.t, w.act, dev(inp["A"]), dev(inp["B"]))
+    dims, t = blk.dims, w.t
+    if sp:
+        Xs = dev(inp["X"]).reshape(t, w.s // t, w.b, w.h)
+        dZs = dev(inp["dZ"]).reshape(t, w.s // t, w.b, w.h)
+        X = torch.empty((w.s, w.b, w.h), dtype=torch.bfloat16, device="cuda")
+        dZ = torch.empty_like(X)
+        Zo = torch.empty_like(Xs)
+        dXo = torch.empty_like(Xs)
+    else:
+        X, dZ = dev(inp["X"]), dev(inp["dZ"])
+        Zo = torch.empty((w.M, w.h), dtype=torch.bfloat16, device="cuda")
+        dXo = torch.empty_like(Zo)
+    del inp
+
+    def step():
+        if sp:
+            L.tp_gather_dim0(dims, Xs, X)
+            blk.forward_ranks(X)
+            L.tp_reduce_scatter_dim0(dims, -1, blk.Zp, None, Zo)
+            L.tp_gather_dim0(dims, dZs, dZ)
+            blk.backward_ranks(X, dZ)
+            L.tp_reduce_scatter_dim0(dims, -1, blk.dXp, None, dXo)
+        else:
+            blk.forward_ranks(X)
+            L.tp_partial_reduce(w.M * w.h, w.h, t, blk.Zp, None, Zo)
+            blk.backward_ranks(X, dZ)
+            L.tp_partial_reduce(w.M * w.h, w.h, t, blk.dXp, None, dXo)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    with L.LaunchTimer(capacity=steps * (6 * t + 4) + 8) as lt:
+        for _ in range(steps):
+            step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n1 = 2 * w.f_l if w.act == "swiglu" else w.f_l
+    step_flops = 2.0 * w.M * w.h * (3 * n1 + 3 * w.f_l) * t
+    n_bytes = w.M * w.h * 2
+    kern = {}
+    for name, kms in lt.results():
+        kern.setdefault(name, []).append(kms)
+    out = {"workload": w.name, "form": "SP: all-gather in, reduce-scatter out" if sp else "all-reduce (g and f)",
+           "ms_per_step": round(ms, 4), "step_gflop": round(step_flops / 1e9, 1),
+           "tflops_step": round(step_flops / (ms * 1e-3) / 1e12, 1),
+           "frac_bf16_peak_step": round(step_flops / (ms * 1e-3) / PEAK_BF16_FLOPS, 4), "kernels": {}}
+    for name, v in kern.items():
+        avg = 1e3 * float(np.mean(v))
+        k = {"launches_per_step": len(v) // steps, "avg_us": round(avg, 2)}
+        fl = mlp_gemm_flops(w, name) if name.startswith("gemm") else 0.0
+        if fl:
+            k["tflops"] = round(fl / (avg * 1e-6) / 1e12, 1)
+            k["frac_bf16_peak"] = round(fl / (avg * 1e-6) / PEAK_BF16_FLOPS, 4)
+        elif name.startswith("reduce"):
+            nb = (t + 1) * n_bytes  # t partials read, the reduced tensor (every rank's slice) written once
+            k["gbps"] = round(nb / (avg * 1e-6) / 1e9, 1)
+            k["frac_hbm"] = round(nb / (avg * 1e-6) / PEAK_HBM_BYTES, 4)
+        elif name.startswith("copy"):
+            k["gbps"] = round(2 * n_bytes / (avg * 1e-6) / 1e9, 1)
+            k["frac_hbm"] = round(2 * n_bytes / (avg * 1e-6) / PEAK_HBM_BYTES, 4)
+        out["kernels"][name] = k
+    del blk, X, dZ, Zo, dXo
+    return out
+
+
+def output_layer_measure(L, reps: int) -> dict:
+    """The vocab-parallel output layer and its cross entropy at s=2048, b=8 (16384 token rows), h=4096, a
+    51200-entry vocab, t=8, bf16: per step, every rank's logits GEMM X E_r^T [16384, 6400] and the CE local pass,
+    the combine, then every rank's CE backward and its two backward GEMMs (dE_r = dlogits^T X, dX_r = dlogits E_r),
+    and the all-reduce of the dX partials.  Each GEMM is 2 * 16384 * 6400 * 4096 = 859 GFLOP."""
+    import numpy as np
+    import torch
+
+    import tp_inputs as TI
+
+    rows, h, V, t = 16384, 4096, 51200, 8
+    v = V // t
+    inp = TI.vocab_logits_inputs(rows, h, V, "bf16", seed=0)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    X = dev(inp["X"])
+    E = dev(inp["E"])
+    Es = [E[r * v:(r + 1) * v].contiguous() for r in range(t)]
+    del E
+    tg = torch.from_numpy(inp["targets"]).cuda()
+    dl = torch.from_numpy(inp["dloss"]).cuda()
+    del inp
+    logits = [torch.empty((rows, v), dtype=torch.bfloat16, device="cuda") for _ in range(t)]
+    dlog = torch.empty((rows, v), dtype=torch.bfloat16, device="cuda")
+    stats = torch.empty((t, rows, 4), dtype=torch.float32, device="cuda")
+    loss = torch.empty(rows, dtype=torch.float32, device="cuda")
+    lse = torch.empty_like(loss)
+    parts = torch.empty((t, rows, h), dtype=torch.bfloat16, device="cuda")
+    dE = [torch.empty((v, h), dtype=torch.bfloat16, device="cuda") for _ in range(t)]
+    dX = torch.empty((rows, h), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        for r in range(t):
+            L.tp_vocab_logits_fwd(rows, h, v, X, Es[r], logits[r])
+            L.tp_vocab_ce_fwd_local(rows, v, r, logits[r], tg, stats[r])
+        L.tp_vocab_ce_combine(rows, t, stats, tg, loss, lse)
+        for r in range(t):
+            L.tp_vocab_ce_bwd(rows, v, r, logits[r], tg, lse, dl, dlog)
+            L.tp_vocab_logits_bwd(rows, h, v, X, Es[r], dlog, parts[r], dE[r])
+        L.tp_partial_reduce(rows * h, h, t, parts, None, dX)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    with L.LaunchTimer(capacity=reps * (6 * t + 2) + 8) as lt:
+        for _ in range(reps):
+            step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gf = 2.0 * rows * v * h
+    alg_bytes = {"vocab_ce_local": rows * v * 2 + rows * 4 + rows * 16,
+                 "vocab_ce_combine": t * rows * 16 + rows * 4 * 3,
+                 "vocab_ce_bwd": rows * v * 2 * 2 + rows * 4 * 3,
+                 "reduce_bf16_t8": (t + 1) * rows * h * 2}
+    kern = {}
+    for name, kms in lt.results():
+        kern.setdefault(name, []).append(kms)
+    out = {"workload": "vocab_output_layer_t8_s2048_b8_h4096_v51200", "ms_per_step": round(ms, 4),
+           "step_gflop": round(3 * gf * t / 1e9, 1),
+           "tflops_gemms_in_step": round(3 * gf * t / (ms * 1e-3) / 1e12, 1), "kernels": {}}
+    for name, vv in kern.items():
+        avg = 1e3 * float(np.mean(vv))
+        k = {"launches_per_step": len(vv) // reps, "avg_us": round(avg, 2)}
+        if name.startswith("gemm"):
+            k["tflops"] = round(gf / (avg * 1e-6) / 1e12, 1)
+            k["frac_bf16_peak"] = round(gf / (avg * 1e-6) / PEAK_BF16_FLOPS, 4)
+        elif name in alg_bytes:
+            k["gbps"] = round(alg_bytes[name] / (avg * 1e-6) / 1e9, 1)
+            k["frac_hbm"] = round(alg_bytes[name] / (avg * 1e-6) / PEAK_HBM_BYTES, 4)
+        out["kernels"][name] = k
+    del X, Es, logits, dlog, parts, dE, dX
+    return out
 
 
 def sp_region_measure(L, reps: int) -> dict:
@@ -420,66 +528,28 @@ def sp_region_measure(L, reps: int) -> dict:
     return out
 
 
-def vocab_ce_measure(L, reps: int) -> dict:
-    """Vocab-parallel cross entropy at s=2048, b=8 (16384 token rows) over a 51200-entry vocab, t=8, bf16 logits:
-    per step every rank's local pass (reads its [16384, 6400] logit shard once), the combine of the 8 ranks'
-    per-row records (the max and sum all-reduces), every rank's backward (reads the shard, writes its gradient)."""
-    import numpy as np
-    import torch
-
-    import tp_inputs as TI
-
-    rows, V, t = 16384, 51200, 8
-    v = V // t
-    inp = TI.vocab_ce_inputs(rows, V, "bf16", seed=0)
-    logits = torch.from_numpy(inp["logits"].view(np.int16)).view(torch.bfloat16).cuda()
-    del inp["logits"]
-    shards = [logits[:, r * v:(r + 1) * v].contiguous() for r in range(t)]
-    del logits
-    tg = torch.from_numpy(inp["targets"]).cuda()
-    dl = torch.from_numpy(inp["dloss"]).cuda()
-    stats = torch.empty((t, rows, 4), dtype=torch.float32, device="cuda")
-    loss = torch.empty(rows, dtype=torch.float32, device="cuda")
-    lse = torch.empty_like(loss)
-    dlog = [torch.empty_like(sh) for sh in shards]
-
-    def step():
-        for r in range(t):
-            L.tp_vocab_ce_fwd_local(rows, v, r, shards[r], tg, stats[r])
-        L.tp_vocab_ce_combine(rows, t, stats, tg, loss, lse)
-        for r in range(t):
-            L.tp_vocab_ce_bwd(rows, v, r, shards[r], tg, lse, dl, dlog[r])
-
-    for _ in range(2):
-        step()
-    torch.cuda.synchronize()
-    with L.LaunchTimer(capacity=reps * (2 * t + 1) + 8) as lt:
-        for _ in range(reps):
-            step()
-    torch.cuda.synchronize()
-    alg = {"vocab_ce_local": rows * v * 2 + rows * 4 + rows * 16,
-           "vocab_ce_combine": t * rows * 16 + rows * 4 * 3,
-           "vocab_ce_bwd": rows * v * 2 * 2 + rows * 4 * 3}
-    kern = {}
-    for name, ms in lt.results():
-        kern.setdefault(name, []).append(ms)
-    out = {"workload": "vocab_ce_t8_s2048_b8_v51200", "rows": rows, "vocab": V, "kernels": {}}
-    for name, vv in kern.items():
-        med = 1e3 * float(np.median(vv))
-        out["kernels"][name] = {"launches_per_step": len(vv) // reps, "median_us": round(med, 2),
-                                "bytes_per_launch": alg[name], "gbps": round(alg[name] / (med * 1e-6) / 1e9, 1),
-                                "frac_hbm": round(alg[name] / (med * 1e-6) / PEAK_HBM_BYTES, 4)}
-    del shards, dlog
-    return out
+def cpu_cores() -> dict:
+    """The host's CPU count, the CPUs this process may run on, and the BLAS threads NumPy uses (the oracle's
+    matrix products run on those)."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    return {"cpu_count": os.cpu_count(), "affinity": aff, "blas_threads": blas_threads()}
 
 
 def cpu_baseline(w, inp, target_s: float) -> dict:
     """The oracle (fp64 NumPy, as it stands) on rank shards' fwd + bwd -- the same computation as the GPU's per-rank
     work.  The sample is R token rows of rank 0's shard when that alone takes about target_s; when rank 0's whole
-    shard takes less, whole shards of ranks 0, 1, ... until target_s has passed.  Reported in algorithmic TFLOP/s."""
+    shard takes less, whole shards of ranks 0, 1, ... until target_s has passed.  Reported in algorithmic TFLOP/s.
+    Two more oracle legs, each on a bounded sample of a few seconds: the causal attention forward of one rank at
+    the 22B-class shape (the first heads of rank 0, each a whole 4096-token sequence; 4 d flops per unmasked
+    query-key pair) and the fp32 rank-order reduce-scatter of the headline step's 8 partial buffers (a slice of
+    the token rows), in GB/s of algorithmic bytes."""
     import numpy as np
 
     import oracle as O
+    import tp_inputs as TI
 
     X = O.as_f64(inp["X"], w.dtype).reshape(w.M, w.h)
     dZ = O.as_f64(inp["dZ"], w.dtype).reshape(w.M, w.h)
@@ -512,8 +582,40 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
         flops = 12.0 * w.M * w.h * w.f_l * ranks
         sample = (f"ranks 0-{ranks - 1} shards fwd+bwd (fp64 NumPy), all {w.M} token rows each: "
                   f"{flops / 1e9:.1f} algorithmic GFLOP in {dt2:.2f} s")
-    return {"value": flops / dt2 / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": sample}
+    del X, dZ, A, B
+    cores = cpu_cores()
+    out = {"value": flops / dt2 / 1e12, "unit": "TFLOP/s", "cores": cores["blas_threads"], "kind": "oracle",
+           "sample": sample, "host": cores}
+
+    # attention forward of rank 0's heads at the 22B-class shape, whole sequences, until ~target_s / 3
+    aw = TI.ATTN_22B
+    rng = np.random.default_rng(0)
+    q, k, vv = (rng.standard_normal((aw.s, aw.d)) for _ in range(3))
+    heads, t_att = 0, 0.0
+    while t_att < target_s / 3 and heads < aw.a // aw.t:
+        t0 = time.perf_counter()
+        O.attention_core(q, k, vv, True)
+        t_att += time.perf_counter() - t0
+        heads += 1
+    att_flops = 4.0 * aw.d * aw.s * (aw.s + 1) / 2 * heads
+    out["attention_fwd"] = {"value": round(att_flops / t_att / 1e12, 4), "unit": "TFLOP/s",
+                            "sample": f"{heads} of rank 0's {aw.a // aw.t} heads (s={aw.s}, d={aw.d}, causal), "
+                                      f"{att_flops / 1e9:.1f} GFLOP in {t_att:.2f} s"}
+
+    # fp32 rank-order reduce-scatter of 8 partial buffers, a slice of the headline step's token rows
+    rows = 2048
+    parts = [rng.standard_normal((rows, w.h)).astype(np.float32) for _ in range(w.t)]
+    n_red, t_red = 0, 0.0
+    while t_red < target_s / 6 and n_red < 50:
+        t0 = time.perf_counter()
+        O.reduce_f32_rank_order(parts)
+        t_red += time.perf_counter() - t0
+        n_red += 1
+    red_bytes = (w.t + 1) * rows * w.h * 2.0 * n_red  # the bf16 step's algorithmic bytes for these rows
+    out["reduce_scatter"] = {"value": round(red_bytes / t_red / 1e9, 2), "unit": "GB/s",
+                             "sample": f"{n_red} passes over {rows} of {w.M} token rows x {w.t} partials "
+                                       f"(fp32 rank-order sums), bytes counted as the bf16 step's"}
+    return out
 
 
 def main(argv=None) -> int:
@@ -665,19 +767,15 @@ def main(argv=None) -> int:
         out["attention_block"] = attention_block_measure(L, max(2, args.steps // 2), 2)
         torch.cuda.empty_cache()
         out["attention_block_gqa"] = attention_block_measure(L, max(2, args.steps // 2), 2, TI.ATTN_GQA_70B)
-        out["gather_dim0"] = gather_measure(L, 20)
+        out["gather_dim0"] = gather_measure(L, 24)
         out["sp_region"] = sp_region_measure(L, 10)
-        out["vocab_ce"] = vocab_ce_measure(L, 10)
         torch.cuda.empty_cache()
-        if w.dtype == "bf16":  # comparison points only: a failure there costs its field, not the bench line
-            for key, fn in (("vendor_gemm", lambda: vendor_gemm_measure(w, out["kernels"])),
-                            ("vendor_sdpa", lambda: vendor_sdpa_measure(out))):
-                try:
-                    out[key] = fn()
-                except Exception as e:
-                    out[key] = {"error": str(e)[:200]}
+        out["output_layer"] = output_layer_measure(L, 5)
+        torch.cuda.empty_cache()
+        for other in ("mlp_h3072_ffn12288_t8_b8_s1024", "sp_swiglu_h8192_ffn28672_t8_s4096"):
+            if other != w.name:
+                out[other] = mlp_leg(L, TI.WORKLOADS[other], max(3, args.steps // 2))
                 torch.cuda.empty_cache()
-        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     else:
