@@ -26,7 +26,7 @@ EXPORTED = ["tp_status_str", "tp_last_hip_error", "tp_abi_version", "tp_shard_we
             "tp_mlp_bwd_phase",
             "tp_attn_fwd", "tp_attn_bwd", "tp_attn_bwd_workspace", "tp_partial_reduce", "tp_reduce_scatter_dim0", "tp_gather_dim0", "tp_sp_dropout_add_ln_fwd",
             "tp_sp_dropout_add_ln_bwd", "tp_sp_dropout_add_ln_bwd_noalloc", "tp_sp_ln_bwd_workspace", "tp_vocab_ce_fwd_local", "tp_vocab_ce_combine",
-            "tp_vocab_ce_bwd", "tp_vocab_logits_fwd", "tp_vocab_logits_bwd", "tp_timing_begin", "tp_timing_end",
+            "tp_vocab_ce_bwd", "tp_vocab_logits_fwd", "tp_vocab_logits_bwd", "tp_ln_fold_weights", "tp_ln_mlp_fwd", "tp_timing_begin", "tp_timing_end",
             "tp_timing_kernel", "tp_timing_filter"]
 
 
@@ -82,6 +82,8 @@ def _load() -> ctypes.CDLL:
         "tp_vocab_ce_bwd": ([I64, I64, I, I, P, P, P, P, P, P], I),
         "tp_vocab_logits_fwd": ([I64, I64, I64, I, P, P, P, P], I),
         "tp_vocab_logits_bwd": ([I64, I64, I64, I, P, P, P, P, P, P], I),
+        "tp_ln_fold_weights": ([D, I, I, P, P, P, P, P, P, P, P], I),
+        "tp_ln_mlp_fwd": ([D, I, I, I, P, P, P, P, P, P, P, P, P, P, P], I),
         "tp_timing_begin": ([ctypes.POINTER(P), ctypes.POINTER(P), I], I),
         "tp_timing_end": ([], I),
         "tp_timing_kernel": ([I], ctypes.c_char_p),
@@ -404,6 +406,32 @@ def tp_vocab_logits_bwd(rows: int, h: int, v_local: int, X, E_i, dlogits_i, dX_i
                                  _ptr(dX_i, rows * h * es if ok else 0, "dX_i"),
                                  _ptr(dE_i, v_local * h * es if ok else 0, "dE_i"), _stream(stream))
     return _check(st, "tp_vocab_logits_bwd", check)
+
+
+def tp_ln_fold_weights(dims: tp_dims, act, gamma, beta, A_i, a_i, A_ln, c_ln, b_ln, stream=None, dtype=None,
+                       check=True) -> int:
+    dt = _dtype_code(A_i, dtype)
+    n = _mlp_bytes(dims, act, dt)
+    nN = n["aN"] // 2 if _es(dt) else 0  # N1 elements
+    hb = dims.h * _es(dt) if _pos(dims.h) else 0
+    st = lib.tp_ln_fold_weights(ctypes.byref(dims), _act(act), dt, _ptr(gamma, hb, "gamma"), _ptr(beta, hb, "beta"),
+                                _ptr(A_i, n["a"], "A_i"), _ptr(a_i, n["aN"], "a_i"), _ptr(A_ln, n["a"], "A_ln"),
+                                _ptr(c_ln, nN * 4, "c_ln"), _ptr(b_ln, nN * 4, "b_ln"), _stream(stream))
+    return _check(st, "tp_ln_fold_weights", check)
+
+
+def tp_ln_mlp_fwd(dims: tp_dims, rank: int, act, X, ln_mean, ln_rstd, A_ln, c_ln, b_ln, B_i, U_i, Y_i, Z_i,
+                  stream=None, dtype=None, check=True) -> int:
+    dt = _dtype_code(X, dtype)
+    n = _mlp_bytes(dims, act, dt)
+    nN = n["aN"] // 2 if _es(dt) else 0
+    rows = dims.s * dims.b if _pos(dims.s, dims.b) else 0
+    st = lib.tp_ln_mlp_fwd(ctypes.byref(dims), int(rank), _act(act), dt, _ptr(X, n["act"], "X"),
+                           _ptr(ln_mean, rows * 4, "ln_mean"), _ptr(ln_rstd, rows * 4, "ln_rstd"),
+                           _ptr(A_ln, n["a"], "A_ln"), _ptr(c_ln, nN * 4, "c_ln"), _ptr(b_ln, nN * 4, "b_ln"),
+                           _ptr(B_i, n["b"], "B_i"), _ptr(U_i, n["u"], "U_i"), _ptr(Y_i, n["y"], "Y_i"),
+                           _ptr(Z_i, n["act"], "Z_i"), _stream(stream))
+    return _check(st, "tp_ln_mlp_fwd", check)
 
 
 class LaunchTimer:

@@ -581,11 +581,18 @@ __device__ __forceinline__ float2 lds_bf16x2(const uint16_t* ax, int i) {
 // same reason.
 template <int EPI, int ACT>
 __device__ __forceinline__ void chunk_rows(const GemmParams& p, const float* ep, int ep_pitch, int m0, int col, int lane,
-                                           const uint16_t* ax, float b0, float b1, int rows) {
+                                           const uint16_t* ax, float b0, float b1, int rows, float c0 = 0.f,
+                                           float c1 = 0.f) {
   auto row = [&](int r) {
     const float v0 = ep[r * ep_pitch + 2 * lane], v1 = ep[r * ep_pitch + 2 * lane + 1];
     const int64_t m = m0 + r;
-    if constexpr (EPI == EPI_STORE) {
+    if constexpr (EPI == EPI_LN_ACT) {
+      // LayerNorm(u) W + bias = rstd (u W' - mean c) + b, with W' = diag(gamma) W and c its column sums
+      const float mu = p.ln_mean[m], rs = p.ln_rstd[m];
+      const float u0 = fmaf(rs, fmaf(-mu, c0, v0), b0), u1 = fmaf(rs, fmaf(-mu, c1, v1), b1);
+      stg_bf16x2(p.C, m * p.ldc + col, u0, u1);
+      stg_bf16x2(p.C2, m * p.ldc2 + col, act_apply(ACT, u0), act_apply(ACT, u1));
+    } else if constexpr (EPI == EPI_STORE) {
       stg_bf16x2(p.C, m * p.ldc + col, v0, v1);
     } else if constexpr (EPI == EPI_BIAS) {
       stg_bf16x2(p.C, m * p.ldc + col, v0 + b0, v1 + b1);
@@ -613,15 +620,30 @@ __device__ __forceinline__ void chunk_rows(const GemmParams& p, const float* ep,
 template <int EPI>
 __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float* ep, int ep_pitch, int m0, int tile_n,
                                                int wn, int lane, const uint16_t* ax) {
-  if constexpr (EPI == EPI_SWIGLU_FWD) {
+  if constexpr (epi_swiglu_fwd(EPI)) {
     const int j = tile_n * 128 + wn * 64 + lane;
     if (j >= p.fhalf) return;
-    const float bg = p.bias ? bf16_to_f32(ldg_bf16(p.bias, j)) : 0.f;
-    const float bu = p.bias ? bf16_to_f32(ldg_bf16(p.bias, p.fhalf + j)) : 0.f;
+    float bg, bu, cg = 0.f, cu = 0.f;
+    if constexpr (epi_ln(EPI)) {
+      bg = p.ln_b[j];
+      bu = p.ln_b[p.fhalf + j];
+      cg = p.ln_c[j];
+      cu = p.ln_c[p.fhalf + j];
+    } else {
+      bg = p.bias ? bf16_to_f32(ldg_bf16(p.bias, j)) : 0.f;
+      bu = p.bias ? bf16_to_f32(ldg_bf16(p.bias, p.fhalf + j)) : 0.f;
+    }
     const int rows = min(16, p.M - m0);
     for (int r = 0; r < rows; ++r) {
-      const float g = ep[r * ep_pitch + lane] + bg;
-      const float u = ep[r * ep_pitch + 64 + lane] + bu;
+      float g, u;
+      if constexpr (epi_ln(EPI)) {
+        const float mu = p.ln_mean[m0 + r], rs = p.ln_rstd[m0 + r];
+        g = fmaf(rs, fmaf(-mu, cg, ep[r * ep_pitch + lane]), bg);
+        u = fmaf(rs, fmaf(-mu, cu, ep[r * ep_pitch + 64 + lane]), bu);
+      } else {
+        g = ep[r * ep_pitch + lane] + bg;
+        u = ep[r * ep_pitch + 64 + lane] + bu;
+      }
       const int64_t m = m0 + r;
       stg_bf16(p.C, m * p.ldc + j, g);
       stg_bf16(p.C, m * p.ldc + p.fhalf + j, u);
@@ -639,7 +661,19 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
       }
     }
     const int rows = min(16, p.M - m0);
-    if constexpr (EPI == EPI_BIAS_ACT || EPI == EPI_ACT_BWD) {  // the activation chosen once per chunk
+    if constexpr (EPI == EPI_LN_ACT) {
+      const float2 bb = make_float2(p.ln_b[col], p.ln_b[col + 1]);
+      const float2 cc = make_float2(p.ln_c[col], p.ln_c[col + 1]);
+      switch (p.act) {
+        case TP_ACT_GELU:
+          chunk_rows<EPI, TP_ACT_GELU>(p, ep, ep_pitch, m0, col, lane, ax, bb.x, bb.y, rows, cc.x, cc.y);
+          break;
+        case TP_ACT_GELU_TANH:
+          chunk_rows<EPI, TP_ACT_GELU_TANH>(p, ep, ep_pitch, m0, col, lane, ax, bb.x, bb.y, rows, cc.x, cc.y);
+          break;
+        default: chunk_rows<EPI, TP_ACT_RELU>(p, ep, ep_pitch, m0, col, lane, ax, bb.x, bb.y, rows, cc.x, cc.y);
+      }
+    } else if constexpr (EPI == EPI_BIAS_ACT || EPI == EPI_ACT_BWD) {  // the activation chosen once per chunk
       switch (p.act) {
         case TP_ACT_GELU: chunk_rows<EPI, TP_ACT_GELU>(p, ep, ep_pitch, m0, col, lane, ax, b0, b1, rows); break;
         case TP_ACT_GELU_TANH:
@@ -673,7 +707,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   constexpr int NSTAGE = 4;  // (a fifth 32 KB stage, filling the 160 KB LDS, measured slower)
   constexpr int D = NSTAGE - 1;                 // k-tiles in flight ahead of the one being multiplied
   constexpr int STAGE_B = (BM + BN) * BK2 * 2;  // bytes per stage (A tile then B tile)
-  constexpr bool SWIG = (EPI == EPI_SWIGLU_FWD);
+  constexpr bool SWIG = epi_swiglu_fwd(EPI);
   constexpr int EP = 132;  // epilogue fp32 row pitch: 16-byte writes of 16 consecutive rows hit distinct banks
   constexpr int NAUX = EPI == EPI_SWIGLU_BWD ? 8 : EPI == EPI_ACT_BWD ? 4 : 0;  // 16-byte aux loads per lane
   constexpr int EPW = 16 * EP * 4 + NAUX * 1024;                                  // epilogue bytes per wave
@@ -940,7 +974,8 @@ int num_cus() {
   }
   return v;
 }
-const char* const kEpiNames[] = {"store", "bias", "bias_act", "swiglu_fwd", "act_bwd", "swiglu_bwd"};
+const char* const kEpiNames[] = {"store", "bias", "bias_act", "swiglu_fwd", "act_bwd", "swiglu_bwd", "ln_act",
+                                 "ln_swiglu"};
 
 int choose_cfg(int M, int ntiles_cols_of_bn256, int N, bool swig, int fhalf) {
   (void)ntiles_cols_of_bn256;
@@ -987,8 +1022,8 @@ hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st
   GemmPair pp;
   pp.g[0] = p0;
   pp.g[1] = p1 ? *p1 : p0;
-  pp.tiles0 = big_tiles(p0, EPI == EPI_SWIGLU_FWD);
-  pp.tiles1 = p1 ? big_tiles(*p1, EPI == EPI_SWIGLU_FWD) : 0;
+  pp.tiles0 = big_tiles(p0, epi_swiglu_fwd(EPI));
+  pp.tiles1 = p1 ? big_tiles(*p1, epi_swiglu_fwd(EPI)) : 0;
   pp.ksplit = 1;
   pp.nfull = 0;
   pp.part = nullptr;
@@ -1160,6 +1195,71 @@ hipError_t gemm_bf16(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi,
   }
   if (!a_kmajor && !b_kmajor && epi == EPI_STORE) return launch_cfg<false, false, EPI_STORE>(ci, p, st);  // wgrad
   return hipErrorInvalidValue;
+}
+
+hipError_t gemm_bf16_ln(const GemmParams& p, int epi, hipStream_t st) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (!big_fits(p, true, false)) return hipErrorInvalidValue;
+  if (epi == EPI_LN_ACT) return launch_big<true, false, EPI_LN_ACT>(p, nullptr, st);
+  if (epi == EPI_LN_SWIGLU) return launch_big<true, false, EPI_LN_SWIGLU>(p, nullptr, st);
+  return hipErrorInvalidValue;
+}
+
+// The LayerNorm fold: 16 waves per workgroup, 128 columns (2 per lane); wave w takes rows w, w + 16, ...; the 16
+// partial sums of a column are added in wave order.
+__global__ __launch_bounds__(1024) void ln_fold_kernel(const uint16_t* __restrict__ gamma,
+                                                       const uint16_t* __restrict__ beta,
+                                                       const uint16_t* __restrict__ A, const uint16_t* __restrict__ a,
+                                                       int64_t h, int64_t n, uint16_t* __restrict__ A_ln,
+                                                       float* __restrict__ c, float* __restrict__ b) {
+  __shared__ float red[2][16][128];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t j = (int64_t)blockIdx.x * 128 + 2 * lane;
+  float c0 = 0.f, c1 = 0.f, b0 = 0.f, b1 = 0.f;
+  if (j < n) {
+#pragma unroll 4
+    for (int64_t k = wave; k < h; k += 16) {
+      const float g = bf16_to_f32(gamma[k]), be = bf16_to_f32(beta[k]);
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(A + k * n + j);
+      const float a0 = bf16_to_f32(w & 0xFFFFu), a1 = bf16_to_f32(w >> 16);
+      const uint32_t o = pack_bf16x2(g * a0, g * a1);  // the product of two bf16 values is exact in fp32
+      *reinterpret_cast<uint32_t*>(A_ln + k * n + j) = o;
+      c0 += bf16_to_f32(o & 0xFFFFu);
+      c1 += bf16_to_f32(o >> 16);
+      b0 = fmaf(be, a0, b0);
+      b1 = fmaf(be, a1, b1);
+    }
+  }
+  red[0][wave][2 * lane] = c0;
+  red[0][wave][2 * lane + 1] = c1;
+  red[1][wave][2 * lane] = b0;
+  red[1][wave][2 * lane + 1] = b1;
+  __syncthreads();
+  if (wave == 0 && j < n) {
+    float sc0 = 0.f, sc1 = 0.f, sb0 = 0.f, sb1 = 0.f;
+    for (int w = 0; w < 16; ++w) {
+      sc0 += red[0][w][2 * lane];
+      sc1 += red[0][w][2 * lane + 1];
+      sb0 += red[1][w][2 * lane];
+      sb1 += red[1][w][2 * lane + 1];
+    }
+    if (a != nullptr) {
+      sb0 += bf16_to_f32(a[j]);
+      sb1 += bf16_to_f32(a[j + 1]);
+    }
+    c[j] = sc0;
+    c[j + 1] = sc1;
+    b[j] = sb0;
+    b[j + 1] = sb1;
+  }
+}
+
+hipError_t ln_fold_weights(const void* gamma, const void* beta, const void* A, const void* a, int64_t h, int64_t n,
+                           void* A_ln, float* c, float* b, hipStream_t st) {
+  return TP_LAUNCH("ln_fold_weights", ln_fold_kernel, dim3((unsigned)((n + 127) / 128)), dim3(1024), 0, st,
+                   static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(beta),
+                   static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(a), h, n,
+                   static_cast<uint16_t*>(A_ln), c, b);
 }
 
 // The two weight-gradient GEMMs of a backward (both MN-major x MN-major, same K = s*b): one launch over both tile

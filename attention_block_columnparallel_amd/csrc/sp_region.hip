@@ -251,12 +251,14 @@ __global__ __launch_bounds__(NT) void sp_fwd_kernel(SpFwd p) {
     if (c < nch) {
       const int64_t e = rbase + 8 * c;
       if (p.out != nullptr) Io<T>::store(p.out, e, u[j]);
-      float g[8], b[8], y[8];
-      Io<T>::unpack(wg[j], g);
-      Io<T>::unpack(wb[j], b);
+      if (p.y != nullptr) {
+        float g[8], b[8], y[8];
+        Io<T>::unpack(wg[j], g);
+        Io<T>::unpack(wb[j], b);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = fmaf((u[j][i] - mean) * rstd, g[i], b[i]);
-      Io<T>::store(p.y, e, y);
+        for (int i = 0; i < 8; ++i) y[i] = fmaf((u[j][i] - mean) * rstd, g[i], b[i]);
+        Io<T>::store(p.y, e, y);
+      }
       if (p.mask != nullptr) p.mask[row * nch + c] = (uint8_t)kb[j];
     }
   }

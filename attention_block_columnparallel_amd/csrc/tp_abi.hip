@@ -525,7 +525,9 @@ int sp_check_sizes(int64_t rows, int64_t h, tp_dtype dtype, double p) {
 int tp_sp_dropout_add_ln_fwd(int64_t rows, int64_t h, tp_dtype dtype, double p, double eps, const void* z,
                              const void* residual, const uint32_t* bits, const void* gamma, const void* beta,
                              void* out, void* y, float* mean, float* rstd, uint8_t* mask, hipStream_t stream) {
-  if (z == nullptr || gamma == nullptr || beta == nullptr || y == nullptr) return TP_E_NULL;
+  if (z == nullptr || gamma == nullptr || beta == nullptr) return TP_E_NULL;
+  // without y the call is the first half of the LayerNorm-folded column GEMM: u and the statistics are its outputs
+  if (y == nullptr && (out == nullptr || mean == nullptr || rstd == nullptr)) return TP_E_NULL;
   if (p > 0.0 && bits == nullptr) return TP_E_NULL;
   if (!(eps >= 0.0) || eps > 1e30) return TP_E_SHAPE;
   int st = sp_check_sizes(rows, h, dtype, p);
@@ -665,6 +667,73 @@ int tp_vocab_ce_bwd(int64_t rows, int64_t v_local, int rank, tp_dtype dtype, con
   if (any_alias(outs, 1, ins, 4)) return TP_E_ALIAS;
   return hip_status(tp::vocab_ce_bwd(dtype, logits_i, targets, lse, dloss, rows, (int)v_local, rank, dlogits_i,
                                      stream));
+}
+
+namespace {
+// Sizes, dtype and alignment shared by the two LayerNorm-folded calls; the large-tile kernel needs h % 64 == 0.
+int ln_check(const tp_dims* dims, tp_act act, tp_dtype dtype) {
+  const int64_t s = dims->s, b = dims->b, h = dims->h, ffn = dims->ffn, t = dims->t;
+  if (h <= 0 || ffn <= 0 || t <= 0 || s < 0 || b < 0) return TP_E_SHAPE;
+  if (s * b >= kMaxDim || h >= kMaxDim || ffn >= kMaxDim) return TP_E_SHAPE;
+  if (ffn % t != 0) return TP_E_DIVISIBILITY;
+  if (bad_dtype(dtype)) return TP_E_DTYPE;
+  if (dtype != TP_BF16) return TP_E_UNSUPPORTED;
+  if (act != TP_ACT_GELU && act != TP_ACT_GELU_TANH && act != TP_ACT_SWIGLU && act != TP_ACT_RELU)
+    return TP_E_UNSUPPORTED;
+  if (h % 64 != 0 || h < 128 || (ffn / t) % 8 != 0) return TP_E_UNSUPPORTED;
+  return TP_OK;
+}
+}  // namespace
+
+int tp_ln_fold_weights(const tp_dims* dims, tp_act act, tp_dtype dtype, const void* gamma, const void* beta,
+                       const void* A_i, const void* a_i, void* A_ln, float* c_ln, float* b_ln, hipStream_t stream) {
+  if (dims == nullptr || gamma == nullptr || beta == nullptr || A_i == nullptr || A_ln == nullptr ||
+      c_ln == nullptr || b_ln == nullptr)
+    return TP_E_NULL;
+  const int st = ln_check(dims, act, dtype);
+  if (st != TP_OK) return st;
+  const int64_t h = dims->h, f = dims->ffn / dims->t, n1 = act == TP_ACT_SWIGLU ? 2 * f : f;
+  if (misaligned16({gamma, beta, A_i, a_i, A_ln})) return TP_E_UNSUPPORTED;
+  const Buf outs[] = {{A_ln, h * n1 * 2}, {c_ln, n1 * 4}, {b_ln, n1 * 4}};
+  const Buf ins[] = {{gamma, h * 2}, {beta, h * 2}, {A_i, h * n1 * 2}, {a_i, n1 * 2}};
+  if (any_alias(outs, 3, ins, 4)) return TP_E_ALIAS;
+  return hip_status(tp::ln_fold_weights(gamma, beta, A_i, a_i, h, n1, A_ln, c_ln, b_ln, stream));
+}
+
+int tp_ln_mlp_fwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const void* X, const float* ln_mean,
+                  const float* ln_rstd, const void* A_ln, const float* c_ln, const float* b_ln, const void* B_i,
+                  void* U_i, void* Y_i, void* Z_i, hipStream_t stream) {
+  if (dims == nullptr || X == nullptr || ln_mean == nullptr || ln_rstd == nullptr || A_ln == nullptr ||
+      c_ln == nullptr || b_ln == nullptr || B_i == nullptr || U_i == nullptr || Y_i == nullptr || Z_i == nullptr)
+    return TP_E_NULL;
+  int st = ln_check(dims, act, dtype);
+  if (st != TP_OK) return st;
+  if (dims->s <= 0 || dims->b <= 0) return TP_E_SHAPE;
+  if (rank < 0 || rank >= dims->t) return TP_E_RANK;
+  const int64_t M = dims->s * dims->b, h = dims->h, f = dims->ffn / dims->t;
+  const int64_t n1 = act == TP_ACT_SWIGLU ? 2 * f : f;
+  if (misaligned16({X, A_ln, B_i, U_i, Y_i, Z_i})) return TP_E_UNSUPPORTED;
+  const Buf outs[] = {{U_i, M * n1 * 2}, {Y_i, M * f * 2}, {Z_i, M * h * 2}};
+  const Buf ins[] = {{X, M * h * 2}, {ln_mean, M * 4}, {ln_rstd, M * 4}, {A_ln, h * n1 * 2}, {c_ln, n1 * 4},
+                     {b_ln, n1 * 4}, {B_i, f * h * 2}};
+  if (any_alias(outs, 3, ins, 7)) return TP_E_ALIAS;
+  tp::GemmParams g1 = {};
+  g1.A = X; g1.lda = h;
+  g1.B = A_ln; g1.ldb = n1;
+  g1.M = (int)M; g1.N = (int)n1; g1.K = (int)h;
+  g1.C = U_i; g1.ldc = n1;
+  g1.C2 = Y_i; g1.ldc2 = f;
+  g1.fhalf = (int)f;
+  g1.act = (int)act;
+  g1.ln_mean = ln_mean; g1.ln_rstd = ln_rstd; g1.ln_c = c_ln; g1.ln_b = b_ln;
+  tp::GemmParams g2 = {};
+  g2.A = Y_i; g2.lda = f;
+  g2.B = B_i; g2.ldb = h;
+  g2.M = (int)M; g2.N = (int)h; g2.K = (int)f;
+  g2.C = Z_i; g2.ldc = h;
+  hipError_t e = tp::gemm_bf16_ln(g1, act == TP_ACT_SWIGLU ? tp::EPI_LN_SWIGLU : tp::EPI_LN_ACT, stream);
+  if (e == hipSuccess) e = tp::gemm_bf16(g2, true, false, tp::EPI_STORE, stream);
+  return hip_status(e);
 }
 
 namespace {

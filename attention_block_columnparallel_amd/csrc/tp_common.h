@@ -132,8 +132,15 @@ enum Epi {
   EPI_BIAS_ACT = 2,    // C = u = acc + bias[n] (bias nullable); C2 = act(u)
   EPI_SWIGLU_FWD = 3,  // column pair (j, fhalf + j): C = [g | u] (+bias), C2[:, j] = silu(g) * u
   EPI_ACT_BWD = 4,     // C = acc * act'(aux[m][n])
-  EPI_SWIGLU_BWD = 5   // acc = dY[m][j]; aux = [g | u]: C[:, j] = dY*u*silu'(g), C[:, fhalf+j] = dY*silu(g)
+  EPI_SWIGLU_BWD = 5,  // acc = dY[m][j]; aux = [g | u]: C[:, j] = dY*u*silu'(g), C[:, fhalf+j] = dY*silu(g)
+  // LayerNorm folded into the column GEMM: A holds the LayerNorm input u and B the weight with gamma folded in
+  // (diag(gamma) W); acc -> ln_rstd[m] * (acc - ln_mean[m] * ln_c[n]) + ln_b[n] (fp32 vectors), which is
+  // LayerNorm(u) W + bias, then as EPI_BIAS_ACT / EPI_SWIGLU_FWD (p.bias unused).  Large-tile kernel only.
+  EPI_LN_ACT = 6,
+  EPI_LN_SWIGLU = 7
 };
+__host__ __device__ constexpr bool epi_swiglu_fwd(int e) { return e == EPI_SWIGLU_FWD || e == EPI_LN_SWIGLU; }
+__host__ __device__ constexpr bool epi_ln(int e) { return e == EPI_LN_ACT || e == EPI_LN_SWIGLU; }
 
 struct GemmParams {
   const void* A;
@@ -150,6 +157,12 @@ struct GemmParams {
   int64_t ldaux;
   int fhalf;
   int act;
+  // EPI_LN_*: per-row mean and 1/std of the LayerNorm input [M], per-column sum of the folded weight's columns
+  // and folded bias [N] (all fp32)
+  const float* ln_mean;
+  const float* ln_rstd;
+  const float* ln_c;
+  const float* ln_b;
 };
 
 // Launchers (return hipGetLastError after the launch).
@@ -166,6 +179,13 @@ hipError_t gemm_bf16_splitk(const GemmParams& p, bool a_kmajor, bool b_kmajor, i
 hipError_t gemm_bf16_wgrad_pair_splitk(const GemmParams& p0, const GemmParams& p1, float* part, int64_t part_floats,
                                        hipStream_t st);
 hipError_t gemm_f32(const GemmParams& p, bool a_kmajor, bool b_kmajor, int epi, hipStream_t st);
+// The LayerNorm-folded column GEMM (EPI_LN_ACT or EPI_LN_SWIGLU; A K-major, B MN-major) on the large-tile kernel;
+// hipErrorInvalidValue when that kernel does not take the shape (K % 64 != 0 or K < 128).
+hipError_t gemm_bf16_ln(const GemmParams& p, int epi, hipStream_t st);
+// The fold: A_ln[k][j] = bf16(gamma[k] * A[k][j]), c[j] = sum_k A_ln[k][j], b[j] = sum_k beta[k] * A[k][j] + a[j]
+// (a nullable), fp32 sums in a fixed order.  A [h, n] bf16 row-major, n % 2 == 0.
+hipError_t ln_fold_weights(const void* gamma, const void* beta, const void* A, const void* a, int64_t h, int64_t n,
+                           void* A_ln, float* c, float* b, hipStream_t st);
 hipError_t colsum(tp_dtype dt, const void* x, int64_t rows, int64_t cols, void* out, hipStream_t st);
 
 hipError_t reduce_partials(tp_dtype dt, const void* partials, int t, int64_t stride, int64_t in_off, int64_t count,

@@ -16,12 +16,13 @@ MFMA peak.  rs_dim0 = the reduce-scatter kernel (census pass) against HBM bandwi
 launch from the committed rocprofv3 counter summary under profiles/ (null once the kernel source differs from the
 one profiled).  cpu_baseline = the fp64 oracle on a bounded sample.
 
-overlap, attention_block(_gqa), gather_dim0, sp_region, output_layer and the two other MLP workloads = the other
+overlap, attention_block(_gqa), gather_dim0, sp_region, ln_fused, output_layer and the two other MLP workloads = the other
 rows of the hot path, timed after the step (not part of value): the same step with its reductions on a second
 stream beside the GEMMs (serial vs overlapped ms/step); the attention block forward and backward at the 22B-class
 shape and at the Llama-70B-sized grouped-query shape; the dim-0 gather at the Llama-70B-sized SP shape (rotating
 over buffer sets larger than the Infinity Cache); the sequence-parallel region (dropout + residual + LayerNorm,
-forward and backward) on every rank's rows at that same shape; the vocab-parallel output layer (logits GEMM, cross
+forward and backward) on every rank's rows at that same shape; the SP entry with the LayerNorm folded into the
+column GEMM against the LayerNorm output written and read back; the vocab-parallel output layer (logits GEMM, cross
 entropy, backward GEMMs, dX all-reduce) at 16384 token rows, h=4096 and a 51200-entry vocab; the 8.3B-width MLP
 (h=3072, ffn=12288, s=1024, b=8; all-reduce form) and the sequence-parallel SwiGLU MLP (h=8192, ffn=28672,
 s=4096, b=1; all-gather in, reduce-scatter out), each a whole fwd+bwd step with per-kernel rates.
@@ -528,6 +529,111 @@ def sp_region_measure(L, reps: int) -> dict:
     return out
 
 
+def ln_fused_measure(L, reps: int) -> dict:
+    """The sequence-parallel entry of the SP SwiGLU MLP (s=4096, b=1, h=8192, ffn=28672, t=8, bf16, p=0.1) two ways,
+    each for all 8 ranks: (a) every rank's dropout + residual + LayerNorm writes u (the residual stream) and y into
+    its rows of the gathered buffer, then every rank's column GEMM (SwiGLU) and row GEMM read y; (b) every rank's
+    dropout + residual writes u into the gathered buffer and the row statistics only, then every rank's
+    LayerNorm-folded GEMM reads u (tp_ln_mlp_fwd).  The fold of the weights (tp_ln_fold_weights, once per weight
+    update) is timed on its own.  Per-kernel HIP-event durations from a bracketed pass, the two forms' ms from
+    passes without those events, alternated over three rounds (medians)."""
+    import numpy as np
+    import torch
+
+    import tp_inputs as TI
+
+    w = TI.MLP_SP_SWIGLU
+    s, b, h, t, p, eps = w.s, w.b, w.h, w.t, 0.1, 1e-5
+    rows, M = s // t * b, s * b
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    inp = TI.mlp_inputs(w, seed=0)
+    sp = TI.sp_region_inputs(M, h, "bf16", seed=0)
+    dims = L.make_dims(s=s, b=b, h=h, ffn=w.ffn, t=t)
+    A_d, B_d = dev(inp["A"]), dev(inp["B"])
+    del inp
+    z, res, gam, bet = (dev(sp[k]) for k in ("z", "residual", "gamma", "beta"))
+    bits = torch.from_numpy(sp["bits"].view(np.int32)).cuda()
+    del sp
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    A = [torch.empty((h, w.n1), **bf) for _ in range(t)]
+    B = [torch.empty((w.f_l, h), **bf) for _ in range(t)]
+    A_ln = [torch.empty((h, w.n1), **bf) for _ in range(t)]
+    cv = [torch.empty(w.n1, device="cuda") for _ in range(t)]
+    bv = [torch.empty(w.n1, device="cuda") for _ in range(t)]
+    for r in range(t):
+        L.tp_shard_weights(dims, r, "fc1_gate_up", A_d, A[r])
+        L.tp_shard_weights(dims, r, "fc2", B_d, B[r])
+    del A_d, B_d
+    u_res = torch.empty((M, h), **bf)      # (a) the residual stream
+    gath = torch.empty((M, h), **bf)       # (a) gathered y, (b) gathered u
+    mean, rstd = torch.empty(M, device="cuda"), torch.empty(M, device="cuda")
+    U, Y, Z = torch.empty((M, w.n1), **bf), torch.empty((M, w.f_l), **bf), torch.empty((t, M, h), **bf)
+
+    def fold():
+        for r in range(t):
+            L.tp_ln_fold_weights(dims, "swiglu", gam, bet, A[r], None, A_ln[r], cv[r], bv[r])
+
+    def unfused():
+        for r in range(t):
+            sl = slice(r * rows, (r + 1) * rows)
+            L.tp_sp_dropout_add_ln_fwd(rows, h, p, eps, z[sl], res[sl], bits[sl], gam, bet, u_res[sl], gath[sl],
+                                       mean[sl], rstd[sl], None)
+        for r in range(t):
+            L.tp_mlp_fwd(dims, r, "swiglu", gath, A[r], None, B[r], U, Y, Z[r])
+
+    def fused():
+        for r in range(t):
+            sl = slice(r * rows, (r + 1) * rows)
+            L.tp_sp_dropout_add_ln_fwd(rows, h, p, eps, z[sl], res[sl], bits[sl], gam, bet, gath[sl], None,
+                                       mean[sl], rstd[sl], None)
+        for r in range(t):
+            L.tp_ln_mlp_fwd(dims, r, "swiglu", gath, mean, rstd, A_ln[r], cv[r], bv[r], B[r], U, Y, Z[r])
+
+    fold()
+    for fn in (unfused, fused):
+        fn()
+    torch.cuda.synchronize()
+    kern = {}
+    for name, fn in (("fold", fold), ("unfused", unfused), ("fused", fused)):
+        with L.LaunchTimer(capacity=reps * 3 * t + 8) as lt:
+            for _ in range(reps):
+                fn()
+        torch.cuda.synchronize()
+        per = {}
+        for kn, kms in lt.results():
+            per.setdefault(kn, []).append(kms)
+        kern[name] = {kn: {"launches_per_call": len(v) // reps, "avg_us": round(1e3 * float(np.mean(v)), 2)}
+                      for kn, v in per.items()}
+    times = {"unfused": [], "fused": []}
+    for _ in range(3):
+        for name, fn in (("unfused", unfused), ("fused", fused)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times[name].append(e0.elapsed_time(e1) / reps)
+    med = {k: sorted(v)[1] for k, v in times.items()}
+    gf = 2.0 * M * h * (w.n1 + w.f_l) * t
+    col = kern["fused"].get("gemm_bf16_big_KM_ln_swiglu", {}).get("avg_us")
+    out = {"workload": "sp_entry_ln_swiglu_h8192_ffn28672_t8_s4096", "unfused_ms": round(med["unfused"], 4),
+           "fused_ms": round(med["fused"], 4), "speedup": round(med["unfused"] / med["fused"], 4),
+           "gemm_gflop": round(gf / 1e9, 1), "kernels": kern,
+           "bytes_saved_per_layer": M * h * 2 * 2,  # the LayerNorm output's write and (a) the residual copy
+           "fold_us_all_ranks": round(sum(k["avg_us"] * k["launches_per_call"] for k in kern["fold"].values()), 1)}
+    if col:
+        fl = 2.0 * M * h * w.n1
+        out["ln_column_gemm"] = {"avg_us": col, "tflops": round(fl / (col * 1e-6) / 1e12, 1),
+                                 "frac_bf16_peak": round(fl / (col * 1e-6) / PEAK_BF16_FLOPS, 4)}
+    del A, B, A_ln, cv, bv, u_res, gath, U, Y, Z, z, res
+    return out
+
+
 def cpu_cores() -> dict:
     """The host's CPU count, the CPUs this process may run on, and the BLAS threads NumPy uses (the oracle's
     matrix products run on those)."""
@@ -769,6 +875,8 @@ def main(argv=None) -> int:
         out["attention_block_gqa"] = attention_block_measure(L, max(2, args.steps // 2), 2, TI.ATTN_GQA_70B)
         out["gather_dim0"] = gather_measure(L, 24)
         out["sp_region"] = sp_region_measure(L, 10)
+        torch.cuda.empty_cache()
+        out["ln_fused"] = ln_fused_measure(L, 5)
         torch.cuda.empty_cache()
         out["output_layer"] = output_layer_measure(L, 5)
         torch.cuda.empty_cache()

@@ -199,6 +199,9 @@ int tp_gather_dim0(const tp_dims* dims, tp_dtype dtype, const void* slices, void
  *   u    = (residual or 0) + (keep ? z / (1 - p) : 0)   rounded once to dtype; written to out if out != NULL
  *   y    = (u - mean) * rstd * gamma + beta,  mean / biased variance over the row, rstd = 1 / sqrt(var + eps)
  * with the LayerNorm reading the rounded u.  mean, rstd: fp32 [rows] (nullable; the backward needs them).
+ * y may be NULL when out, mean and rstd are given: the call then writes only u and the row statistics, which is
+ * what tp_ln_mlp_fwd (the LayerNorm folded into the column GEMM) reads -- out pointing into rank r's rows of the
+ * gathered [s, b, h] buffer makes that buffer the gathered LayerNorm input.
  * mask (nullable): [rows, h/8] bytes, bit i of byte k = keep of column 8k + i (LSB first); the backward reads it
  * instead of the words.  p == 0 keeps every element (bits may be NULL; scale 1).  y may point into rank r's rows
  * of the gathered [s, b, h] buffer (offset r*(s/t)*b*h): the local part of the all-gather is then this write.
@@ -271,6 +274,30 @@ int tp_vocab_ce_combine(int64_t rows, int t, const float* stats, const int32_t* 
 int tp_vocab_ce_bwd(int64_t rows, int64_t v_local, int rank, tp_dtype dtype, const void* logits_i,
                     const int32_t* targets, const float* lse, const float* dloss, void* dlogits_i,
                     hipStream_t stream);
+
+/* LayerNorm folded into the column GEMM ([MEGA] the TE LayerNormColumnParallelLinear remark: the LayerNorm before
+ * a column-parallel GEMM is fused with it; [ATLAS] §5, SP rows: under sequence parallelism the LayerNorm runs on
+ * each rank's rows and its output is all-gathered into the GEMM).  With y = LayerNorm(u) = (u - mean) rstd gamma
+ * + beta per row, y A_i = rstd (u A' - mean c) + b with A' = diag(gamma) A_i, c = the column sums of A' and
+ * b = beta A_i: the GEMM reads the gathered LayerNorm input u itself and applies the row statistics in its
+ * epilogue, so the LayerNorm output is never written or read.
+ *
+ * tp_ln_fold_weights: A_ln = bf16(gamma[k] A_i[k][j]) [h, N1] (the product of two bf16 values is exact in fp32, so
+ *   this is one rounding), c_ln[j] = sum_k A_ln[k][j] and b_ln[j] = sum_k beta[k] A_i[k][j] + a_i[j] (fp32 [N1],
+ *   fixed summation order).  gamma, beta [h]; A_i [h, N1] and a_i [N1] (nullable) as for tp_mlp_fwd.  Runs once
+ *   per weight (and gamma / beta) update, off the step.
+ * tp_ln_mlp_fwd: tp_mlp_fwd on y = LayerNorm(X) without forming y: U_i = rstd (X A_ln - mean c_ln) + b_ln
+ *   (= y A_i + a_i), Y_i = act(U_i), Z_i = Y_i B_i.  X [s, b, h] is the LayerNorm input (u, gathered under SP);
+ *   ln_mean, ln_rstd fp32 [s*b] its row statistics as tp_sp_dropout_add_ln_fwd writes them.  The backward is
+ *   tp_mlp_bwd with X = y: the weight gradient needs y, which tp_sp_dropout_add_ln_fwd gives again from u (p = 0,
+ *   z = u, no residual), bit for bit the y of the unfolded forward.
+ * Both: bf16 only, h % 64 == 0 and h >= 128 (the large-tile kernel), ffn/t % 8 == 0, pointers 16-byte aligned
+ * (else TP_E_UNSUPPORTED); other rules as tp_mlp_fwd. */
+int tp_ln_fold_weights(const tp_dims* dims, tp_act act, tp_dtype dtype, const void* gamma, const void* beta,
+                       const void* A_i, const void* a_i, void* A_ln, float* c_ln, float* b_ln, hipStream_t stream);
+int tp_ln_mlp_fwd(const tp_dims* dims, int rank, tp_act act, tp_dtype dtype, const void* X, const float* ln_mean,
+                  const float* ln_rstd, const void* A_ln, const float* c_ln, const float* b_ln, const void* B_i,
+                  void* U_i, void* Y_i, void* Z_i, hipStream_t stream);
 
 /* Vocab-parallel output layer ([MEGA] output-logits remark: the output (embedding) weight E [V, h] is split by
  * vocab rows, so each rank's GEMM gives its own logit columns and feeds the cross entropy above directly, with only

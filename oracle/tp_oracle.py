@@ -713,6 +713,28 @@ def layernorm_backward(x: np.ndarray, gamma: np.ndarray, dy: np.ndarray, eps: fl
     return dx, (dy * xh).sum(axis=0), dy.sum(axis=0)
 
 
+def ln_fold(gamma: np.ndarray, beta: np.ndarray, A: np.ndarray, a: Optional[np.ndarray] = None,
+            store: Optional[str] = None):
+    """The LayerNorm folded into the following column GEMM ([MEGA] remark on TE's LayerNormColumnParallelLinear,
+    the LayerNorm fused with the column-parallel linear after it).  With y = (u - mean) rstd gamma + beta per row,
+    y A + a = rstd (u A' - mean c) + b where A' = diag(gamma) A, c = the column sums of A' and b = beta A + a.
+    store="bf16": A' is kept in bf16 (the product of two bf16 values is exact in fp32, so one rounding) and c sums
+    the kept values, so the identity stays exact for the stored A'.  Returns A', c, b."""
+    Af = np.asarray(gamma, dtype=np.float64)[:, None] * np.asarray(A, dtype=np.float64)
+    Af = _keep(Af, store)
+    b = np.asarray(beta, dtype=np.float64) @ np.asarray(A, dtype=np.float64)
+    if a is not None:
+        b = b + np.asarray(a, dtype=np.float64)
+    return Af, Af.sum(axis=0), b
+
+
+def ln_folded_linear(u: np.ndarray, mean: np.ndarray, rstd: np.ndarray, A_fold: np.ndarray, c: np.ndarray,
+                     b: np.ndarray) -> np.ndarray:
+    """rstd (u A' - mean c) + b per row: the column GEMM of the LayerNorm output computed from its input."""
+    u = np.asarray(u, dtype=np.float64)
+    return np.asarray(rstd, dtype=np.float64)[:, None] * (u @ A_fold - np.outer(mean, c)) + b
+
+
 def dropout_keep(bits: np.ndarray, p: float) -> np.ndarray:
     """Keep decision from 32-bit random words: keep iff bits >= floor(p * 2^32), so P(keep) = 1 - p to 2^-32."""
     return np.asarray(bits, dtype=np.uint64) >= np.uint64(math.floor(p * 2.0 ** 32))

@@ -177,8 +177,13 @@ def test_sp_region_validation(L):
         q = ptrs or P[:12]  # u, gamma, mean, rstd, dy, dres_in, mask, dres, dz, dgamma, dbeta, ws
         return L.tp_sp_dropout_add_ln_bwd(rows, h, p, *q, stream=0, dtype=dt, check=False)
 
-    for i in (0, 3, 4, 6):                                   # z, gamma, beta, y are required
+    for i in (0, 3, 4):                                      # z, gamma, beta are required
         assert fwd(ptrs=P[:i] + [None] + P[i + 1:10]) == -1, i
+    # y may be left out only when out, mean and rstd are written (the LayerNorm-folded GEMM's input)
+    assert fwd(ptrs=P[:5] + [None, None] + P[7:10]) == -1
+    assert fwd(ptrs=P[:6] + [None, None] + P[8:10]) == -1
+    assert fwd(ptrs=P[:6] + [None] + P[7:8] + [None] + P[9:10]) == -1
+    assert fwd(ptrs=P[:5] + [P[0], None] + P[7:10]) == -6    # without y, out over z is still caught
     assert fwd(ptrs=P[:2] + [None] + P[3:10]) == -1          # random words required when p > 0
     # ... not when p == 0: then the misaligned y decides (every case here must fail validation: nothing launches)
     assert fwd(p=0.0, ptrs=P[:2] + [None] + P[3:6] + [P[6] + 2] + P[7:10]) == -7
@@ -361,3 +366,30 @@ def test_vocab_logits_validation(L):
     assert bwd(ptrs=[None, P[1], P[2], None, P[4]]) == -1              # dE needs X
     assert bwd(ptrs=[P[0], P[1], P[2], P[2], P[4]]) == -6              # dX over dlogits
     assert bwd(v=12) == -7
+
+
+def test_ln_fold_validation(L):
+    P = [addr(i) for i in range(11)]
+    dims = L.make_dims(s=16, b=2, h=128, ffn=256, t=2)
+
+    def fold(dims=dims, act="gelu", dt=BF16, ptrs=None):
+        q = ptrs or P[:7]  # gamma, beta, A_i, a_i, A_ln, c_ln, b_ln
+        return L.tp_ln_fold_weights(dims, act, *q, stream=0, dtype=dt, check=False)
+
+    def fwd(dims=dims, rank=0, act="gelu", dt=BF16, ptrs=None):
+        q = ptrs or P[:10]  # X, mean, rstd, A_ln, c_ln, b_ln, B_i, U_i, Y_i, Z_i
+        return L.tp_ln_mlp_fwd(dims, rank, act, *q, stream=0, dtype=dt, check=False)
+
+    for i in (0, 1, 2, 4, 5, 6):
+        assert fold(ptrs=P[:i] + [None] + P[i + 1:7]) == -1, i
+    for i in range(10):
+        assert fwd(ptrs=P[:i] + [None] + P[i + 1:10]) == -1, i
+    assert fold(dt=F32) == -7 and fwd(dt=F32) == -7          # bf16 only
+    assert fwd(dims=L.make_dims(s=16, b=2, h=96, ffn=256, t=2)) == -7   # h % 64
+    assert fwd(dims=L.make_dims(s=16, b=2, h=64, ffn=256, t=2)) == -7   # h >= 128
+    assert fwd(dims=L.make_dims(s=16, b=2, h=128, ffn=255, t=2)) == -3  # ffn % t
+    assert fwd(dims=L.make_dims(s=16, b=2, h=128, ffn=250, t=2)) == -7  # ffn/t % 8
+    assert fwd(rank=2) == -5
+    assert fwd(dims=L.make_dims(s=0, b=2, h=128, ffn=256, t=2)) == -2
+    assert fold(ptrs=P[:4] + [P[2]] + P[5:7]) == -6           # A_ln over A_i
+    assert fwd(ptrs=P[:7] + [P[0]] + P[8:10]) == -6           # U_i over X

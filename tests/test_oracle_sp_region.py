@@ -83,3 +83,29 @@ def test_dropout_backward_is_the_linear_map():
 
     assert np.allclose(dz, _fd(loss, z), rtol=1e-6, atol=1e-8)
     assert np.allclose(dres, _fd(loss, res), rtol=1e-6, atol=1e-8)
+
+
+def test_ln_fold_identity_and_its_ingredients():
+    """The folded form rstd (u A' - mean c) + b equals LayerNorm(u) A + a (exact chain); a dropped beta term, a
+    wrong sign on the mean term or gamma left out of A' breaks it (checked by planting each); with A' kept in
+    bf16 the identity holds for the kept A' exactly, and against the unrounded A to within its rounding."""
+    rng = np.random.default_rng(41)
+    rows, h, n = 7, 16, 10
+    u = rng.standard_normal((rows, h)) * 1.5 + 0.7     # a non-zero mean, so the mean term matters
+    g, be = 1 + 0.1 * rng.standard_normal(h), 0.1 * rng.standard_normal(h)
+    A, a = rng.standard_normal((h, n)) * 0.3, rng.standard_normal(n) * 0.02
+    y, mean, rstd = O.layernorm(u, g, be, 1e-5)
+    ref = y @ A + a
+    Af, c, b = O.ln_fold(g, be, A, a)
+    assert np.allclose(O.ln_folded_linear(u, mean, rstd, Af, c, b), ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(c, (g[:, None] * A).sum(axis=0), rtol=1e-14) and np.allclose(b, be @ A + a, rtol=1e-14)
+    # planted mistakes
+    assert not np.allclose(O.ln_folded_linear(u, mean, rstd, Af, c, b - be @ A), ref, atol=1e-6)
+    assert not np.allclose(O.ln_folded_linear(u, -mean, rstd, Af, c, b), ref, atol=1e-6)
+    assert not np.allclose(O.ln_folded_linear(u, mean, rstd, A, A.sum(axis=0), b), ref, atol=1e-6)
+    # bf16-kept A': exact identity for the kept weight, close to the exact chain
+    As, cs, bs = O.ln_fold(g, be, A, a, store="bf16")
+    assert np.array_equal(As, O.stored(g[:, None] * A, "bf16"))
+    assert np.allclose(O.ln_folded_linear(u, mean, rstd, As, cs, bs), ((u - mean[:, None]) * rstd[:, None]) @ As + bs,
+                       rtol=1e-12, atol=1e-12)
+    assert np.max(np.abs(O.ln_folded_linear(u, mean, rstd, As, cs, bs) - ref)) < 2e-2 * np.sqrt(np.mean(ref ** 2))
