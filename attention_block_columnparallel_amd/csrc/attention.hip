@@ -209,17 +209,34 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) 
     ccol[i] = (c * 8 < d) ? c * 8 : 0;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
+  // this lane's source of copy i in key tile 0; a whole tile further on is the same source plus a tile's rows
+  const uint16_t* csrc[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) csrc[i] = kbase + (int64_t)crow[i] * tok_stride + ccol[i];
+  const int64_t tile_elems = (int64_t)KT * tok_stride;
   auto issue_tile = [&](int kt, int st) {
     if (kh != 0) return;
-    const int kv0 = min(kt, nkt - 1) * KT;
+    const int ktc = min(kt, nkt - 1);
+    const int kv0 = ktc * KT;
     const uint32_t sb = lds0 + st * STAGE_B;
+    if (kv0 + KT <= p.s) {  // every row of the tile exists: no per-row clamp
+      const int64_t off = (int64_t)ktc * tile_elems;
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int row = min(kv0 + crow[i], p.s - 1);
-      const uint16_t* src = kbase + (int64_t)row * tok_stride + ccol[i];
-      const uint32_t dst = sb + (qw + 4 * i) * 1024;
-      dma16(src, __builtin_amdgcn_readfirstlane(dst));
-      dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
+      for (int i = 0; i < CPW; ++i) {
+        const uint16_t* src = csrc[i] + off;
+        const uint32_t dst = sb + (qw + 4 * i) * 1024;
+        dma16(src, __builtin_amdgcn_readfirstlane(dst));
+        dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int row = min(kv0 + crow[i], p.s - 1);
+        const uint16_t* src = kbase + (int64_t)row * tok_stride + ccol[i];
+        const uint32_t dst = sb + (qw + 4 * i) * 1024;
+        dma16(src, __builtin_amdgcn_readfirstlane(dst));
+        dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
+      }
     }
   };
   auto chunk_off = [&](int r, int c) { return r * CH * 16 + tile_chunk<CH>(r, c) * 16; };
@@ -292,7 +309,11 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) 
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[i][e]);
     mx = max_over_groups(mx);
     const float m_new = fmaxf(m_run, mx);
-    if (__any(m_new > m_run)) {
+    // lazy rescale: the running maximum moves (and the sums are rescaled) only when some row's maximum rose by more
+    // than 2^8 in the exp2 domain; until then probabilities of up to 2^8 are taken against the kept maximum, which
+    // the sum and the output share, so the result is the same up to rounding (and the first finite maximum always
+    // moves it: -inf to finite is an infinite rise)
+    if (__any((m_new - m_run) * c2 > 8.f)) {
       const float corr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       l_part *= corr;
 #pragma unroll
