@@ -721,6 +721,22 @@ def cpu_baseline(w, inp, target_s: float) -> dict:
     out["reduce_scatter"] = {"value": round(red_bytes / t_red / 1e9, 2), "unit": "GB/s",
                              "sample": f"{n_red} passes over {rows} of {w.M} token rows x {w.t} partials "
                                        f"(fp32 rank-order sums), bytes counted as the bf16 step's"}
+
+    # the 8.3B-width MLP: rank 0's whole shard fwd + bwd (about 0.46 TFLOP of fp64 work)
+    w2 = TI.WORKLOADS["mlp_h3072_ffn12288_t8_b8_s1024"]
+    if w2.name != w.name:
+        inp2 = TI.mlp_inputs(w2)
+        X2 = O.as_f64(inp2["X"], w2.dtype).reshape(w2.M, w2.h)
+        dZ2 = O.as_f64(inp2["dZ"], w2.dtype).reshape(w2.M, w2.h)
+        A2, B2 = O.as_f64(inp2["A"], w2.dtype), O.as_f64(inp2["B"], w2.dtype)
+        t0 = time.perf_counter()
+        O.mlp_shard_forward(X2, A2, B2, w2.t, 0, w2.act)
+        O.mlp_shard_backward(X2, A2, B2, dZ2, w2.t, 0, w2.act)
+        t2 = time.perf_counter() - t0
+        fl2 = 12.0 * w2.M * w2.h * w2.f_l
+        out[w2.name] = {"value": round(fl2 / t2 / 1e12, 4), "unit": "TFLOP/s",
+                        "sample": f"rank 0's whole shard fwd+bwd (fp64 NumPy): {fl2 / 1e9:.1f} algorithmic GFLOP "
+                                  f"in {t2:.2f} s"}
     return out
 
 
