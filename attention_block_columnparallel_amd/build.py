@@ -39,14 +39,16 @@ COMMON_FLAGS = [
 
 
 def source_hash(extra_flags=()) -> str:
-    """sha256 over every file under csrc/, the C header, the source list and the compile flags."""
+    """sha256 over every file under csrc/, the C header, the source list and the compile flags (include paths
+    relative to the repository, so a copy of the tree at another path hashes the same)."""
     h = hashlib.sha256()
     files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if not f.startswith("."))
     for path in files + [os.path.join(INCLUDE, "tpshard.h")]:
         h.update(os.path.basename(path).encode() + b"\0")
         with open(path, "rb") as fh:
             h.update(fh.read())
-    h.update("\0".join(SOURCES + COMMON_FLAGS + list(extra_flags)).encode())
+    flags = [f.replace(ROOT, "<root>") for f in COMMON_FLAGS + list(extra_flags)]
+    h.update("\0".join(SOURCES + flags).encode())
     return h.hexdigest()
 
 

@@ -406,6 +406,13 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
 }
+// The same copy from a wave-uniform base held in scalar registers plus a per-lane 32-bit byte offset: the address
+// arithmetic of a copy stays on the scalar unit.  (A vector instruction next to a matrix instruction runs in the
+// matrix instruction's shadow only two or so at a time; longer runs of them hold the matrix core idle.)
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // wait until at most T k-tiles' copies (2 CPW per wave each) are still in flight
@@ -475,6 +482,174 @@ struct Dma<false, SWIG, CPW> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (5
   // copy q only; koff = k0 * ld (the element offset of the k-tile's first row)
   __device__ __forceinline__ void issue1(int q, const uint16_t* base, uint32_t koff, uint32_t lds_op, int wave) const {
     dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (CPW * wave + q) * 1024));
+  }
+};
+
+// The large-tile kernel's LDS: the A tiles of the 4 stages at byte 16 KB * s, the B tiles at 64 KB + 16 KB * s, so
+// that a fragment's address in any stage is one per-lane register plus an immediate offset below 64 KB.
+constexpr int kLdsB = 65536;
+constexpr int kStageOp = 16384;
+
+// Per-lane source byte offsets of a wave's copies of one operand tile (relative to the k-tile's first element), for
+// the scalar-base copy; the same chunk placement as Dma.
+template <bool KMAJ, bool SWIG, int CPW>
+struct DmaS;
+
+template <bool SWIG, int CPW>
+struct DmaS<true, SWIG, CPW> {  // K-major: copy i holds rows 16 i .. 16 i + 15 (64 bytes each); a k-tile is 64 bytes on
+  uint32_t voff[CPW];
+  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) {
+      const int r = 16 * (CPW * wave + q) + (lane >> 2);
+      const int c = (lane & 3) ^ swz_k(r);
+      const int row = min(tile * 256 + r, rows - 1);
+      voff[q] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
+    }
+  }
+  static __device__ __forceinline__ int64_t kstride(int64_t ld) { return 2 * BK2; }
+};
+
+template <bool SWIG, int CPW>
+struct DmaS<false, SWIG, CPW> {  // MN-major: copy i holds k rows 2 i, 2 i + 1; a k-tile is 32 rows on
+  uint32_t voff[CPW];
+  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) {
+      const int k = 2 * (CPW * wave + q) + (lane >> 5);
+      const int cl = 8 * ((lane & 31) ^ swz_mn(k));
+      int col;
+      if (SWIG) {
+        const int wn = cl / 128, cw = cl % 128;
+        const int half = cw / 64, jj = min(tile * 128 + wn * 64 + (cw % 64), fhalf - 8);
+        col = half * fhalf + jj;
+      } else {
+        col = min(tile * 256 + cl, rows - 8);
+      }
+      voff[q] = (uint32_t)((col + (int64_t)k * ld) * 2);
+    }
+  }
+  static __device__ __forceinline__ int64_t kstride(int64_t ld) { return 2 * BK2 * ld; }
+};
+
+// LDS byte addresses (stage 0) of a wave's fragments of one operand; OPB = 0 for A, kLdsB for B.  K-major: fragment
+// i is one 16-byte read at base + 1024 i.  MN-major: two transposing 8-byte reads at a[i] and a[i] + 2048.
+template <bool KMAJ, int NFR, int OPB>
+struct FragAddr {
+  uint32_t a[KMAJ ? 1 : NFR];
+  __device__ __forceinline__ void init(int rbase, int lane) {
+    if constexpr (KMAJ) {
+      const int r = rbase + (lane & 15);
+      a[0] = OPB + r * 64 + (((lane >> 4) ^ swz_k(r)) << 4);
+    } else {
+      const int g = lane >> 4, kq = lane & 15;
+      const int k1 = 8 * g + (kq >> 2);
+      const int cq = 4 * (kq & 3);
+#pragma unroll
+      for (int i = 0; i < NFR; ++i) {
+        const int col = rbase + i * 16 + cq;
+        const int ch = col >> 3, hf = (col >> 2) & 1;
+        a[i] = OPB + k1 * 512 + ((ch ^ swz_mn(k1)) << 4) + (hf << 3);
+      }
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void read(const char* ldsc, int i, bf16x8_t& f) const {
+    if constexpr (KMAJ) {
+      f = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ldsc + a[0] + (S * kStageOp + i * 1024)));
+    } else {
+      const char* b = ldsc + a[i] + S * kStageOp;
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(b));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(b + 2048));
+      typedef short v8i16_t __attribute__((ext_vector_type(8)));
+      const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+};
+
+// Pair buffers of the 8-wave kernel: an operand's pair of k-tiles is 32 KB (256 rows of 64 k, or 64 k rows of
+// 256), buffer b at 32 KB * b (A) and 64 KB + 32 KB * b (B).  K-major rows are 128 bytes; chunk c of row r sits at
+// c ^ (r & 7).  A 16-byte read is served 8 lanes (128 bytes) at a time, and with 128-byte rows those 8 lanes' rows
+// all start on the same bank, so their 8 chunks must differ (the counter showed 2-way conflicts with a 2-bit
+// permutation).  A copy is 8 rows.
+constexpr int kPairOp = 32768;
+
+template <bool KMAJ, bool SWIG, int CPP>
+struct DmaP;
+
+template <bool SWIG, int CPP>
+struct DmaP<true, SWIG, CPP> {  // K-major: copy i holds rows 8 i .. 8 i + 7, 128 bytes each
+  uint32_t voff[CPP];
+  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < CPP; ++q) {
+      const int r = 8 * (CPP * wave + q) + (lane >> 3);
+      const int c = (lane & 7) ^ (r & 7);  // the logical chunk this slot holds
+      const int row = min(tile * 256 + r, rows - 1);
+      voff[q] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
+    }
+  }
+  static __device__ __forceinline__ int64_t pstride(int64_t ld) { return 4 * BK2; }  // bytes per pair along a row
+};
+
+template <bool SWIG, int CPP>
+struct DmaP<false, SWIG, CPP> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 bytes each)
+  uint32_t voff[CPP];
+  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < CPP; ++q) {
+      const int k = 2 * (CPP * wave + q) + (lane >> 5);
+      const int cl = 8 * ((lane & 31) ^ swz_mn(k));
+      int col;
+      if (SWIG) {
+        const int wn = cl / 128, cw = cl % 128;
+        const int half = cw / 64, jj = min(tile * 128 + wn * 64 + (cw % 64), fhalf - 8);
+        col = half * fhalf + jj;
+      } else {
+        col = min(tile * 256 + cl, rows - 8);
+      }
+      voff[q] = (uint32_t)((col + (int64_t)k * ld) * 2);
+    }
+  }
+  static __device__ __forceinline__ int64_t pstride(int64_t ld) { return 4 * BK2 * ld; }  // 64 k rows
+};
+
+// Fragment addresses in buffer 0 (K-major: one per half of the pair); read<B, H> takes buffer B, half H (k-tile
+// 2m + H of the pair) through immediate offsets.  K-major: fragment i one 16-byte read; MN-major: two transposing
+// 8-byte reads 2048 apart.
+template <bool KMAJ, int NFR, int OPB>
+struct FragP {
+  uint32_t a[KMAJ ? 2 : NFR];
+  __device__ __forceinline__ void init(int rbase, int lane) {
+    if constexpr (KMAJ) {
+      const int r = rbase + (lane & 15);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) a[h] = OPB + r * 128 + (((4 * h + (lane >> 4)) ^ (r & 7)) << 4);
+    } else {
+      const int g = lane >> 4, kq = lane & 15;
+      const int k1 = 8 * g + (kq >> 2);
+      const int cq = 4 * (kq & 3);
+#pragma unroll
+      for (int i = 0; i < NFR; ++i) {
+        const int col = rbase + i * 16 + cq;
+        const int ch = col >> 3, hf = (col >> 2) & 1;
+        a[i] = OPB + k1 * 512 + ((ch ^ swz_mn(k1)) << 4) + (hf << 3);
+      }
+    }
+  }
+  template <int B, int H>
+  __device__ __forceinline__ void read(const char* ldsc, int i, bf16x8_t& f) const {
+    if constexpr (KMAJ) {
+      f = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ldsc + a[H] + (B * kPairOp + i * 2048)));
+    } else {
+      const char* b = ldsc + a[i] + (B * kPairOp + H * 16384);
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(b));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(b + 2048));
+      typedef short v8i16_t __attribute__((ext_vector_type(8)));
+      const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      f = __builtin_bit_cast(bf16x8_t, w);
+    }
   }
 };
 
@@ -715,7 +890,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   __shared__ u32x4_t lds[LDS_U4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   // ---- problem and tile: XCD-aware remap over the whole launch (the hardware deals workgroup i to XCD i % 8;
@@ -746,6 +921,127 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   const int tile_m = first_m + (bid % (gm * nbn)) % gsz;
   const int tile_n = (bid % (gm * nbn)) / gsz;
 
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (NW == 8) {
+  // Pair buffers: k-tiles 2m and 2m+1 (64 k) of each operand sit in buffer m % 2, so a K-major row's 64 k (128
+  // bytes, a whole cache line) comes in one piece; copying one k-tile (64 bytes of each line) reads every line
+  // twice at half the rate of whole lines from L2.  Layout: A buffers at 0 and 32 KB, B buffers at 64 and 96 KB.
+  constexpr int CPP = 32 / NW;  // copies per wave per operand and pair
+  DmaP<AK, false, CPP> da;
+  DmaP<BKM, SWIG, CPP> db;
+  da.init(p.lda, tile_m, p.M, p.fhalf, wave, lane);
+  db.init(p.ldb, tile_n, p.N, p.fhalf, wave, lane);
+  int kp0 = 0, kp1 = p.K / (2 * BK2);  // pairs of k-tiles: all of K, or split `split` of pp.ksplit runs
+  if (SPLIT && split >= 0) {
+    const int np = kp1, base = np / pp.ksplit, rem = np % pp.ksplit;
+    kp0 = split * base + min(split, rem);
+    kp1 = kp0 + base + (split < rem ? 1 : 0);
+  }
+  const int64_t astr = DmaP<AK, false, CPP>::pstride(p.lda), bstr = DmaP<BKM, SWIG, CPP>::pstride(p.ldb);
+  const char* const Ab = static_cast<const char*>(p.A) + kp0 * astr;  // uniform: pair 0 of the range
+  const char* const Bb = static_cast<const char*>(p.B) + kp0 * bstr;
+  const int npair = kp1 - kp0, nk = 2 * npair;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
+  const char* const ldsc = reinterpret_cast<const char*>(&lds[0]);
+  FragP<AK, TM, 0> fra;
+  FragP<BKM, TN, kLdsB> frb;
+  fra.init(wm * WM, lane);
+  frb.init(wn * WN, lane);
+  // copy q of this wave's share of pair pr into buffer BUF (A copies q < CPP, B copies after)
+  auto copy = [&](auto bufc, int q, int pr) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (q < CPP)
+      dma16s(Ab + pr * astr, da.voff[q], lds0 + BUF * kPairOp + (CPP * wave + q) * 1024);
+    else
+      dma16s(Bb + pr * bstr, db.voff[q - CPP], lds0 + kLdsB + BUF * kPairOp + (CPP * wave + q - CPP) * 1024);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // prologue: pairs 0 and 1 into buffers 0 and 1; pair 0 landed (pair 1's copies may be in flight)
+#pragma unroll
+  for (int q = 0; q < 2 * CPP; ++q) copy(I0{}, q, 0);
+  if (npair > 1) {
+#pragma unroll
+    for (int q = 0; q < 2 * CPP; ++q) copy(I1{}, q, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPP) : "memory");
+  } else {
+    wait_vmcnt0();
+  }
+  __syncthreads();
+  bf16x8_t fa[TM], fb[TN], ga[TM], gb[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fra.template read<0, 0>(ldsc, i, fa[i]);
+#pragma unroll
+  for (int i = 0; i < TN; ++i) frb.template read<0, 0>(ldsc, i, fb[i]);
+
+  // Step j (U = j % 4; k-tile j's fragments in FC): read k-tile j+1's fragments into FN, run k-tile j's MFMAs.
+  // An odd step first waits for its own copies of pair (j+1)/2, the pair k-tile j+1 opens (issued two steps
+  // earlier; nothing was issued since), and barriers, which publishes that pair and proves every wave done with
+  // the buffer of pair (j-1)/2 (its last fragments were read in step j-1); then it copies pair (j+3)/2 into that
+  // buffer (past the last pair: the last pair again, into a free buffer or over its own identical bytes, so the
+  // step has no branch).  Even steps neither wait nor barrier: k-tile j+1 is in the pair of k-tile j.
+  // TM segments: segment G holds its share of the copies, its share of the reads and the 8 MFMAs of fragment row
+  // G, the copies and reads slotted between the MFMAs (a wave waits at each MFMA issue, so anything placed there
+  // runs while the matrix core is busy).
+  auto step = [&](auto uc, int j, bf16x8_t(&FCA)[TM], bf16x8_t(&FCB)[TN], bf16x8_t(&FNA)[TM], bf16x8_t(&FNB)[TN]) {
+    constexpr int U = decltype(uc)::value;
+    constexpr bool ODD = U & 1;
+    constexpr int RB = ((U + 1) >> 1) & 1, RH = (U + 1) & 1;  // buffer and half of k-tile j+1
+    constexpr int CB = ((U + 3) >> 1) & 1;                      // buffer of pair (j+3)/2
+    using IC = std::integral_constant<int, CB>;
+    const int pc = min((j + 3) >> 1, npair - 1);
+    if constexpr (ODD) {
+      wait_vmcnt0();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    constexpr int NCP = ODD ? 2 * 2 * CPP : 0;  // copies this step: the pair's A and B shares
+    auto segment = [&](auto segc) {
+      constexpr int G = decltype(segc)::value;
+      if constexpr (NCP > 0) {
+#pragma unroll
+        for (int q = 0; q < NCP / 2; ++q)
+          if (q * TM / (NCP / 2) == G) copy(IC{}, q, pc);
+      }
+#pragma unroll
+      for (int f = 0; f < TM + TN; ++f) {
+        if (frag_seg<TM, TN>(f) == G) {
+          if (frag_is_a<TM>(f)) fra.template read<RB, RH>(ldsc, frag_idx<TM>(f), FNA[frag_idx<TM>(f)]);
+          else frb.template read<RB, RH>(ldsc, frag_idx<TM>(f), FNB[frag_idx<TM>(f)]);
+        }
+      }
+      mfma_rows_t<G, G + 1, TN>(acc, FCA, FCB);
+      constexpr int nds = seg_ds_count<AK, BKM, TM, TN>(G);
+      if constexpr (nds > 0) {
+#pragma unroll
+        for (int r = 0; r < nds; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, TN - nds, 0);
+    };
+    segment(I0{});
+    segment(I1{});
+    segment(I2{});
+    segment(I3{});
+  };
+  for (int j = 0; j < nk; j += 4) {
+    step(I0{}, j, fa, fb, ga, gb);
+    step(I1{}, j + 1, ga, gb, fa, fb);
+    if (j + 2 < nk) {
+      step(I2{}, j + 2, fa, fb, ga, gb);
+      step(I3{}, j + 3, ga, gb, fa, fb);
+    }
+  }
+  wait_vmcnt0();
+  } else {
   Dma<AK, false, CPW> da;
   Dma<BKM, SWIG, CPW> db;
   da.init(p.lda, tile_m, p.M, p.fhalf, wave, lane);
@@ -779,11 +1075,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   frags2<AK, TM>(stage_a(0), wm * WM, lane, fa);
   frags2<BKM, TN>(stage_b(0), wn * WN, lane, fb);
 
-  f32x4_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Segment S of a step: copy S of k-tile j+D (S < 4: A rows, else B), this segment's share of the reads of
   // k-tile j+1's fragments, and the 8 MFMAs of fragment row S of k-tile j, the copy and reads slotted between the
@@ -876,6 +1167,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   }
 #undef TP_GEMM_STEP
   wait_vmcnt0();
+  }
 
   // (a run-time test on purpose: with the LDS epilogue below still compiled in, the kernel keeps the plain kernel's
   // register allocation; as a compile-time branch the compiler spills around the partial-tile stores)
@@ -1033,10 +1325,8 @@ hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st
                                   kEpiNames[EPI];
   static const std::string name2 = std::string("gemm_bf16_big_pair_") + (AK ? "K" : "M") + (BKM ? "K" : "M") + "_" +
                                    kEpiNames[EPI];
-  // 8 waves (two per SIMD) where measured faster: a K-major A with an MN-major B, and the act' epilogues; 4 for the
-  // rest (h = 4096, ffn/t = 2048, per launch: column GEMM + GeLU 251 -> 241 us, row GEMM 240 -> 235, dY + GeLU'
-  // 267 -> 256; with 8 the dX GEMM 236 -> 241 and the weight-gradient pair 405 -> 412)
-  constexpr int NW = ((AK && !BKM) || EPI == EPI_ACT_BWD || EPI == EPI_SWIGLU_BWD) ? 8 : 4;
+  // 8 waves (two per SIMD, the pair-buffer loop) for every layout
+  constexpr int NW = 8;
   return TP_LAUNCH(p1 ? name2.c_str() : name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI, false, NW>),
                    dim3((unsigned)total), dim3(NW * 64), 0, st, pp);
 }
@@ -1148,12 +1438,13 @@ __global__ __launch_bounds__(256) void splitk_tail_sum_kernel(GemmPair pp, int n
 }
 
 // The large-tile kernel needs an even number of 32-deep k-tiles, more than it keeps in flight (K >= 128), and
-// every element offset of its operands below 2^32.
+// every per-lane copy offset below 2^32 bytes: the whole operand for a K-major one, one k-tile's 32 rows for an
+// MN-major one (whose k-tiles advance a 64-bit base).
 bool big_fits(const GemmParams& p, bool a_kmajor, bool b_kmajor) {
   if (p.K % (2 * BK2) != 0 || p.K < 4 * BK2) return false;
-  const int64_t lim = (int64_t)1 << 32;
-  const int64_t a_end = a_kmajor ? (int64_t)(p.M - 1) * p.lda + p.K : (int64_t)(p.K - 1) * p.lda + p.M;
-  const int64_t b_end = b_kmajor ? (int64_t)(p.N - 1) * p.ldb + p.K : (int64_t)(p.K - 1) * p.ldb + p.N;
+  const int64_t lim = (int64_t)1 << 31;  // elements of 2 bytes
+  const int64_t a_end = a_kmajor ? (int64_t)(p.M - 1) * p.lda + p.K : (int64_t)(BK2 - 1) * p.lda + p.M;
+  const int64_t b_end = b_kmajor ? (int64_t)(p.N - 1) * p.ldb + p.K : (int64_t)(BK2 - 1) * p.ldb + p.N;
   return a_end < lim && b_end < lim;
 }
 

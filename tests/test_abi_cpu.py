@@ -343,6 +343,28 @@ def test_built_library_matches_the_sources():
     assert source_hash(("-DSOMETHING_ELSE",)) != source_hash()
 
 
+def test_source_hash_does_not_depend_on_where_the_tree_is(tmp_path):
+    """The same sources at another path (a copy of the tree elsewhere, as on a machine that runs it from a scratch
+    directory) hash the same, so a library built here is not rebuilt there; a changed source still changes it."""
+    import importlib
+    import importlib.util
+    import shutil
+
+    B = importlib.import_module("attention_block_columnparallel_amd.build")  # the module, not the build() it exports
+
+    root2 = tmp_path / "elsewhere"
+    shutil.copytree(B.CSRC, root2 / "attention_block_columnparallel_amd" / "csrc")
+    shutil.copytree(B.INCLUDE, root2 / "include")
+    shutil.copy(B.__file__, root2 / "attention_block_columnparallel_amd" / "build.py")
+    spec = importlib.util.spec_from_file_location("build_copy", root2 / "attention_block_columnparallel_amd" / "build.py")
+    B2 = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(B2)
+    assert B2.ROOT != B.ROOT and B2.source_hash() == B.source_hash()
+    with open(root2 / "include" / "tpshard.h", "a") as f:
+        f.write("\n")
+    assert B2.source_hash() != B.source_hash()
+
+
 def test_vocab_logits_validation(L):
     P = [addr(i) for i in range(6)]
 
