@@ -863,11 +863,15 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
 }
 
 // Row tiles per group of the large-tile kernel's walk over its tiles (each XCD walks its tiles a group of row tiles
-// at a time, column by column): 8 for a two-GEMM (pair) launch and for the act' epilogues, 2 for the plain K-major A
-// x MN-major B store (the row GEMM), 4 otherwise -- measured best for each at h = 4096, ffn/t = 2048.  The split-K
-// tail sum decodes tiles with the same rule.
+// at a time, column by column): 8 for a two-GEMM (pair) launch, the act' epilogues and the activation epilogues of
+// the column GEMM, 2 for the plain K-major A x MN-major B store (the row GEMM), 4 otherwise -- measured best for
+// each at h = 4096, ffn/t = 2048 (column GEMM + GeLU 247 -> 240 us with 8 against 4).  The split-K tail sum decodes
+// tiles with the same rule.
 __host__ __device__ constexpr int big_row_group(bool pair, int epi, bool ak, bool bkm) {
-  return pair ? 8 : (epi == EPI_ACT_BWD || epi == EPI_SWIGLU_BWD) ? 8 : (ak && !bkm && epi == EPI_STORE) ? 2 : 4;
+  return pair ? 8
+              : (epi == EPI_ACT_BWD || epi == EPI_SWIGLU_BWD) ? 8
+              : (ak && !bkm) ? (epi == EPI_STORE ? 2 : epi == EPI_BIAS ? 4 : 8)
+                             : 4;
 }
 
 // Large-tile kernel: one 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (one wave per SIMD, fp32
