@@ -319,44 +319,25 @@ __global__ __launch_bounds__(NWM* NWN * 64) void gemm_bf16_kernel(GemmParams p) 
 }
 
 // ------------------------------------------------------------------------------------------------------------------
-// Large-tile kernel: 256 x 256 output tile, either 4 waves (2 x 2), each wave 128 x 128 = 8 x 8 MFMA subtiles whose
-// 256 fp32 accumulators per lane live in the accumulation registers (one wave per SIMD, 512 registers), or 8 waves
-// (4 x 2) of 64 x 128 = 4 x 8 subtiles, 128 accumulators per lane (two waves per SIMD, 256 registers each), where
-// one wave's waits and epilogue overlap the other's MFMAs at the price of half again as many LDS reads.  Needs
-// K % 64 == 0 (an even number of 32-deep K tiles).  Out-of-range rows of either operand are clamped to the last valid row: they only feed output rows
-// or columns that are never stored, so no load needs a bounds branch.
+// Large-tile kernel: 256 x 256 output tile, 8 waves (4 x 2) of 64 x 128 = 4 x 8 MFMA subtiles, 128 fp32
+// accumulators per lane (two waves per SIMD, 256 registers each), so one wave's waits and epilogue run beside the
+// other's MFMAs.  Needs K % 64 == 0 (whole pairs of 32-deep k-tiles).  Out-of-range rows of either operand are
+// clamped to the last valid row: they only feed output rows or columns that are never stored, so no load needs a
+// bounds branch.
 //
-// Each operand tile is kept in LDS in the orientation it has in HBM, 32 k deep:
-//   * K-major ([rows][k]): 256 rows x 64 bytes; 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 3).  An MFMA
+// Each operand is kept in LDS in the orientation it has in HBM, a pair of k-tiles (64 k) per buffer:
+//   * K-major ([rows][k]): 256 rows x 128 bytes; 16-byte chunk c of row r sits at chunk c ^ (r & 7).  An MFMA
 //     fragment (16 rows x 8 consecutive k per lane) is one 16-byte read.
-//   * MN-major ([k][cols]): 32 k rows x 512 bytes; chunk c of row k sits at chunk c ^ (2 (k & 3)).  A fragment is
+//   * MN-major ([k][cols]): 64 k rows x 512 bytes; chunk c of row k sits at chunk c ^ swz_mn(k).  A fragment is
 //     built by two transposing reads (ds_read_b64_tr_b16): in each 16-lane group, lane k' points at row k0 + k'/4,
 //     columns n0 + 4 (k' % 4) .. +3, and lane i receives column n0 + i of rows k0 .. k0 + 3.
-// Both swizzles make the 16 lanes served together touch distinct bank groups.
+// Both permutations make the lanes served together touch distinct banks.
 //
-// Pipeline per K tile kt (fragment set F holds its fragments): wait for the copies of tile kt+1, barrier; copies of
-// tile kt+3 into the stage tile kt-1 used; fragments of tile kt+1 -> F' interleaved with the MFMAs on F.  Every LDS
-// read is issued one MFMA burst (one k-tile of MFMAs) ahead of its use.
+// Pipeline: step j computes k-tile j from registers while reading k-tile j+1's fragments; odd steps wait for the
+// copies of the pair k-tile j+1 opens, barrier, and copy the pair after it into the buffer just freed.
 // Two GEMMs of the same layout can share one launch (the two weight gradients): workgroups [0, tiles0) take the
 // first, the rest the second.
 // ------------------------------------------------------------------------------------------------------------------
-template <int TM, int TN>
-__device__ __forceinline__ void mfma_block(f32x4_t (&acc)[TM][TN], const bf16x8_t (&af)[TM],
-                                           const bf16x8_t (&bfr)[TN]) {
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-}
-
-template <int T0, int T1, int TN, int TM>
-__device__ __forceinline__ void mfma_rows(f32x4_t (&acc)[TM][TN], const bf16x8_t (&af)[TM], const bf16x8_t (&bfr)[TN]) {
-#pragma unroll
-  for (int i = T0; i < T1; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-}
-
 // Transposed 16x16 blocks: the B fragment goes first, so the accumulator holds (A B)^T block by block.
 template <int T0, int T1, int TN, int TM>
 __device__ __forceinline__ void mfma_rows_t(f32x4_t (&acc)[TM][TN], const bf16x8_t (&af)[TM],
@@ -389,191 +370,34 @@ __device__ __forceinline__ int xcd_remap(int u, int nb) {
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-constexpr int BK2 = 32;
-// Waves of the large-tile kernel: 4 (2 x 2 waves of 128 x 128, one per SIMD) or 8 (4 x 2 waves of 64 x 128, two per
-// SIMD).  An operand tile is 16 copies of 1 KB, so a wave issues CPW = 16 / NW of them per operand and k-tile.
+constexpr int BK2 = 32;  // k-tile depth of the large-tile kernel
 
-__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 3; }   // K-major tiles (4 chunks per row)
 __device__ __forceinline__ int swz_mn(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)); }  // MN-major tiles
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte address m0 + 16 l.  Issued as
-// inline assembly so that the compiler does not wait for these copies at every barrier; the kernel waits for them
-// itself (s_waitcnt vmcnt) before the barrier that publishes a stage.
+// Direct global -> LDS copy of 16 bytes per lane from a wave-uniform base held in scalar registers plus a per-lane
+// 32-bit byte offset: lane l's bytes land at LDS byte address m0 + 16 l, and the address arithmetic stays on the
+// scalar unit.  Issued as inline assembly so that the compiler does not wait for these copies at every barrier; the
+// kernel waits for them itself (s_waitcnt vmcnt) before the barrier that publishes a buffer.  (A vector instruction
+// next to a matrix instruction runs in the matrix instruction's shadow only two or so at a time; longer runs of them
+// hold the matrix core idle.)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
-}
-// The same copy from a wave-uniform base held in scalar registers plus a per-lane 32-bit byte offset: the address
-// arithmetic of a copy stays on the scalar unit.  (A vector instruction next to a matrix instruction runs in the
-// matrix instruction's shadow only two or so at a time; longer runs of them hold the matrix core idle.)
 __device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// wait until at most T k-tiles' copies (2 CPW per wave each) are still in flight
-template <int T, int CPW>
-__device__ __forceinline__ void wait_vmcnt_tiles() {
-  static_assert(T >= 0 && T <= 3, "k-tiles in flight");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(T * 2 * CPW) : "memory");
-}
-
-// One operand tile (256 rows or columns x 32 k) is 16 KB = 16 wave-wide copies of 1 KB; wave w issues copies
-// 4w .. 4w+3.  The source address of each lane is chosen so that the lane's fixed LDS slot receives the chunk the
-// swizzled layout puts there.
-template <bool KMAJ, bool SWIG, int CPW>
-struct Dma;
-
-// Per-lane source positions are 32-bit element offsets from the operand's base (the launcher only takes this
-// kernel when every offset fits).
-template <bool SWIG, int CPW>
-struct Dma<true, SWIG, CPW> {  // K-major: copy i holds rows 16 i .. 16 i + 15 (64 bytes each)
-  uint32_t off[CPW];
-  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      const int r = 16 * (CPW * wave + q) + (lane >> 2);
-      const int c = (lane & 3) ^ swz_k(r);
-      const int row = min(tile * 256 + r, rows - 1);
-      off[q] = (uint32_t)((int64_t)row * ld + c * 8);
-    }
-  }
-  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, int k0, uint32_t lds_op, int wave) const {
-#pragma unroll
-    for (int q = 0; q < CPW; ++q)
-      dma16(base + (off[q] + (uint32_t)k0), __builtin_amdgcn_readfirstlane(lds_op + (CPW * wave + q) * 1024));
-  }
-  // copy q only; koff = k0 (the k offset of the k-tile)
-  __device__ __forceinline__ void issue1(int q, const uint16_t* base, uint32_t koff, uint32_t lds_op, int wave) const {
-    dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (CPW * wave + q) * 1024));
-  }
-};
-
-template <bool SWIG, int CPW>
-struct Dma<false, SWIG, CPW> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 bytes each)
-  uint32_t off[CPW];
-  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      const int k = 2 * (CPW * wave + q) + (lane >> 5);
-      const int cl = 8 * ((lane & 31) ^ swz_mn(k));  // first logical column of the chunk this slot holds
-      int col;
-      if (SWIG) {
-        // per 128-column wave slice: 64 gate columns then the same 64 up columns
-        const int wn = cl / 128, cw = cl % 128;
-        const int half = cw / 64, jj = min(tile * 128 + wn * 64 + (cw % 64), fhalf - 8);
-        col = half * fhalf + jj;
-      } else {
-        col = min(tile * 256 + cl, rows - 8);
-      }
-      off[q] = (uint32_t)(col + (int64_t)k * ld);
-    }
-  }
-  __device__ __forceinline__ void issue(const uint16_t* base, int64_t ld, int k0, uint32_t lds_op, int wave) const {
-    const uint32_t koff = (uint32_t)((int64_t)k0 * ld);
-#pragma unroll
-    for (int q = 0; q < CPW; ++q)
-      dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (CPW * wave + q) * 1024));
-  }
-  // copy q only; koff = k0 * ld (the element offset of the k-tile's first row)
-  __device__ __forceinline__ void issue1(int q, const uint16_t* base, uint32_t koff, uint32_t lds_op, int wave) const {
-    dma16(base + (off[q] + koff), __builtin_amdgcn_readfirstlane(lds_op + (CPW * wave + q) * 1024));
-  }
-};
-
-// The large-tile kernel's LDS: the A tiles of the 4 stages at byte 16 KB * s, the B tiles at 64 KB + 16 KB * s, so
-// that a fragment's address in any stage is one per-lane register plus an immediate offset below 64 KB.
-constexpr int kLdsB = 65536;
-constexpr int kStageOp = 16384;
-
-// Per-lane source byte offsets of a wave's copies of one operand tile (relative to the k-tile's first element), for
-// the scalar-base copy; the same chunk placement as Dma.
-template <bool KMAJ, bool SWIG, int CPW>
-struct DmaS;
-
-template <bool SWIG, int CPW>
-struct DmaS<true, SWIG, CPW> {  // K-major: copy i holds rows 16 i .. 16 i + 15 (64 bytes each); a k-tile is 64 bytes on
-  uint32_t voff[CPW];
-  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      const int r = 16 * (CPW * wave + q) + (lane >> 2);
-      const int c = (lane & 3) ^ swz_k(r);
-      const int row = min(tile * 256 + r, rows - 1);
-      voff[q] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
-    }
-  }
-  static __device__ __forceinline__ int64_t kstride(int64_t ld) { return 2 * BK2; }
-};
-
-template <bool SWIG, int CPW>
-struct DmaS<false, SWIG, CPW> {  // MN-major: copy i holds k rows 2 i, 2 i + 1; a k-tile is 32 rows on
-  uint32_t voff[CPW];
-  __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
-#pragma unroll
-    for (int q = 0; q < CPW; ++q) {
-      const int k = 2 * (CPW * wave + q) + (lane >> 5);
-      const int cl = 8 * ((lane & 31) ^ swz_mn(k));
-      int col;
-      if (SWIG) {
-        const int wn = cl / 128, cw = cl % 128;
-        const int half = cw / 64, jj = min(tile * 128 + wn * 64 + (cw % 64), fhalf - 8);
-        col = half * fhalf + jj;
-      } else {
-        col = min(tile * 256 + cl, rows - 8);
-      }
-      voff[q] = (uint32_t)((col + (int64_t)k * ld) * 2);
-    }
-  }
-  static __device__ __forceinline__ int64_t kstride(int64_t ld) { return 2 * BK2 * ld; }
-};
-
-// LDS byte addresses (stage 0) of a wave's fragments of one operand; OPB = 0 for A, kLdsB for B.  K-major: fragment
-// i is one 16-byte read at base + 1024 i.  MN-major: two transposing 8-byte reads at a[i] and a[i] + 2048.
-template <bool KMAJ, int NFR, int OPB>
-struct FragAddr {
-  uint32_t a[KMAJ ? 1 : NFR];
-  __device__ __forceinline__ void init(int rbase, int lane) {
-    if constexpr (KMAJ) {
-      const int r = rbase + (lane & 15);
-      a[0] = OPB + r * 64 + (((lane >> 4) ^ swz_k(r)) << 4);
-    } else {
-      const int g = lane >> 4, kq = lane & 15;
-      const int k1 = 8 * g + (kq >> 2);
-      const int cq = 4 * (kq & 3);
-#pragma unroll
-      for (int i = 0; i < NFR; ++i) {
-        const int col = rbase + i * 16 + cq;
-        const int ch = col >> 3, hf = (col >> 2) & 1;
-        a[i] = OPB + k1 * 512 + ((ch ^ swz_mn(k1)) << 4) + (hf << 3);
-      }
-    }
-  }
-  template <int S>
-  __device__ __forceinline__ void read(const char* ldsc, int i, bf16x8_t& f) const {
-    if constexpr (KMAJ) {
-      f = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(ldsc + a[0] + (S * kStageOp + i * 1024)));
-    } else {
-      const char* b = ldsc + a[i] + S * kStageOp;
-      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(b));
-      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(b + 2048));
-      typedef short v8i16_t __attribute__((ext_vector_type(8)));
-      const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      f = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
-};
 
 // Pair buffers of the 8-wave kernel: an operand's pair of k-tiles is 32 KB (256 rows of 64 k, or 64 k rows of
 // 256), buffer b at 32 KB * b (A) and 64 KB + 32 KB * b (B).  K-major rows are 128 bytes; chunk c of row r sits at
 // c ^ (r & 7).  A 16-byte read is served 8 lanes (128 bytes) at a time, and with 128-byte rows those 8 lanes' rows
 // all start on the same bank, so their 8 chunks must differ (the counter showed 2-way conflicts with a 2-bit
 // permutation).  A copy is 8 rows.
-constexpr int kPairOp = 32768;
+constexpr int kPairOp = 32768;  // bytes of one operand's pair buffer
+constexpr int kLdsB = 65536;    // the B buffers start 64 KB in
 
 template <bool KMAJ, bool SWIG, int CPP>
 struct DmaP;
@@ -652,57 +476,6 @@ struct FragP {
     }
   }
 };
-
-// Fragments of one operand for a wave's 128 rows (8 subtiles of 16) over the tile's 32 k.
-template <bool KMAJ, int NFR>
-__device__ __forceinline__ void frags2(const u32x4_t* lds, int rbase, int lane, bf16x8_t (&f)[NFR]) {
-  if constexpr (KMAJ) {
-#pragma unroll
-    for (int i = 0; i < NFR; ++i) {
-      const int r = rbase + i * 16 + (lane & 15);
-      f[i] = __builtin_bit_cast(bf16x8_t, lds[r * 4 + ((lane >> 4) ^ swz_k(r))]);
-    }
-  } else {
-    const int g = lane >> 4, kq = lane & 15;
-    const int k1 = 8 * g + (kq >> 2), k2 = k1 + 4;
-    const int cq = 4 * (kq & 3);  // column offset of this lane's 4-element piece
-    const char* base = reinterpret_cast<const char*>(lds);
-#pragma unroll
-    for (int i = 0; i < NFR; ++i) {
-      const int col = rbase + i * 16 + cq;
-      const int ch = col >> 3, hf = (col >> 2) & 1;
-      const int o1 = k1 * 512 + ((ch ^ swz_mn(k1)) << 4) + (hf << 3);
-      const int o2 = k2 * 512 + ((ch ^ swz_mn(k2)) << 4) + (hf << 3);
-      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o1));
-      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o2));
-      typedef short v8i16_t __attribute__((ext_vector_type(8)));
-      const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      f[i] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
-}
-
-// One fragment (subtile i) of the same.
-template <bool KMAJ>
-__device__ __forceinline__ void frag1(const u32x4_t* lds, int rbase, int lane, int i, bf16x8_t& f) {
-  if constexpr (KMAJ) {
-    const int r = rbase + i * 16 + (lane & 15);
-    f = __builtin_bit_cast(bf16x8_t, lds[r * 4 + ((lane >> 4) ^ swz_k(r))]);
-  } else {
-    const int g = lane >> 4, kq = lane & 15;
-    const int k1 = 8 * g + (kq >> 2), k2 = k1 + 4;
-    const int col = rbase + i * 16 + 4 * (kq & 3);
-    const int ch = col >> 3, hf = (col >> 2) & 1;
-    const char* base = reinterpret_cast<const char*>(lds);
-    const int o1 = k1 * 512 + ((ch ^ swz_mn(k1)) << 4) + (hf << 3);
-    const int o2 = k2 * 512 + ((ch ^ swz_mn(k2)) << 4) + (hf << 3);
-    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o1));
-    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(base + o2));
-    typedef short v8i16_t __attribute__((ext_vector_type(8)));
-    const v8i16_t w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    f = __builtin_bit_cast(bf16x8_t, w);
-  }
-}
 
 // Fragment reads of one k-tile, spread over the first 3/4 of a step's TM MFMA segments: fragments are taken in
 // the order A0 B0 A1 B1 ... (then the B fragments past TM) and fragment f goes to segment f (3 TM / 4) / (TM + TN).
@@ -874,23 +647,20 @@ __host__ __device__ constexpr int big_row_group(bool pair, int epi, bool ak, boo
                              : 4;
 }
 
-// Large-tile kernel: one 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (one wave per SIMD, fp32
-// accumulators in AGPRs), K in steps of 32 through a ring of 4 LDS stages fed by direct global -> LDS copies that
-// run 3 k-tiles ahead of the MFMAs.  The MFMAs take the B fragment first, so each 16 x 16 accumulator block is the
-// transposed product: lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3 of the wave's sub-tile,
+// Large-tile kernel: one 256 x 256 output tile per workgroup, 8 waves of 64 x 128 (two per SIMD), K in pairs of
+// 32-deep k-tiles through two LDS pair buffers fed by direct global -> LDS copies two steps ahead of their use.  The
+// MFMAs take the B fragment first, so each 16 x 16 accumulator block is the transposed product: lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3 of the wave's sub-tile,
 // which the epilogue stages through LDS with one 16-byte write per block.
-template <bool AK, bool BKM, int EPI, bool SPLIT = false, int NW = 4>
+template <bool AK, bool BKM, int EPI, bool SPLIT = false, int NW = 8>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) {
-  constexpr int CPW = 16 / NW;
+  static_assert(NW == 8, "the pair-buffer loop is written for 8 waves of 64 x 128");
   constexpr int BM = 256, BN = 256, WM = 512 / NW, WN = 128, TM = WM / 16, TN = 8;
-  constexpr int NSTAGE = 4;  // (a fifth 32 KB stage, filling the 160 KB LDS, measured slower)
-  constexpr int D = NSTAGE - 1;                 // k-tiles in flight ahead of the one being multiplied
-  constexpr int STAGE_B = (BM + BN) * BK2 * 2;  // bytes per stage (A tile then B tile)
+  constexpr int RING_B = 2 * 2 * kPairOp;  // two pair buffers of A and B
   constexpr bool SWIG = epi_swiglu_fwd(EPI);
   constexpr int EP = 132;  // epilogue fp32 row pitch: 16-byte writes of 16 consecutive rows hit distinct banks
   constexpr int NAUX = EPI == EPI_SWIGLU_BWD ? 8 : EPI == EPI_ACT_BWD ? 4 : 0;  // 16-byte aux loads per lane
   constexpr int EPW = 16 * EP * 4 + NAUX * 1024;                                  // epilogue bytes per wave
-  constexpr int LDS_U4 = (NSTAGE * STAGE_B > NW * EPW ? NSTAGE * STAGE_B : NW * EPW) / 16;
+  constexpr int LDS_U4 = (RING_B > NW * EPW ? RING_B : NW * EPW) / 16;
   __shared__ u32x4_t lds[LDS_U4];
 
   const int tid = threadIdx.x;
@@ -930,7 +700,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if constexpr (NW == 8) {
   // Pair buffers: k-tiles 2m and 2m+1 (64 k) of each operand sit in buffer m % 2, so a K-major row's 64 k (128
   // bytes, a whole cache line) comes in one piece; copying one k-tile (64 bytes of each line) reads every line
   // twice at half the rate of whole lines from L2.  Layout: A buffers at 0 and 32 KB, B buffers at 64 and 96 KB.
@@ -1045,133 +814,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
     }
   }
   wait_vmcnt0();
-  } else {
-  Dma<AK, false, CPW> da;
-  Dma<BKM, SWIG, CPW> db;
-  da.init(p.lda, tile_m, p.M, p.fhalf, wave, lane);
-  db.init(p.ldb, tile_n, p.N, p.fhalf, wave, lane);
-  const int64_t lda = p.lda, ldb = p.ldb;  // held in registers: no argument loads inside the K loop
-  // K range: all of K, or split `split` of pp.ksplit near-equal runs of 64-deep pairs of k-tiles
-  int kp0 = 0, kp1 = p.K / (2 * BK2);
-  if (SPLIT && split >= 0) {
-    const int np = kp1, base = np / pp.ksplit, rem = np % pp.ksplit;
-    kp0 = split * base + min(split, rem);
-    kp1 = kp0 + base + (split < rem ? 1 : 0);
-  }
-  const int64_t k0 = (int64_t)kp0 * 2 * BK2;
-  const uint16_t* const Ab = static_cast<const uint16_t*>(p.A) + (AK ? k0 : k0 * lda);
-  const uint16_t* const Bb = static_cast<const uint16_t*>(p.B) + (BKM ? k0 : k0 * ldb);
-  const int nk = (kp1 - kp0) * 2;  // even, > D
-
-  const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
-  auto stage_a = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B); };
-  auto stage_b = [&](int st) { return reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(&lds[0]) + st * STAGE_B + BM * BK2 * 2); };
-
-  // prologue: k-tiles 0 .. D-1 into stages 0 .. D-1
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    da.issue(Ab, lda, d * BK2, lds0 + d * STAGE_B, wave);
-    db.issue(Bb, ldb, d * BK2, lds0 + d * STAGE_B + BM * BK2 * 2, wave);
-  }
-  wait_vmcnt_tiles<D - 1, CPW>();  // k-tile 0 has landed (D - 1 k-tiles may still be in flight)
-  __syncthreads();
-  bf16x8_t fa[TM], fb[TN], ga[TM], gb[TN];
-  frags2<AK, TM>(stage_a(0), wm * WM, lane, fa);
-  frags2<BKM, TN>(stage_b(0), wn * WN, lane, fb);
-
-
-  // Segment S of a step: copy S of k-tile j+D (S < 4: A rows, else B), this segment's share of the reads of
-  // k-tile j+1's fragments, and the 8 MFMAs of fragment row S of k-tile j, the copy and reads slotted between the
-  // MFMAs (a wave waits at each MFMA issue, so anything else placed there runs while the matrix core is busy).
-  auto segment = [&](auto sc, bf16x8_t(&FCA)[TM], bf16x8_t(&FCB)[TN], bf16x8_t(&FNA)[TM], bf16x8_t(&FNB)[TN],
-                     const u32x4_t* na, const u32x4_t* nb, uint32_t sb, uint32_t ka, uint32_t kb) {
-    constexpr int S = decltype(sc)::value;
-    constexpr int NCP = 2 * CPW;  // copies per wave per k-tile, one per segment
-#pragma unroll
-    for (int q = 0; q < NCP; ++q) {
-      if (q * TM / NCP == S) {
-        if (q < CPW) da.issue1(q, Ab, ka, sb, wave);
-        else db.issue1(q - CPW, Bb, kb, sb + BM * BK2 * 2, wave);
-      }
-    }
-#pragma unroll
-    for (int f = 0; f < TM + TN; ++f) {
-      if (frag_seg<TM, TN>(f) == S) {
-        if (frag_is_a<TM>(f)) frag1<AK>(na, wm * WM, lane, frag_idx<TM>(f), FNA[frag_idx<TM>(f)]);
-        else frag1<BKM>(nb, wn * WN, lane, frag_idx<TM>(f), FNB[frag_idx<TM>(f)]);
-      }
-    }
-    mfma_rows_t<S, S + 1, TN>(acc, FCA, FCB);
-    constexpr int nds = seg_ds_count<AK, BKM, TM, TN>(S);
-    if constexpr (nds > 0) {
-#pragma unroll
-      for (int r = 0; r < nds; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, TN - nds, 0);
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  using I4 = std::integral_constant<int, 4>;
-  using I5 = std::integral_constant<int, 5>;
-  using I6 = std::integral_constant<int, 6>;
-  using I7 = std::integral_constant<int, 7>;
-
-  // Step j (fragments of k-tile j in FC): wait until this wave's copies of k-tile j+1 have landed (k-tiles j+1
-  // and j+2 were in flight, so at most 8 copies may remain) and barrier, which publishes k-tile j+1 and proves that
-  // every wave is done with the stage k-tile j-1 used; then the 8 segments, which copy k-tile j+D into that stage
-  // (past the last k-tile: a harmless re-copy of it, so every step issues the same 8 copies).
-#define TP_GEMM_STEP(J, FCA, FCB, FNA, FNB)                                                      \
-  {                                                                                              \
-    const int j_ = (J);                                                                          \
-    wait_vmcnt_tiles<D - 2, CPW>();                                                                   \
-    __syncthreads();                                                                             \
-    __builtin_amdgcn_sched_barrier(0);                                                           \
-    const int kt_ = min(j_ + D, nk - 1);                                                         \
-    const uint32_t sb_ = lds0 + ((j_ + D) & (NSTAGE - 1)) * STAGE_B;                                   \
-    const uint32_t ka_ = AK ? (uint32_t)(kt_ * BK2) : (uint32_t)((int64_t)kt_ * BK2 * lda);      \
-    const uint32_t kb_ = BKM ? (uint32_t)(kt_ * BK2) : (uint32_t)((int64_t)kt_ * BK2 * ldb);     \
-    const u32x4_t* na_ = stage_a((j_ + 1) & (NSTAGE - 1));                                             \
-    const u32x4_t* nb_ = stage_b((j_ + 1) & (NSTAGE - 1));                                             \
-    __builtin_amdgcn_sched_barrier(0);                                                           \
-    if constexpr (!AK && !BKM) {                                                                 \
-      /* both operands MN-major (the weight-gradient pair): measured faster with the eight */    \
-      /* copies first and the 32 transposing reads one per MFMA over the first half */           \
-      da.issue(Ab, lda, kt_ * BK2, sb_, wave);                                                   \
-      db.issue(Bb, ldb, kt_ * BK2, sb_ + BM * BK2 * 2, wave);                                    \
-      frags2<AK, TM>(na_, wm * WM, lane, FNA);                                                   \
-      frags2<BKM, TN>(nb_, wn * WN, lane, FNB);                                                  \
-      mfma_rows_t<0, TM, TN>(acc, FCA, FCB);                                                     \
-      _Pragma("unroll") for (int s_ = 0; s_ < 2 * (TM + TN); ++s_) {                             \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                       \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                       \
-      }                                                                                          \
-      __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - 2 * (TM + TN), 0);                   \
-      __builtin_amdgcn_sched_barrier(0);                                                         \
-    } else {                                                                                     \
-    segment(I0{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
-    segment(I1{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
-    segment(I2{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
-    segment(I3{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                  \
-    if constexpr (TM == 8) {                                                                     \
-      segment(I4{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                \
-      segment(I5{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                \
-      segment(I6{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                \
-      segment(I7{}, FCA, FCB, FNA, FNB, na_, nb_, sb_, ka_, kb_);                                \
-    }                                                                                            \
-    }                                                                                            \
-  }
-  for (int kt = 0; kt < nk; kt += 2) {
-    TP_GEMM_STEP(kt, fa, fb, ga, gb)
-    TP_GEMM_STEP(kt + 1, ga, gb, fa, fb)
-  }
-#undef TP_GEMM_STEP
-  wait_vmcnt0();
-  }
 
   // (a run-time test on purpose: with the LDS epilogue below still compiled in, the kernel keeps the plain kernel's
   // register allocation; as a compile-time branch the compiler spills around the partial-tile stores)
@@ -1397,8 +1039,8 @@ hipError_t launch_big_split(const GemmParams& p, int ksplit, float* part, hipStr
   pp.nfull = 0;
   pp.part = part;
   static const std::string name = std::string("gemm_bf16_big_splitk_") + (AK ? "K" : "M") + (BKM ? "K" : "M");
-  hipError_t e = TP_LAUNCH(name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI_STORE, true>),
-                           dim3((unsigned)(pp.tiles0 * ksplit)), dim3(256), 0, st, pp);
+  hipError_t e = TP_LAUNCH(name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI_STORE, true, 8>),
+                           dim3((unsigned)(pp.tiles0 * ksplit)), dim3(512), 0, st, pp);
   if (e != hipSuccess) return e;
   const int64_t nq = (int64_t)p.M * (p.N / 4);
   return TP_LAUNCH("gemm_bf16_splitk_sum", splitk_sum_kernel<EPI>, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0,
@@ -1596,8 +1238,8 @@ hipError_t gemm_bf16_wgrad_pair_splitk(const GemmParams& p0, const GemmParams& p
         pp.ksplit = ks;
         pp.nfull = t - ntail;
         pp.part = part;
-        hipError_t e = TP_LAUNCH("gemm_bf16_big_pair_splitk_MM", (gemm_bf16_big_kernel<false, false, EPI_STORE, true>),
-                                 dim3((unsigned)(pp.nfull + ntail * ks)), dim3(256), 0, st, pp);
+        hipError_t e = TP_LAUNCH("gemm_bf16_big_pair_splitk_MM", (gemm_bf16_big_kernel<false, false, EPI_STORE, true, 8>),
+                                 dim3((unsigned)(pp.nfull + ntail * ks)), dim3(512), 0, st, pp);
         if (e != hipSuccess) return e;
         const int64_t nq = (int64_t)ntail * 16384;
         return TP_LAUNCH("gemm_bf16_splitk_tail_sum", splitk_tail_sum_kernel, dim3((unsigned)((nq + 255) / 256)),
