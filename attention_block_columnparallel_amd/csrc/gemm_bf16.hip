@@ -649,8 +649,10 @@ __host__ __device__ constexpr int big_row_group(bool pair, int epi, bool ak, boo
 
 // Large-tile kernel: one 256 x 256 output tile per workgroup, 8 waves of 64 x 128 (two per SIMD), K in pairs of
 // 32-deep k-tiles through two LDS pair buffers fed by direct global -> LDS copies two steps ahead of their use.  The
-// MFMAs take the B fragment first, so each 16 x 16 accumulator block is the transposed product: lane l holds row 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3 of the wave's sub-tile,
-// which the epilogue stages through LDS with one 16-byte write per block.
+// MFMAs take the B fragment first, so each 16 x 16 accumulator block is the transposed product: lane l holds row
+// 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3 of the wave's sub-tile, which the epilogue stages through LDS
+// with one 16-byte write per block.  (A persistent launch, one workgroup per CU walking its tiles so that a tile's
+// stores drain under the next tile's first copies, measured no faster than one workgroup per tile.)
 template <bool AK, bool BKM, int EPI, bool SPLIT = false, int NW = 8>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   static_assert(NW == 8, "the pair-buffer loop is written for 8 waves of 64 x 128");
