@@ -80,15 +80,28 @@ __device__ __forceinline__ QkvCols qkv_cols(int hl, int G, int d, int jj) {
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
 }
+// The same from a wave-uniform base (scalar registers) plus a 32-bit per-lane byte offset: no per-lane address
+// arithmetic when the base moves.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+// max(a, b) of two finite-or-infinite values, one instruction: fmaxf on values fresh from a lane swap costs two
+// more, which quiet signalling NaNs that cannot occur here.
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 #pragma clang diagnostic pop
 // Max / sum over the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48) with the gfx950 lane swaps: with
 // both operands equal, permlane32_swap returns {v[l], v[l^32]} in some order in its two results, permlane16_swap
 // {v[l], v[l^16]}.  Every lane of a column ends with the same value.
 __device__ __forceinline__ float max_over_groups(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_over_groups(float v) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -154,8 +167,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // SIMD hold four waves over the same K / V tiles instead of two.  Only the kh = 0 waves issue the copies (their
 // waits count them); a key half that is entirely masked (the diagonal block's upper half for the tile's first 32
 // queries, every block when s <= 32) keeps m = -inf, and its probabilities are taken as 0, not exp2(-inf + inf).
+//
+// Two workgroups share a CU (LDS), so four waves share a SIMD; the kernel asks the compiler for that register budget
+// (128), which the d = 128 instance otherwise overran (136 registers, one workgroup per CU; grouped-query shape,
+// per rank: 77 -> 63 us).  Measured slower at d = 96: computing the next block's scores ahead of this block's softmax
+// (52 against 50 us), and splitting the key range of the heaviest causal tiles over two workgroups merged by a
+// second kernel (49 us + 12 us of merge against 53 us).
 template <int DP>
-__global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void attn_fwd_bf16_ks_kernel(AttnParams p) {
   constexpr int CH = DP / 8;
   constexpr int TILE_B = KT * CH * 16;
   constexpr int STAGE_B = 2 * TILE_B;
@@ -169,7 +188,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) 
   __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_B];
   constexpr int D = NS - 1;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4;
+  const int l16 = lane & 15;
   const int qw = wave & 3, kh = wave >> 2;
   const int nq = (p.s + QT - 1) / QT;
   const int nbh = p.b * p.hl;
@@ -209,24 +229,25 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) 
     ccol[i] = (c * 8 < d) ? c * 8 : 0;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
-  // this lane's source of copy i in key tile 0; a whole tile further on is the same source plus a tile's rows
-  const uint16_t* csrc[CPW];
+  // this lane's byte offset of copy i within a key tile (the keys; the values at 2 d bytes further), from the
+  // tile's first key row; whole tiles move only the wave-uniform base
+  uint32_t coff[CPW];
 #pragma unroll
-  for (int i = 0; i < CPW; ++i) csrc[i] = kbase + (int64_t)crow[i] * tok_stride + ccol[i];
+  for (int i = 0; i < CPW; ++i) coff[i] = (uint32_t)(((int64_t)crow[i] * tok_stride + ccol[i]) * 2);
+  const bool off32 = (int64_t)KT * tok_stride * 2 < (int64_t)1 << 32;
   const int64_t tile_elems = (int64_t)KT * tok_stride;
   auto issue_tile = [&](int kt, int st) {
     if (kh != 0) return;
     const int ktc = min(kt, nkt - 1);
     const int kv0 = ktc * KT;
     const uint32_t sb = lds0 + st * STAGE_B;
-    if (kv0 + KT <= p.s) {  // every row of the tile exists: no per-row clamp
-      const int64_t off = (int64_t)ktc * tile_elems;
+    if (kv0 + KT <= p.s && off32) {  // every row of the tile exists: no per-row clamp
+      const uint16_t* tb = kbase + (int64_t)ktc * tile_elems;
 #pragma unroll
       for (int i = 0; i < CPW; ++i) {
-        const uint16_t* src = csrc[i] + off;
         const uint32_t dst = sb + (qw + 4 * i) * 1024;
-        dma16(src, __builtin_amdgcn_readfirstlane(dst));
-        dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
+        dma16s(tb, coff[i], dst);
+        dma16s(tb + d, coff[i], dst + TILE_B);
       }
     } else {
 #pragma unroll
@@ -256,7 +277,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) 
     }
 
   const float c2 = p.scale * 1.4426950408889634f;
-  float m_run = -INFINITY, l_part = 0.f;
+  const float thr = 8.f / c2;  // a rise of 2^8 in the exp2 domain, in score units
+  // m_thr = m_run + thr and nm = -m_run c2 (0 while m_run = -inf) change only with m_run
+  float m_run = -INFINITY, l_part = 0.f, m_thr = -INFINITY, nm = 0.f;
   f32x4_t acc_o[NST];
 #pragma unroll
   for (int st = 0; st < NST; ++st) acc_o[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -287,6 +310,8 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) 
 #pragma unroll
       for (int u = 0; u < NDS; ++u) sc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[i][u], qf[u], sc[i], 0, 0, 0);
     }
+    // the V fragments are read only once the K fragments are dead (their latency hides under the softmax)
+    if constexpr (DP >= 128) __builtin_amdgcn_sched_barrier(0);
     bf16x8_t vfr[NST];
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
@@ -308,19 +333,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) 
 #pragma unroll
       for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sc[i][e]);
     mx = max_over_groups(mx);
-    const float m_new = fmaxf(m_run, mx);
+    const float m_new = max2(m_run, mx);
     // lazy rescale: the running maximum moves (and the sums are rescaled) only when some row's maximum rose by more
     // than 2^8 in the exp2 domain; until then probabilities of up to 2^8 are taken against the kept maximum, which
     // the sum and the output share, so the result is the same up to rounding (and the first finite maximum always
     // moves it: -inf to finite is an infinite rise)
-    if (__any((m_new - m_run) * c2 > 8.f)) {
+    if (__any(m_new > m_thr)) {
       const float corr = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
       l_part *= corr;
 #pragma unroll
       for (int st = 0; st < NST; ++st) acc_o[st] *= corr;
       m_run = m_new;
+      m_thr = m_run + thr;
+      nm = m_run == -INFINITY ? 0.f : -m_run * c2;  // a fully masked half: every p is exp2(-inf) = 0
     }
-    const float nm = m_run == -INFINITY ? 0.f : -m_run * c2;  // a fully masked half: every p is exp2(-inf) = 0
     float psum = 0.f;
     uint32_t pk[2][2];
 #pragma unroll
@@ -338,6 +364,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16_ks_kernel(AttnParams p) 
     const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]));
 #pragma unroll
     for (int st = 0; st < NST; ++st) acc_o[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vfr[st], pf, acc_o[st], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);  // the wait and the barrier after the products are issued
     wait_vmcnt<(D - 1) * NC>();
     __syncthreads();
   };

@@ -66,6 +66,26 @@ def test_attention_small_ragged(L, dtype, d, causal):
         assert np.max(np.abs(lse - ref["lse"])) < (1e-4 if dtype == "f32" else 2e-2)
 
 
+
+@pytest.mark.parametrize("d", [40, 96, 128])
+def test_attention_causal_long_ragged(L, d):
+    # s = 1100: 18 query tiles of up to 18 key blocks each, the last tile ragged (12 queries, a 12-key last block)
+    a, t, s = 4, 2, 1100
+    w = TI.Workload("attn_long", "attn", s=s, b=2, h=a * d, a=a, d=d, t=t, causal=True, dtype="bf16")
+    say(f"attention s={s} b=2 a=4 d={d} t=2 causal bf16")
+    inp = TI.attn_inputs(w, with_bias=True, seed=200 + d)
+    X = O.as_f64(inp["X"], "bf16").reshape(w.M, w.h)
+    Wqkv, Wo, bq = O.as_f64(inp["Wqkv"], "bf16"), O.as_f64(inp["Wo"], "bf16"), O.as_f64(inp["bqkv"], "bf16")
+    r = 1
+    got = run_rank(L, w, inp, r, "bf16", True, True)
+    ref = O.attention_shard_forward(X, Wqkv, Wo, w.s, w.b, a, d, t, r, True, bq)
+    rst = O.attention_shard_forward(X, Wqkv, Wo, w.s, w.b, a, d, t, r, True, bq, store="bf16")
+    check_close(f64(got["O"]), ref["O"], "bf16", "O", row_unit=True, elem_ref=rst["O"])
+    check_close(f64(got["Z"]), ref["Z"], "bf16", "Z", row_unit=True, elem_ref=rst["Z"])
+    lse = got["lse"].cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(lse - ref["lse"])) < 2e-2
+    assert np.max(np.abs(lse - rst["lse"])) < 2e-3
+
 @pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_attention_short_sequence_masked_key_half(L, d, causal):
