@@ -462,7 +462,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams p) {
 //     D += sum_k P dP, so dQ = (A - D B) scale comes out of one walk over the keys; D is written to the record.
 // ================================================================================================================
 
-// Per (batch, head, 64-query block) record: [lse(64) | D(64) | 0(128)].
+// Per (batch, head, 64-query block) record: [-lse log2 e (64) | D (64) | 0 (128)].
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdParams p) {
   const int nqb = (p.s + 63) / 64;
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdParams p) {
   float* rec = p.rec + (int64_t)rec_id * 256;
   if (t < 64) {
     const int q = qb * 64 + t;
-    rec[t] = q < p.s ? p.lse[(int64_t)bh * p.s + q] : 0.f;
+    rec[t] = q < p.s ? -p.lse[(int64_t)bh * p.s + q] * 1.4426950408889634f : 0.f;
   } else if (t < 128) {
     // fp32 path: D from the stored O (fp32, so as good as the row sum of P * dP); the bf16 path gets D from its
     // walk over the keys in the dQ kernel (attn_bwd_dq_bf16_kernel) and starts from zero here
@@ -512,7 +512,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   constexpr int D = NS - 1;  // query blocks in flight ahead of the one being used
   __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_B];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4;
+  const int l16 = lane & 15;
   const int nqb = (p.s + 63) / 64;
   // one workgroup per (64-key block, batch, local KV group, head split): split sp walks query heads
   // sp*HS .. sp*HS + HS - 1 of the group (HS = G / splits) and, with more than one split, writes fp32 partial dK / dV
@@ -565,22 +566,51 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
     ccol[i] = (c * 8 < d) ? c * 8 : 0;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
-  auto issue_tile = [&](int i, int st) {
-    const int ii = min(i, ntot - 1);  // past the last step: a harmless re-copy of it
-    const int hs = ii / nblk, qb = qb0 + (ii - hs * nblk);
+  // this lane's byte offsets of copy c within a full 64-query tile of Q and of dO, from the tile's first row
+  uint32_t qoff[CPW], doff[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    qoff[c] = (uint32_t)(((int64_t)crow[c] * tok_stride + ccol[c]) * 2);
+    doff[c] = (uint32_t)(((int64_t)crow[c] * ldo + ccol[c]) * 2);
+  }
+  const bool off32 = (int64_t)64 * (tok_stride > ldo ? tok_stride : ldo) * 2 < (int64_t)1 << 32;
+  // Q columns of the split's first query head (the group's heads follow d apart: qkv_cols)
+  const uint16_t* __restrict__ qh0 = qkv0 + kc.q + (int64_t)sp * HS * d;
+  // steps are copied in order, head by head: the next one's head within the split and query block, and its index
+  int cp_hs = 0, cp_qb = qb0, cp_i = 0;
+  auto issue_tile = [&](int st) {
+    const int hs = cp_hs, qb = cp_qb;
+    if (cp_i + 1 < ntot) {  // past the last step: a harmless re-copy of it
+      ++cp_i;
+      if (++cp_qb == nqb) {
+        cp_qb = qb0;
+        ++cp_hs;
+      }
+    }
     const int jh = jg * p.G + sp * HS + hs;  // the step's query head
-    const uint16_t* qsrc = qkv0 + qkv_cols(p.hl, p.G, d, jh).q;
+    const uint16_t* qsrc = qh0 + (int64_t)hs * d;
     const uint16_t* dsrc = dob0 + (int64_t)jh * d;
     const float* rsrc = p.rec + ((int64_t)(bidx * p.hl + jh) * nqb + qb) * 256;
     const uint32_t sb = lds0 + st * STAGE_B;
+    if (qb * 64 + 64 <= p.s && off32) {  // every row of the tile exists
+      const uint16_t* qt = qsrc + (int64_t)qb * 64 * tok_stride;
+      const uint16_t* dt = dsrc + (int64_t)qb * 64 * ldo;
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int row = min(qb * 64 + crow[c], p.s - 1);
-      const uint32_t dst = sb + (wave + 4 * c) * 1024;
-      dma16(qsrc + (int64_t)row * tok_stride + ccol[c], __builtin_amdgcn_readfirstlane(dst));
-      dma16(dsrc + (int64_t)row * ldo + ccol[c], __builtin_amdgcn_readfirstlane(dst + TILE_B));
+      for (int c = 0; c < CPW; ++c) {
+        const uint32_t dst = sb + (wave + 4 * c) * 1024;
+        dma16s(qt, qoff[c], dst);
+        dma16s(dt, doff[c], dst + TILE_B);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const int row = min(qb * 64 + crow[c], p.s - 1);
+        const uint32_t dst = sb + (wave + 4 * c) * 1024;
+        dma16(qsrc + (int64_t)row * tok_stride + ccol[c], __builtin_amdgcn_readfirstlane(dst));
+        dma16(dsrc + (int64_t)row * ldo + ccol[c], __builtin_amdgcn_readfirstlane(dst + TILE_B));
+      }
     }
-    if (wave == 0) dma16(rsrc + 4 * lane, __builtin_amdgcn_readfirstlane(sb + 2 * TILE_B));
+    if (wave == 0) dma16s(rsrc, (uint32_t)lane * 16u, sb + 2 * TILE_B);
   };
   auto chunk_off = [&](int r, int c) { return r * CH * 16 + tile_chunk<CH>(r, c) * 16; };
   int roff[4][NDS];  // A fragments of Q / dO rows (queries 16 qs + l16), d = 32u + 8g
@@ -612,20 +642,22 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
   for (int st = 0; st < NST; ++st) dv[st] = dk[st] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int i = 0; i < D; ++i) issue_tile(i, i);
+  for (int i = 0; i < D; ++i) issue_tile(i);
   // step 0 has landed (wave 0 also copies the record: one more copy per step)
   if (wave == 0) wait_vmcnt<(D - 1) * (2 * CPW + 1)>(); else wait_vmcnt<(D - 1) * 2 * CPW>();
   __syncthreads();
 
   // one query block; the ring stage is a template constant, as in the forward
+  int cur_qb = qb0;  // the query block of the step being multiplied
   auto step = [&](int i, auto stage) {
     constexpr int st_cur = decltype(stage)::value;
     constexpr int st_new = (st_cur + D) % NS;
-    issue_tile(i + D, st_new);
+    issue_tile(st_new);  // step i + D
     const char* Qt = &lds[st_cur * STAGE_B];
     const char* Dt = Qt + TILE_B;
     const float* R = reinterpret_cast<const float*>(Qt + 2 * TILE_B);
-    const int qbi = qb0 + i % nblk;
+    const int qbi = cur_qb;
+    if (++cur_qb == nqb) cur_qb = qb0;
     const int q0 = qbi * 64;
 
     // S and dP in two halves of 32 queries, each half's Q and dO fragments read before its MFMAs (as in dQ)
@@ -671,12 +703,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkv_bf16_kernel(AttnBwdParams
     uint32_t pp[4][2], pl[4][2], dd2[4][2], dl2[4][2];
 #pragma unroll
     for (int qs = 0; qs < 4; ++qs) {
-      const f32x4_t lse4 = *reinterpret_cast<const f32x4_t*>(R + 16 * qs + 4 * g);
+      const f32x4_t nl4 = *reinterpret_cast<const f32x4_t*>(R + 16 * qs + 4 * g);  // -lse log2 e
       const f32x4_t D4 = *reinterpret_cast<const f32x4_t*>(R + 64 + 16 * qs + 4 * g);
       float pe[4], ds[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[qs][e], c2, -lse4[e] * 1.4426950408889634f));
+        pe[e] = __builtin_amdgcn_exp2f(fmaf(sc[qs][e], c2, nl4[e]));
         ds[e] = pe[e] * (dp[qs][e] - D4[e]);
       }
       split_hi_lo(pe, pp[qs], pl[qs]);
@@ -758,7 +790,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
   constexpr int D = NS - 1;  // blocks in flight ahead of the one being multiplied
   __shared__ __attribute__((aligned(16))) char lds[NS * STAGE_B];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 4;
+  const int l16 = lane & 15;
   const int nq = (p.s + QT - 1) / QT;
   const int nbh = p.b * p.hl;
   const int qtile = nq - 1 - work_rank((int)blockIdx.x / nbh, nq, p.fold);
@@ -806,16 +839,32 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
     ccol[i] = (c * 8 < d) ? c * 8 : 0;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)&lds[0];
-  auto issue_tile = [&](int kt, int st) {
-    const int kv0 = min(kt, nkt - 1) * KT;
-    const uint32_t sb = lds0 + st * STAGE_B;
+  // this lane's byte offset of copy i within a full key tile (the keys; the values at 2 d bytes further)
+  uint32_t coff[CPW];
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int row = min(kv0 + crow[i], p.s - 1);
-      const uint16_t* src = kbase + (int64_t)row * tok_stride + ccol[i];
-      const uint32_t dst = sb + (wave + 4 * i) * 1024;
-      dma16(src, __builtin_amdgcn_readfirstlane(dst));
-      dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
+  for (int i = 0; i < CPW; ++i) coff[i] = (uint32_t)(((int64_t)crow[i] * tok_stride + ccol[i]) * 2);
+  const bool off32 = (int64_t)KT * tok_stride * 2 < (int64_t)1 << 32;
+  auto issue_tile = [&](int kt, int st) {
+    const int ktc = min(kt, nkt - 1);
+    const int kv0 = ktc * KT;
+    const uint32_t sb = lds0 + st * STAGE_B;
+    if (kv0 + KT <= p.s && off32) {  // every row of the tile exists
+      const uint16_t* tb = kbase + (int64_t)kv0 * tok_stride;
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const uint32_t dst = sb + (wave + 4 * i) * 1024;
+        dma16s(tb, coff[i], dst);
+        dma16s(tb + d, coff[i], dst + TILE_B);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int row = min(kv0 + crow[i], p.s - 1);
+        const uint16_t* src = kbase + (int64_t)row * tok_stride + ccol[i];
+        const uint32_t dst = sb + (wave + 4 * i) * 1024;
+        dma16(src, __builtin_amdgcn_readfirstlane(dst));
+        dma16(src + d, __builtin_amdgcn_readfirstlane(dst + TILE_B));
+      }
     }
   };
   auto chunk_off = [&](int r, int c) { return r * CH * 16 + tile_chunk<CH>(r, c) * 16; };
