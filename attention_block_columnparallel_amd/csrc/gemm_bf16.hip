@@ -399,26 +399,28 @@ __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)
 constexpr int kPairOp = 32768;  // bytes of one operand's pair buffer
 constexpr int kLdsB = 65536;    // the B buffers start 64 KB in
 
-template <bool KMAJ, bool SWIG, int CPP>
+template <bool KMAJ, bool SWIG, int CPP, int TW = 256>
 struct DmaP;
 
-template <bool SWIG, int CPP>
-struct DmaP<true, SWIG, CPP> {  // K-major: copy i holds rows 8 i .. 8 i + 7, 128 bytes each
+// (TW: the operand's rows per tile -- 256, or 192 for the narrower column tiles; an MN-major copy still moves 256
+// columns, the ones past the tile clamped inside the matrix and never read)
+template <bool SWIG, int CPP, int TW>
+struct DmaP<true, SWIG, CPP, TW> {  // K-major: copy i holds rows 8 i .. 8 i + 7, 128 bytes each
   uint32_t voff[CPP];
   __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
 #pragma unroll
     for (int q = 0; q < CPP; ++q) {
       const int r = 8 * (CPP * wave + q) + (lane >> 3);
       const int c = (lane & 7) ^ (r & 7);  // the logical chunk this slot holds
-      const int row = min(tile * 256 + r, rows - 1);
+      const int row = min(tile * TW + r, rows - 1);
       voff[q] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
     }
   }
   static __device__ __forceinline__ int64_t pstride(int64_t ld) { return 4 * BK2; }  // bytes per pair along a row
 };
 
-template <bool SWIG, int CPP>
-struct DmaP<false, SWIG, CPP> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 bytes each)
+template <bool SWIG, int CPP, int TW>
+struct DmaP<false, SWIG, CPP, TW> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (512 bytes each)
   uint32_t voff[CPP];
   __device__ __forceinline__ void init(int64_t ld, int tile, int rows, int fhalf, int wave, int lane) {
 #pragma unroll
@@ -431,7 +433,7 @@ struct DmaP<false, SWIG, CPP> {  // MN-major: copy i holds k rows 2 i, 2 i + 1 (
         const int half = cw / 64, jj = min(tile * 128 + wn * 64 + (cw % 64), fhalf - 8);
         col = half * fhalf + jj;
       } else {
-        col = min(tile * 256 + cl, rows - 8);
+        col = min(tile * TW + cl, rows - 8);
       }
       voff[q] = (uint32_t)((col + (int64_t)k * ld) * 2);
     }
@@ -565,7 +567,7 @@ __device__ __forceinline__ void chunk_rows(const GemmParams& p, const float* ep,
 
 // ax: this wave's 16 x 128 tile of the epilogue's auxiliary input (U for act', [gate | up] at +2048 for SwiGLU),
 // staged in LDS.
-template <int EPI>
+template <int EPI, int WN = 128>
 __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float* ep, int ep_pitch, int m0, int tile_n,
                                                int wn, int lane, const uint16_t* ax) {
   if constexpr (epi_swiglu_fwd(EPI)) {
@@ -598,7 +600,8 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
       stg_bf16(p.C2, m * p.ldc2 + j, g * act_sigmoid(g) * u);
     }
   } else {
-    const int col = tile_n * 256 + wn * 128 + 2 * lane;
+    if (2 * lane >= WN) return;  // a 96-column wave: lanes 48 .. 63 have no columns
+    const int col = tile_n * 2 * WN + wn * WN + 2 * lane;
     if (col >= p.N) return;  // N % 8 == 0: a column pair is entirely in or out
     float b0 = 0.f, b1 = 0.f;
     if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_ACT) {
@@ -653,10 +656,13 @@ __host__ __device__ constexpr int big_row_group(bool pair, int epi, bool ak, boo
 // 16 i + (l & 15), columns 16 j + 4 (l >> 4) .. + 3 of the wave's sub-tile, which the epilogue stages through LDS
 // with one 16-byte write per block.  (A persistent launch, one workgroup per CU walking its tiles so that a tile's
 // stores drain under the next tile's first copies, measured no faster than one workgroup per tile.)
-template <bool AK, bool BKM, int EPI, bool SPLIT = false, int NW = 8>
+template <bool AK, bool BKM, int EPI, bool SPLIT = false, int NW = 8, int BNT = 256>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) {
   static_assert(NW == 8, "the pair-buffer loop is written for 8 waves of 64 x 128");
-  constexpr int BM = 256, BN = 256, WM = 512 / NW, WN = 128, TM = WM / 16, TN = 8;
+  // BNT: 256 columns per tile (waves of 64 x 128), or 192 (waves of 64 x 96) where 256-column tiles would leave
+  // most of a round of CUs idle; not for the SwiGLU forward's interleaved halves or the pair's split tail blocks
+  static_assert(BNT == 256 || (BNT == 192 && !epi_swiglu_fwd(EPI) && !(SPLIT && !AK)), "192-column tiles");
+  constexpr int BM = 256, BN = BNT, WM = 512 / NW, WN = BN / 2, TM = WM / 16, TN = WN / 16;
   constexpr int RING_B = 2 * 2 * kPairOp;  // two pair buffers of A and B
   constexpr bool SWIG = epi_swiglu_fwd(EPI);
   constexpr int EP = 132;  // epilogue fp32 row pitch: 16-byte writes of 16 consecutive rows hit distinct banks
@@ -705,9 +711,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   // Pair buffers: k-tiles 2m and 2m+1 (64 k) of each operand sit in buffer m % 2, so a K-major row's 64 k (128
   // bytes, a whole cache line) comes in one piece; copying one k-tile (64 bytes of each line) reads every line
   // twice at half the rate of whole lines from L2.  Layout: A buffers at 0 and 32 KB, B buffers at 64 and 96 KB.
-  constexpr int CPP = 32 / NW;  // copies per wave per operand and pair
+  constexpr int CPP = 32 / NW;  // copies per wave per operand and pair (A; and B at 256 columns)
+  constexpr int CPPB = BKM ? BN / 64 : CPP;  // B's: a K-major copy is 8 rows; an MN-major one 2 k rows of 256
+  constexpr int NCPY = CPP + CPPB;
   DmaP<AK, false, CPP> da;
-  DmaP<BKM, SWIG, CPP> db;
+  DmaP<BKM, SWIG, CPPB, BN> db;
   da.init(p.lda, tile_m, p.M, p.fhalf, wave, lane);
   db.init(p.ldb, tile_n, p.N, p.fhalf, wave, lane);
   int kp0 = 0, kp1 = p.K / (2 * BK2);  // pairs of k-tiles: all of K, or split `split` of pp.ksplit runs
@@ -716,7 +724,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
     kp0 = split * base + min(split, rem);
     kp1 = kp0 + base + (split < rem ? 1 : 0);
   }
-  const int64_t astr = DmaP<AK, false, CPP>::pstride(p.lda), bstr = DmaP<BKM, SWIG, CPP>::pstride(p.ldb);
+  const int64_t astr = DmaP<AK, false, CPP>::pstride(p.lda), bstr = DmaP<BKM, SWIG, CPPB, BN>::pstride(p.ldb);
   const char* const Ab = static_cast<const char*>(p.A) + kp0 * astr;  // uniform: pair 0 of the range
   const char* const Bb = static_cast<const char*>(p.B) + kp0 * bstr;
   const int npair = kp1 - kp0, nk = 2 * npair;
@@ -732,7 +740,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
     if (q < CPP)
       dma16s(Ab + pr * astr, da.voff[q], lds0 + BUF * kPairOp + (CPP * wave + q) * 1024);
     else
-      dma16s(Bb + pr * bstr, db.voff[q - CPP], lds0 + kLdsB + BUF * kPairOp + (CPP * wave + q - CPP) * 1024);
+      dma16s(Bb + pr * bstr, db.voff[q - CPP], lds0 + kLdsB + BUF * kPairOp + (CPPB * wave + q - CPP) * 1024);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -740,11 +748,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   using I3 = std::integral_constant<int, 3>;
   // prologue: pairs 0 and 1 into buffers 0 and 1; pair 0 landed (pair 1's copies may be in flight)
 #pragma unroll
-  for (int q = 0; q < 2 * CPP; ++q) copy(I0{}, q, 0);
+  for (int q = 0; q < NCPY; ++q) copy(I0{}, q, 0);
   if (npair > 1) {
 #pragma unroll
-    for (int q = 0; q < 2 * CPP; ++q) copy(I1{}, q, 1);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPP) : "memory");
+    for (int q = 0; q < NCPY; ++q) copy(I1{}, q, 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCPY) : "memory");
   } else {
     wait_vmcnt0();
   }
@@ -776,13 +784,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     }
-    constexpr int NCP = ODD ? 2 * 2 * CPP : 0;  // copies this step: the pair's A and B shares
     auto segment = [&](auto segc) {
       constexpr int G = decltype(segc)::value;
-      if constexpr (NCP > 0) {
+      if constexpr (ODD) {  // this step copies the pair's A and B shares, spread over the segments
 #pragma unroll
-        for (int q = 0; q < NCP / 2; ++q)
-          if (q * TM / (NCP / 2) == G) copy(IC{}, q, pc);
+        for (int q = 0; q < NCPY; ++q)
+          if (q * TM / NCPY == G) copy(IC{}, q, pc);
       }
 #pragma unroll
       for (int f = 0; f < TM + TN; ++f) {
@@ -793,6 +800,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
       }
       mfma_rows_t<G, G + 1, TN>(acc, FCA, FCB);
       constexpr int nds = seg_ds_count<AK, BKM, TM, TN>(G);
+      static_assert(nds <= TN, "a segment's fragment reads pair with its MFMAs");
       if constexpr (nds > 0) {
 #pragma unroll
         for (int r = 0; r < nds; ++r) {
@@ -877,7 +885,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
       float* const blk = pp.part + ((int64_t)(tile_id - pp.nfull) * pp.ksplit + split) * (BM * BN);
       partial_chunk(p, ep, EP, row0 + tm * 16, tile_m * BM, tile_n, wn, lane, blk);
     } else {
-      epilogue_chunk<EPI>(p, ep, EP, row0 + tm * 16, tile_n, wn, lane, ax);
+      epilogue_chunk<EPI, WN>(p, ep, EP, row0 + tm * 16, tile_n, wn, lane, ax);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -951,31 +959,54 @@ hipError_t launch_one(const GemmParams& p, hipStream_t st) {
                    dim3(NWM * NWN * 64), 0, st, p);
 }
 
-int big_tiles(const GemmParams& p, bool swig) {
+int big_tiles(const GemmParams& p, bool swig, int bn = 256) {
   const int nbm = (p.M + 255) / 256;
-  const int nbn = swig ? (p.fhalf + 127) / 128 : (p.N + 255) / 256;
+  const int nbn = swig ? (p.fhalf + 127) / 128 : (p.N + bn - 1) / bn;
   return nbm * nbn;
 }
 
-template <bool AK, bool BKM, int EPI>
+// Throughput per flop of the 192-column tiles relative to the 256-column ones (more copy bytes and fragment reads
+// per MFMA): 0.82, measured where both widths take one round (the 22B attention block's QKV GEMM, 144 tiles of
+// 256 or 192 of 192 columns: 120.5 -> 109 us).
+constexpr double kEff192 = 0.82;
+
+// Relative time of a large-tile launch of `tiles` workgroups of bn columns, ksplit K runs each: rounds of one tile
+// per CU, each as long as a tile's share of the work.
+double big_time(int tiles, int bn, int ksplit) {
+  const int ncu = num_cus();
+  const long wg = (long)tiles * ksplit;
+  const long rounds = (wg + ncu - 1) / ncu;
+  return (double)rounds * (bn / 256.0) / ksplit / (bn == 256 ? 1.0 : kEff192);
+}
+
+// 192-column tiles where they finish sooner: a GEMM whose 256-column tiles leave much of their last round of CUs
+// idle (the attention block's per-rank GEMMs, the 8.3B-width MLP).  K-major A only, and not for the SwiGLU
+// epilogues (their column halves are laid out for 256).
+bool use_n192(const GemmParams& p, bool ak, int epi) {
+  if (!ak || epi == EPI_SWIGLU_FWD || epi == EPI_SWIGLU_BWD || epi == EPI_LN_SWIGLU) return false;
+  return big_time(big_tiles(p, false, 192), 192, 1) < big_time(big_tiles(p, false), 256, 1);
+}
+
+template <bool AK, bool BKM, int EPI, int BNT = 256>
 hipError_t launch_big(const GemmParams& p0, const GemmParams* p1, hipStream_t st) {
   GemmPair pp;
   pp.g[0] = p0;
   pp.g[1] = p1 ? *p1 : p0;
-  pp.tiles0 = big_tiles(p0, epi_swiglu_fwd(EPI));
-  pp.tiles1 = p1 ? big_tiles(*p1, epi_swiglu_fwd(EPI)) : 0;
+  pp.tiles0 = big_tiles(p0, epi_swiglu_fwd(EPI), BNT);
+  pp.tiles1 = p1 ? big_tiles(*p1, epi_swiglu_fwd(EPI), BNT) : 0;
   pp.ksplit = 1;
   pp.nfull = 0;
   pp.part = nullptr;
   const int total = pp.tiles0 + pp.tiles1;
 
-  static const std::string name = std::string("gemm_bf16_big_") + (AK ? "K" : "M") + (BKM ? "K" : "M") + "_" +
-                                  kEpiNames[EPI];
-  static const std::string name2 = std::string("gemm_bf16_big_pair_") + (AK ? "K" : "M") + (BKM ? "K" : "M") + "_" +
-                                   kEpiNames[EPI];
+  const std::string w = BNT == 256 ? "" : std::to_string(BNT);
+  static const std::string name = std::string("gemm_bf16_big") + w + "_" + (AK ? "K" : "M") + (BKM ? "K" : "M") +
+                                  "_" + kEpiNames[EPI];
+  static const std::string name2 = std::string("gemm_bf16_big") + w + "_pair_" + (AK ? "K" : "M") +
+                                   (BKM ? "K" : "M") + "_" + kEpiNames[EPI];
   // 8 waves (two per SIMD, the pair-buffer loop) for every layout
   constexpr int NW = 8;
-  return TP_LAUNCH(p1 ? name2.c_str() : name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI, false, NW>),
+  return TP_LAUNCH(p1 ? name2.c_str() : name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI, false, NW, BNT>),
                    dim3((unsigned)total), dim3(NW * 64), 0, st, pp);
 }
 
@@ -1030,18 +1061,19 @@ int choose_ksplit(const GemmParams& p, int tiles, int64_t part_floats) {
   return best;
 }
 
-template <bool AK, bool BKM, int EPI>
+template <bool AK, bool BKM, int EPI, int BNT = 256>
 hipError_t launch_big_split(const GemmParams& p, int ksplit, float* part, hipStream_t st) {
   GemmPair pp;
   pp.g[0] = p;
   pp.g[1] = p;
-  pp.tiles0 = big_tiles(p, false);
+  pp.tiles0 = big_tiles(p, false, BNT);
   pp.tiles1 = 0;
   pp.ksplit = ksplit;
   pp.nfull = 0;
   pp.part = part;
-  static const std::string name = std::string("gemm_bf16_big_splitk_") + (AK ? "K" : "M") + (BKM ? "K" : "M");
-  hipError_t e = TP_LAUNCH(name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI_STORE, true, 8>),
+  const std::string w = BNT == 256 ? "" : std::to_string(BNT);
+  static const std::string name = std::string("gemm_bf16_big") + w + "_splitk_" + (AK ? "K" : "M") + (BKM ? "K" : "M");
+  hipError_t e = TP_LAUNCH(name.c_str(), (gemm_bf16_big_kernel<AK, BKM, EPI_STORE, true, 8, BNT>),
                            dim3((unsigned)(pp.tiles0 * ksplit)), dim3(512), 0, st, pp);
   if (e != hipSuccess) return e;
   const int64_t nq = (int64_t)p.M * (p.N / 4);
@@ -1100,7 +1132,12 @@ template <bool AK, bool BKM, int EPI>
 hipError_t launch_cfg(int ci, const GemmParams& p, hipStream_t st) {
   switch (ci) {
     case 0:
-      if (big_fits(p, AK, BKM)) return launch_big<AK, BKM, EPI>(p, nullptr, st);
+      if (big_fits(p, AK, BKM)) {
+        if constexpr (AK && !epi_swiglu_fwd(EPI) && EPI != EPI_SWIGLU_BWD) {
+          if (use_n192(p, AK, EPI)) return launch_big<AK, BKM, EPI, 192>(p, nullptr, st);
+        }
+        return launch_big<AK, BKM, EPI>(p, nullptr, st);
+      }
       return launch_one<256, 256, 2, 4, AK, BKM, EPI>(p, st);
     case 1: return launch_one<256, 128, 2, 2, AK, BKM, EPI>(p, st);
     case 2: return launch_one<128, 128, 2, 2, AK, BKM, EPI>(p, st);
@@ -1256,8 +1293,18 @@ hipError_t gemm_bf16_splitk(const GemmParams& p, bool a_kmajor, bool b_kmajor, i
                             int64_t part_floats, hipStream_t st) {
   if (part != nullptr && p.M > 0 && p.N > 0 && (epi == EPI_STORE || epi == EPI_BIAS) && a_kmajor &&
       big_fits(p, a_kmajor, b_kmajor)) {
+    // the tile width and the split together: each width's best split, then the sooner of the two
     const int ks = choose_ksplit(p, big_tiles(p, false), part_floats);
-    if (ks > 1) {
+    const int ks192 = choose_ksplit(p, big_tiles(p, false, 192), part_floats);
+    const bool n192 = big_time(big_tiles(p, false, 192), 192, ks192) < big_time(big_tiles(p, false), 256, ks);
+    if (n192 && ks192 > 1) {
+      if (b_kmajor)
+        return epi == EPI_STORE ? launch_big_split<true, true, EPI_STORE, 192>(p, ks192, part, st)
+                                : launch_big_split<true, true, EPI_BIAS, 192>(p, ks192, part, st);
+      return epi == EPI_STORE ? launch_big_split<true, false, EPI_STORE, 192>(p, ks192, part, st)
+                              : launch_big_split<true, false, EPI_BIAS, 192>(p, ks192, part, st);
+    }
+    if (!n192 && ks > 1) {
       if (b_kmajor)
         return epi == EPI_STORE ? launch_big_split<true, true, EPI_STORE>(p, ks, part, st)
                                 : launch_big_split<true, true, EPI_BIAS>(p, ks, part, st);

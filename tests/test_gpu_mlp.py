@@ -195,8 +195,22 @@ def test_bf16_large_tile_kernels_ragged_sampled(L, act):
     with L.LaunchTimer(256, only="gemm_bf16") as lt:
         _sampled_check(L, w, 1, with_bias=True, seed=11)
     fwd_epi, bwd_epi = ("swiglu_fwd", "swiglu_bwd") if act == "swiglu" else ("bias_act", "act_bwd")
-    want = {f"gemm_bf16_big_KM_{fwd_epi}", "gemm_bf16_big_KM_store", f"gemm_bf16_big_KK_{bwd_epi}",
-            "gemm_bf16_big_KK_store", "gemm_bf16_big_pair_MM_store"}
+    # each GEMM on the large-tile kernel, at 256 or (where fewer rounds of CUs pay) 192 columns per tile
+    for role in (f"KM_{fwd_epi}", "KM_store", f"KK_{bwd_epi}", "KK_store", "pair_MM_store"):
+        assert {f"gemm_bf16_big_{role}", f"gemm_bf16_big192_{role}"} & set(lt.names), (role, lt.names)
+
+
+@pytest.mark.parametrize("act", ["gelu", "relu"])
+def test_bf16_192_column_tiles_ragged_sampled(L, act):
+    # h = 1216 and f_l = 704 (multiples of 64, not of 192) at M = 16320: 192-column tiles take one or two rounds of
+    # CUs fewer than 256-column ones, so the column, row, dY and dX GEMMs take them, each with a ragged last column
+    # tile (and a ragged last row tile)
+    w = TI.Workload("n192_ragged", "mlp", s=2040, b=8, h=1216, ffn=2 * 704, t=2, act=act, dtype="bf16")
+    say(f"bf16 MLP 192-column tiles ragged M=16320 h=1216 f_l=704 act={act} (sampled)")
+    with L.LaunchTimer(256, only="gemm_bf16") as lt:
+        _sampled_check(L, w, 1, with_bias=True, seed=12)
+    want = {"gemm_bf16_big192_KM_bias_act", "gemm_bf16_big192_KM_store", "gemm_bf16_big192_KK_act_bwd",
+            "gemm_bf16_big192_KK_store"}
     assert want <= set(lt.names), (want - set(lt.names), lt.names)
 
 
