@@ -462,9 +462,10 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnParams p) {
 //     D += sum_k P dP, so dQ = (A - D B) scale comes out of one walk over the keys; D is written to the record.
 // ================================================================================================================
 
-// Per (batch, head, 64-query block) record: [-lse log2 e (64) | D (64) | 0 (128)].
-template <typename T>
-__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdParams p) {
+// Per (batch, head, 64-query block) record: [-lse log2 e (64) | D (64) | padding (128)], read by the dK / dV pass.
+// The fp32 backward's is written here, with D from the stored fp32 O (as good as the row sum of P dP); the bf16
+// backward's by its dQ kernel, which gets D from its own walk over the keys (attn_bwd_dq_bf16_kernel).
+__global__ __launch_bounds__(256) void attn_bwd_prep_f32_kernel(AttnBwdParams p) {
   const int nqb = (p.s + 63) / 64;
   const int rec_id = blockIdx.x;  // bh * nqb + qb
   const int bh = rec_id / nqb, qb = rec_id % nqb;
@@ -475,25 +476,13 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(AttnBwdParams p) {
     const int q = qb * 64 + t;
     rec[t] = q < p.s ? -p.lse[(int64_t)bh * p.s + q] * 1.4426950408889634f : 0.f;
   } else if (t < 128) {
-    // fp32 path: D from the stored O (fp32, so as good as the row sum of P * dP); the bf16 path gets D from its
-    // walk over the keys in the dQ kernel (attn_bwd_dq_bf16_kernel) and starts from zero here
     const int q = qb * 64 + (t - 64);
     float acc = 0.f;
-    if (sizeof(T) == 4 && q < p.s) {
+    if (q < p.s) {
       const int64_t off = ((int64_t)q * p.b + bidx) * ((int64_t)p.hl * p.d) + (int64_t)jj * p.d;
-      const T* dO = static_cast<const T*>(p.dout) + off;
-      const T* O = static_cast<const T*>(p.o) + off;
-      for (int e = 0; e < p.d; ++e) {
-        float a, b;
-        if constexpr (sizeof(T) == 2) {
-          a = bf16_to_f32(dO[e]);
-          b = bf16_to_f32(O[e]);
-        } else {
-          a = dO[e];
-          b = O[e];
-        }
-        acc = fmaf(a, b, acc);
-      }
+      const float* dO = static_cast<const float*>(p.dout) + off;
+      const float* O = static_cast<const float*>(p.o) + off;
+      for (int e = 0; e < p.d; ++e) acc = fmaf(dO[e], O[e], acc);
     }
     rec[t] = acc;
   } else {
@@ -983,7 +972,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_bf16_kernel(AttnBwdParams 
   wait_vmcnt<0>();
 
   dsum = sum_over_groups(dsum);  // D for this lane's query
-  if (q < p.s && g == 0) *drec = dsum;
+  if (g == 0) {  // this query's record entries: -lse log2 e and D (zeros past the sequence, which dK / dV masks)
+    drec[-64] = -lse2;
+    *drec = q < p.s ? dsum : 0.f;
+  }
 #pragma unroll
   for (int st = 0; st < NST; ++st)
 #pragma unroll
@@ -1190,16 +1182,13 @@ hipError_t attention_bwd(tp_dtype dt, const AttnBwdParams& p, hipStream_t st) {
   if (p.s <= 0 || p.b <= 0 || p.hl <= 0) return hipSuccess;
   const int nqb = (p.s + 63) / 64;
   hipError_t e;
-  if (dt == TP_BF16) {
-    e = TP_LAUNCH("attn_bwd_prep_bf16", attn_bwd_prep_kernel<uint16_t>, dim3((unsigned)(nqb * p.b * p.hl)), dim3(256), 0,
-                  st, p);
-    if (e != hipSuccess) return e;
+  if (dt == TP_BF16) {  // the dQ kernel writes the records
     if (p.d <= 32) return launch_bwd_bf16<32>(p, st);
     if (p.d <= 64) return launch_bwd_bf16<64>(p, st);
     if (p.d <= 96) return launch_bwd_bf16<96>(p, st);
     return launch_bwd_bf16<128>(p, st);
   }
-  e = TP_LAUNCH("attn_bwd_prep_f32", attn_bwd_prep_kernel<float>, dim3((unsigned)(nqb * p.b * p.hl)), dim3(256), 0, st,
+  e = TP_LAUNCH("attn_bwd_prep_f32", attn_bwd_prep_f32_kernel, dim3((unsigned)(nqb * p.b * p.hl)), dim3(256), 0, st,
                 p);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((p.s + 63) / 64), (unsigned)(p.b * p.hl));
