@@ -151,7 +151,8 @@ int tp_attn_fwd(const tp_dims* dims, int rank, tp_dtype dtype, int causal, const
  * row-parallel projection's weight gradient and the column-parallel QKV's weight gradient stay local, the data
  * gradient dX is a partial that f sums over ranks; [SPLIT] backward of the column and row splits):
  *   dO_ws   = dZ Wo_i^T                          [s, b, (a/t)*d]    caller workspace (activation dtype)
- *   rec_ws  = per (b, local head, 64-query block) [lse(64) | D(64) | 0(128)], D[q] = sum_e dO[q,e] O[q,e]
+ *   rec_ws  = per (b, local head, 64-query block) [-lse*log2(e) (64) | D (64) | padding (128)], D[q] =
+ *             sum_e dO[q,e] O[q,e] (0 past the sequence)
  *                                                fp32 [b, a/t, ceil(s/64), 256], caller workspace; with g < a it
  *             also holds the per-query-head partial dK | dV of each KV head (fp32 [a/g][s*b][g/t][2d]), summed in a
  *             fixed order: size tp_attn_bwd_workspace(dims) bytes
