@@ -137,3 +137,26 @@ def test_attention_full_size_one_rank_sampled(L):
     lse = got["lse"].cpu().numpy()[0][:, rows].T.astype(np.float64)  # [rows, hl]
     assert np.max(np.abs(lse - ref["lse"])) < 2e-2
     assert np.max(np.abs(lse - ref_st["lse"])) < 2e-3
+
+
+def test_attention_split_k_qkv_192_column_tiles_sampled(L):
+    # t = 16 at h = 4096, d = 128: the rank's QKV GEMM is 4096 x 768 x 4096, whose 256-column tiles (48) leave most
+    # CUs idle, and Z_i lends room for two K runs; 64 tiles of 192 columns split in two finish sooner, so the QKV GEMM
+    # takes the split 192-column kernel with the bias applied by the partial sum
+    w = TI.Workload("attn_t16", "attn", s=4096, b=1, h=4096, a=32, d=128, t=16, causal=True, dtype="bf16")
+    r = 11
+    say("attention h=4096 a=32 d=128 s=4096 t=16 rank 11 (split-K 192-column QKV; sampled query rows)")
+    inp = TI.attn_inputs(w, with_bias=True, seed=5)
+    with L.LaunchTimer(16, only="gemm_bf16") as lt:
+        got = run_rank(L, w, inp, r, "bf16", True, True)
+    assert "gemm_bf16_big192_splitk_KM" in lt.names, lt.names
+    X = O.as_f64(inp["X"], "bf16").reshape(w.M, w.h)
+    Wqkv, bq = O.as_f64(inp["Wqkv"], "bf16"), O.as_f64(inp["bqkv"], "bf16")
+    cols = O.qkv_shard_columns(w.a, w.d, w.t, r)
+    QKV = X @ Wqkv[:, cols] + bq[cols]
+    check_close(f64(got["QKV"]), QKV, "bf16", "QKV")
+    rng = np.random.default_rng(13)
+    rows = np.sort(rng.choice(w.M, size=64, replace=False))
+    rows[0], rows[-1] = 0, w.M - 1
+    ref_st = O.attention_rows(O.stored(QKV, "bf16"), w.s, w.b, w.a // w.t, w.d, rows, True)
+    check_close(f64(got["O"])[rows], ref_st["O"], "bf16", "O vs stored QKV", row_unit=True)

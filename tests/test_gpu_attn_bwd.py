@@ -104,6 +104,25 @@ def test_attention_backward_small_ragged(L, dtype, d, causal):
                 _rel_frob(f64(nat[k]), ref[k], f"{k} (own forward)")
 
 
+
+@pytest.mark.parametrize("d", [64, 96])
+def test_attention_backward_causal_long_ragged(L, d):
+    # s = 1100: 18 query and key blocks, the last ragged (12 rows); the dK / dV pass walks up to 18 query blocks per
+    # key block and reads the records the dQ pass wrote, zeros for the 52 positions past the sequence
+    a, t, s = 4, 2, 1100
+    w = TI.Workload("attn_long", "attn", s=s, b=2, h=a * d, a=a, d=d, t=t, causal=True, dtype="bf16")
+    say(f"attention backward s={s} b=2 a=4 d={d} t=2 causal bf16")
+    inp = TI.attn_inputs(w, with_bias=True, seed=300 + d)
+    X = O.as_f64(inp["X"], "bf16").reshape(w.M, w.h)
+    dZ = O.as_f64(inp["dZ"], "bf16").reshape(w.M, w.h)
+    Wqkv, Wo, bq = O.as_f64(inp["Wqkv"], "bf16"), O.as_f64(inp["Wo"], "bf16"), O.as_f64(inp["bqkv"], "bf16")
+    r = 0
+    ref = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, a, d, t, r, True, bq)
+    rst = O.attention_shard_backward(X, Wqkv, Wo, dZ, w.s, w.b, a, d, t, r, True, bq, store="bf16")
+    got = run_rank(L, w, inp, r, "bf16", True, True, saved=oracle_saved(rst, "bf16"))
+    for k in ("dO", "dQKV", "dWqkv", "dbqkv", "dWo", "dX"):
+        check_close(f64(got[k]), ref[k], "bf16", k, elem_ref=rst[k])
+
 def test_attention_backward_full_size_one_rank_sampled(L):
     w = TI.ATTN_22B
     r = 5
