@@ -696,7 +696,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmPair pp) 
   if (which) bid -= pp.tiles0;
   const int nbm = (p.M + BM - 1) / BM;
   const int nbn = SWIG ? (p.fhalf + BN / 2 - 1) / (BN / 2) : (p.N + BN - 1) / BN;
-  const int gm = big_row_group(pp.tiles1 > 0, EPI, AK, BKM);
+  // (the split K-major x K-major kernel on 192-column tiles, the attention backward's dO GEMM, walks groups of 2:
+  // 54 -> 49 us per rank at the 22B shape against 4)
+  const int gm = (SPLIT && BNT == 192 && AK && BKM) ? 2 : big_row_group(pp.tiles1 > 0, EPI, AK, BKM);
   const int group = bid / (gm * nbn);
   const int first_m = group * gm;
   const int gsz = min(nbm - first_m, gm);
