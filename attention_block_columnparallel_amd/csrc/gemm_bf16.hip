@@ -524,45 +524,92 @@ __device__ __forceinline__ float2 lds_bf16x2(const uint16_t* ax, int i) {
   return make_float2(bf16_to_f32(w & 0xFFFFu), bf16_to_f32(w >> 16));
 }
 
-// The plain epilogues' rows of one chunk: lane l owns columns col, col + 1.  The activation is a template argument,
-// picked once per chunk: with the choice made per element, each of the kernel's 8 unrolled chunks carried the code
-// of every activation, and since a tile runs its epilogue once, that code ran mostly from instruction-cache misses
-// (the GeLU epilogues took 25-30 us longer per launch at h=4096, ffn/t=2048).  The row loop stays rolled for the
-// same reason.
+// Eight fp32 values -> bf16, one 16-byte store (the column is a multiple of 8 and rows are 16-byte aligned).
+__device__ __forceinline__ void stg_bf16x8(void* p, int64_t i, const float (&v)[8]) {
+  uint4 w;
+  w.x = pack_bf16x2(v[0], v[1]);
+  w.y = pack_bf16x2(v[2], v[3]);
+  w.z = pack_bf16x2(v[4], v[5]);
+  w.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) = w;
+}
+// Eight bf16 values of the staged auxiliary input (16-byte LDS read).
+__device__ __forceinline__ void lds_bf16x8(const uint16_t* ax, int i, float (&v)[8]) {
+  const uint4 w = *reinterpret_cast<const uint4*>(ax + i);
+  const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = bf16_to_f32(q[k] & 0xFFFFu);
+    v[2 * k + 1] = bf16_to_f32(q[k] >> 16);
+  }
+}
+
+// The plain epilogues' rows of one chunk: lane l owns the 8 columns col .. col + 7 (cl .. cl + 7 of the wave's) of
+// rows rr, rr + 4, rr + 8, rr + 12 (rr = l / 16), so a chunk row leaves as 16-byte stores of 16 lanes.  The
+// activation is a template argument, picked once per chunk: with the choice made per element, each of the kernel's
+// 8 unrolled chunks carried the code of every activation, and since a tile runs its epilogue once, that code ran
+// mostly from instruction-cache misses (the GeLU epilogues took 25-30 us longer per launch at h=4096, ffn/t=2048).
+// The row loop stays rolled for the same reason.
 template <int EPI, int ACT>
-__device__ __forceinline__ void chunk_rows(const GemmParams& p, const float* ep, int ep_pitch, int m0, int col, int lane,
-                                           const uint16_t* ax, float b0, float b1, int rows, float c0 = 0.f,
-                                           float c1 = 0.f) {
-  auto row = [&](int r) {
-    const float v0 = ep[r * ep_pitch + 2 * lane], v1 = ep[r * ep_pitch + 2 * lane + 1];
+__device__ __forceinline__ void chunk_rows(const GemmParams& p, const float* ep, int ep_pitch, int m0, int col, int cl,
+                                           int rr, const uint16_t* ax, const float (&b)[8], const float (&c)[8],
+                                           int rows) {
+#pragma unroll 1
+  for (int r = rr; r < rows; r += 4) {
+    float v[8];
+    {
+      const float4 x0 = *reinterpret_cast<const float4*>(ep + r * ep_pitch + cl);
+      const float4 x1 = *reinterpret_cast<const float4*>(ep + r * ep_pitch + cl + 4);
+      v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+      v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+    }
     const int64_t m = m0 + r;
     if constexpr (EPI == EPI_LN_ACT) {
       // LayerNorm(u) W + bias = rstd (u W' - mean c) + b, with W' = diag(gamma) W and c its column sums
       const float mu = p.ln_mean[m], rs = p.ln_rstd[m];
-      const float u0 = fmaf(rs, fmaf(-mu, c0, v0), b0), u1 = fmaf(rs, fmaf(-mu, c1, v1), b1);
-      stg_bf16x2(p.C, m * p.ldc + col, u0, u1);
-      stg_bf16x2(p.C2, m * p.ldc2 + col, act_apply(ACT, u0), act_apply(ACT, u1));
+      float u[8], y[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        u[k] = fmaf(rs, fmaf(-mu, c[k], v[k]), b[k]);
+        y[k] = act_apply(ACT, u[k]);
+      }
+      stg_bf16x8(p.C, m * p.ldc + col, u);
+      stg_bf16x8(p.C2, m * p.ldc2 + col, y);
     } else if constexpr (EPI == EPI_STORE) {
-      stg_bf16x2(p.C, m * p.ldc + col, v0, v1);
+      stg_bf16x8(p.C, m * p.ldc + col, v);
     } else if constexpr (EPI == EPI_BIAS) {
-      stg_bf16x2(p.C, m * p.ldc + col, v0 + b0, v1 + b1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] += b[k];
+      stg_bf16x8(p.C, m * p.ldc + col, v);
     } else if constexpr (EPI == EPI_BIAS_ACT) {
-      const float u0 = v0 + b0, u1 = v1 + b1;
-      stg_bf16x2(p.C, m * p.ldc + col, u0, u1);
-      stg_bf16x2(p.C2, m * p.ldc2 + col, act_apply(ACT, u0), act_apply(ACT, u1));
+      float y[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        v[k] += b[k];
+        y[k] = act_apply(ACT, v[k]);
+      }
+      stg_bf16x8(p.C, m * p.ldc + col, v);
+      stg_bf16x8(p.C2, m * p.ldc2 + col, y);
     } else if constexpr (EPI == EPI_ACT_BWD) {
-      const float2 u = lds_bf16x2(ax, r * 128 + 2 * lane);
-      stg_bf16x2(p.C, m * p.ldc + col, v0 * act_grad(ACT, u.x), v1 * act_grad(ACT, u.y));
+      float u[8];
+      lds_bf16x8(ax, r * 128 + cl, u);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] *= act_grad(ACT, u[k]);
+      stg_bf16x8(p.C, m * p.ldc + col, v);
     } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-      const float2 g = lds_bf16x2(ax, r * 128 + 2 * lane);
-      const float2 u = lds_bf16x2(ax, 2048 + r * 128 + 2 * lane);
-      const float s0 = act_sigmoid(g.x), s1 = act_sigmoid(g.y);
-      stg_bf16x2(p.C, m * p.ldc + col, v0 * u.x * s0 * (1.f + g.x * (1.f - s0)),
-                 v1 * u.y * s1 * (1.f + g.y * (1.f - s1)));
-      stg_bf16x2(p.C, m * p.ldc + p.fhalf + col, v0 * g.x * s0, v1 * g.y * s1);
+      float g[8], u[8], dg[8], du[8];
+      lds_bf16x8(ax, r * 128 + cl, g);
+      lds_bf16x8(ax, 2048 + r * 128 + cl, u);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float s = act_sigmoid(g[k]);
+        dg[k] = v[k] * u[k] * s * (1.f + g[k] * (1.f - s));
+        du[k] = v[k] * g[k] * s;
+      }
+      stg_bf16x8(p.C, m * p.ldc + col, dg);
+      stg_bf16x8(p.C, m * p.ldc + p.fhalf + col, du);
     }
-  };
-  for (int r = 0; r < rows; ++r) row(r);
+  }
 }
 
 // ax: this wave's 16 x 128 tile of the epilogue's auxiliary input (U for act', [gate | up] at +2048 for SwiGLU),
@@ -600,40 +647,40 @@ __device__ __forceinline__ void epilogue_chunk(const GemmParams& p, const float*
       stg_bf16(p.C2, m * p.ldc2 + j, g * act_sigmoid(g) * u);
     }
   } else {
-    if (2 * lane >= WN) return;  // a 96-column wave: lanes 48 .. 63 have no columns
-    const int col = tile_n * 2 * WN + wn * WN + 2 * lane;
-    if (col >= p.N) return;  // N % 8 == 0: a column pair is entirely in or out
-    float b0 = 0.f, b1 = 0.f;
+    const int cl = 8 * (lane & 15), rr = lane >> 4;
+    if (cl >= WN) return;  // a 96-column wave: lanes with cl >= 96 have no columns
+    const int col = tile_n * 2 * WN + wn * WN + cl;
+    if (col >= p.N) return;  // N % 8 == 0: a group of 8 columns is entirely in or out
+    float b[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, c[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if constexpr (EPI == EPI_BIAS || EPI == EPI_BIAS_ACT) {
       if (p.bias) {
-        const float2 bb = ldg_bf16x2(p.bias, col);
-        b0 = bb.x;
-        b1 = bb.y;
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.bias) + col);
+        const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          b[2 * k] = bf16_to_f32(q[k] & 0xFFFFu);
+          b[2 * k + 1] = bf16_to_f32(q[k] >> 16);
+        }
+      }
+    }
+    if constexpr (EPI == EPI_LN_ACT) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        b[k] = p.ln_b[col + k];
+        c[k] = p.ln_c[col + k];
       }
     }
     const int rows = min(16, p.M - m0);
-    if constexpr (EPI == EPI_LN_ACT) {
-      const float2 bb = make_float2(p.ln_b[col], p.ln_b[col + 1]);
-      const float2 cc = make_float2(p.ln_c[col], p.ln_c[col + 1]);
+    if constexpr (EPI == EPI_BIAS_ACT || EPI == EPI_ACT_BWD || EPI == EPI_LN_ACT) {  // the activation chosen once per chunk
       switch (p.act) {
-        case TP_ACT_GELU:
-          chunk_rows<EPI, TP_ACT_GELU>(p, ep, ep_pitch, m0, col, lane, ax, bb.x, bb.y, rows, cc.x, cc.y);
-          break;
+        case TP_ACT_GELU: chunk_rows<EPI, TP_ACT_GELU>(p, ep, ep_pitch, m0, col, cl, rr, ax, b, c, rows); break;
         case TP_ACT_GELU_TANH:
-          chunk_rows<EPI, TP_ACT_GELU_TANH>(p, ep, ep_pitch, m0, col, lane, ax, bb.x, bb.y, rows, cc.x, cc.y);
+          chunk_rows<EPI, TP_ACT_GELU_TANH>(p, ep, ep_pitch, m0, col, cl, rr, ax, b, c, rows);
           break;
-        default: chunk_rows<EPI, TP_ACT_RELU>(p, ep, ep_pitch, m0, col, lane, ax, bb.x, bb.y, rows, cc.x, cc.y);
-      }
-    } else if constexpr (EPI == EPI_BIAS_ACT || EPI == EPI_ACT_BWD) {  // the activation chosen once per chunk
-      switch (p.act) {
-        case TP_ACT_GELU: chunk_rows<EPI, TP_ACT_GELU>(p, ep, ep_pitch, m0, col, lane, ax, b0, b1, rows); break;
-        case TP_ACT_GELU_TANH:
-          chunk_rows<EPI, TP_ACT_GELU_TANH>(p, ep, ep_pitch, m0, col, lane, ax, b0, b1, rows);
-          break;
-        default: chunk_rows<EPI, TP_ACT_RELU>(p, ep, ep_pitch, m0, col, lane, ax, b0, b1, rows); break;
+        default: chunk_rows<EPI, TP_ACT_RELU>(p, ep, ep_pitch, m0, col, cl, rr, ax, b, c, rows); break;
       }
     } else {
-      chunk_rows<EPI, TP_ACT_RELU>(p, ep, ep_pitch, m0, col, lane, ax, b0, b1, rows);
+      chunk_rows<EPI, TP_ACT_RELU>(p, ep, ep_pitch, m0, col, cl, rr, ax, b, c, rows);
     }
   }
 }
